@@ -1,0 +1,63 @@
+"""Build libsgemm.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m fp32_sgemm_tuning_amd.build [--isa]
+
+Flags: -O3 for gfx950 only, packed-FP32 instructions disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass warns
+that it does not know the feature, which is harmless), and the kernel
+resource report (VGPR/AGPR/spill/LDS/occupancy) written to
+``_build/resource_usage.txt``.  ``--isa`` also keeps the gfx950 assembly in
+``_build/``.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsgemm.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+SOURCES = [os.path.join(CSRC, "sgemm.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, "sgemm_kernels.hpp"), os.path.join(INCLUDE, "sgemm.h")]
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def needs_build() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(p) > t for p in DEPS)
+
+
+def build(verbose: bool = False, isa: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", *SOURCES, "-o", tmp]
+    if isa:
+        cmd += ["-save-temps"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD_DIR)
+    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+        f.write(r.stderr)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError(f"hipcc failed ({r.returncode})")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, isa="--isa" in sys.argv))

@@ -1,0 +1,207 @@
+// C ABI of the gfx950 SGEMM library: argument checks, kernel-variant choice
+// and launch on the caller's stream.  The operation and its contract are
+// documented in include/sgemm.h.
+//
+// The host picks between separately compiled kernel instantiations instead
+// of branching inside the kernel: beta == 0 selects an epilogue that never
+// reads C ("The Final Kernel: Retuning Against the Pipeline", Skipping The
+// Read Of C), and shapes that are whole multiples of the block tile select
+// the instantiation without edge guards.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "sgemm.h"
+#include "sgemm_kernels.hpp"
+
+#define SGEMM_LIB_VERSION 1
+
+using namespace sgemm_mi355x;
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int record_hip_error(hipError_t e, const char *what) {
+    snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s (%d)", what,
+             hipGetErrorString(e), (int)e);
+    return SGEMM_STATUS_HIP_ERROR;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Process-wide tuning knobs read once from the environment (tile raster
+// group height and the XCD remap), for sweeps; defaults otherwise.
+struct Knobs {
+    int group_m = 8;
+    int xcd_remap = 1;
+    Knobs() {
+        if (const char *s = getenv("SGEMM_GROUP_M")) {
+            int v = atoi(s);
+            if (v >= 1 && v <= 1024) group_m = v;
+        }
+        if (const char *s = getenv("SGEMM_XCD_REMAP")) xcd_remap = atoi(s) != 0;
+    }
+};
+
+const Knobs &knobs() {
+    static const Knobs k;
+    return k;
+}
+
+struct VariantDesc {
+    const char *name;
+    int bm, bn, bk;
+    bool needs_vec;
+};
+
+const VariantDesc kVariants[] = {
+    {"simple_64x64x16", 64, 64, 16, false},
+    {"db_128x128x32_vec", 128, 128, 32, true},
+    {"db_128x128x32_scalar", 128, 128, 32, false},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+// Argument checks shared by every entry point.  No HIP call happens here.
+int check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+               const float *C, int ldc) {
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    const int kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldb < nmin || ldc < nmin) return SGEMM_STATUS_INVALID_DIM;
+    if (M == 0 || N == 0) return SGEMM_STATUS_OK;
+    if (C == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_STATUS_NULL_POINTER;
+    return SGEMM_STATUS_OK;
+}
+
+bool vec_ok(int K, const float *A, int lda, const float *B, int ldb, float beta, const float *C,
+            int ldc) {
+    (void)beta;
+    const bool ab = K == 0 || (aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0);
+    return ab && aligned16(C) && ldc % 4 == 0;
+}
+
+int auto_variant(int K, const float *A, int lda, const float *B, int ldb, float beta,
+                 const float *C, int ldc) {
+    return vec_ok(K, A, lda, B, ldb, beta, C, ldc) ? SGEMM_VARIANT_DB128_VEC
+                                                   : SGEMM_VARIANT_DB128_SCALAR;
+}
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
+int launch_db(const Args &a, hipStream_t stream) {
+    const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
+    const bool beta0 = a.beta == 0.0f;
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
+#define SGEMM_LAUNCH(G, Z) \
+    hipLaunchKernelGGL((sgemm_db_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
+    if (guard) {
+        if (beta0) SGEMM_LAUNCH(true, true);
+        else SGEMM_LAUNCH(true, false);
+    } else {
+        if (beta0) SGEMM_LAUNCH(false, true);
+        else SGEMM_LAUNCH(false, false);
+    }
+#undef SGEMM_LAUNCH
+    return SGEMM_STATUS_OK;
+}
+
+int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+        float beta, float *C, int ldc, void *stream, int variant) {
+    int st = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_STATUS_OK) return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    if (M == 0 || N == 0) return SGEMM_STATUS_OK;
+    if (variant == SGEMM_VARIANT_AUTO) variant = auto_variant(K, A, lda, B, ldb, beta, C, ldc);
+    const VariantDesc &d = kVariants[variant];
+    if (d.needs_vec && !vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_STATUS_UNSUPPORTED;
+
+    const long tiles_m = ceil_div(M, d.bm), tiles_n = ceil_div(N, d.bn);
+    if (tiles_m * tiles_n > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
+
+    Args a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = (int)tiles_m;
+    a.tiles_n = (int)tiles_n;
+    a.group_m = knobs().group_m;
+    a.xcd_remap = knobs().xcd_remap;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    switch (variant) {
+        case SGEMM_VARIANT_SIMPLE:
+            hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, a);
+            break;
+        case SGEMM_VARIANT_DB128_VEC:
+            launch_db<128, 128, 32, 2, 2, true>(a, s);
+            break;
+        case SGEMM_VARIANT_DB128_SCALAR:
+            launch_db<128, 128, 32, 2, 2, false>(a, s);
+            break;
+        default:
+            return SGEMM_STATUS_INVALID_VARIANT;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip_error(e, "kernel launch");
+    return SGEMM_STATUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+          float beta, float *C, int ldc, void *stream) {
+    return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
+}
+
+int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream, int variant) {
+    return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+int sgemm_select_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                         float beta, const float *C, int ldc) {
+    const int st = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_STATUS_OK) return st;
+    return auto_variant(K, A, lda, B, ldb, beta, C, ldc);
+}
+
+int sgemm_num_variants(void) { return kNumVariants; }
+
+const char *sgemm_variant_name(int variant) {
+    if (variant < 0 || variant >= kNumVariants) return nullptr;
+    return kVariants[variant].name;
+}
+
+const char *sgemm_strerror(int status) {
+    switch (status) {
+        case SGEMM_STATUS_OK: return "ok";
+        case SGEMM_STATUS_INVALID_DIM: return "invalid dimension or leading dimension";
+        case SGEMM_STATUS_NULL_POINTER: return "NULL pointer with a non-empty extent";
+        case SGEMM_STATUS_HIP_ERROR: return "HIP runtime error";
+        case SGEMM_STATUS_INVALID_VARIANT: return "unknown kernel variant";
+        case SGEMM_STATUS_UNSUPPORTED: return "variant needs 16-byte aligned pointers and leading dimensions";
+        default: return "unknown status";
+    }
+}
+
+const char *sgemm_last_hip_error(void) { return g_last_hip_error; }
+
+int sgemm_version(void) { return SGEMM_LIB_VERSION; }
+
+}  // extern "C"

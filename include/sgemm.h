@@ -1,0 +1,109 @@
+/*
+ * sgemm.h - C ABI of the MI355X (gfx950) single-precision GEMM library
+ * (libsgemm.so).
+ *
+ * Operation.  C = alpha * A * B + beta * C for row-major FP32 matrices
+ * A [M,K], B [K,N] and C [M,N]; each output is a length-K dot product and the
+ * whole product counts 2*M*N*K FLOPs ("Matmul I: tiling and shared memory",
+ * section 1).  The epilogue has the form alpha*acc + beta*C ("2D Register
+ * Tiling: The Outer Product", The Kernel) and, when beta == 0, C is never
+ * read ("The Final Kernel: Retuning Against the Pipeline", Skipping The Read
+ * Of C), so NaN or Inf already in C cannot reach the result.  Elements outside
+ * the matrices contribute nothing and only in-range outputs are written
+ * ("Matmul I", section 6).
+ *
+ * Layout.  Element (i,k) of A is A[i*lda + k], (k,j) of B is B[k*ldb + j],
+ * (i,j) of C is C[i*ldc + j]; lda >= max(1,K), ldb >= max(1,N),
+ * ldc >= max(1,N).  Columns j in [N, ldc) of C are never written.
+ * Arithmetic is FP32 (v_mfma_f32_16x16x4_f32 matrix instructions, FP32
+ * accumulate); no reduced-precision inputs are used.
+ *
+ * Pointers.  A, B and C are device pointers of the current HIP device.
+ * C must not overlap A or B (not checked).  Any alignment is accepted: when
+ * A, B and C are 16-byte aligned and lda, ldb, ldc are multiples of 4 the
+ * library uses 128-bit loads and stores, otherwise 32-bit ones.
+ *
+ * Ownership and execution.  The caller owns every buffer.  The library
+ * allocates nothing and keeps no per-call state.  A call validates its
+ * arguments, enqueues one kernel on `stream` (a hipStream_t; NULL is the
+ * null stream) and returns without synchronising.  Calls are thread-safe
+ * and deterministic: the same inputs give the same bits (no atomics, no
+ * split-K reduction).
+ *
+ * Errors.  Arguments are checked before anything is enqueued, so a call that
+ * returns an error has written nothing.  M == 0 or N == 0 returns
+ * SGEMM_STATUS_OK without launching.  K == 0 writes alpha*0 + beta*C
+ * (alpha*0 when beta == 0).
+ */
+#ifndef SGEMM_MI355X_H
+#define SGEMM_MI355X_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_STATUS_OK 0
+#define SGEMM_STATUS_INVALID_DIM (-1)       /* M, N, K < 0, or a leading dimension too small, or too many tiles */
+#define SGEMM_STATUS_NULL_POINTER (-2)      /* NULL A, B or C with a non-empty extent */
+#define SGEMM_STATUS_HIP_ERROR (-3)         /* the HIP runtime reported an error; see sgemm_last_hip_error() */
+#define SGEMM_STATUS_INVALID_VARIANT (-4)   /* sgemm_ex: no such variant */
+#define SGEMM_STATUS_UNSUPPORTED (-5)       /* sgemm_ex: variant needs 16-byte alignment the arguments lack */
+
+/* Variant ids for sgemm_ex(). */
+#define SGEMM_VARIANT_AUTO (-1)             /* what sgemm() picks */
+#define SGEMM_VARIANT_SIMPLE 0              /* 64x64 tile, single LDS buffer, 32-bit loads: the plain cross-check kernel */
+#define SGEMM_VARIANT_DB128_VEC 1           /* 128x128x32 tile, double-buffered LDS, 128-bit loads/stores (needs alignment) */
+#define SGEMM_VARIANT_DB128_SCALAR 2        /* the same tile with 32-bit loads/stores (any alignment) */
+
+/*
+ * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
+ * the alignment class, beta == 0 and the shape.  Returns SGEMM_STATUS_*.
+ */
+int sgemm(int M, int N, int K, float alpha,
+          const float *A, int lda,
+          const float *B, int ldb,
+          float beta, float *C, int ldc,
+          void *stream);
+
+/*
+ * sgemm_ex: as sgemm() with the kernel variant forced (SGEMM_VARIANT_*; AUTO
+ * behaves like sgemm()).  Intended for tests and tile sweeps.  Returns
+ * SGEMM_STATUS_INVALID_VARIANT for an unknown id and SGEMM_STATUS_UNSUPPORTED
+ * when a 128-bit variant is forced on arguments that lack its alignment.
+ */
+int sgemm_ex(int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream, int variant);
+
+/*
+ * sgemm_select_variant: the variant id sgemm() would run for these arguments
+ * (no launch, no HIP call; pointers are only inspected for alignment).
+ * Returns a negative status for invalid arguments.
+ */
+int sgemm_select_variant(int M, int N, int K,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         float beta, const float *C, int ldc);
+
+/* Number of variant ids (valid ids are 0 .. n-1). */
+int sgemm_num_variants(void);
+
+/* Static name of a variant, or NULL for an unknown id. */
+const char *sgemm_variant_name(int variant);
+
+/* Static text for a status code. */
+const char *sgemm_strerror(int status);
+
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char *sgemm_last_hip_error(void);
+
+/* Library version (monotonic integer). */
+int sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_MI355X_H */

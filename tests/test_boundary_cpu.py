@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/sgemm.h declares, and rejects bad arguments before any HIP call.
+
+Nothing here launches a kernel: every call below returns from the argument
+checks, which run before the library touches the HIP runtime.
+"""
+import os
+import re
+
+import pytest
+
+from fp32_sgemm_tuning_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+# Fake device addresses: only inspected for alignment, never dereferenced.
+AL = 0x10000          # 16-byte aligned
+MIS = 0x10004         # 4-byte aligned only
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return capi.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(capi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"libsgemm.so does not export {name}"
+
+
+def test_version_and_variants(lib):
+    assert capi.sgemm_version() >= 1
+    n = capi.sgemm_num_variants()
+    assert n >= 3
+    names = [capi.sgemm_variant_name(v) for v in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert capi.sgemm_variant_name(n) is None
+    assert capi.sgemm_variant_name(-1) is None
+    assert capi.sgemm_last_hip_error() == ""
+
+
+@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5])
+def test_strerror_known(status):
+    s = capi.sgemm_strerror(status)
+    assert s and s != "unknown status"
+
+
+def test_strerror_unknown():
+    assert capi.sgemm_strerror(42) == "unknown status"
+
+
+GOOD = dict(M=8, N=8, K=8, alpha=1.0, A=AL, lda=8, B=AL, ldb=8, beta=0.0, C=AL, ldc=8, stream=None)
+
+
+def _call(**kw):
+    a = {**GOOD, **kw}
+    return capi.sgemm(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"], a["ldb"],
+                      a["beta"], a["C"], a["ldc"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(lda=7), dict(ldb=7), dict(ldc=7),
+    dict(K=0, lda=0), dict(N=0, ldb=0), dict(N=0, ldc=0),
+])
+def test_invalid_dimensions(kw):
+    assert _call(**kw) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+@pytest.mark.parametrize("kw", [dict(A=None), dict(B=None), dict(C=None)])
+def test_null_pointers(kw):
+    assert _call(**kw) == capi.SGEMM_STATUS_NULL_POINTER
+
+
+def test_empty_extents_are_noops():
+    # M == 0 or N == 0: OK without launching, even with NULL pointers.
+    assert _call(M=0, A=None, C=None) == capi.SGEMM_STATUS_OK
+    assert _call(N=0, B=None, C=None) == capi.SGEMM_STATUS_OK
+    # K == 0 needs only C (A and B are never read)
+    assert capi.sgemm_select_variant(4, 4, 0, None, 1, None, 4, 1.0, AL, 4) >= 0
+
+
+def test_forced_variant_checks():
+    a = GOOD
+    args = (a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"], a["ldb"], a["beta"], a["C"],
+            a["ldc"], None)
+    assert capi.sgemm_ex(*args, capi.sgemm_num_variants()) == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert capi.sgemm_ex(*args, -2) == capi.SGEMM_STATUS_INVALID_VARIANT
+    # a 128-bit variant forced on misaligned data is refused before launch
+    mis = list(args)
+    mis[4] = MIS
+    assert capi.sgemm_ex(*mis, capi.SGEMM_VARIANT_DB128_VEC) == capi.SGEMM_STATUS_UNSUPPORTED
+    odd = list(args)
+    odd[5] = 9
+    assert capi.sgemm_ex(*odd, capi.SGEMM_VARIANT_DB128_VEC) == capi.SGEMM_STATUS_UNSUPPORTED
+
+
+def test_variant_selection_by_alignment():
+    sel = capi.sgemm_select_variant
+    assert sel(64, 64, 64, AL, 64, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_VEC
+    assert sel(64, 64, 64, MIS, 64, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
+    assert sel(64, 64, 64, AL, 64, MIS, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
+    assert sel(64, 64, 64, AL, 64, AL, 64, 0.0, MIS, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
+    assert sel(64, 64, 64, AL, 66, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
+    # the ragged workload's leading dimensions (2047, 4999) are not multiples of 4
+    assert sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999) == capi.SGEMM_VARIANT_DB128_SCALAR
+    assert sel(-1, 4, 4, AL, 4, AL, 4, 0.0, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM

@@ -1,0 +1,125 @@
+"""GPU cases with a unique exact answer, compared bit for bit against the
+oracle's exact value (identity, permutation, all-ones, small integers whose
+partial sums are exact in FP32 in any order, half-integer epilogue, beta == 0
+with NaN in C, K == 0)."""
+import numpy as np
+import pytest
+
+import oracle
+from fp32_sgemm_tuning_amd import capi, sgemm
+from fp32_sgemm_tuning_amd.inputs import small_int_matrix
+from gpu_util import padded_device, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [capi.SGEMM_VARIANT_SIMPLE, capi.SGEMM_VARIANT_DB128_VEC, capi.SGEMM_VARIANT_DB128_SCALAR]
+
+
+def _up4(n):
+    return max(4, (n + 3) // 4 * 4)
+
+
+def _gemm(A, B, Cin=None, alpha=1.0, beta=0.0, variant=None):
+    """Operands live in buffers whose leading dimensions are rounded up to a
+    multiple of 4 (so every variant applies) with NaN in the padding."""
+    torch = torch_cuda()
+    M, K = A.shape
+    N = B.shape[1]
+    dA, _ = padded_device(A, _up4(K), torch)
+    dB, _ = padded_device(B, _up4(N), torch)
+    if Cin is None:
+        Cin = np.full((M, N), np.nan, np.float32)
+    dC, _ = padded_device(Cin, _up4(N), torch)
+    sgemm(dA, dB, dC, alpha=alpha, beta=beta, variant=variant)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
+def _exact(A, B, Cin=None, alpha=1.0, beta=0.0):
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=alpha, beta=beta)
+    f = ref.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), ref), "case is not exact in FP32"
+    return f
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_identity(variant):
+    rng = np.random.default_rng(1)
+    A = np.eye(300, dtype=np.float32)
+    B = rng.standard_normal((300, 257), dtype=np.float32)
+    np.testing.assert_array_equal(_gemm(A, B, variant=variant), B)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_permutations(variant):
+    rng = np.random.default_rng(2)
+    n = 260
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), dtype=np.float32)
+    P[np.arange(n), perm] = 1.0
+    X = rng.standard_normal((n, n), dtype=np.float32)
+    np.testing.assert_array_equal(_gemm(P, X, variant=variant), X[perm])
+    Y = _gemm(X, P, variant=variant)
+    expect = np.empty_like(X)
+    expect[:, perm] = X
+    np.testing.assert_array_equal(Y, expect)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("shape", [(64, 64, 2047), (129, 300, 2047), (5, 7, 33)])
+def test_all_ones(variant, shape):
+    M, N, K = shape
+    C = _gemm(np.ones((M, K), np.float32), np.ones((K, N), np.float32), variant=variant)
+    np.testing.assert_array_equal(C, np.full((M, N), K, np.float32))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("shape", [(256, 256, 8192), (200, 333, 1000), (1024, 1024, 1024)])
+def test_small_integers(variant, shape):
+    """|A|, |B| <= 32 and K <= 8192: every partial sum is an integer below
+    2^24, so any FP32 summation order is exact."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    A = small_int_matrix(rng, (M, K), -32, 32)
+    B = small_int_matrix(rng, (K, N), -32, 32)
+    np.testing.assert_array_equal(_gemm(A, B, variant=variant), _exact(A, B))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_epilogue_half_integers(variant):
+    """alpha = 1.5, beta = -0.5 on integer data: results are half-integers
+    below 2^23, exact in FP32."""
+    rng = np.random.default_rng(9)
+    M, N, K = 300, 260, 2050
+    A = small_int_matrix(rng, (M, K), -16, 16)
+    B = small_int_matrix(rng, (K, N), -16, 16)
+    Cin = small_int_matrix(rng, (M, N), -1000, 1000)
+    got = _gemm(A, B, Cin, alpha=1.5, beta=-0.5, variant=variant)
+    np.testing.assert_array_equal(got, _exact(A, B, Cin, alpha=1.5, beta=-0.5))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_beta_zero_never_reads_c(variant):
+    rng = np.random.default_rng(10)
+    A = small_int_matrix(rng, (130, 70), -8, 8)
+    B = small_int_matrix(rng, (70, 140), -8, 8)
+    for fill in (np.nan, np.inf):
+        Cin = np.full((130, 140), fill, np.float32)
+        got = _gemm(A, B, Cin, alpha=1.0, beta=0.0, variant=variant)
+        np.testing.assert_array_equal(got, _exact(A, B))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_k_zero(variant):
+    torch = torch_cuda()
+    Cin = np.arange(12 * 20, dtype=np.float32).reshape(12, 20) - 100
+    dA = torch.empty((12, 0), device="cuda")
+    dB = torch.empty((0, 20), device="cuda")
+    dC = to_dev(Cin, torch)
+    sgemm(dA, dB, dC, alpha=3.0, beta=-2.0, variant=variant)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dC.cpu().numpy(), -2.0 * Cin)
+    dC.fill_(float("nan"))
+    sgemm(dA, dB, dC, alpha=3.0, beta=0.0, variant=variant)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dC.cpu().numpy(), np.zeros((12, 20), np.float32))

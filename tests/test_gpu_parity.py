@@ -1,0 +1,138 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle,
+element by element, |C - C_ref| <= 1e-3 + 1e-4 |C_ref|.
+
+Workloads: the five SGEMM configurations (256^3, 1024^3, 4096^3 with
+beta = 0 and with alpha = 0.5, beta = 2, the ragged 3001 x 4999 x 2047 with
+alpha = 1.5, beta = -0.5, and 512^3 / 2048^3 / 8192^3).  Sizes the oracle
+finishes in seconds are compared in full; 4096^3 and 8192^3 are compared on
+a seeded 4096-entry sample plus the four corners, and 4096^3 also on two
+full 128-row slabs (the first and the last tile row).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp32_sgemm_tuning_amd import capi, sgemm
+from fp32_sgemm_tuning_amd.inputs import WORKLOADS, make_problem, sample_indices, workload_inputs
+from gpu_util import check_close, padded_device, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["sq256", "sq512", "sq1024", "sq2048", "ragged"]
+SAMPLED = ["sq4096", "sq4096_beta", "sq8192"]
+
+
+def _run(w, torch):
+    A, B, Cin = workload_inputs(w)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    dC = to_dev(Cin, torch) if Cin is not None else torch.empty((w.M, w.N), device="cuda")
+    sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta)
+    torch.cuda.synchronize()
+    return A, B, Cin, dC.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full(name):
+    torch = torch_cuda()
+    w = WORKLOADS[name]
+    print(f"[parity] {w.describe()}", flush=True)
+    A, B, Cin, C = _run(w, torch)
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=w.alpha, beta=w.beta)
+    check_close(C, ref, name)
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_workload_sampled(name):
+    torch = torch_cuda()
+    w = WORKLOADS[name]
+    print(f"[parity] {w.describe()} (sampled)", flush=True)
+    A, B, Cin, C = _run(w, torch)
+    I, J = sample_indices(w.M, w.N, w.seed)
+    ref = oracle.sgemm_ref_sampled(A, B, I, J, Cin, alpha=w.alpha, beta=w.beta)
+    check_close(C[I, J], ref, name + " sample")
+    if w.M == 4096:
+        for r0 in (0, w.M - 128):
+            sl = slice(r0, r0 + 128)
+            ref = oracle.sgemm_ref(A[sl], B, None if Cin is None else Cin[sl], alpha=w.alpha, beta=w.beta)
+            check_close(C[sl], ref, f"{name} rows {r0}..{r0 + 127}")
+
+
+def _up4(n):
+    return max(4, (n + 3) // 4 * 4)
+
+
+SHAPES = [
+    (1, 1, 1), (1, 129, 3), (7, 5, 3), (16, 64, 16), (64, 64, 64), (127, 129, 31),
+    (128, 128, 32), (129, 127, 33), (256, 384, 96), (300, 200, 500), (131, 517, 1029),
+]
+
+
+@pytest.mark.parametrize("variant", [capi.SGEMM_VARIANT_SIMPLE, capi.SGEMM_VARIANT_DB128_VEC,
+                                     capi.SGEMM_VARIANT_DB128_SCALAR])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+@pytest.mark.parametrize("ab", [(1.0, 0.0), (1.5, -0.5)], ids=["b0", "b1"])
+def test_variant_shapes(variant, shape, ab):
+    torch = torch_cuda()
+    M, N, K = shape
+    alpha, beta = ab
+    A, B, Cin = make_problem(M, N, K, seed=M * 7 + N * 3 + K, dist="normal", with_c=True)
+    # Leading dimensions rounded up to a multiple of 4 (so the 128-bit variant
+    # applies); the padding columns hold NaN, so a read past column K-1 of A
+    # would poison the result.
+    dA, _ = padded_device(A, _up4(K), torch)
+    dB, _ = padded_device(B, _up4(N), torch)
+    dC, _ = padded_device(Cin, _up4(N), torch)
+    if beta == 0.0:
+        dC.fill_(float("nan"))       # must never be read
+    sgemm(dA, dB, dC, alpha=alpha, beta=beta, variant=variant)
+    torch.cuda.synchronize()
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=alpha, beta=beta)
+    check_close(dC.cpu().numpy(), ref, f"variant {variant} {shape} {ab}")
+
+
+@pytest.mark.parametrize("variant", [capi.SGEMM_VARIANT_SIMPLE, capi.SGEMM_VARIANT_DB128_SCALAR])
+def test_unaligned_views(variant):
+    """Odd leading dimensions and base pointers 4 bytes off 16-byte alignment."""
+    torch = torch_cuda()
+    M, N, K = 203, 157, 301
+    A, B, Cin = make_problem(M, N, K, 31, dist="normal", with_c=True)
+    dA, _ = padded_device(A, K + 3, torch, offset=1)
+    dB, _ = padded_device(B, N + 5, torch, offset=3)
+    dC, bufC = padded_device(Cin, N + 1, torch, offset=1)
+    assert capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K + 3, dB.data_ptr(), N + 5, 0.75,
+                                     dC.data_ptr(), N + 1) == capi.SGEMM_VARIANT_DB128_SCALAR
+    sgemm(dA, dB, dC, alpha=1.25, beta=0.75, variant=variant)
+    torch.cuda.synchronize()
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=0.75)
+    check_close(dC.cpu().numpy(), ref, "unaligned")
+    # padding columns of C stay NaN (never written)
+    pad = bufC[1:1 + M * (N + 1)].view(M, N + 1)[:, N]
+    assert torch.isnan(pad).all()
+
+
+def test_auto_matches_forced_variants_bitwise_shape_classes():
+    """Auto dispatch picks the 128-bit variant for packed aligned tensors and
+    gives the same bits as forcing it."""
+    torch = torch_cuda()
+    A, B, _ = make_problem(256, 256, 256, 0)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    auto = sgemm(dA, dB)
+    forced = sgemm(dA, dB, variant=capi.SGEMM_VARIANT_DB128_VEC)
+    torch.cuda.synchronize()
+    assert torch.equal(auto, forced)
+    assert capi.sgemm_select_variant(256, 256, 256, dA.data_ptr(), 256, dB.data_ptr(), 256, 0.0,
+                                     auto.data_ptr(), 256) == capi.SGEMM_VARIANT_DB128_VEC
+
+
+def test_aligned_vs_scalar_variant_agree():
+    """128-bit and 32-bit load paths of the same tile compute the same sums."""
+    torch = torch_cuda()
+    A, B, Cin = make_problem(384, 256, 320, 5, with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    c1 = to_dev(Cin, torch)
+    c2 = c1.clone()
+    sgemm(dA, dB, c1, alpha=0.5, beta=2.0, variant=capi.SGEMM_VARIANT_DB128_VEC)
+    sgemm(dA, dB, c2, alpha=0.5, beta=2.0, variant=capi.SGEMM_VARIANT_DB128_SCALAR)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    np.testing.assert_array_equal(c1.cpu().numpy(), c2.cpu().numpy())
