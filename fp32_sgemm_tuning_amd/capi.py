@@ -23,7 +23,8 @@ SGEMM_VARIANT_DB128_SCALAR = 2
 
 # Every symbol include/sgemm.h declares.
 EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
-           "sgemm_variant_name", "sgemm_strerror", "sgemm_last_hip_error", "sgemm_version")
+           "sgemm_variant_name", "sgemm_variant_info", "sgemm_strerror", "sgemm_last_hip_error",
+           "sgemm_version")
 
 _lib = None
 
@@ -37,6 +38,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # libsgemm.so needs libamdhip64.so.7.  PyTorch-ROCm ships its own copy of
+    # that runtime under the same soname; whichever copy is loaded first is
+    # the one the whole process uses.  Import torch first so this library
+    # binds to torch's runtime and the process holds exactly one HIP runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise LibraryMissing(
             f"{path} is not built; run `python -m fp32_sgemm_tuning_amd.build` "
@@ -54,6 +63,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_num_variants.restype = i
     lib.sgemm_variant_name.argtypes = [i]
     lib.sgemm_variant_name.restype = cp
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.sgemm_variant_info.argtypes = [i, ip, ip, ip, ip]
+    lib.sgemm_variant_info.restype = i
     lib.sgemm_strerror.argtypes = [i]
     lib.sgemm_strerror.restype = cp
     lib.sgemm_last_hip_error.argtypes = []
@@ -84,6 +96,18 @@ def sgemm_num_variants():
 def sgemm_variant_name(variant):
     s = load().sgemm_variant_name(variant)
     return None if s is None else s.decode()
+
+
+def sgemm_variant_info(variant):
+    """(status, bm, bn, bk, needs_vec) of a variant."""
+    v = [ctypes.c_int(0) for _ in range(4)]
+    st = load().sgemm_variant_info(variant, *[ctypes.byref(x) for x in v])
+    return (st,) + tuple(x.value for x in v)
+
+
+def all_variants():
+    """Every variant id the library offers."""
+    return list(range(sgemm_num_variants()))
 
 
 def sgemm_strerror(status):

@@ -52,19 +52,6 @@ const Knobs &knobs() {
     return k;
 }
 
-struct VariantDesc {
-    const char *name;
-    int bm, bn, bk;
-    bool needs_vec;
-};
-
-const VariantDesc kVariants[] = {
-    {"simple_64x64x16", 64, 64, 16, false},
-    {"db_128x128x32_vec", 128, 128, 32, true},
-    {"db_128x128x32_scalar", 128, 128, 32, false},
-};
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
 // Argument checks shared by every entry point.  No HIP call happens here.
 int check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                const float *C, int ldc) {
@@ -93,7 +80,7 @@ int auto_variant(int K, const float *A, int lda, const float *B, int ldb, float 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
-int launch_db(const Args &a, hipStream_t stream) {
+void launch_db(const Args &a, hipStream_t stream) {
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
@@ -107,8 +94,40 @@ int launch_db(const Args &a, hipStream_t stream) {
         else SGEMM_LAUNCH(false, false);
     }
 #undef SGEMM_LAUNCH
-    return SGEMM_STATUS_OK;
 }
+
+void launch_simple(const Args &a, hipStream_t stream) {
+    hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream, a);
+}
+
+typedef void (*Launcher)(const Args &, hipStream_t);
+
+struct VariantDesc {
+    const char *name;
+    int bm, bn, bk;
+    bool needs_vec;
+    Launcher launch;
+};
+
+// Ids 0..2 are the stable ones named in sgemm.h; the rest are tile shapes
+// kept for sweeps (128-bit access only).
+const VariantDesc kVariants[] = {
+    {"simple_64x64x16", 64, 64, 16, false, launch_simple},
+    {"db_128x128x32_w2x2_vec", 128, 128, 32, true, launch_db<128, 128, 32, 2, 2, true>},
+    {"db_128x128x32_w2x2_scalar", 128, 128, 32, false, launch_db<128, 128, 32, 2, 2, false>},
+    {"db_128x128x16_w2x2_vec", 128, 128, 16, true, launch_db<128, 128, 16, 2, 2, true>},
+    {"db_128x128x64_w2x2_vec", 128, 128, 64, true, launch_db<128, 128, 64, 2, 2, true>},
+    {"db_256x128x32_w4x2_vec", 256, 128, 32, true, launch_db<256, 128, 32, 4, 2, true>},
+    {"db_128x256x32_w2x4_vec", 128, 256, 32, true, launch_db<128, 256, 32, 2, 4, true>},
+    {"db_256x128x32_w2x2_vec", 256, 128, 32, true, launch_db<256, 128, 32, 2, 2, true>},
+    {"db_128x256x32_w2x2_vec", 128, 256, 32, true, launch_db<128, 256, 32, 2, 2, true>},
+    {"db_256x256x32_w2x2_vec", 256, 256, 32, true, launch_db<256, 256, 32, 2, 2, true>},
+    {"db_256x256x32_w4x2_vec", 256, 256, 32, true, launch_db<256, 256, 32, 4, 2, true>},
+    {"db_256x256x16_w4x4_vec", 256, 256, 16, true, launch_db<256, 256, 16, 4, 4, true>},
+    {"db_256x128x16_w4x2_vec", 256, 128, 16, true, launch_db<256, 128, 16, 4, 2, true>},
+    {"db_256x256x16_w2x4_vec", 256, 256, 16, true, launch_db<256, 256, 16, 2, 4, true>},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
         float beta, float *C, int ldc, void *stream, int variant) {
@@ -142,19 +161,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    switch (variant) {
-        case SGEMM_VARIANT_SIMPLE:
-            hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, a);
-            break;
-        case SGEMM_VARIANT_DB128_VEC:
-            launch_db<128, 128, 32, 2, 2, true>(a, s);
-            break;
-        case SGEMM_VARIANT_DB128_SCALAR:
-            launch_db<128, 128, 32, 2, 2, false>(a, s);
-            break;
-        default:
-            return SGEMM_STATUS_INVALID_VARIANT;
-    }
+    d.launch(a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
@@ -186,6 +193,16 @@ int sgemm_num_variants(void) { return kNumVariants; }
 const char *sgemm_variant_name(int variant) {
     if (variant < 0 || variant >= kNumVariants) return nullptr;
     return kVariants[variant].name;
+}
+
+int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    const VariantDesc &d = kVariants[variant];
+    if (bm) *bm = d.bm;
+    if (bn) *bn = d.bn;
+    if (bk) *bk = d.bk;
+    if (needs_vec) *needs_vec = d.needs_vec ? 1 : 0;
+    return SGEMM_STATUS_OK;
 }
 
 const char *sgemm_strerror(int status) {

@@ -137,9 +137,9 @@ __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
 // of 64) held in (WM/16) x (WN/16) MFMA accumulators.
 //
 // LDS layout (two stages, no padding, every access 16-byte aligned):
-//   A stage: [BM][BK] k-contiguous.  The 16-byte chunks of row r are stored
-//            in XOR-permuted order (a_swizzle) so that the fragment reads
-//            below touch distinct banks.
+//   A stage: BM x BK floats, k-contiguous 16-byte chunks in the permuted
+//            order of ALayout<BK>, so that the fragment reads below touch
+//            distinct banks.
 //   B stage: [BK][BN] n-contiguous, natural order.
 //
 // Fragment reads use one ds_read_b128 per lane and rely on two freedoms of
@@ -164,23 +164,61 @@ __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
 //         out-of-range outputs are not stored.
 // BETA0 : beta == 0; C is never read.
 // ---------------------------------------------------------------------------
+// Bank behaviour of 128-bit LDS accesses on gfx950, as measured with
+// SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE on single-wave access patterns:
+//   ds_write_b128: 8 consecutive lanes per pass over 32 banks (128 bytes).
+//   ds_read_b128 : 16 lanes per pass, the passes pairing lanes {0-7, 24-31},
+//                  {8-15, 16-23}, {32-39, 56-63} and {40-47, 48-55}; a pass
+//                  whose lanes hit distinct 16-byte bank slots takes one
+//                  cycle, so a conflict-free read costs 4 cycles per wave.
+//                  The slot is address bits 4..7 with some higher address
+//                  bits folded in: 16 rows of 64 bytes always collide
+//                  pairwise, 16 rows of 128 bytes with the swizzle below do
+//                  not.
+// Hence every A stage is stored as rows of 128 bytes (8 chunks of 4 k):
+//   BK = 32: one logical row per LDS row, chunk c at c ^ s(row).
+//   BK = 16: two logical rows per LDS row: rows 32g + r and 32g + 16 + r
+//            (r < 16) share LDS row 16g + r, in chunks 0..3 and 4..7, XOR
+//            s(r).  A fragment read of a 16-row slab then has exactly the
+//            access pattern of the BK = 32 layout.
+//   BK = 64: rows of 256 bytes, chunk c at c ^ (row % 16).
+// with s(r) = (r / 2) % 8.  Fragment reads (lane l on row l % 16 of a slab,
+// chunk l / 16) are then conflict-free, and so are the stage writes, since
+// each 8-lane write pass covers one whole 128-byte LDS row.  The B tile needs
+// no swizzle: 16 lanes read 256 contiguous bytes of one row.
 template <int BK>
-__device__ __forceinline__ int a_swizzle(int row, int chunk);
+struct ALayout;
 
-// 8 chunks per row (128 bytes).  Rows 0..7 of a slab get distinct chunk
-// positions, and so do the even and the odd rows among 0..15, which keeps
-// the 16-byte reads conflict-free whether the LDS serves 128 or 256 bytes
-// per pass.
 template <>
-__device__ __forceinline__ int a_swizzle<32>(int row, int chunk) {
-    return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-}
+struct ALayout<32> {
+    // float offset of (row m, chunk c) inside the A stage
+    static __host__ __device__ __forceinline__ int offset(int m, int c) { return m * 32 + 4 * (c ^ ((m >> 1) & 7)); }
+    // global-load assignment: 8 consecutive loaders share one row
+    static __host__ __device__ __forceinline__ void coords(int e, int &m, int &c) { m = e >> 3; c = e & 7; }
+};
 
-// 4 chunks per row (64 bytes).
 template <>
-__device__ __forceinline__ int a_swizzle<16>(int row, int chunk) {
-    return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
-}
+struct ALayout<16> {
+    static __host__ __device__ __forceinline__ int offset(int m, int c) {
+        const int r = m & 15;
+        const int lds_row = ((m >> 5) << 4) + r;
+        const int chunk = ((((m >> 4) & 1) << 2) | c) ^ ((r >> 1) & 7);
+        return lds_row * 32 + 4 * chunk;
+    }
+    // 8 consecutive loaders fill one LDS row: 4 chunks of row 32g + r and
+    // 4 chunks of row 32g + 16 + r.
+    static __host__ __device__ __forceinline__ void coords(int e, int &m, int &c) {
+        c = e & 3;
+        const int q = e >> 2;
+        m = ((q >> 5) << 5) + ((q & 1) << 4) + ((q & 31) >> 1);
+    }
+};
+
+template <>
+struct ALayout<64> {
+    static __host__ __device__ __forceinline__ int offset(int m, int c) { return m * 64 + 4 * (c ^ (m & 15)); }
+    static __host__ __device__ __forceinline__ void coords(int e, int &m, int &c) { m = e >> 4; c = e & 15; }
+};
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD, bool BETA0>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
@@ -195,11 +233,11 @@ sgemm_db_kernel(Args p) {
     constexpr int B_CHUNKS = BK * BN / 4;
     constexpr int A_PER = A_CHUNKS / NT;
     constexpr int B_PER = B_CHUNKS / NT;
-    constexpr int A_CPR = BK / 4;        // chunks per A row
     constexpr int B_CPR = BN / 4;        // chunks per B row
     constexpr int STAGE = BM * BK + BK * BN;
     static_assert(BM % (16 * WAVES_M) == 0 && BN % (64 * WAVES_N) == 0, "wave tile");
-    static_assert(BK % 16 == 0, "BK");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "BK");
+    static_assert(BM % 32 == 0, "A layout pairs 16-row slabs");
     static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "load split");
 
     __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
@@ -220,7 +258,8 @@ sgemm_db_kernel(Args p) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int e = tid + NT * i;
-            const int r = e / A_CPR, c = e % A_CPR;
+            int r, c;
+            ALayout<BK>::coords(e, r, c);
             const int gi = m0 + r, gk = k0 + 4 * c;
             const float *src = p.A + (long)gi * p.lda + gk;
             if (!GUARD) {
@@ -271,8 +310,9 @@ sgemm_db_kernel(Args p) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int e = tid + NT * i;
-            const int r = e / A_CPR, c = e % A_CPR;
-            *reinterpret_cast<f32x4 *>(As + r * BK + 4 * a_swizzle<BK>(r, c)) = ra[i];
+            int r, c;
+            ALayout<BK>::coords(e, r, c);
+            *reinterpret_cast<f32x4 *>(As + ALayout<BK>::offset(r, c)) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
@@ -302,7 +342,7 @@ sgemm_db_kernel(Args p) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int r = wm * WM + mi * 16 + lrow;
-                a[mi] = *reinterpret_cast<const f32x4 *>(As + r * BK + 4 * a_swizzle<BK>(r, 4 * h + lq));
+                a[mi] = *reinterpret_cast<const f32x4 *>(As + ALayout<BK>::offset(r, 4 * h + lq));
             }
             f32x4 b[4][NJ];
 #pragma unroll

@@ -54,6 +54,8 @@ extern "C" {
 #define SGEMM_VARIANT_SIMPLE 0              /* 64x64 tile, single LDS buffer, 32-bit loads: the plain cross-check kernel */
 #define SGEMM_VARIANT_DB128_VEC 1           /* 128x128x32 tile, double-buffered LDS, 128-bit loads/stores (needs alignment) */
 #define SGEMM_VARIANT_DB128_SCALAR 2        /* the same tile with 32-bit loads/stores (any alignment) */
+/* Ids 3 .. sgemm_num_variants()-1 are further double-buffered tile shapes with
+ * 128-bit access, kept for tile sweeps; sgemm_variant_info() describes them. */
 
 /*
  * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
@@ -92,6 +94,13 @@ int sgemm_num_variants(void);
 
 /* Static name of a variant, or NULL for an unknown id. */
 const char *sgemm_variant_name(int variant);
+
+/*
+ * sgemm_variant_info: block tile (bm x bn, K step bk) of a variant and whether
+ * it needs 16-byte aligned operands (needs_vec = 1).  Any output pointer may
+ * be NULL.  Returns SGEMM_STATUS_OK or SGEMM_STATUS_INVALID_VARIANT.
+ */
+int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
 
 /* Static text for a status code. */
 const char *sgemm_strerror(int status);

@@ -38,6 +38,18 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"libsgemm.so does not export {name}"
 
 
+def test_variant_info(lib):
+    for v in capi.all_variants():
+        st, bm, bn, bk, vec = capi.sgemm_variant_info(v)
+        assert st == capi.SGEMM_STATUS_OK
+        assert bm % 16 == 0 and bn % 16 == 0 and bk % 4 == 0 and vec in (0, 1)
+        assert f"{bm}x{bn}x{bk}" in capi.sgemm_variant_name(v)
+    assert capi.sgemm_variant_info(capi.sgemm_num_variants())[0] == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert capi.sgemm_variant_info(capi.SGEMM_VARIANT_DB128_VEC)[1:] == (128, 128, 32, 1)
+    assert capi.sgemm_variant_info(capi.SGEMM_VARIANT_DB128_SCALAR)[1:] == (128, 128, 32, 0)
+    assert capi.sgemm_variant_info(capi.SGEMM_VARIANT_SIMPLE)[4] == 0
+
+
 def test_version_and_variants(lib):
     assert capi.sgemm_version() >= 1
     n = capi.sgemm_num_variants()
@@ -115,3 +127,22 @@ def test_variant_selection_by_alignment():
     # the ragged workload's leading dimensions (2047, 4999) are not multiples of 4
     assert sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999) == capi.SGEMM_VARIANT_DB128_SCALAR
     assert sel(-1, 4, 4, AL, 4, AL, 4, 0.0, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+def test_single_hip_runtime_in_process():
+    """Loading the library must not bring in a second HIP runtime next to the
+    one PyTorch ships (same soname, different build): the binding imports
+    torch first, so exactly one libamdhip64 is mapped and it is torch's."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from fp32_sgemm_tuning_amd import capi\n"
+            "capi.load()\n"
+            "import torch, os\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths)); print(list(paths)[0]); print(os.path.dirname(torch.__file__))\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    n, path, torch_dir = r.stdout.split("\n")[:3]
+    assert n == "1", r.stdout
+    assert os.path.realpath(path).startswith(os.path.realpath(torch_dir)), (path, torch_dir)

@@ -57,6 +57,12 @@ def test_workload_sampled(name):
             check_close(C[sl], ref, f"{name} rows {r0}..{r0 + 127}")
 
 
+try:
+    ALL_VARIANTS = capi.all_variants()
+except capi.LibraryMissing:      # collection without a built library
+    ALL_VARIANTS = [0, 1, 2]
+
+
 def _up4(n):
     return max(4, (n + 3) // 4 * 4)
 
@@ -67,8 +73,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [capi.SGEMM_VARIANT_SIMPLE, capi.SGEMM_VARIANT_DB128_VEC,
-                                     capi.SGEMM_VARIANT_DB128_SCALAR])
+@pytest.mark.parametrize("variant", ALL_VARIANTS)
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (1.5, -0.5)], ids=["b0", "b1"])
 def test_variant_shapes(variant, shape, ab):
