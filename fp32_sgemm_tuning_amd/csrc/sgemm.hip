@@ -71,12 +71,6 @@ bool vec_ok(int K, const float *A, int lda, const float *B, int ldb, float beta,
     return ab && aligned16(C) && ldc % 4 == 0;
 }
 
-int auto_variant(int K, const float *A, int lda, const float *B, int ldb, float beta,
-                 const float *C, int ldc) {
-    return vec_ok(K, A, lda, B, ldb, beta, C, ldc) ? SGEMM_VARIANT_DB128_VEC
-                                                   : SGEMM_VARIANT_DB128_SCALAR;
-}
-
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
@@ -94,6 +88,56 @@ void launch_db(const Args &a, hipStream_t stream) {
         else SGEMM_LAUNCH(false, false);
     }
 #undef SGEMM_LAUNCH
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
+void launch_pipe(const Args &a, hipStream_t stream) {
+    const bool guard = (a.M % BM) || (a.N % BN) || (a.K % 16);
+    const bool beta0 = a.beta == 0.0f;
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
+#define SGEMM_LAUNCH(G, Z) \
+    hipLaunchKernelGGL((sgemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
+    if (guard) {
+        if (beta0) SGEMM_LAUNCH(true, true);
+        else SGEMM_LAUNCH(true, false);
+    } else {
+        if (beta0) SGEMM_LAUNCH(false, true);
+        else SGEMM_LAUNCH(false, false);
+    }
+#undef SGEMM_LAUNCH
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
+void launch_sec(const Args &a, hipStream_t stream) {
+    const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
+    const bool beta0 = a.beta == 0.0f;
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
+#define SGEMM_LAUNCH(G, Z) \
+    hipLaunchKernelGGL((sgemm_sec_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
+    if (guard) {
+        if (beta0) SGEMM_LAUNCH(true, true);
+        else SGEMM_LAUNCH(true, false);
+    } else {
+        if (beta0) SGEMM_LAUNCH(false, true);
+        else SGEMM_LAUNCH(false, false);
+    }
+#undef SGEMM_LAUNCH
+}
+
+// Direct-to-LDS kernel for whole tiles; shapes that are not whole tiles
+// fall back to the section-pipelined kernel of the same tile (guarded loads).
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES>
+void launch_dtl(const Args &a, hipStream_t stream) {
+    const bool whole = !(a.M % BM) && !(a.N % BN) && !(a.K % BK);
+    if (!whole) {
+        launch_sec<BM, BN, BK, WAVES_M, WAVES_N, true>(a, stream);
+        return;
+    }
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
+    if (a.beta == 0.0f)
+        hipLaunchKernelGGL((sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, false>), grid, block, 0, stream, a);
 }
 
 void launch_simple(const Args &a, hipStream_t stream) {
@@ -126,8 +170,33 @@ const VariantDesc kVariants[] = {
     {"db_256x256x16_w4x4_vec", 256, 256, 16, true, launch_db<256, 256, 16, 4, 4, true>},
     {"db_256x128x16_w4x2_vec", 256, 128, 16, true, launch_db<256, 128, 16, 4, 2, true>},
     {"db_256x256x16_w2x4_vec", 256, 256, 16, true, launch_db<256, 256, 16, 2, 4, true>},
+    {"pipe_256x128x16_w2x2_vec", 256, 128, 16, true, launch_pipe<256, 128, 2, 2, true>},
+    {"pipe_128x128x16_w2x2_vec", 128, 128, 16, true, launch_pipe<128, 128, 2, 2, true>},
+    {"sec_128x128x64_w2x2_vec", 128, 128, 64, true, launch_sec<128, 128, 64, 2, 2, true>},
+    {"sec_128x128x32_w2x2_vec", 128, 128, 32, true, launch_sec<128, 128, 32, 2, 2, true>},
+    {"sec_256x128x32_w2x2_vec", 256, 128, 32, true, launch_sec<256, 128, 32, 2, 2, true>},
+    {"sec_128x256x32_w2x2_vec", 128, 256, 32, true, launch_sec<128, 256, 32, 2, 2, true>},
+    {"dtl_128x128x64_w2x2_s2", 128, 128, 64, true, launch_dtl<128, 128, 64, 2, 2, 2>},
+    {"dtl_128x128x32_w2x2_s3", 128, 128, 32, true, launch_dtl<128, 128, 32, 2, 2, 3>},
+    {"dtl_256x128x32_w2x2_s3", 256, 128, 32, true, launch_dtl<256, 128, 32, 2, 2, 3>},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+// Variants the automatic choice uses (indices into kVariants).
+constexpr int kLarge = 11;    // db_256x256x16_w4x4_vec: 16 waves, 64x64 wave tiles
+constexpr int kMedium = 20;   // dtl_128x128x64_w2x2_s2: direct-to-LDS, falls back to guarded loads
+constexpr int kNumCUs = 256;  // MI355X
+
+// Automatic choice (measured at 4096^3 and 8192^3 for the large tile, 512^3
+// to 2048^3 for the medium one): 32-bit access unless the operands allow
+// 128-bit access; then the 256x256 tile while it still gives every CU a
+// tile, else the 128x128 tile.  No HIP call.
+int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
+                 const float *C, int ldc) {
+    if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_VARIANT_DB128_SCALAR;
+    const long tiles256 = ceil_div(M, 256) * ceil_div(N, 256);
+    return tiles256 >= kNumCUs ? kLarge : kMedium;
+}
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
         float beta, float *C, int ldc, void *stream, int variant) {
@@ -135,7 +204,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     if (st != SGEMM_STATUS_OK) return st;
     if (variant < SGEMM_VARIANT_AUTO || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
     if (M == 0 || N == 0) return SGEMM_STATUS_OK;
-    if (variant == SGEMM_VARIANT_AUTO) variant = auto_variant(K, A, lda, B, ldb, beta, C, ldc);
+    if (variant == SGEMM_VARIANT_AUTO) variant = auto_variant(M, N, K, A, lda, B, ldb, beta, C, ldc);
     const VariantDesc &d = kVariants[variant];
     if (d.needs_vec && !vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_STATUS_UNSUPPORTED;
 
@@ -185,7 +254,7 @@ int sgemm_select_variant(int M, int N, int K, const float *A, int lda, const flo
                          float beta, const float *C, int ldc) {
     const int st = check_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != SGEMM_STATUS_OK) return st;
-    return auto_variant(K, A, lda, B, ldb, beta, C, ldc);
+    return auto_variant(M, N, K, A, lda, B, ldb, beta, C, ldc);
 }
 
 int sgemm_num_variants(void) { return kNumVariants; }

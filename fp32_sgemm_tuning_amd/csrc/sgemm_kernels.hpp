@@ -195,6 +195,11 @@ struct ALayout<32> {
     static __host__ __device__ __forceinline__ int offset(int m, int c) { return m * 32 + 4 * (c ^ ((m >> 1) & 7)); }
     // global-load assignment: 8 consecutive loaders share one row
     static __host__ __device__ __forceinline__ void coords(int e, int &m, int &c) { m = e >> 3; c = e & 7; }
+    // logical (row, chunk) stored at 16-byte LDS chunk position q
+    static __host__ __device__ __forceinline__ void inverse(int q, int &m, int &c) {
+        m = q >> 3;
+        c = (q & 7) ^ ((m >> 1) & 7);
+    }
 };
 
 template <>
@@ -212,35 +217,226 @@ struct ALayout<16> {
         const int q = e >> 2;
         m = ((q >> 5) << 5) + ((q & 1) << 4) + ((q & 31) >> 1);
     }
+    static __host__ __device__ __forceinline__ void inverse(int q, int &m, int &c) {
+        const int lds_row = q >> 3;
+        const int r = lds_row & 15;
+        const int chunk = (q & 7) ^ ((r >> 1) & 7);
+        m = ((lds_row >> 4) << 5) + ((chunk >> 2) << 4) + r;
+        c = chunk & 3;
+    }
 };
 
 template <>
 struct ALayout<64> {
     static __host__ __device__ __forceinline__ int offset(int m, int c) { return m * 64 + 4 * (c ^ (m & 15)); }
     static __host__ __device__ __forceinline__ void coords(int e, int &m, int &c) { m = e >> 4; c = e & 15; }
+    static __host__ __device__ __forceinline__ void inverse(int q, int &m, int &c) {
+        m = q >> 4;
+        c = (q & 15) ^ (m & 15);
+    }
+};
+
+// Pieces shared by the staged kernels: global loads of one K tile into
+// registers, their store into an LDS stage, MFMA fragment reads, the MFMAs
+// of one K tile and the epilogue.  Block tile BM x BN, K step BK, WAVES_M x
+// WAVES_N waves of 64 lanes, each owning a WM x WN register tile.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD>
+struct TileOps {
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int WM = BM / WAVES_M;
+    static constexpr int WN = BN / WAVES_N;
+    static constexpr int MI = WM / 16;          // 16-row MFMA tiles per wave
+    static constexpr int NJ = WN / 64;          // 64-column slabs per wave
+    static constexpr int KH = BK / 16;          // 16-deep halves of a K step
+    static constexpr int A_PER = BM * BK / 4 / NT;   // 16-byte loads per thread
+    static constexpr int B_PER = BK * BN / 4 / NT;
+    static constexpr int B_CPR = BN / 4;        // chunks per B row
+    static constexpr int STAGE = BM * BK + BK * BN;  // floats per LDS stage
+    static_assert(BM % (16 * WAVES_M) == 0 && BN % (64 * WAVES_N) == 0, "wave tile");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "BK");
+    static_assert(BM % 32 == 0, "A layout pairs 16-row slabs");
+    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "load split");
+
+    struct Staging {
+        f32x4 a[A_PER];
+        f32x4 b[B_PER];
+    };
+    struct Frags {
+        f32x4 a[MI];        // A chunk of 4 k per 16-row slab
+        f32x4 b[4][NJ];     // B: per k step j, 4 columns per 64-column slab
+    };
+
+    static __device__ __forceinline__ f32x4 load4(const float *src) {
+        if (VEC) return *reinterpret_cast<const f32x4 *>(src);
+        return f32x4{src[0], src[1], src[2], src[3]};
+    }
+
+    // Global loads of the K tile starting at k0 (zero outside the matrices).
+    static __device__ __forceinline__ void load(const Args &p, int m0, int n0, int k0, int tid, Staging &st) {
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            int r, c;
+            ALayout<BK>::coords(tid + NT * i, r, c);
+            const int gi = m0 + r, gk = k0 + 4 * c;
+            const float *src = p.A + (long)gi * p.lda + gk;
+            if (!GUARD) {
+                st.a[i] = load4(src);
+            } else if (gi < p.M && gk + 3 < p.K) {
+                st.a[i] = load4(src);
+            } else {
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (gi < p.M) {
+                    if (gk + 0 < p.K) v[0] = src[0];
+                    if (gk + 1 < p.K) v[1] = src[1];
+                    if (gk + 2 < p.K) v[2] = src[2];
+                }
+                st.a[i] = v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int e = tid + NT * i;
+            const int r = e / B_CPR, c = e % B_CPR;
+            const int gk = k0 + r, gj = n0 + 4 * c;
+            const float *src = p.B + (long)gk * p.ldb + gj;
+            if (!GUARD) {
+                st.b[i] = load4(src);
+            } else if (gk < p.K && gj + 3 < p.N) {
+                st.b[i] = load4(src);
+            } else {
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (gk < p.K) {
+                    if (gj + 0 < p.N) v[0] = src[0];
+                    if (gj + 1 < p.N) v[1] = src[1];
+                    if (gj + 2 < p.N) v[2] = src[2];
+                }
+                st.b[i] = v;
+            }
+        }
+    }
+
+    // Registers -> LDS stage.
+    static __device__ __forceinline__ void store(float *stage, int tid, const Staging &st) {
+        float *As = stage;
+        float *Bs = stage + BM * BK;
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            int r, c;
+            ALayout<BK>::coords(tid + NT * i, r, c);
+            *reinterpret_cast<f32x4 *>(As + ALayout<BK>::offset(r, c)) = st.a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int e = tid + NT * i;
+            const int r = e / B_CPR, c = e % B_CPR;
+            *reinterpret_cast<f32x4 *>(Bs + r * BN + 4 * c) = st.b[i];
+        }
+    }
+
+    // MFMA fragments of the 16-deep half h of the stage.
+    static __device__ __forceinline__ void read_frags(const float *stage, int wm, int wn, int lane, int h,
+                                                      Frags &f) {
+        const float *As = stage;
+        const float *Bs = stage + BM * BK;
+        const int lrow = lane & 15;
+        const int lq = lane >> 4;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            f.a[mi] = *reinterpret_cast<const f32x4 *>(As + ALayout<BK>::offset(wm * WM + mi * 16 + lrow, 4 * h + lq));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj)
+                f.b[j][nj] = *reinterpret_cast<const f32x4 *>(Bs + (16 * h + 4 * lq + j) * BN + wn * WN + nj * 64 +
+                                                              4 * lrow);
+    }
+
+    // Single items, for kernels that place every instruction explicitly.
+    static constexpr int NMFMA = MI * NJ * 16;     // MFMAs per fragment set
+    static constexpr int NREAD = MI + 4 * NJ;      // fragment reads per set
+    // MFMA number q: q = ((j * MI + mi) * NJ + nj) * 4 + i
+    template <int Q>
+    static __device__ __forceinline__ void mma_one(f32x4 (&acc)[MI][NJ][4], const Frags &f) {
+        constexpr int i = Q % 4, nj = (Q / 4) % NJ, mi = (Q / (4 * NJ)) % MI, j = Q / (4 * NJ * MI);
+        acc[mi][nj][i] = mfma_16x16x4(f.a[mi][j], f.b[j][nj][i], acc[mi][nj][i]);
+    }
+    // fragment read number r: A slabs first, then B (j, nj)
+    template <int R>
+    static __device__ __forceinline__ void read_one(const float *stage, int wm, int wn, int lane, int h, Frags &f) {
+        const int lrow = lane & 15;
+        const int lq = lane >> 4;
+        if constexpr (R < MI) {
+            f.a[R] = *reinterpret_cast<const f32x4 *>(stage + ALayout<BK>::offset(wm * WM + R * 16 + lrow, 4 * h + lq));
+        } else {
+            constexpr int j = (R - MI) / NJ, nj = (R - MI) % NJ;
+            f.b[j][nj] = *reinterpret_cast<const f32x4 *>(stage + BM * BK + (16 * h + 4 * lq + j) * BN + wn * WN +
+                                                          nj * 64 + 4 * lrow);
+        }
+    }
+
+    // The 16 k of one fragment set: MI x NJ x 4 column groups x 4 k steps.
+    static __device__ __forceinline__ void mma(f32x4 (&acc)[MI][NJ][4], const Frags &f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[mi][nj][i] = mfma_16x16x4(f.a[mi][j], f.b[j][nj][i], acc[mi][nj][i]);
+    }
+
+    // C = alpha*acc (+ beta*C).  Lane l holds, for row 4(l/16) + r of each
+    // 16-row slab, the four consecutive columns 4(l%16) .. +3 of each
+    // 64-column slab (column group i of the MFMA is real column 4c + i).
+    template <bool BETA0>
+    static __device__ __forceinline__ void epilogue(const Args &p, int m0, int n0, int wm, int wn, int lane,
+                                                    const f32x4 (&acc)[MI][NJ][4]) {
+        const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + r;
+                    const int col = n0 + wn * WN + nj * 64 + 4 * (lane & 15);
+                    f32x4 v = {acc[mi][nj][0][r], acc[mi][nj][1][r], acc[mi][nj][2][r], acc[mi][nj][3][r]};
+                    v *= alpha;
+                    float *dst = p.C + (long)row * p.ldc + col;
+                    const bool full = !GUARD || (row < p.M && col + 3 < p.N);
+                    if (full) {
+                        if (VEC) {
+                            if (!BETA0) v += beta * *reinterpret_cast<const f32x4 *>(dst);
+                            *reinterpret_cast<f32x4 *>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float o = v[e];
+                                if (!BETA0) o += beta * dst[e];
+                                dst[e] = o;
+                            }
+                        }
+                    } else if (row < p.M) {
+#pragma unroll
+                        for (int e = 0; e < 3; ++e) {
+                            if (col + e < p.N) {
+                                float o = v[e];
+                                if (!BETA0) o += beta * dst[e];
+                                dst[e] = o;
+                            }
+                        }
+                    }
+                }
+    }
 };
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD, bool BETA0>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_db_kernel(Args p) {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
-    constexpr int WM = BM / WAVES_M;
-    constexpr int WN = BN / WAVES_N;
-    constexpr int MI = WM / 16;          // 16-row MFMA tiles per wave
-    constexpr int NJ = WN / 64;          // 64-column slabs per wave
-    constexpr int KH = BK / 16;          // 16-deep halves of a K step
-    constexpr int A_CHUNKS = BM * BK / 4;
-    constexpr int B_CHUNKS = BK * BN / 4;
-    constexpr int A_PER = A_CHUNKS / NT;
-    constexpr int B_PER = B_CHUNKS / NT;
-    constexpr int B_CPR = BN / 4;        // chunks per B row
-    constexpr int STAGE = BM * BK + BK * BN;
-    static_assert(BM % (16 * WAVES_M) == 0 && BN % (64 * WAVES_N) == 0, "wave tile");
-    static_assert(BK == 16 || BK == 32 || BK == 64, "BK");
-    static_assert(BM % 32 == 0, "A layout pairs 16-row slabs");
-    static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "load split");
-
-    __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, VEC, GUARD>;
+    __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -249,177 +445,430 @@ sgemm_db_kernel(Args p) {
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int M = p.M, N = p.N, K = p.K;
 
-    // ---- global -> registers ------------------------------------------------
-    f32x4 ra[A_PER], rb[B_PER];
-
-    auto load_a = [&](int k0) {
+    f32x4 acc[T::MI][T::NJ][4];
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int e = tid + NT * i;
-            int r, c;
-            ALayout<BK>::coords(e, r, c);
-            const int gi = m0 + r, gk = k0 + 4 * c;
-            const float *src = p.A + (long)gi * p.lda + gk;
-            if (!GUARD) {
-                if (VEC) ra[i] = *reinterpret_cast<const f32x4 *>(src);
-                else ra[i] = f32x4{src[0], src[1], src[2], src[3]};
-            } else if (gi < M && gk + 3 < K) {
-                if (VEC) ra[i] = *reinterpret_cast<const f32x4 *>(src);
-                else ra[i] = f32x4{src[0], src[1], src[2], src[3]};
-            } else {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (gi < M) {
-                    if (gk + 0 < K) v[0] = src[0];
-                    if (gk + 1 < K) v[1] = src[1];
-                    if (gk + 2 < K) v[2] = src[2];
-                }
-                ra[i] = v;
-            }
-        }
-    };
-    auto load_b = [&](int k0) {
+    for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int e = tid + NT * i;
-            const int r = e / B_CPR, c = e % B_CPR;
-            const int gk = k0 + r, gj = n0 + 4 * c;
-            const float *src = p.B + (long)gk * p.ldb + gj;
-            if (!GUARD) {
-                if (VEC) rb[i] = *reinterpret_cast<const f32x4 *>(src);
-                else rb[i] = f32x4{src[0], src[1], src[2], src[3]};
-            } else if (gk < K && gj + 3 < N) {
-                if (VEC) rb[i] = *reinterpret_cast<const f32x4 *>(src);
-                else rb[i] = f32x4{src[0], src[1], src[2], src[3]};
-            } else {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (gk < K) {
-                    if (gj + 0 < N) v[0] = src[0];
-                    if (gj + 1 < N) v[1] = src[1];
-                    if (gj + 2 < N) v[2] = src[2];
-                }
-                rb[i] = v;
-            }
-        }
-    };
-    // ---- registers -> LDS stage ---------------------------------------------
-    auto store_stage = [&](int s) {
-        float *As = lds + s * STAGE;
-        float *Bs = As + BM * BK;
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int e = tid + NT * i;
-            int r, c;
-            ALayout<BK>::coords(e, r, c);
-            *reinterpret_cast<f32x4 *>(As + ALayout<BK>::offset(r, c)) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int e = tid + NT * i;
-            const int r = e / B_CPR, c = e % B_CPR;
-            *reinterpret_cast<f32x4 *>(Bs + r * BN + 4 * c) = rb[i];
-        }
-    };
-
-    f32x4 acc[MI][NJ][4];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
+        for (int nj = 0; nj < T::NJ; ++nj)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- MFMAs of one LDS stage -----------------------------------------------
-    auto compute_stage = [&](int s) {
-        const float *As = lds + s * STAGE;
-        const float *Bs = As + BM * BK;
-        const int lrow = lane & 15;
-        const int lq = lane >> 4;
-#pragma unroll
-        for (int h = 0; h < KH; ++h) {
-            f32x4 a[MI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const int r = wm * WM + mi * 16 + lrow;
-                a[mi] = *reinterpret_cast<const f32x4 *>(As + ALayout<BK>::offset(r, 4 * h + lq));
-            }
-            f32x4 b[4][NJ];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int nj = 0; nj < NJ; ++nj) {
-                    const int k = 16 * h + 4 * lq + j;
-                    const int c = wn * WN + nj * 64 + 4 * lrow;
-                    b[j][nj] = *reinterpret_cast<const f32x4 *>(Bs + k * BN + c);
-                }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                    for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mi][nj][i] = mfma_16x16x4(a[mi][j], b[j][nj][i], acc[mi][nj][i]);
-        }
-    };
-
-    const int T = (K + BK - 1) / BK;
-    if (T > 0) {
-        load_a(0);
-        load_b(0);
-        store_stage(0);
+    typename T::Staging st;
+    const int ntiles = (p.K + BK - 1) / BK;
+    if (ntiles > 0) {
+        T::load(p, m0, n0, 0, tid, st);
+        T::store(lds, tid, st);
         __syncthreads();
-        for (int t = 0; t < T; ++t) {
-            const bool more = (t + 1 < T);
-            if (more) {
-                load_a((t + 1) * BK);
-                load_b((t + 1) * BK);
+        for (int t = 0; t < ntiles; ++t) {
+            const bool more = (t + 1 < ntiles);
+            if (more) T::load(p, m0, n0, (t + 1) * BK, tid, st);
+            const float *stage = lds + (t & 1) * T::STAGE;
+#pragma unroll
+            for (int h = 0; h < T::KH; ++h) {
+                typename T::Frags f;
+                T::read_frags(stage, wm, wn, lane, h, f);
+                T::mma(acc, f);
             }
-            compute_stage(t & 1);
-            if (more) store_stage((t + 1) & 1);
+            if (more) T::store(lds + ((t + 1) & 1) * T::STAGE, tid, st);
             __syncthreads();
         }
     }
+    T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
+}
 
-    // ---- epilogue: C = alpha*acc (+ beta*C) -----------------------------------
-    const float alpha = p.alpha, beta = p.beta;
+// ---------------------------------------------------------------------------
+// Three-stage kernel with fragment prefetch (BK = 16).
+//
+// The K loop of the double-buffered kernel ends every tile with its LDS
+// writes and a barrier, and starts the next with fragment reads that its
+// first MFMAs must wait for; with every wave of the block in step, the
+// matrix units idle at each tile boundary.  Here the LDS holds three stages
+// and the fragments live in two register sets, so that while the MFMAs of
+// tile t run from registers:
+//   - the global loads of tile t+2 are issued into staging registers,
+//   - the fragments of tile t+1 are read from stage (t+1) % 3 into the
+//     other register set (tile t+1 was written before the previous
+//     barrier),
+//   - the staged tile t+2 is written into stage (t+2) % 3 (last read for
+//     tile t-1, before the previous barrier),
+// and one barrier closes the tile.  The loop body is branch-free (the tile
+// index of the loads is clamped to the last tile) so that the instruction
+// scheduler can spread the loads and LDS accesses between the MFMAs, in the
+// order fixed by the scheduling groups below.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool GUARD, bool BETA0>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+sgemm_pipe_kernel(Args p) {
+    constexpr int BK = 16;
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, VEC, GUARD>;
+    constexpr int NMFMA = T::MI * T::NJ * 16;
+    constexpr int NDSR = T::MI + 4 * T::NJ;
+    constexpr int NVMEM = VEC ? (T::A_PER + T::B_PER) : 4 * (T::A_PER + T::B_PER);
+    constexpr int NDSW = T::A_PER + T::B_PER;
+    __shared__ __attribute__((aligned(16))) float lds[3 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    f32x4 acc[T::MI][T::NJ][4];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
+        for (int nj = 0; nj < T::NJ; ++nj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + r;
-                const int col = n0 + wn * WN + nj * 64 + 4 * (lane & 15);
-                f32x4 v = {acc[mi][nj][0][r], acc[mi][nj][1][r], acc[mi][nj][2][r], acc[mi][nj][3][r]};
-                v *= alpha;
-                float *dst = p.C + (long)row * p.ldc + col;
-                const bool full = !GUARD || (row < M && col + 3 < N);
-                if (full) {
-                    if (VEC) {
-                        if (!BETA0) v += beta * *reinterpret_cast<const f32x4 *>(dst);
-                        *reinterpret_cast<f32x4 *>(dst) = v;
-                    } else {
+            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (p.K + BK - 1) / BK;
+    typename T::Staging st;
+    typename T::Frags f0, f1;
+
+    // one tile: MFMAs from `cur`, prefetch tile t+1 into `nxt`, stage tile t+2
+    auto step = [&](int t, int s_cur, const typename T::Frags &cur, typename T::Frags &nxt) {
+        const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+        const int s_far = s_nxt == 2 ? 0 : s_nxt + 1;
+        const int t_far = min(t + 2, ntiles - 1);
+        T::load(p, m0, n0, t_far * BK, tid, st);
+        T::read_frags(lds + s_nxt * T::STAGE, wm, wn, lane, 0, nxt);
+        T::mma(acc, cur);
+        T::store(lds + s_far * T::STAGE, tid, st);
+        // Order within the tile: MFMAs interleaved first with the global
+        // loads, then with the fragment reads; the LDS writes go in once most
+        // MFMAs are issued, so the loads have landed and the writes drain
+        // before the barrier.
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float o = v[e];
-                            if (!BETA0) o += beta * dst[e];
-                            dst[e] = o;
-                        }
-                    }
-                } else if (row < M) {
+        for (int i = 0; i < NVMEM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        }
 #pragma unroll
-                    for (int e = 0; e < 3; ++e) {
-                        if (col + e < N) {
-                            float o = v[e];
-                            if (!BETA0) o += beta * dst[e];
-                            dst[e] = o;
-                        }
-                    }
-                }
+        for (int i = 0; i < NDSR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+        constexpr int MID = NMFMA - NVMEM - 2 * NDSR - 2 * NDSW - 16;
+        __builtin_amdgcn_sched_group_barrier(0x008, MID > 0 ? MID : 0, 0);
+#pragma unroll
+        for (int i = 0; i < NDSW; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __syncthreads();
+    };
+
+    if (ntiles > 0) {
+        T::load(p, m0, n0, 0, tid, st);
+        T::store(lds, tid, st);
+        T::load(p, m0, n0, min(1, ntiles - 1) * BK, tid, st);
+        T::store(lds + T::STAGE, tid, st);
+        __syncthreads();
+        T::read_frags(lds, wm, wn, lane, 0, f0);
+        int s = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            step(t, s, f0, f1);
+            f0 = f1;
+            s = s == 2 ? 0 : s + 1;
+        }
+    }
+    T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Section-pipelined kernel (two LDS stages, BK = 32 or 64).
+//
+// A K tile is worked through in KH = BK/16 sections of 16 k.  Section h runs
+// its MFMAs from fragment register set F[h % 2] while the fragments of
+// section h+1 are read into the other set, so an MFMA never waits on the LDS
+// read that feeds it.  The barrier that publishes the next tile sits before
+// the last section: after it, the first fragments of tile t+1 are read while
+// the last section's MFMAs of tile t (already in registers) keep the matrix
+// unit busy.  Global loads run two tiles ahead through staging registers:
+// the loads of tile t+2 are issued in the middle of tile t and written into
+// the free LDS stage during tile t+1.
+//
+// Per tile t (stage cur = t % 2 holds tile t, stage nxt holds tile t+1):
+//   sections 0 .. KH-2 : MFMAs F[h%2] | read F[(h+1)%2] <- cur, section h+1
+//                        section WS: write staged tile t+1 into nxt
+//                        section GS: issue global loads of tile t+2
+//   barrier            : nxt complete; every read of cur issued and drained
+//   section KH-1       : read F[0] <- nxt, section 0 | MFMAs F[(KH-1)%2]
+// WAR on nxt: its previous tile (t-1) was last read before the barrier of
+// tile t-1.  The loop body has no branches: the tile index of the loads is
+// clamped to the last tile, whose re-staging into a dead stage is harmless.
+// ---------------------------------------------------------------------------
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+template <int NM, int NR, int NW, int NG>
+__device__ __forceinline__ void sched_section() {
+    // NR fragment reads, then NW LDS writes, then NG global loads, each one
+    // paired with MFMAs; the remaining MFMAs close the section.
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    constexpr int rest = NM - NR - NW - NG;
+    __builtin_amdgcn_sched_group_barrier(0x008, rest > 0 ? rest : 0, 0);
+}
+
+// Spread NR fragment reads over the first RSPAN of NM MFMAs, and NG memory
+// instructions (scheduling-group mask GMASK; the scheduler files the
+// direct-to-LDS loads under LDS writes, 0x200) evenly from MFMA G0 to G1,
+// one instruction per
+// slot: with every wave of a block in step, a burst of loads makes each wave
+// wait at issue while the address unit drains the whole block's requests,
+// and with one wave per SIMD nothing else keeps the matrix unit busy.
+template <int NM, int NR, int RSPAN, int NG, int G0, int G1, int GMASK, int I = 0, int R = 0, int G = 0>
+__device__ __forceinline__ void sched_spread() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr bool doR = (R < NR) && (I * NR >= R * RSPAN);
+        constexpr bool doG = (G < NG) && (I >= G0) && ((I - G0) * NG >= G * (G1 - G0));
+        if constexpr (doR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (doG) __builtin_amdgcn_sched_group_barrier(GMASK, 1, 0);
+        sched_spread<NM, NR, RSPAN, NG, G0, G1, GMASK, I + 1, R + (doR ? 1 : 0), G + (doG ? 1 : 0)>();
+    }
+}
+
+// Emit NM MFMAs in order with NR fragment reads spread over the first RSPAN
+// of them and NG memory operations spread evenly over all of them; a
+// scheduling fence follows each memory operation so the placement holds.
+template <int NM, int NR, int RSPAN, int NG, int I = 0, int R = 0, int G = 0, class FM, class FR, class FG>
+__device__ __forceinline__ void emit_spread(FM &&mfma, FR &&rd, FG &&mem) {
+    if constexpr (I < NM) {
+        mfma(IntC<I>{});
+        constexpr bool doR = (R < NR) && (I * NR >= R * RSPAN);
+        constexpr bool doG = (G < NG) && (I * NG >= G * NM);
+        if constexpr (doR) rd(IntC<R>{});
+        if constexpr (doG) mem(IntC<G>{});
+        if constexpr (doR || doG) __builtin_amdgcn_sched_barrier(0);
+        emit_spread<NM, NR, RSPAN, NG, I + 1, R + (doR ? 1 : 0), G + (doG ? 1 : 0)>(mfma, rd, mem);
+    }
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD, bool BETA0>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+sgemm_sec_kernel(Args p) {
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, VEC, GUARD>;
+    constexpr int KH = T::KH;
+    static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
+    constexpr int NM = T::MI * T::NJ * 16;                 // MFMAs per section
+    constexpr int NR = T::MI + 4 * T::NJ;                  // fragment reads per section
+    constexpr int NW = T::A_PER + T::B_PER;                // LDS writes per tile
+    constexpr int NG = VEC ? NW : 4 * NW;                  // global load instructions per tile
+    constexpr int WS = 0;                                  // section of the LDS writes
+    constexpr int GS = KH == 2 ? 0 : 1;                    // section of the global loads
+    __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    f32x4 acc[T::MI][T::NJ][4];
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < T::NJ; ++nj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (p.K + BK - 1) / BK;
+    if (ntiles > 0) {
+        typename T::Staging st;
+        typename T::Frags F[2];
+        T::load(p, m0, n0, 0, tid, st);
+        T::store(lds, tid, st);
+        T::load(p, m0, n0, min(1, ntiles - 1) * BK, tid, st);
+        __syncthreads();
+        T::read_frags(lds, wm, wn, lane, 0, F[0]);
+
+        for (int t = 0; t < ntiles; ++t) {
+            const float *cur = lds + (t & 1) * T::STAGE;
+            float *nxt = lds + ((t + 1) & 1) * T::STAGE;
+            const int k_far = min(t + 2, ntiles - 1) * BK;
+            auto section = [&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                T::mma(acc, F[h & 1]);
+                T::read_frags(cur, wm, wn, lane, h + 1, F[(h + 1) & 1]);
+                if (h == WS) T::store(nxt, tid, st);
+                if (h == GS) T::load(p, m0, n0, k_far, tid, st);
+                sched_section<NM, NR, h == WS ? NW : 0, h == GS ? NG : 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            section(IntC<0>{});
+            if constexpr (KH == 4) {
+                section(IntC<1>{});
+                section(IntC<2>{});
             }
+            __syncthreads();
+            T::read_frags(nxt, wm, wn, lane, 0, F[0]);
+            T::mma(acc, F[(KH - 1) & 1]);
+            sched_section<NM, NR, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel (whole tiles, 16-byte aligned operands).
+//
+// gfx950 loads global memory straight into LDS (global_load_lds_dwordx4):
+// lane l of one instruction deposits its 16 bytes at LDS base + 16 l, from
+// any address it chooses.  Each instruction therefore fills 1 KiB of a stage
+// contiguously, and the stage keeps the bank-conflict-free layouts above by
+// giving every lane the global address of the logical (row, chunk) that the
+// layout stores at that position.  No staging registers, no LDS write
+// instructions, and the only wait on the loads is the vmcnt before the
+// barrier that publishes a stage.
+//
+// STAGES = 2 or 3 LDS stages; the loads issued during tile t fill tile
+// t + STAGES - 1.  The sections and the barrier placement are those of the
+// section-pipelined kernel above; with three stages the barrier of tile t
+// waits only for the loads of tile t+1 (issued one tile earlier).
+// Requires M % BM == N % BN == K % BK == 0; other shapes use the kernels
+// with guarded register-staged loads.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool BETA0>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+sgemm_dtl_kernel(Args p) {
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, true, false>;
+    constexpr int NWAVES = WAVES_M * WAVES_N;
+    constexpr int KH = T::KH;
+    static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
+    static_assert(STAGES == 2 || STAGES == 3, "stages");
+    constexpr int NA = BM * BK / 4 / T::NT;                // direct loads per thread for A
+    constexpr int NB = BK * BN / 4 / T::NT;                // and for B
+    constexpr int NM = T::MI * T::NJ * 16;
+    constexpr int NR = T::MI + 4 * T::NJ;
+    __shared__ __attribute__((aligned(16))) float lds[STAGES * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Per-lane sources of this wave's direct loads, at k0 = 0.
+    const float *srcA[NA];
+    const float *srcB[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        int m, c;
+        ALayout<BK>::inverse((i * NWAVES + wave) * 64 + lane, m, c);
+        srcA[i] = p.A + (long)(m0 + m) * p.lda + 4 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int q = (i * NWAVES + wave) * 64 + lane;
+        srcB[i] = p.B + (long)(q / T::B_CPR) * p.ldb + n0 + 4 * (q % T::B_CPR);
+    }
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    // direct load number i of this thread (A loads first, then B) for tile t
+    auto issue_one = [&](int t, float *stage, int i) {
+        if (i < NA)
+            __builtin_amdgcn_global_load_lds((const void *)(srcA[i] + (long)t * BK),
+                                             (lds_ptr)(stage + (i * NWAVES + wave) * 256), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((const void *)(srcB[i - NA] + (long)t * BK * p.ldb),
+                                             (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * 256), 16, 0, 0);
+    };
+    auto issue_range = [&](int t, float *stage, auto lo, auto hi) {
+#pragma unroll
+        for (int i = decltype(lo)::value; i < decltype(hi)::value; ++i) issue_one(t, stage, i);
+    };
+    auto issue = [&](int t, float *stage) { issue_range(t, stage, IntC<0>{}, IntC<NA + NB>{}); };
+
+    f32x4 acc[T::MI][T::NJ][4];
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < T::NJ; ++nj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = p.K / BK;
+    if (ntiles > 0) {
+        typename T::Frags F[2];
+#pragma unroll
+        for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(min(s0, ntiles - 1), lds + s0 * T::STAGE);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        T::read_frags(lds, wm, wn, lane, 0, F[0]);
+
+        int cur = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int nxt = cur + 1 == STAGES ? 0 : cur + 1;
+            const int far = STAGES == 2 ? nxt : (nxt + 1 == STAGES ? 0 : nxt + 1);
+            const float *cs = lds + cur * T::STAGE;
+            const int t_far = min(t + STAGES - 1, ntiles - 1);
+            // The tile's direct loads are spread over sections 0 .. LS-1
+            // (with two stages they must land before this tile's barrier, so
+            // the last section before it is kept free of them).
+            constexpr int LS = STAGES == 3 ? KH - 1 : (KH == 4 ? 2 : 1);
+            constexpr int PER = (NA + NB + LS - 1) / LS;
+            auto section = [&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                constexpr int g_lo = h * PER < NA + NB ? h * PER : NA + NB;
+                constexpr int g_hi = (h + 1) * PER < NA + NB ? (h + 1) * PER : NA + NB;
+                float *fs = lds + far * T::STAGE;
+                emit_spread<NM, NR, NM * 3 / 4, (h < LS) ? g_hi - g_lo : 0>(
+                    [&](auto q) { T::template mma_one<decltype(q)::value>(acc, F[h & 1]); },
+                    [&](auto r) { T::template read_one<decltype(r)::value>(cs, wm, wn, lane, h + 1, F[(h + 1) & 1]); },
+                    [&](auto g) { issue_one(t_far, fs, g_lo + decltype(g)::value); });
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            section(IntC<0>{});
+            if constexpr (KH == 4) {
+                section(IntC<1>{});
+                section(IntC<2>{});
+            }
+            // the loads of tile t+1 have landed (with three stages the loads
+            // of tile t+2, just issued, may still be in flight)
+            if constexpr (STAGES == 3) {
+                static_assert(NA + NB <= 63, "vmcnt");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NA + NB) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            {
+                const float *ns = lds + nxt * T::STAGE;
+                emit_spread<NM, NR, NR, 0>(
+                    [&](auto q) { T::template mma_one<decltype(q)::value>(acc, F[(KH - 1) & 1]); },
+                    [&](auto r) { T::template read_one<decltype(r)::value>(ns, wm, wn, lane, 0, F[0]); },
+                    [&](auto) {});
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            cur = nxt;
+        }
+    }
+    T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
 }
 
 }  // namespace sgemm_mi355x

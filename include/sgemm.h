@@ -59,7 +59,11 @@ extern "C" {
 
 /*
  * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
- * the alignment class, beta == 0 and the shape.  Returns SGEMM_STATUS_*.
+ * the alignment class and the shape: 32-bit access (variant
+ * SGEMM_VARIANT_DB128_SCALAR) unless the operands allow 128-bit access; then
+ * a 256x256 block tile when that still gives each of the 256 compute units a
+ * tile, else a 128x128 tile.  beta == 0 selects an epilogue that never reads
+ * C.  Returns SGEMM_STATUS_*.
  */
 int sgemm(int M, int N, int K, float alpha,
           const float *A, int lda,

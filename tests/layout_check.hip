@@ -1,7 +1,8 @@
 // Host-side check of the LDS A-stage layouts of the double-buffered kernel
 // (ALayout<BK> in sgemm_kernels.hpp), run on the CPU:
 //   - the loader assignment e -> (row, chunk) is a bijection onto the tile;
-//   - offsets are a bijection onto the stage, 16-byte aligned;
+//   - offsets are a bijection onto the stage, 16-byte aligned, and inverse()
+//     maps each 16-byte LDS position back to its (row, chunk);
 //   - each group of 8 consecutive loaders writes 128 contiguous bytes
 //     (one ds_write_b128 pass without bank conflicts);
 //   - for every 16-row slab and k-chunk group, the 16 lanes of each
@@ -27,6 +28,9 @@ static int check() {
         if (m < 0 || m >= BM || c < 0 || c >= CPR) { ++bad; continue; }
         rc.insert({m, c});
         const int o = ALayout<BK>::offset(m, c);
+        int mi, ci;                                      // the direct-load inverse
+        ALayout<BK>::inverse(o / 4, mi, ci);
+        if (mi != m || ci != c) ++bad;
         if (o % 4 || o < 0 || o >= BM * BK) ++bad;
         offs.insert(o);
         off_of_e[e] = o;
@@ -63,5 +67,6 @@ int main() {
     bad += check<16, 256>();
     bad += check<32, 128>();
     bad += check<32, 256>();
+    bad += check<64, 128>();
     return bad ? 1 : 0;
 }

@@ -117,9 +117,26 @@ def test_forced_variant_checks():
     assert capi.sgemm_ex(*odd, capi.SGEMM_VARIANT_DB128_VEC) == capi.SGEMM_STATUS_UNSUPPORTED
 
 
+def _needs_vec(v):
+    return capi.sgemm_variant_info(v)[4] == 1
+
+
+def test_variant_selection_by_shape():
+    """Aligned operands take a 128-bit variant: the 256x256 tile once there
+    are at least 256 such tiles (one per compute unit), else a 128x128 one."""
+    sel = capi.sgemm_select_variant
+    for (M, N, K) in [(64, 64, 64), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
+                      (4096, 4000, 100), (4, 4, 4)]:
+        v = sel(M, N, K, AL, K, AL, N, 0.0, AL, N)
+        assert v >= 0 and _needs_vec(v), (M, N, K, v)
+        st, bm, bn, bk, vec = capi.sgemm_variant_info(v)
+        tiles256 = -(-M // 256) * -(-N // 256)
+        assert (bm, bn) == ((256, 256) if tiles256 >= 256 else (128, 128)), (M, N, K, bm, bn)
+
+
 def test_variant_selection_by_alignment():
     sel = capi.sgemm_select_variant
-    assert sel(64, 64, 64, AL, 64, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_VEC
+    assert _needs_vec(sel(64, 64, 64, AL, 64, AL, 64, 0.0, AL, 64))
     assert sel(64, 64, 64, MIS, 64, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
     assert sel(64, 64, 64, AL, 64, MIS, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
     assert sel(64, 64, 64, AL, 64, AL, 64, 0.0, MIS, 64) == capi.SGEMM_VARIANT_DB128_SCALAR

@@ -115,18 +115,19 @@ def test_unaligned_views(variant):
     assert torch.isnan(pad).all()
 
 
-def test_auto_matches_forced_variants_bitwise_shape_classes():
-    """Auto dispatch picks the 128-bit variant for packed aligned tensors and
-    gives the same bits as forcing it."""
+@pytest.mark.parametrize("n", [256, 4096])
+def test_auto_matches_forced_variant_bitwise(n):
+    """Auto dispatch picks a 128-bit variant for packed aligned tensors and
+    gives the same bits as forcing that variant."""
     torch = torch_cuda()
-    A, B, _ = make_problem(256, 256, 256, 0)
+    A, B, _ = make_problem(n, n, n, 0)
     dA, dB = to_dev(A, torch), to_dev(B, torch)
     auto = sgemm(dA, dB)
-    forced = sgemm(dA, dB, variant=capi.SGEMM_VARIANT_DB128_VEC)
+    v = capi.sgemm_select_variant(n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, 0.0, auto.data_ptr(), n)
+    assert capi.sgemm_variant_info(v)[4] == 1
+    forced = sgemm(dA, dB, variant=v)
     torch.cuda.synchronize()
     assert torch.equal(auto, forced)
-    assert capi.sgemm_select_variant(256, 256, 256, dA.data_ptr(), 256, dB.data_ptr(), 256, 0.0,
-                                     auto.data_ptr(), 256) == capi.SGEMM_VARIANT_DB128_VEC
 
 
 def test_aligned_vs_scalar_variant_agree():

@@ -23,4 +23,4 @@ def test_lds_layouts(tmp_path):
                    check=True, capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("ok") == 4, r.stdout
+    assert r.stdout.count("ok") == 5, r.stdout
