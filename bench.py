@@ -4,12 +4,19 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sq4096]
                     [--variant V] [--cpu-seconds S] [--no-cpu-baseline]
                     [--copy-calibration-mib N]
+    python bench.py --sweep VARIANTS --sweep-sizes SIZES [--rounds R]
 
 A step is one SGEMM call (the whole path: one kernel launch over the
 device-resident A, B and C).  W untimed warm-up steps, then exactly K timed
 steps between two device synchronisations.  Per-launch kernel time comes
 from HIP events recorded on the stream the kernel is launched on.  Prints
 one JSON line.
+
+--sweep times the given variant ids (comma separated; -1 = the automatic
+choice, "mm" = torch.mm in FP32 for context) on square problems of the given
+sizes, interleaved round by round in one process so that clock drift hits
+every variant alike, and prints one JSON line per (size, variant) with the
+median kernel time.  It is the evidence behind the automatic tile choice.
 
 The CPU baseline times the fp64 oracle on a bounded slab of rows of the
 same problem (host cores, OpenMP over rows) and checks the GPU result on
@@ -92,6 +99,55 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
     }
 
 
+def sweep(variants, sizes, rounds):
+    import statistics
+
+    import torch
+
+    from fp32_sgemm_tuning_amd import capi, sgemm
+    from fp32_sgemm_tuning_amd.inputs import make_problem
+    torch.backends.cuda.matmul.allow_tf32 = False
+    capi.load()
+    for n in sizes:
+        A, B, _ = make_problem(n, n, n, 7)
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dC = torch.empty((n, n), device="cuda")
+        reps = max(5, min(200, int(2e11 / (2 * n ** 3))))
+
+        def run(v):
+            if v == "mm":
+                torch.mm(dA, dB, out=dC)
+            else:
+                sgemm(dA, dB, dC, variant=None if v == -1 else v)
+        for v in variants:
+            for _ in range(3):
+                run(v)
+        torch.cuda.synchronize()
+        times = {v: [] for v in variants}
+        for _ in range(rounds):
+            for v in variants:
+                evs = []
+                for _ in range(reps):
+                    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    st.record()
+                    run(v)
+                    en.record()
+                    evs.append((st, en))
+                torch.cuda.synchronize()
+                times[v] += [a.elapsed_time(b) for a, b in evs]
+        for v in variants:
+            ms = statistics.median(times[v])
+            if v == "mm":
+                name = "torch.mm fp32"
+            elif v == -1:
+                name = "auto:" + capi.sgemm_variant_name(capi.sgemm_select_variant(
+                    n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, 0.0, dC.data_ptr(), n))
+            else:
+                name = capi.sgemm_variant_name(v)
+            print(json.dumps({"sweep": name, "variant": v, "n": n, "median_ms": round(ms, 5),
+                              "tflops": round(2 * n ** 3 / ms / 1e9, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +158,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--sweep", default=None)
+    ap.add_argument("--sweep-sizes", default="4096")
+    ap.add_argument("--rounds", type=int, default=4)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,6 +168,11 @@ def main():
               "(row-slab sharding across GPUs is described in the design notes but not built)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep is not None:
+        variants = [v if v == "mm" else int(v) for v in args.sweep.split(",")]
+        sweep(variants, [int(n) for n in args.sweep_sizes.split(",")], args.rounds)
+        return
 
     import numpy as np
     import torch
