@@ -38,11 +38,17 @@ METRIC = "SGEMM TFLOP/s (2MNK/t) at M=N=K=4096 FP32; % of MI355X FP32 matrix pea
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_sq4096.txt")
 
 
+KERNEL_SOURCES = ("sgemm.hip", "sgemm_kernels.hpp", "sgemm_lean.hip")
+
+
 def kernel_source_hash():
-    """Hash of the kernel source: a counter record taken on other kernel code
-    no longer describes the kernel that runs."""
-    with open(os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc", "sgemm_kernels.hpp"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the library's device and launch sources: a counter record taken
+    on other kernel code no longer describes the kernel that runs."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(variant_name):

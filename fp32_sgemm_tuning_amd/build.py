@@ -20,14 +20,22 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgemm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = [os.path.join(CSRC, "sgemm.hip")]
+# (source, extra flags): each translation unit is compiled on its own, then
+# linked into one shared library.  sgemm_lean.hip keeps MFMA results in
+# ordinary VGPRs; that flag is per translation unit and would make the
+# shared header's 256-accumulator kernels spill.
+UNITS = [
+    ("sgemm.hip", []),
+    ("sgemm_lean.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+]
+SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS]
 DEPS = SOURCES + [os.path.join(CSRC, "sgemm_kernels.hpp"), os.path.join(INCLUDE, "sgemm.h")]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
@@ -44,17 +52,37 @@ def needs_build() -> bool:
 def build(verbose: bool = False, isa: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", *SOURCES, "-o", tmp]
-    if isa:
-        cmd += ["-save-temps"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD_DIR)
+    procs, objs = [], []
+    for unit, extra in UNITS:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(unit)[0] + ".o")
+        cmd = [HIPCC, *HIP_FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(CSRC, unit), "-o", obj]
+        if isa:
+            cmd += ["-save-temps"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((unit, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                                             cwd=BUILD_DIR)))
+        objs.append(obj)
+    report, failed = [], []
+    for unit, p in procs:
+        out, err = p.communicate()
+        report.append(f"==== {unit}\n{err}")
+        if p.returncode != 0:
+            failed.append((unit, err))
     with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
-        f.write(r.stderr)
+        f.write("\n".join(report))
+    for unit, err in failed:
+        sys.stderr.write(err)
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(u for u, _ in failed))
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True, cwd=BUILD_DIR)
     if r.returncode != 0:
         sys.stderr.write(r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
+        raise RuntimeError(f"hipcc link failed ({r.returncode})")
     os.replace(tmp, LIB)
     return LIB
 

@@ -19,6 +19,16 @@
 
 #define SGEMM_LIB_VERSION 1
 
+namespace sgemm_mi355x {
+// Lean direct-to-LDS kernels (sgemm_lean.hip, built with MFMA results in
+// VGPRs): whole tiles only, offsets within the 31-bit buffer range.
+void launch_lean_128x128x64_w2x2(const Args &a, hipStream_t stream);
+void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t stream);
+void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t stream);
+void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t stream);
+void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t stream);
+}  // namespace sgemm_mi355x
+
 using namespace sgemm_mi355x;
 
 namespace {
@@ -140,11 +150,25 @@ void launch_dtl(const Args &a, hipStream_t stream) {
         hipLaunchKernelGGL((sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, false>), grid, block, 0, stream, a);
 }
 
+typedef void (*Launcher)(const Args &, hipStream_t);
+
+// The lean kernel takes whole tiles whose every byte offset within A's row
+// block and B's column block stays below 2^31 (the buffer descriptors'
+// range); other shapes go to FALLBACK, a guarded kernel of the same tile.
+template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
+void launch_lean_or(const Args &a, hipStream_t stream) {
+    const bool whole = !(a.M % BM) && !(a.N % BN) && !(a.K % BK);
+    const long lim = 0x7fffffffL;
+    const bool fits = 4L * ((long)(BM - 1) * a.lda + a.K) < lim && 4L * ((long)a.K * a.ldb + BN) < lim;
+    if (whole && fits)
+        LEAN(a, stream);
+    else
+        FALLBACK(a, stream);
+}
+
 void launch_simple(const Args &a, hipStream_t stream) {
     hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream, a);
 }
-
-typedef void (*Launcher)(const Args &, hipStream_t);
 
 struct VariantDesc {
     const char *name;
@@ -179,23 +203,35 @@ const VariantDesc kVariants[] = {
     {"dtl_128x128x64_w2x2_s2", 128, 128, 64, true, launch_dtl<128, 128, 64, 2, 2, 2>},
     {"dtl_128x128x32_w2x2_s3", 128, 128, 32, true, launch_dtl<128, 128, 32, 2, 2, 3>},
     {"dtl_256x128x32_w2x2_s3", 256, 128, 32, true, launch_dtl<256, 128, 32, 2, 2, 3>},
+    {"lean_128x128x64_w2x2", 128, 128, 64, true,
+     launch_lean_or<128, 128, 64, launch_lean_128x128x64_w2x2, launch_sec<128, 128, 64, 2, 2, true>>},
+    {"lean_128x128x32_w2x2", 128, 128, 32, true,
+     launch_lean_or<128, 128, 32, launch_lean_128x128x32_w2x2, launch_sec<128, 128, 32, 2, 2, true>>},
+    {"lean_256x128x32_w4x2", 256, 128, 32, true,
+     launch_lean_or<256, 128, 32, launch_lean_256x128x32_w4x2, launch_db<256, 128, 32, 4, 2, true>>},
+    {"lean_128x256x32_w2x4", 128, 256, 32, true,
+     launch_lean_or<128, 256, 32, launch_lean_128x256x32_w2x4, launch_db<128, 256, 32, 2, 4, true>>},
+    {"lean_256x256x32_w4x2", 256, 256, 32, true,
+     launch_lean_or<256, 256, 32, launch_lean_256x256x32_w4x2, launch_db<256, 256, 32, 4, 2, true>>},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Variants the automatic choice uses (indices into kVariants).
-constexpr int kLarge = 11;    // db_256x256x16_w4x4_vec: 16 waves, 64x64 wave tiles
-constexpr int kMedium = 20;   // dtl_128x128x64_w2x2_s2: direct-to-LDS, falls back to guarded loads
-constexpr int kNumCUs = 256;  // MI355X
+// Variant the automatic choice uses for 128-bit operands (index into
+// kVariants): the lean direct-to-LDS kernel on 128x128x32 tiles, which falls
+// back to the guarded section-pipelined kernel of the same tile on shapes
+// that are not whole tiles.  Measured against the other lean tiles and the
+// earlier kernels at 1024^3 to 8192^3 (bench.py --sweep): best or within
+// 0.3% of the best at every size from 2048^3 up.
+constexpr int kVec = 24;  // lean_128x128x32_w2x2
 
-// Automatic choice (measured at 4096^3 and 8192^3 for the large tile, 512^3
-// to 2048^3 for the medium one): 32-bit access unless the operands allow
-// 128-bit access; then the 256x256 tile while it still gives every CU a
-// tile, else the 128x128 tile.  No HIP call.
+// Automatic choice: 32-bit access unless the operands allow 128-bit access.
+// No HIP call.
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
+    (void)M;
+    (void)N;
     if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_VARIANT_DB128_SCALAR;
-    const long tiles256 = ceil_div(M, 256) * ceil_div(N, 256);
-    return tiles256 >= kNumCUs ? kLarge : kMedium;
+    return kVec;
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,

@@ -75,7 +75,7 @@ __device__ __forceinline__ void tile_coords(const Args &p, int &tm, int &tn) {
 // per-thread multiply-add replaced by MFMA.  Four waves in a 2x2 grid, each
 // owning a 32x32 sub-tile (2x2 MFMA tiles).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
+static __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
     constexpr int BM = 64, BN = 64, BK = 16;
     __shared__ float As[BM][BK + 1];
     __shared__ float Bs[BK][BN + 1];

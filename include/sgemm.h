@@ -54,16 +54,19 @@ extern "C" {
 #define SGEMM_VARIANT_SIMPLE 0              /* 64x64 tile, single LDS buffer, 32-bit loads: the plain cross-check kernel */
 #define SGEMM_VARIANT_DB128_VEC 1           /* 128x128x32 tile, double-buffered LDS, 128-bit loads/stores (needs alignment) */
 #define SGEMM_VARIANT_DB128_SCALAR 2        /* the same tile with 32-bit loads/stores (any alignment) */
-/* Ids 3 .. sgemm_num_variants()-1 are further double-buffered tile shapes with
- * 128-bit access, kept for tile sweeps; sgemm_variant_info() describes them. */
+/* Ids 3 .. sgemm_num_variants()-1 are further kernels and tile shapes with
+ * 128-bit access (double-buffered, section-pipelined, direct-to-LDS and the
+ * lean direct-to-LDS kernels), kept for tile sweeps; sgemm_variant_name() and
+ * sgemm_variant_info() describe them.  The direct-to-LDS kernels run on whole
+ * tiles only and use the guarded kernel of the same tile otherwise. */
 
 /*
  * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
- * the alignment class and the shape: 32-bit access (variant
- * SGEMM_VARIANT_DB128_SCALAR) unless the operands allow 128-bit access; then
- * a 256x256 block tile when that still gives each of the 256 compute units a
- * tile, else a 128x128 tile.  beta == 0 selects an epilogue that never reads
- * C.  Returns SGEMM_STATUS_*.
+ * the alignment class: 32-bit access (variant SGEMM_VARIANT_DB128_SCALAR)
+ * unless the operands allow 128-bit access; then the lean direct-to-LDS
+ * kernel on 128x128x32 block tiles, with its guarded fallback where the shape
+ * is not a whole number of tiles.  beta == 0 selects an epilogue that never
+ * reads C.  Returns SGEMM_STATUS_*.
  */
 int sgemm(int M, int N, int K, float alpha,
           const float *A, int lda,

@@ -122,16 +122,17 @@ def _needs_vec(v):
 
 
 def test_variant_selection_by_shape():
-    """Aligned operands take a 128-bit variant: the 256x256 tile once there
-    are at least 256 such tiles (one per compute unit), else a 128x128 one."""
+    """Aligned operands take the lean 128x128x32 direct-to-LDS variant at every
+    shape (it hands shapes that are not whole tiles to its guarded
+    fallback)."""
     sel = capi.sgemm_select_variant
+    lean = [v for v in capi.all_variants() if capi.sgemm_variant_name(v) == "lean_128x128x32_w2x2"]
+    assert len(lean) == 1
     for (M, N, K) in [(64, 64, 64), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
                       (4096, 4000, 100), (4, 4, 4)]:
         v = sel(M, N, K, AL, K, AL, N, 0.0, AL, N)
-        assert v >= 0 and _needs_vec(v), (M, N, K, v)
-        st, bm, bn, bk, vec = capi.sgemm_variant_info(v)
-        tiles256 = -(-M // 256) * -(-N // 256)
-        assert (bm, bn) == ((256, 256) if tiles256 >= 256 else (128, 128)), (M, N, K, bm, bn)
+        assert v == lean[0], (M, N, K, v)
+        assert _needs_vec(v)
 
 
 def test_variant_selection_by_alignment():

@@ -70,6 +70,9 @@ def _up4(n):
 SHAPES = [
     (1, 1, 1), (1, 129, 3), (7, 5, 3), (16, 64, 16), (64, 64, 64), (127, 129, 31),
     (128, 128, 32), (129, 127, 33), (256, 384, 96), (300, 200, 500), (131, 517, 1029),
+    # whole 256x256 tiles with one, two and five 64-deep K tiles (odd and even
+    # counts of the two-stage loop)
+    (256, 256, 64), (256, 512, 128), (512, 768, 320),
 ]
 
 

@@ -39,6 +39,32 @@ def test_guard_bands_and_ldc_padding(variant, shape):
     check_close(C.cpu().numpy(), ref, "guard-band case")
 
 
+@pytest.mark.parametrize("variant", list(range(capi.sgemm_num_variants())))
+def test_whole_tiles_with_padded_leading_dimensions(variant):
+    """Whole 256x256 tiles (so every variant runs its unguarded path) with
+    lda, ldb and ldc all larger than the logical width: the kernels must step
+    rows by the leading dimensions and leave C's padding and surroundings
+    alone."""
+    torch = torch_cuda()
+    M, N, K = 256, 512, 192
+    lda, ldb, ldc = K + 8, N + 4, N + 12
+    guard = 1024
+    A, B, Cin = make_problem(M, N, K, 43, dist="normal", with_c=True)
+    dA, _ = padded_device(A, lda, torch)
+    dB, _ = padded_device(B, ldb, torch)
+    buf = torch.full((2 * guard + M * ldc,), CANARY, dtype=torch.float32, device="cuda")
+    C = buf[guard:guard + M * ldc].view(M, ldc)[:, :N]
+    C.copy_(to_dev(Cin, torch))
+    sgemm(dA, dB, C, alpha=-0.75, beta=0.25, variant=variant)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:guard] == CANARY), "write before C"
+    assert np.all(host[guard + M * ldc:] == CANARY), "write after C"
+    assert np.all(host[guard:guard + M * ldc].reshape(M, ldc)[:, N:] == CANARY), "write into ldc padding"
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=-0.75, beta=0.25)
+    check_close(C.cpu().numpy(), ref, f"whole tiles, padded ld, variant {variant}")
+
+
 def test_non_default_stream_ordering():
     torch = torch_cuda()
     A, B, _ = make_problem(512, 512, 512, 42)
