@@ -13,8 +13,8 @@ from HIP events recorded on the stream the kernel is launched on.  Prints
 one JSON line.
 
 --sweep times the given variant ids (comma separated; -1 = the automatic
-choice, "mm" = torch.mm in FP32 for context) on square problems of the given
-sizes, interleaved round by round in one process so that clock drift hits
+choice, "mm" = torch.mm in FP32 for context) on problems of the given sizes
+("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike, and prints one JSON line per (size, variant) with the
 median kernel time.  It is the evidence behind the automatic tile choice.
 
@@ -105,33 +105,50 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
     }
 
 
+def parse_shape(text):
+    """'4096' -> (4096, 4096, 4096); '3001x4999x2047' -> (3001, 4999, 2047)."""
+    parts = [int(x) for x in text.lower().split("x")]
+    if len(parts) == 1:
+        parts *= 3
+    if len(parts) != 3 or min(parts) < 1:
+        raise SystemExit(f"bad --sweep-sizes entry {text!r}")
+    return tuple(parts)
+
+
 def sweep(variants, sizes, rounds):
     import statistics
 
     import torch
 
-    from fp32_sgemm_tuning_amd import capi, sgemm
+    from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm
     from fp32_sgemm_tuning_amd.inputs import make_problem
     torch.backends.cuda.matmul.allow_tf32 = False
     capi.load()
-    for n in sizes:
-        A, B, _ = make_problem(n, n, n, 7)
+    for M, N, K in sizes:
+        A, B, _ = make_problem(M, N, K, 7)
         dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
-        dC = torch.empty((n, n), device="cuda")
-        reps = max(5, min(200, int(2e11 / (2 * n ** 3))))
+        dC = torch.empty((M, N), device="cuda")
+        flop = 2 * M * N * K
+        reps = max(5, min(200, int(2e11 / max(flop, 1))))
 
         def run(v):
             if v == "mm":
                 torch.mm(dA, dB, out=dC)
             else:
                 sgemm(dA, dB, dC, variant=None if v == -1 else v)
+        usable = []
         for v in variants:
-            for _ in range(3):
-                run(v)
+            try:
+                for _ in range(3):
+                    run(v)
+                usable.append(v)
+            except SgemmError as e:      # e.g. a 128-bit variant on unaligned rows
+                print(json.dumps({"sweep": capi.sgemm_variant_name(v), "variant": v, "shape": f"{M}x{N}x{K}",
+                                  "skipped": str(e)}), flush=True)
         torch.cuda.synchronize()
-        times = {v: [] for v in variants}
+        times = {v: [] for v in usable}
         for _ in range(rounds):
-            for v in variants:
+            for v in usable:
                 evs = []
                 for _ in range(reps):
                     st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -141,17 +158,17 @@ def sweep(variants, sizes, rounds):
                     evs.append((st, en))
                 torch.cuda.synchronize()
                 times[v] += [a.elapsed_time(b) for a, b in evs]
-        for v in variants:
+        for v in usable:
             ms = statistics.median(times[v])
             if v == "mm":
                 name = "torch.mm fp32"
             elif v == -1:
                 name = "auto:" + capi.sgemm_variant_name(capi.sgemm_select_variant(
-                    n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, 0.0, dC.data_ptr(), n))
+                    M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dC.data_ptr(), N))
             else:
                 name = capi.sgemm_variant_name(v)
-            print(json.dumps({"sweep": name, "variant": v, "n": n, "median_ms": round(ms, 5),
-                              "tflops": round(2 * n ** 3 / ms / 1e9, 2)}), flush=True)
+            print(json.dumps({"sweep": name, "variant": v, "shape": f"{M}x{N}x{K}", "median_ms": round(ms, 5),
+                              "tflops": round(flop / ms / 1e9, 2)}), flush=True)
 
 
 def main():
@@ -177,7 +194,7 @@ def main():
 
     if args.sweep is not None:
         variants = [v if v == "mm" else int(v) for v in args.sweep.split(",")]
-        sweep(variants, [int(n) for n in args.sweep_sizes.split(",")], args.rounds)
+        sweep(variants, [parse_shape(x) for x in args.sweep_sizes.split(",")], args.rounds)
         return
 
     import numpy as np

@@ -152,15 +152,16 @@ void launch_dtl(const Args &a, hipStream_t stream) {
 
 typedef void (*Launcher)(const Args &, hipStream_t);
 
-// The lean kernel takes whole tiles whose every byte offset within A's row
-// block and B's column block stays below 2^31 (the buffer descriptors'
-// range); other shapes go to FALLBACK, a guarded kernel of the same tile.
+// The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
+// be whole tiles) and byte offsets within A's row block and B's column block
+// below 2^31 (the buffer descriptors' range); other shapes go to FALLBACK, a
+// guarded kernel of the same tile.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_or(const Args &a, hipStream_t stream) {
-    const bool whole = !(a.M % BM) && !(a.N % BN) && !(a.K % BK);
+    const bool shape = a.K >= BK && !(a.K % 4) && !(a.N % 4);
     const long lim = 0x7fffffffL;
     const bool fits = 4L * ((long)(BM - 1) * a.lda + a.K) < lim && 4L * ((long)a.K * a.ldb + BN) < lim;
-    if (whole && fits)
+    if (shape && fits)
         LEAN(a, stream);
     else
         FALLBACK(a, stream);

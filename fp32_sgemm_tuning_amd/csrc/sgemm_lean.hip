@@ -15,6 +15,15 @@
 
 namespace sgemm_mi355x {
 
+// A buffer offset past every descriptor's range (ranges are below 2^31).
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+// Byte range of a buffer descriptor: the distance to the operand's end,
+// clamped to [0, 2^31 - 1] (an empty range makes every load out of range).
+__device__ __forceinline__ int buffer_range(long bytes) {
+    return (int)(bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes));
+}
+
 // s_waitcnt with vmcnt 0 and the other counters at their maximum
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -34,14 +43,29 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 //     and a scalar offset that advances one tile per iteration;
 //   - the tile loop is unrolled by the two LDS stages, so every fragment read
 //     address is a loop-invariant register plus an immediate.
-// Whole tiles only, and every byte offset inside A's row block and B's
-// column block must fit the 31-bit buffer range (BM * lda + K and K * ldb
-// below 2^29 elements); other cases take the guarded kernels.
+// Every byte offset inside A's row block and B's column block must fit the
+// 31-bit buffer range (BM * lda + K and K * ldb below 2^29 elements).
+//
+// EDGE = false: M, N and K are whole numbers of tiles.
+// EDGE = true: any M and N, and any K of at least BK, with K and N multiples
+// of 4.  The hardware range check of buffer loads does the edges without a
+// branch in the K loop (it compares the per-lane offset with the
+// descriptor's range; the scalar offset is not part of the check):
+//   - A's descriptor ends at the last element of A, so rows at or past M are
+//     out of range;
+//   - B chunks at or past column N get an offset beyond every range;
+//   - a K remainder kr = K % BK is taken as the first tile, k in [0, kr), whose
+//     chunks at k >= kr get that offset too, and the full tiles follow from
+//     k = kr on descriptors based there.
+// Out-of-range loads access no memory and deposit zeros, which is what the
+// K remainder needs (A's padding past column K may hold anything).  Rows past
+// M and columns past N only reach accumulators that the guarded epilogue
+// does not store.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lean_kernel(Args p) {
-    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, true, false>;
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, true, EDGE>;
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int KH = T::KH;
     static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
@@ -73,25 +97,60 @@ sgemm_lean_kernel(Args p) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int q = (i * NWAVES + wave) * 64 + lane;
-        offB[i] = 4u * (unsigned)((q / T::B_CPR) * (int)p.ldb + 4 * (q % T::B_CPR));
+        const int col = 4 * (q % T::B_CPR);
+        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)((q / T::B_CPR) * (int)p.ldb + col);
     }
-    // Buffer descriptors at the block's first row of A and first column of
-    // B; the per-tile advance goes in the scalar offset of each load.
+    // K remainder taken first (EDGE only): tile 0 covers k in [0, kr), full
+    // tiles follow from k = kr.
+    const int kr = EDGE ? p.K % BK : 0;
+    const int tail = kr != 0;
+    const int ntiles = p.K / BK + tail;
+
+    // Buffer descriptors for the full tiles, from the block's first row of A
+    // and first column of B at k = kr to the last element of each operand
+    // (clamped to [0, 2^31 - 1]; the offsets in use stay below the cap); the
+    // per-tile advance goes in the scalar offset of each load.
+    const long endA = 4L * ((long)(p.M - 1 - m0) * p.lda + p.K);
+    const long endB = 4L * ((long)(p.K - 1) * p.ldb + p.N - n0);
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.A + (long)m0 * p.lda), (short)0, 0x7fffffff, 0x00020000);
+        (void *)(p.A + (long)m0 * p.lda + kr), (short)0, buffer_range(endA - 4L * kr), 0x00020000);
     const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.B + n0), (short)0, 0x7fffffff, 0x00020000);
+        (void *)(p.B + (long)kr * p.ldb + n0), (short)0, buffer_range(endB - 4L * kr * p.ldb), 0x00020000);
     const unsigned stepA = 4u * BK, stepB = 4u * BK * (unsigned)p.ldb;
 
-    // (The explicit int conversions matter: with the array element passed
-    // as is, the host pass drops the kernel and its launch stub.)
+    // Loads of tile t >= tail (a full tile).  (The explicit int conversions
+    // matter: with the array element passed as is, the host pass drops the
+    // kernel and its launch stub.)
     auto issue_one = [&](int t, float *stage, int i) {
+        const unsigned tf = (unsigned)max(t - tail, 0);
         if (i < NA)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)(stage + (i * NWAVES + wave) * 256), 16,
-                                                     (int)offA[i], (int)(t * stepA), 0, 0);
+                                                     (int)offA[i], (int)(tf * stepA), 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * 256),
-                                                     16, (int)offB[i - NA], (int)(t * stepB), 0, 0);
+                                                     16, (int)offB[i - NA], (int)(tf * stepB), 0, 0);
+    };
+    // Loads of the K remainder tile, on descriptors based at k = 0.
+    auto issue_remainder = [&](float *stage) {
+        const __amdgpu_buffer_rsrc_t rA0 = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.A + (long)m0 * p.lda), (short)0, buffer_range(endA), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.B + n0), (short)0, buffer_range(endB), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            int m, c;
+            ALayout<BK>::inverse((i * NWAVES + wave) * 64 + lane, m, c);
+            const unsigned off = 4 * c < kr ? offA[i] : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA0, (lds_ptr)(stage + (i * NWAVES + wave) * 256), 16, (int)off,
+                                                     0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int q = (i * NWAVES + wave) * 64 + lane;
+            const unsigned off = q / T::B_CPR < kr ? offB[i] : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, (lds_ptr)(stage + BM * BK + (i * NWAVES + wave) * 256), 16,
+                                                     (int)off, 0, 0, 0);
+        }
     };
 
     f32x4 acc[T::MI][T::NJ][4];
@@ -102,7 +161,6 @@ sgemm_lean_kernel(Args p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int ntiles = p.K / BK;
     typename T::Frags F[2];
 
     // one K tile held in stage SC (compile time); loads of tile t+1 go to
@@ -138,8 +196,12 @@ sgemm_lean_kernel(Args p) {
     };
 
     if (ntiles > 0) {
+        if (tail) {
+            issue_remainder(lds);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NA + NB; ++i) issue_one(0, lds, i);
+            for (int i = 0; i < NA + NB; ++i) issue_one(0, lds, i);
+        }
         wait_vmcnt0();
         __syncthreads();
         T::read_frags(lds, wm, wn, lane, 0, F[0]);
@@ -157,10 +219,17 @@ sgemm_lean_kernel(Args p) {
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
 void launch_lean(const Args &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
-    if (a.beta == 0.0f)
-        hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, false>), grid, block, 0, stream, a);
+    const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
+#define SGEMM_LAUNCH(Z, E) \
+    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E>), grid, block, 0, stream, a)
+    if (edge) {
+        if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
+        else SGEMM_LAUNCH(false, true);
+    } else {
+        if (a.beta == 0.0f) SGEMM_LAUNCH(true, false);
+        else SGEMM_LAUNCH(false, false);
+    }
+#undef SGEMM_LAUNCH
 }
 
 // Launchers called from the C ABI's translation unit.

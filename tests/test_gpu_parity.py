@@ -73,6 +73,12 @@ SHAPES = [
     # whole 256x256 tiles with one, two and five 64-deep K tiles (odd and even
     # counts of the two-stage loop)
     (256, 256, 64), (256, 512, 128), (512, 768, 320),
+    # K a whole number of 64-deep tiles, N a multiple of 4, M and N ragged:
+    # the direct-to-LDS kernels' edge path (out-of-range buffer loads)
+    (200, 300, 256), (17, 260, 320), (1, 4, 64), (520, 772, 192),
+    # K a multiple of 4 but not of the K tile: the K remainder tile (with
+    # NaN in A's padding columns when lda > K)
+    (256, 256, 100), (130, 200, 36), (300, 260, 1028), (256, 128, 68),
 ]
 
 
