@@ -14,6 +14,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "sgemm.h"
 #include "sgemm_kernels.hpp"
 
@@ -27,6 +31,7 @@ void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t stream);
 void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t stream);
 void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t stream);
+void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 }  // namespace sgemm_mi355x
 
 using namespace sgemm_mi355x;
@@ -48,12 +53,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Knobs {
     int group_m = 8;
     int xcd_remap = 1;
+    int splitk = 0;         // 0: automatic split-K factor; >= 1: forced
     Knobs() {
         if (const char *s = getenv("SGEMM_GROUP_M")) {
             int v = atoi(s);
             if (v >= 1 && v <= 1024) group_m = v;
         }
         if (const char *s = getenv("SGEMM_XCD_REMAP")) xcd_remap = atoi(s) != 0;
+        if (const char *s = getenv("SGEMM_SPLITK")) {
+            int v = atoi(s);
+            if (v >= 0 && v <= 64) splitk = v;
+        }
     }
 };
 
@@ -152,6 +162,88 @@ void launch_dtl(const Args &a, hipStream_t stream) {
 
 typedef void (*Launcher)(const Args &, hipStream_t);
 
+// ---------------------------------------------------------------------------
+// Split-K (128x128x32 lean kernel).  Below about one tile per compute unit a
+// 128x128 tile grid leaves most of the 256 CUs idle while each busy CU walks
+// all of K; splitting K over S blocks per tile multiplies the parallelism by
+// S at the price of writing and re-reading S partial tiles.
+constexpr int kSplitBM = 128, kSplitBN = 128, kSplitBK = 32;
+constexpr long kSplitMaxBlocks = 512;   // splits x tiles
+constexpr long kSplitMaxTiles = 256;    // tiles with counters
+constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxBlocks * kSplitBM * kSplitBN * sizeof(float);
+constexpr size_t kSplitWorkspaceBytes = kSplitPartialBytes + kSplitMaxTiles * sizeof(unsigned);
+
+// Split factor for an M x N x K problem on 128x128x32 tiles (1 = no split):
+// up to 512 blocks in all (two per CU), at least four K tiles per split, at
+// most 16 splits, only while the tile grid has fewer than 160 tiles
+// (measured: 144 tiles gain from three splits, 180 tiles lose with two or
+// four).  SGEMM_SPLITK forces a factor (clamped to the same limits) for
+// sweeps.
+int choose_splits(int M, int N, int K) {
+    const long tiles = ceil_div(M, kSplitBM) * ceil_div(N, kSplitBN);
+    const long kt = ceil_div(K, kSplitBK);
+    if (tiles > kSplitMaxTiles || kt < 2) return 1;
+    long s;
+    if (knobs().splitk > 0) {
+        s = knobs().splitk;
+    } else {
+        if (tiles >= 160) return 1;
+        s = kSplitMaxBlocks / tiles;
+        if (s > kt / 4) s = kt / 4;
+        if (s > 16) s = 16;
+    }
+    if (s > kt) s = kt;
+    if (s * tiles > kSplitMaxBlocks) s = kSplitMaxBlocks / tiles;
+    return s < 1 ? 1 : (int)s;
+}
+
+// One split-K workspace per (device, stream), allocated on first use and
+// kept until the process ends: calls on one stream run in order, so they
+// can share it; calls on different streams get different ones.  The
+// counters are zeroed once, on the stream, before the first kernel that uses
+// them; every split-K kernel leaves them zero.
+struct Workspace {
+    float *partials = nullptr;
+    unsigned *counters = nullptr;
+};
+
+int get_workspace(hipStream_t stream, Workspace &out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Workspace> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, stream);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+        out = it->second;
+        return SGEMM_STATUS_OK;
+    }
+    void *mem = nullptr;
+    e = hipMalloc(&mem, kSplitWorkspaceBytes);
+    if (e != hipSuccess) return record_hip_error(e, "hipMalloc (split-K workspace)");
+    Workspace w;
+    w.partials = static_cast<float *>(mem);
+    w.counters = reinterpret_cast<unsigned *>(static_cast<char *>(mem) + kSplitPartialBytes);
+    e = hipMemsetAsync(w.counters, 0, kSplitMaxTiles * sizeof(unsigned), stream);
+    if (e != hipSuccess) {
+        (void)hipFree(mem);
+        return record_hip_error(e, "hipMemsetAsync (split-K counters)");
+    }
+    cache[key] = w;
+    out = w;
+    return SGEMM_STATUS_OK;
+}
+
+// The split variant: split-K when a.splits > 1, else the plain lean kernel.
+void launch_lean_splitk_or_plain(const Args &a, hipStream_t stream) {
+    if (a.splits > 1)
+        launch_lean_splitk_128x128x32_w2x2(a, a.splits, stream);
+    else
+        launch_lean_128x128x32_w2x2(a, stream);
+}
+
 // The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
 // be whole tiles) and byte offsets within A's row block and B's column block
 // below 2^31 (the buffer descriptors' range); other shapes go to FALLBACK, a
@@ -176,6 +268,7 @@ struct VariantDesc {
     int bm, bn, bk;
     bool needs_vec;
     Launcher launch;
+    bool split_k = false;   // may split K (needs the workspace)
 };
 
 // Ids 0..2 are the stable ones named in sgemm.h; the rest are tile shapes
@@ -214,6 +307,8 @@ const VariantDesc kVariants[] = {
      launch_lean_or<128, 256, 32, launch_lean_128x256x32_w2x4, launch_db<128, 256, 32, 2, 4, true>>},
     {"lean_256x256x32_w4x2", 256, 256, 32, true,
      launch_lean_or<256, 256, 32, launch_lean_256x256x32_w4x2, launch_db<256, 256, 32, 4, 2, true>>},
+    {"lean_128x128x32_w2x2_splitk", 128, 128, 32, true,
+     launch_lean_or<128, 128, 32, launch_lean_splitk_or_plain, launch_sec<128, 128, 32, 2, 2, true>>, true},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -223,16 +318,15 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // that are not whole tiles.  Measured against the other lean tiles and the
 // earlier kernels at 1024^3 to 8192^3 (bench.py --sweep): best or within
 // 0.3% of the best at every size from 2048^3 up.
-constexpr int kVec = 24;  // lean_128x128x32_w2x2
+constexpr int kVec = 24;       // lean_128x128x32_w2x2
+constexpr int kVecSplit = 28;  // lean_128x128x32_w2x2_splitk: the same tile, K split over blocks
 
 // Automatic choice: 32-bit access unless the operands allow 128-bit access.
 // No HIP call.
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
-    (void)M;
-    (void)N;
     if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_VARIANT_DB128_SCALAR;
-    return kVec;
+    return choose_splits(M, N, K) > 1 ? kVecSplit : kVec;
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -264,6 +358,25 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.tiles_n = (int)tiles_n;
     a.group_m = knobs().group_m;
     a.xcd_remap = knobs().xcd_remap;
+    a.splits = 1;
+    a.ws = nullptr;
+    a.counters = nullptr;
+    if (d.split_k) {
+        const int splits = choose_splits(M, N, K);
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        // A stream under graph capture cannot allocate or clear memory, so
+        // K is split only outside capture.
+        const bool capturing = hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+                               cap != hipStreamCaptureStatusNone;
+        if (splits > 1 && !capturing) {
+            Workspace w;
+            const int ws = get_workspace(reinterpret_cast<hipStream_t>(stream), w);
+            if (ws != SGEMM_STATUS_OK) return ws;
+            a.splits = splits;
+            a.ws = w.partials;
+            a.counters = w.counters;
+        }
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours

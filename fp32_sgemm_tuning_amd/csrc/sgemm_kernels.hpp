@@ -37,6 +37,12 @@ struct Args {
     int tiles_m, tiles_n;   // block tiles along M and N
     int group_m;            // tile rows per raster group (>= 1)
     int xcd_remap;          // 1: give each XCD a contiguous run of tiles
+    // split-K only: blocks per tile along K (the launch's gridDim.y), partial
+    // tiles (splits x BM x BN floats per tile) and one arrival counter per
+    // tile, zero between calls
+    int splits;
+    float *ws;
+    unsigned *counters;
 };
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {

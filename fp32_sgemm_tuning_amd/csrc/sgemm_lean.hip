@@ -28,6 +28,66 @@ __device__ __forceinline__ int buffer_range(long bytes) {
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Split-K hand-off of one output tile.  Every block stores its partial
+// accumulators to workspace slot blockIdx.y of the tile (chunk-major: chunk c
+// of thread t at c * NT + t, so each store and load instruction covers one
+// contiguous run) and takes a ticket from the tile's counter.  Returns false
+// for all blocks but the last; the last one reads the other partials, leaves
+// their sum in split order in acc and resets the counter for the next call.
+//
+// Every XCD has its own L2, so the partials move at device scope: the
+// stores and loads carry the device-scope cache policy (sc1, the encoding
+// the compiler uses for relaxed agent-scope atomics), each block waits for
+// its stores to complete before the barrier that precedes its ticket, and
+// the ticket is a device-scope atomic.  No cache-wide write-back or
+// invalidate is needed, so other blocks keep their cached A and B.
+template <class T>
+__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, f32x4 (&acc)[T::MI][T::NJ][4]) {
+    constexpr int TILE = T::NT * T::MI * T::NJ * 16;   // floats per partial tile (BM x BN)
+    constexpr int kDeviceScope = 16;                    // cache policy bits: sc1
+    const int S = gridDim.y, y = blockIdx.y;
+    const __amdgpu_buffer_rsrc_t slab = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.ws + (long)tile_id * S * TILE), (short)0, S * TILE * 4, 0x00020000);
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < T::NJ; ++nj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(acc[mi][nj][i], slab,
+                                                       (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16, y * TILE * 4,
+                                                       kDeviceScope);
+    wait_vmcnt0();
+    __syncthreads();
+    __shared__ unsigned ticket;
+    if (tid == 0) ticket = atomicAdd(p.counters + tile_id, 1u);
+    __syncthreads();
+    if (ticket != (unsigned)(S - 1)) return false;
+    f32x4 sum[T::MI][T::NJ][4];
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < T::NJ; ++nj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 x = s == y ? acc[mi][nj][i]
+                                           : __builtin_amdgcn_raw_buffer_load_b128(
+                                                 slab, (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16,
+                                                 s * TILE * 4, kDeviceScope);
+                    sum[mi][nj][i] = s == 0 ? x : sum[mi][nj][i] + x;
+                }
+    }
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < T::NJ; ++nj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = sum[mi][nj][i];
+    if (tid == 0) atomicExch(p.counters + tile_id, 0u);
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // Lean direct-to-LDS kernel: the section schedule of sgemm_dtl_kernel with
 // the per-tile address arithmetic taken out of the K loop.
@@ -61,8 +121,16 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // K remainder needs (A's padding past column K may hold anything).  Rows past
 // M and columns past N only reach accumulators that the guarded epilogue
 // does not store.
+//
+// SPLIT = true: split-K.  gridDim.y = S blocks share each output tile; block
+// y takes K tiles [y * T / S, (y + 1) * T / S) of the T tiles (the remainder
+// tile, if any, goes to y = 0), writes its partial tile to the workspace and
+// counts itself in on the tile's counter.  The block that arrives last adds
+// the S partials in the fixed order y = 0 .. S-1 (so the result does not
+// depend on arrival order), resets the counter and runs the epilogue.  No
+// block waits for another.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lean_kernel(Args p) {
     using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, true, EDGE>;
@@ -105,6 +173,13 @@ sgemm_lean_kernel(Args p) {
     const int kr = EDGE ? p.K % BK : 0;
     const int tail = kr != 0;
     const int ntiles = p.K / BK + tail;
+    // K tiles of this block: all of them, or this split's share
+    int t_begin = 0, t_end = ntiles;
+    if constexpr (SPLIT) {
+        const int S = gridDim.y, y = blockIdx.y;
+        t_begin = (int)((long)ntiles * y / S);
+        t_end = (int)((long)ntiles * (y + 1) / S);
+    }
 
     // Buffer descriptors for the full tiles, from the block's first row of A
     // and first column of B at k = kr to the last element of each operand
@@ -170,7 +245,7 @@ sgemm_lean_kernel(Args p) {
         constexpr int SN = 1 - SC;
         const float *cs = lds + SC * T::STAGE;
         float *ns = lds + SN * T::STAGE;
-        const int t_next = min(t + 1, ntiles - 1);
+        const int t_next = min(t + 1, t_end - 1);
         auto section = [&](auto hc) {
             constexpr int h = decltype(hc)::value;
             constexpr int g_lo = h * PER < NA + NB ? h * PER : NA + NB;
@@ -195,33 +270,36 @@ sgemm_lean_kernel(Args p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (ntiles > 0) {
-        if (tail) {
+    if (t_end > t_begin) {
+        if (tail && t_begin == 0) {
             issue_remainder(lds);
         } else {
 #pragma unroll
-            for (int i = 0; i < NA + NB; ++i) issue_one(0, lds, i);
+            for (int i = 0; i < NA + NB; ++i) issue_one(t_begin, lds, i);
         }
         wait_vmcnt0();
         __syncthreads();
         T::read_frags(lds, wm, wn, lane, 0, F[0]);
-        int t = 0;
-        for (; t + 1 < ntiles; t += 2) {
+        int t = t_begin;
+        for (; t + 1 < t_end; t += 2) {
             tile(t, IntC<0>{});
             tile(t + 1, IntC<1>{});
         }
-        if (t < ntiles) tile(t, IntC<0>{});
+        if (t < t_end) tile(t, IntC<0>{});
+    }
+    if constexpr (SPLIT) {
+        if (!split_reduce<T>(p, tm * p.tiles_n + tn, tid, acc)) return;
     }
     T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
 }
 
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
-void launch_lean(const Args &a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT>
+void launch_lean(const Args &a, int splits, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits), block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E>), grid, block, 0, stream, a)
+    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT>), grid, block, 0, stream, a)
     if (edge) {
         if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
         else SGEMM_LAUNCH(false, true);
@@ -233,10 +311,15 @@ void launch_lean(const Args &a, hipStream_t stream) {
 }
 
 // Launchers called from the C ABI's translation unit.
-void launch_lean_128x128x64_w2x2(const Args &a, hipStream_t s) { launch_lean<128, 128, 64, 2, 2>(a, s); }
-void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t s) { launch_lean<128, 128, 32, 2, 2>(a, s); }
-void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 128, 32, 4, 2>(a, s); }
-void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t s) { launch_lean<128, 256, 32, 2, 4>(a, s); }
-void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 256, 32, 4, 2>(a, s); }
+void launch_lean_128x128x64_w2x2(const Args &a, hipStream_t s) { launch_lean<128, 128, 64, 2, 2, false>(a, 1, s); }
+void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t s) { launch_lean<128, 128, 32, 2, 2, false>(a, 1, s); }
+void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 128, 32, 4, 2, false>(a, 1, s); }
+void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t s) { launch_lean<128, 256, 32, 2, 4, false>(a, 1, s); }
+void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 256, 32, 4, 2, false>(a, 1, s); }
+// Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
+// splits * tiles * 128 * 128 floats and tiles zeroed counters.
+void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t s) {
+    launch_lean<128, 128, 32, 2, 2, true>(a, splits, s);
+}
 
 }  // namespace sgemm_mi355x

@@ -129,10 +129,26 @@ def test_variant_selection_by_shape():
     lean = [v for v in capi.all_variants() if capi.sgemm_variant_name(v) == "lean_128x128x32_w2x2"]
     assert len(lean) == 1
     for (M, N, K) in [(64, 64, 64), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
-                      (4096, 4000, 100), (4, 4, 4)]:
+                      (4096, 4000, 100), (4, 4, 4), (1024, 1024, 64)]:
         v = sel(M, N, K, AL, K, AL, N, 0.0, AL, N)
         assert v == lean[0], (M, N, K, v)
         assert _needs_vec(v)
+
+
+def test_split_k_selection():
+    """Aligned operands whose 128x128 tile grid has fewer than 160 tiles and
+    whose K gives at least two splits of four 32-deep tiles take the split-K
+    variant; larger grids or short K do not."""
+    sel = capi.sgemm_select_variant
+    name = lambda v: capi.sgemm_variant_name(v)
+    for (M, N, K) in [(1024, 1024, 1024), (512, 512, 512), (64, 64, 4096), (1024, 1024, 8192),
+                      (1536, 1536, 1536)]:
+        assert name(sel(M, N, K, AL, K, AL, N, 0.0, AL, N)) == "lean_128x128x32_w2x2_splitk", (M, N, K)
+    for (M, N, K) in [(2048, 2048, 2048), (1024, 1024, 128), (4096, 4096, 4096), (64, 64, 64),
+                      (1920, 1536, 1024)]:
+        assert name(sel(M, N, K, AL, K, AL, N, 0.0, AL, N)) == "lean_128x128x32_w2x2", (M, N, K)
+    # unaligned operands never split
+    assert sel(1024, 1024, 1023, AL, 1023, AL, 1024, 0.0, AL, 1024) == capi.SGEMM_VARIANT_DB128_SCALAR
 
 
 def test_variant_selection_by_alignment():
