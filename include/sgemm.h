@@ -23,12 +23,22 @@
  * A, B and C are 16-byte aligned and lda, ldb, ldc are multiples of 4 the
  * library uses 128-bit loads and stores, otherwise 32-bit ones.
  *
- * Ownership and execution.  The caller owns every buffer.  The library
- * allocates nothing and keeps no per-call state.  A call validates its
- * arguments, enqueues one kernel on `stream` (a hipStream_t; NULL is the
+ * Ownership and execution.  The caller owns A, B and C.  A call validates
+ * its arguments, enqueues one kernel on `stream` (a hipStream_t; NULL is the
  * null stream) and returns without synchronising.  Calls are thread-safe
- * and deterministic: the same inputs give the same bits (no atomics, no
- * split-K reduction).
+ * and deterministic: the same inputs give the same bits.
+ *
+ * Workspace.  Small tile grids split K over several workgroups per output
+ * tile (split-K).  Those calls use a workspace that the library allocates
+ * with hipMalloc on the first such call for each (device, stream) pair and
+ * keeps until the process ends: 32 MiB of partial tiles and 256 tile
+ * counters, the counters cleared once on the stream before first use and
+ * left cleared by every call.  Calls on one stream share the workspace in
+ * stream order; calls on different streams use different workspaces.  The
+ * partial tiles of a tile are added in a fixed order, so split-K results are
+ * deterministic too.  On a stream under graph capture K is never split (no
+ * allocation happens during capture).  An allocation failure returns
+ * SGEMM_STATUS_HIP_ERROR before anything is enqueued.
  *
  * Errors.  Arguments are checked before anything is enqueued, so a call that
  * returns an error has written nothing.  M == 0 or N == 0 returns
@@ -55,18 +65,21 @@ extern "C" {
 #define SGEMM_VARIANT_DB128_VEC 1           /* 128x128x32 tile, double-buffered LDS, 128-bit loads/stores (needs alignment) */
 #define SGEMM_VARIANT_DB128_SCALAR 2        /* the same tile with 32-bit loads/stores (any alignment) */
 /* Ids 3 .. sgemm_num_variants()-1 are further kernels and tile shapes with
- * 128-bit access (double-buffered, section-pipelined, direct-to-LDS and the
- * lean direct-to-LDS kernels), kept for tile sweeps; sgemm_variant_name() and
- * sgemm_variant_info() describe them.  The direct-to-LDS kernels run on whole
- * tiles only and use the guarded kernel of the same tile otherwise. */
+ * 128-bit access (double-buffered, section-pipelined, direct-to-LDS, lean
+ * direct-to-LDS, and the split-K form of the lean 128x128x32 kernel), kept
+ * for tile sweeps; sgemm_variant_name() and sgemm_variant_info() describe
+ * them.  The direct-to-LDS kernels take the shapes they support (whole tiles,
+ * or for the lean kernels K >= the K tile with K and N multiples of 4) and
+ * use the guarded kernel of the same tile otherwise. */
 
 /*
  * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
  * the alignment class: 32-bit access (variant SGEMM_VARIANT_DB128_SCALAR)
  * unless the operands allow 128-bit access; then the lean direct-to-LDS
- * kernel on 128x128x32 block tiles, with its guarded fallback where the shape
- * is not a whole number of tiles.  beta == 0 selects an epilogue that never
- * reads C.  Returns SGEMM_STATUS_*.
+ * kernel on 128x128x32 block tiles (with its guarded fallback for shapes it
+ * does not take), splitting K when the tile grid has fewer than 160 tiles
+ * and K holds at least eight 32-deep tiles.  beta == 0 selects an epilogue
+ * that never reads C.  Returns SGEMM_STATUS_*.
  */
 int sgemm(int M, int N, int K, float alpha,
           const float *A, int lda,
