@@ -23,8 +23,8 @@ SGEMM_VARIANT_DB128_SCALAR = 2
 
 # Every symbol include/sgemm.h declares.
 EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
-           "sgemm_variant_name", "sgemm_variant_info", "sgemm_strerror", "sgemm_last_hip_error",
-           "sgemm_version")
+           "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
+           "sgemm_last_hip_error", "sgemm_version")
 
 _lib = None
 
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     lib.sgemm_variant_info.argtypes = [i, ip, ip, ip, ip]
     lib.sgemm_variant_info.restype = i
+    lib.sgemm_split_factor.argtypes = [i, i, i, i]
+    lib.sgemm_split_factor.restype = i
     lib.sgemm_strerror.argtypes = [i]
     lib.sgemm_strerror.restype = cp
     lib.sgemm_last_hip_error.argtypes = []
@@ -103,6 +105,10 @@ def sgemm_variant_info(variant):
     v = [ctypes.c_int(0) for _ in range(4)]
     st = load().sgemm_variant_info(variant, *[ctypes.byref(x) for x in v])
     return (st,) + tuple(x.value for x in v)
+
+
+def sgemm_split_factor(variant, M, N, K):
+    return load().sgemm_split_factor(variant, M, N, K)
 
 
 def all_variants():

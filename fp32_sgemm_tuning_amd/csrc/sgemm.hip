@@ -31,7 +31,15 @@ void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t stream);
 void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t stream);
 void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t stream);
+void launch_lean_64x64x32_w4x1(const Args &a, hipStream_t stream);
+void launch_lean_64x64x64_w4x1(const Args &a, hipStream_t stream);
+void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t stream);
+void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
+void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
+void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
+void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
+void launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 }  // namespace sgemm_mi355x
 
 using namespace sgemm_mi355x;
@@ -94,7 +102,8 @@ bool vec_ok(int K, const float *A, int lda, const float *B, int ldb, float beta,
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
-void launch_db(const Args &a, hipStream_t stream) {
+void launch_db(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
@@ -111,7 +120,8 @@ void launch_db(const Args &a, hipStream_t stream) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
-void launch_pipe(const Args &a, hipStream_t stream) {
+void launch_pipe(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % 16);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
@@ -128,7 +138,8 @@ void launch_pipe(const Args &a, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
-void launch_sec(const Args &a, hipStream_t stream) {
+void launch_sec(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
@@ -147,7 +158,8 @@ void launch_sec(const Args &a, hipStream_t stream) {
 // Direct-to-LDS kernel for whole tiles; shapes that are not whole tiles
 // fall back to the section-pipelined kernel of the same tile (guarded loads).
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES>
-void launch_dtl(const Args &a, hipStream_t stream) {
+void launch_dtl(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
     const bool whole = !(a.M % BM) && !(a.N % BN) && !(a.K % BK);
     if (!whole) {
         launch_sec<BM, BN, BK, WAVES_M, WAVES_N, true>(a, stream);
@@ -163,37 +175,39 @@ void launch_dtl(const Args &a, hipStream_t stream) {
 typedef void (*Launcher)(const Args &, hipStream_t);
 
 // ---------------------------------------------------------------------------
-// Split-K (128x128x32 lean kernel).  Below about one tile per compute unit a
-// 128x128 tile grid leaves most of the 256 CUs idle while each busy CU walks
-// all of K; splitting K over S blocks per tile multiplies the parallelism by
-// S at the price of writing and re-reading S partial tiles.
-constexpr int kSplitBM = 128, kSplitBN = 128, kSplitBK = 32;
-constexpr long kSplitMaxBlocks = 512;   // splits x tiles
-constexpr long kSplitMaxTiles = 256;    // tiles with counters
-constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxBlocks * kSplitBM * kSplitBN * sizeof(float);
+// Split-K (lean kernels).  A tile grid with fewer blocks than about two per
+// compute unit leaves CUs idle while each busy CU walks all of K; splitting
+// K over S blocks per tile multiplies the parallelism by S at the price of
+// writing and re-reading S partial tiles.  Every split-capable lean tile has
+// four waves, so the limits below count blocks alike for all of them.
+constexpr long kSplitMaxBlocks = 512;                    // splits x tiles (two blocks per CU)
+constexpr long kSplitMaxTiles = 4096;                    // tiles with counters
+constexpr size_t kSplitPartialBytes = 32u << 20;         // 512 partial tiles of 128x128
 constexpr size_t kSplitWorkspaceBytes = kSplitPartialBytes + kSplitMaxTiles * sizeof(unsigned);
 
-// Split factor for an M x N x K problem on 128x128x32 tiles (1 = no split):
-// up to 512 blocks in all (two per CU), at least four K tiles per split, at
-// most 16 splits, only while the tile grid has fewer than 160 tiles
-// (measured: 144 tiles gain from three splits, 180 tiles lose with two or
-// four).  SGEMM_SPLITK forces a factor (clamped to the same limits) for
-// sweeps.
-int choose_splits(int M, int N, int K) {
-    const long tiles = ceil_div(M, kSplitBM) * ceil_div(N, kSplitBN);
-    const long kt = ceil_div(K, kSplitBK);
+// Split factor for an M x N x K problem on bm x bn x bk tiles (1 = no
+// split): up to 512 blocks in all, at least four K tiles per split, at most
+// 16 splits, only while the tile grid has fewer than 160 tiles (measured on
+// 128x128 tiles: 144 tiles gain from three splits, 180 tiles lose with two
+// or four).  SGEMM_SPLITK forces a factor (clamped to the same limits and
+// to the workspace) for sweeps.
+int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
+    const long tiles = ceil_div(M, bm) * ceil_div(N, bn);
+    const long kt = ceil_div(K, bk);
+    const long fit = (long)(kSplitPartialBytes / ((size_t)bm * bn * sizeof(float)));
     if (tiles > kSplitMaxTiles || kt < 2) return 1;
     long s;
     if (knobs().splitk > 0) {
         s = knobs().splitk;
+        if (s * tiles > fit) s = fit / tiles;
     } else {
         if (tiles >= 160) return 1;
         s = kSplitMaxBlocks / tiles;
         if (s > kt / 4) s = kt / 4;
         if (s > 16) s = 16;
+        if (s * tiles > kSplitMaxBlocks) s = kSplitMaxBlocks / tiles;
     }
     if (s > kt) s = kt;
-    if (s * tiles > kSplitMaxBlocks) s = kSplitMaxBlocks / tiles;
     return s < 1 ? 1 : (int)s;
 }
 
@@ -236,18 +250,21 @@ int get_workspace(hipStream_t stream, Workspace &out) {
     return SGEMM_STATUS_OK;
 }
 
-// The split variant: split-K when a.splits > 1, else the plain lean kernel.
-void launch_lean_splitk_or_plain(const Args &a, hipStream_t stream) {
+// A split-capable variant: split-K when a.splits > 1, else the plain lean
+// kernel of the same tile.
+typedef void (*SplitLauncher)(const Args &, int, hipStream_t);
+template <SplitLauncher SPLIT, Launcher PLAIN>
+void launch_split_or_plain(const Args &a, hipStream_t stream) {
     if (a.splits > 1)
-        launch_lean_splitk_128x128x32_w2x2(a, a.splits, stream);
+        SPLIT(a, a.splits, stream);
     else
-        launch_lean_128x128x32_w2x2(a, stream);
+        PLAIN(a, stream);
 }
 
 // The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
 // be whole tiles) and byte offsets within A's row block and B's column block
 // below 2^31 (the buffer descriptors' range); other shapes go to FALLBACK, a
-// guarded kernel of the same tile.
+// guarded kernel.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_or(const Args &a, hipStream_t stream) {
     const bool shape = a.K >= BK && !(a.K % 4) && !(a.N % 4);
@@ -259,7 +276,8 @@ void launch_lean_or(const Args &a, hipStream_t stream) {
         FALLBACK(a, stream);
 }
 
-void launch_simple(const Args &a, hipStream_t stream) {
+void launch_simple(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, 64, 64);
     hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream, a);
 }
 
@@ -308,25 +326,67 @@ const VariantDesc kVariants[] = {
     {"lean_256x256x32_w4x2", 256, 256, 32, true,
      launch_lean_or<256, 256, 32, launch_lean_256x256x32_w4x2, launch_db<256, 256, 32, 4, 2, true>>},
     {"lean_128x128x32_w2x2_splitk", 128, 128, 32, true,
-     launch_lean_or<128, 128, 32, launch_lean_splitk_or_plain, launch_sec<128, 128, 32, 2, 2, true>>, true},
+     launch_lean_or<128, 128, 32,
+                    launch_split_or_plain<launch_lean_splitk_128x128x32_w2x2, launch_lean_128x128x32_w2x2>,
+                    launch_sec<128, 128, 32, 2, 2, true>>,
+     true},
+    // smaller tiles for small problems (guarded fallback: the 128x128x32
+    // section-pipelined kernel)
+    {"lean_64x64x32_w4x1", 64, 64, 32, true,
+     launch_lean_or<64, 64, 32, launch_lean_64x64x32_w4x1, launch_sec<128, 128, 32, 2, 2, true>>},
+    {"lean_64x64x32_w4x1_splitk", 64, 64, 32, true,
+     launch_lean_or<64, 64, 32, launch_split_or_plain<launch_lean_splitk_64x64x32_w4x1, launch_lean_64x64x32_w4x1>,
+                    launch_sec<128, 128, 32, 2, 2, true>>,
+     true},
+    {"lean_64x64x64_w4x1", 64, 64, 64, true,
+     launch_lean_or<64, 64, 64, launch_lean_64x64x64_w4x1, launch_sec<128, 128, 32, 2, 2, true>>},
+    {"lean_64x64x64_w4x1_splitk", 64, 64, 64, true,
+     launch_lean_or<64, 64, 64, launch_split_or_plain<launch_lean_splitk_64x64x64_w4x1, launch_lean_64x64x64_w4x1>,
+                    launch_sec<128, 128, 32, 2, 2, true>>,
+     true},
+    {"lean_64x128x32_w2x2", 64, 128, 32, true,
+     launch_lean_or<64, 128, 32, launch_lean_64x128x32_w2x2, launch_sec<128, 128, 32, 2, 2, true>>},
+    {"lean_64x128x32_w2x2_splitk", 64, 128, 32, true,
+     launch_lean_or<64, 128, 32, launch_split_or_plain<launch_lean_splitk_64x128x32_w2x2, launch_lean_64x128x32_w2x2>,
+                    launch_sec<128, 128, 32, 2, 2, true>>,
+     true},
+    {"lean_128x64x32_w4x1", 128, 64, 32, true,
+     launch_lean_or<128, 64, 32, launch_lean_128x64x32_w4x1, launch_sec<128, 128, 32, 2, 2, true>>},
+    {"lean_128x64x32_w4x1_splitk", 128, 64, 32, true,
+     launch_lean_or<128, 64, 32, launch_split_or_plain<launch_lean_splitk_128x64x32_w4x1, launch_lean_128x64x32_w4x1>,
+                    launch_sec<128, 128, 32, 2, 2, true>>,
+     true},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Variant the automatic choice uses for 128-bit operands (index into
-// kVariants): the lean direct-to-LDS kernel on 128x128x32 tiles, which falls
-// back to the guarded section-pipelined kernel of the same tile on shapes
-// that are not whole tiles.  Measured against the other lean tiles and the
-// earlier kernels at 1024^3 to 8192^3 (bench.py --sweep): best or within
-// 0.3% of the best at every size from 2048^3 up.
+// Variants the automatic choice uses for 128-bit operands (indices into
+// kVariants).
 constexpr int kVec = 24;       // lean_128x128x32_w2x2
-constexpr int kVecSplit = 28;  // lean_128x128x32_w2x2_splitk: the same tile, K split over blocks
+constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below 160 tiles)
+constexpr int kNumCUs = 256;   // MI355X
+
+// Fill of the last wave of blocks: with t tiles spread over the CUs, the
+// busiest CU runs ceil(t / 256) tiles while the average is t / 256.
+double wave_fill(long tiles) {
+    const long rounds = ceil_div(tiles, kNumCUs);
+    return rounds > 0 ? (double)tiles / (double)(rounds * kNumCUs) : 0.0;
+}
 
 // Automatic choice: 32-bit access unless the operands allow 128-bit access.
-// No HIP call.
+// Then the lean kernel on 128x128x32 tiles or on 64x64x64 tiles: the
+// smaller tile when the 128x128 grid has fewer than 160 tiles (it then also
+// splits K below 160 of its own tiles), or when its last wave of tiles is
+// fuller by more than the 3% that the smaller tile costs in throughput at
+// full occupancy.  Measured (bench.py --sweep): 64x64x64 ahead at 768^3 to
+// 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3 and short K.  No HIP
+// call.
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
     if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_VARIANT_DB128_SCALAR;
-    return choose_splits(M, N, K) > 1 ? kVecSplit : kVec;
+    const long t128 = ceil_div(M, 128) * ceil_div(N, 128);
+    const long t64 = ceil_div(M, 64) * ceil_div(N, 64);
+    if (t128 < 160) return kVec64;
+    return wave_fill(t64) * 0.97 > wave_fill(t128) ? kVec64 : kVec;
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -362,7 +422,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.ws = nullptr;
     a.counters = nullptr;
     if (d.split_k) {
-        const int splits = choose_splits(M, N, K);
+        const int splits = choose_splits(M, N, K, d.bm, d.bn, d.bk);
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         // A stream under graph capture cannot allocate or clear memory, so
         // K is split only outside capture.
@@ -422,6 +482,14 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec) {
     if (bk) *bk = d.bk;
     if (needs_vec) *needs_vec = d.needs_vec ? 1 : 0;
     return SGEMM_STATUS_OK;
+}
+
+int sgemm_split_factor(int variant, int M, int N, int K) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    const VariantDesc &d = kVariants[variant];
+    if (!d.split_k || M == 0 || N == 0) return 1;
+    return choose_splits(M, N, K, d.bm, d.bn, d.bk);
 }
 
 const char *sgemm_strerror(int status) {

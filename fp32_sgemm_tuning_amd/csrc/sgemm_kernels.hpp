@@ -45,6 +45,17 @@ struct Args {
     unsigned *counters;
 };
 
+// Launch arguments for a kernel with block tile bm x bn.  Every launcher
+// takes its tile counts from its own tile through this, so a launcher handed
+// arguments sized for another tile (a fallback kernel) still covers C
+// exactly once and never addresses tiles past M or N.
+inline Args tiled(const Args &a, int bm, int bn) {
+    Args t = a;
+    t.tiles_m = (a.M + bm - 1) / bm;
+    t.tiles_n = (a.N + bn - 1) / bn;
+    return t;
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

@@ -295,7 +295,8 @@ sgemm_lean_kernel(Args p) {
 
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT>
-void launch_lean(const Args &a, int splits, hipStream_t stream) {
+void launch_lean(const Args &a0, int splits, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits), block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \
@@ -316,10 +317,26 @@ void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t s) { launch_lean<128
 void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 128, 32, 4, 2, false>(a, 1, s); }
 void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t s) { launch_lean<128, 256, 32, 2, 4, false>(a, 1, s); }
 void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t s) { launch_lean<256, 256, 32, 4, 2, false>(a, 1, s); }
+void launch_lean_64x64x32_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 32, 4, 1, false>(a, 1, s); }
+void launch_lean_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false>(a, 1, s); }
+void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t s) { launch_lean<64, 128, 32, 2, 2, false>(a, 1, s); }
+void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t s) { launch_lean<128, 64, 32, 4, 1, false>(a, 1, s); }
 // Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
-// splits * tiles * 128 * 128 floats and tiles zeroed counters.
+// splits * tiles * BM * BN floats and `tiles` zeroed counters.
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t s) {
     launch_lean<128, 128, 32, 2, 2, true>(a, splits, s);
+}
+void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t s) {
+    launch_lean<64, 64, 32, 4, 1, true>(a, splits, s);
+}
+void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t s) {
+    launch_lean<64, 64, 64, 4, 1, true>(a, splits, s);
+}
+void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t s) {
+    launch_lean<64, 128, 32, 2, 2, true>(a, splits, s);
+}
+void launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t s) {
+    launch_lean<128, 64, 32, 4, 1, true>(a, splits, s);
 }
 
 }  // namespace sgemm_mi355x

@@ -122,6 +122,17 @@ const char *sgemm_variant_name(int variant);
  */
 int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
 
+/*
+ * sgemm_split_factor: the number of workgroups per output tile along K
+ * (1 = no split) that sgemm_ex() with this variant would use for an
+ * M x N x K problem whose operands the variant's split-K kernel takes (see
+ * "Workspace" above; environment variable SGEMM_SPLITK = S forces S for
+ * sweeps).  Always 1 for variants without split-K.  No HIP call.  Returns
+ * the factor, SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM
+ * (negative sizes).
+ */
+int sgemm_split_factor(int variant, int M, int N, int K);
+
 /* Static text for a status code. */
 const char *sgemm_strerror(int status);
 

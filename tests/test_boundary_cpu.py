@@ -121,34 +121,62 @@ def _needs_vec(v):
     return capi.sgemm_variant_info(v)[4] == 1
 
 
-def test_variant_selection_by_shape():
-    """Aligned operands take the lean 128x128x32 direct-to-LDS variant at every
-    shape (it hands shapes that are not whole tiles to its guarded
-    fallback)."""
-    sel = capi.sgemm_select_variant
-    lean = [v for v in capi.all_variants() if capi.sgemm_variant_name(v) == "lean_128x128x32_w2x2"]
-    assert len(lean) == 1
-    for (M, N, K) in [(64, 64, 64), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
-                      (4096, 4000, 100), (4, 4, 4), (1024, 1024, 64)]:
-        v = sel(M, N, K, AL, K, AL, N, 0.0, AL, N)
-        assert v == lean[0], (M, N, K, v)
-        assert _needs_vec(v)
+def _name(v):
+    return capi.sgemm_variant_name(v)
 
 
-def test_split_k_selection():
-    """Aligned operands whose 128x128 tile grid has fewer than 160 tiles and
-    whose K gives at least two splits of four 32-deep tiles take the split-K
-    variant; larger grids or short K do not."""
-    sel = capi.sgemm_select_variant
-    name = lambda v: capi.sgemm_variant_name(v)
-    for (M, N, K) in [(1024, 1024, 1024), (512, 512, 512), (64, 64, 4096), (1024, 1024, 8192),
-                      (1536, 1536, 1536)]:
-        assert name(sel(M, N, K, AL, K, AL, N, 0.0, AL, N)) == "lean_128x128x32_w2x2_splitk", (M, N, K)
-    for (M, N, K) in [(2048, 2048, 2048), (1024, 1024, 128), (4096, 4096, 4096), (64, 64, 64),
-                      (1920, 1536, 1024)]:
-        assert name(sel(M, N, K, AL, K, AL, N, 0.0, AL, N)) == "lean_128x128x32_w2x2", (M, N, K)
-    # unaligned operands never split
-    assert sel(1024, 1024, 1023, AL, 1023, AL, 1024, 0.0, AL, 1024) == capi.SGEMM_VARIANT_DB128_SCALAR
+@pytest.mark.parametrize("shape,expected", [
+    # 128x128 grid below 160 tiles: the 64x64x64 tile (split-capable)
+    ((4, 4, 4), "lean_64x64x64_w4x1_splitk"),
+    ((64, 64, 64), "lean_64x64x64_w4x1_splitk"),
+    ((1024, 1024, 64), "lean_64x64x64_w4x1_splitk"),
+    ((1024, 1024, 1024), "lean_64x64x64_w4x1_splitk"),
+    ((1536, 1536, 1536), "lean_64x64x64_w4x1_splitk"),
+    # last wave of 128x128 tiles fuller than that of 64x64 tiles less 3%
+    ((2048, 2048, 2048), "lean_128x128x32_w2x2"),
+    ((4096, 4096, 4096), "lean_128x128x32_w2x2"),
+    ((8192, 8192, 8192), "lean_128x128x32_w2x2"),
+    ((4096, 4000, 100), "lean_128x128x32_w2x2"),
+    ((6000, 6000, 6000), "lean_128x128x32_w2x2"),
+    # a partly empty last wave of 128x128 tiles
+    ((3072, 3072, 3072), "lean_64x64x64_w4x1_splitk"),
+    ((2560, 2560, 2560), "lean_64x64x64_w4x1_splitk"),
+    ((1920, 1536, 1024), "lean_64x64x64_w4x1_splitk"),
+])
+def test_variant_selection_by_shape(shape, expected):
+    """Aligned operands take a lean variant chosen by the fill of the last
+    wave of tiles over the 256 CUs."""
+    M, N, K = shape
+    v = capi.sgemm_select_variant(M, N, K, AL, K, AL, N, 0.0, AL, N)
+    assert _name(v) == expected, (shape, _name(v))
+    assert _needs_vec(v)
+
+
+def test_split_factors():
+    """K is split only below 160 tiles of the variant's own tile, by at most
+    16, into splits of at least four K tiles, within 512 workgroups."""
+    names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
+    v128, v64 = names["lean_128x128x32_w2x2_splitk"], names["lean_64x64x64_w4x1_splitk"]
+    f = capi.sgemm_split_factor
+    assert f(v128, 1024, 1024, 1024) == 8          # 64 tiles, 32 K tiles
+    assert f(v128, 512, 512, 512) == 4             # 16 tiles, 16 K tiles
+    assert f(v128, 64, 64, 4096) == 16
+    assert f(v128, 1536, 1536, 1536) == 3          # 144 tiles
+    assert f(v128, 1920, 1536, 1024) == 1          # 180 tiles
+    assert f(v128, 1024, 1024, 128) == 1           # 4 K tiles
+    assert f(v64, 1024, 1024, 1024) == 1           # 256 tiles of 64x64
+    assert f(v64, 512, 512, 2048) == 8             # 64 tiles, 32 K tiles of 64
+    assert f(v64, 256, 256, 8192) == 16
+    for v in (v128, v64):
+        for (M, N, K) in [(100, 100, 10000), (300, 200, 500), (1, 1, 100000)]:
+            s = f(v, M, N, K)
+            st, bm, bn, bk, _ = capi.sgemm_variant_info(v)
+            tiles = -(-M // bm) * -(-N // bn)
+            assert 1 <= s <= 16 and s * tiles <= 512 and (s == 1 or -(-K // bk) >= 4 * s), (v, M, N, K, s)
+    # variants without split-K, bad ids, bad sizes
+    assert f(names["lean_128x128x32_w2x2"], 64, 64, 4096) == 1
+    assert f(capi.sgemm_num_variants(), 64, 64, 64) == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert f(v128, -1, 64, 64) == capi.SGEMM_STATUS_INVALID_DIM
 
 
 def test_variant_selection_by_alignment():

@@ -160,8 +160,8 @@ SPLIT_SHAPES = [(1024, 1024, 1024), (512, 512, 512), (64, 64, 4096), (1024, 1024
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLIT_SHAPES])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (-0.75, 1.25)], ids=["b0", "b1"])
 def test_split_k(shape, ab):
-    """Small tile grids with long K take the split-K variant automatically;
-    the result matches the oracle element by element, repeats bit for bit
+    """The 128x128x32 split-K variant on small tile grids with long K splits
+    K; the result matches the oracle element by element, repeats bit for bit
     (partials are added in split order, whichever block arrives last), and
     agrees with the unsplit kernel of the same tile within the tolerance."""
     torch = torch_cuda()
@@ -170,12 +170,12 @@ def test_split_k(shape, ab):
     A, B, Cin = make_problem(M, N, K, seed=M + N + K, dist="normal", with_c=True)
     dA, dB = to_dev(A, torch), to_dev(B, torch)
     C0 = to_dev(Cin, torch)
-    v = capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, beta, C0.data_ptr(), N)
-    assert capi.sgemm_variant_name(v) == "lean_128x128x32_w2x2_splitk", (shape, v)
+    v = [x for x in ALL_VARIANTS if capi.sgemm_variant_name(x) == "lean_128x128x32_w2x2_splitk"][0]
+    assert capi.sgemm_split_factor(v, M, N, K) > 1, shape
     outs = []
     for _ in range(3):
         c = C0.clone()
-        sgemm(dA, dB, c, alpha=alpha, beta=beta)
+        sgemm(dA, dB, c, alpha=alpha, beta=beta, variant=v)
         outs.append(c)
     plain = C0.clone()
     sgemm(dA, dB, plain, alpha=alpha, beta=beta, variant=24)
@@ -190,8 +190,10 @@ def test_split_k(shape, ab):
 def test_split_k_on_two_streams():
     """Two split-K calls in flight on two streams use separate workspaces."""
     torch = torch_cuda()
-    A, B, _ = make_problem(1024, 1024, 2048, 77)
-    A2, B2, _ = make_problem(1024, 1024, 2048, 78)
+    A, B, _ = make_problem(512, 512, 4096, 77)
+    A2, B2, _ = make_problem(512, 512, 4096, 78)
+    v = capi.sgemm_select_variant(512, 512, 4096, 16, 4096, 16, 512, 0.0, 16, 512)
+    assert capi.sgemm_split_factor(v, 512, 512, 4096) > 1
     dA, dB, dA2, dB2 = (to_dev(x, torch) for x in (A, B, A2, B2))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -207,3 +209,26 @@ def test_split_k_on_two_streams():
     check_close(outs[0][1].cpu().numpy(), oracle.sgemm_ref(A2, B2), "stream 2")
     for c1, c2 in outs[1:]:
         assert torch.equal(c1, outs[0][0]) and torch.equal(c2, outs[0][1])
+
+
+SPLIT_VARIANTS = [v for v in ALL_VARIANTS if capi.sgemm_variant_name(v).endswith("_splitk")]
+
+
+@pytest.mark.parametrize("variant", SPLIT_VARIANTS)
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (130, 260, 2000), (256, 256, 4100), (200, 100, 512)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_split_k_variants_forced(variant, shape):
+    """Every split-K tile shape, forced: oracle parity with beta != 0 and
+    bit-identical repeats."""
+    torch = torch_cuda()
+    M, N, K = shape
+    A, B, Cin = make_problem(M, N, K, seed=3 * M + N + K, dist="normal", with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    C0 = to_dev(Cin, torch)
+    c1, c2 = C0.clone(), C0.clone()
+    sgemm(dA, dB, c1, alpha=0.5, beta=-1.5, variant=variant)
+    sgemm(dA, dB, c2, alpha=0.5, beta=-1.5, variant=variant)
+    torch.cuda.synchronize()
+    check_close(c1.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=0.5, beta=-1.5),
+                f"{capi.sgemm_variant_name(variant)} {shape}")
+    assert torch.equal(c1, c2)
