@@ -35,6 +35,8 @@ void launch_lean_64x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
+void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
+void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
@@ -276,6 +278,18 @@ void launch_lean_or(const Args &a, hipStream_t stream) {
         FALLBACK(a, stream);
 }
 
+// The lean kernel with 4-byte loads takes any alignment and any K >= BK, with
+// byte offsets below 2^31 as above; other shapes go to FALLBACK.
+template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
+void launch_lean_dw_or(const Args &a, hipStream_t stream) {
+    const long lim = 0x7fffffffL;
+    const bool fits = 4L * ((long)(BM - 1) * a.lda + a.K) < lim && 4L * ((long)a.K * a.ldb + BN) < lim;
+    if (a.K >= BK && fits)
+        LEAN(a, stream);
+    else
+        FALLBACK(a, stream);
+}
+
 void launch_simple(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
     hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream, a);
@@ -356,6 +370,12 @@ const VariantDesc kVariants[] = {
      launch_lean_or<128, 64, 32, launch_split_or_plain<launch_lean_splitk_128x64x32_w4x1, launch_lean_128x64x32_w4x1>,
                     launch_sec<128, 128, 32, 2, 2, true>>,
      true},
+    // any alignment (4-byte direct loads; guarded fallback: the 32-bit
+    // double-buffered kernel)
+    {"lean_dw_128x128x32_w2x2", 128, 128, 32, false,
+     launch_lean_dw_or<128, 128, 32, launch_lean_dw_128x128x32_w2x2, launch_db<128, 128, 32, 2, 2, false>>},
+    {"lean_dw_64x64x64_w4x1", 64, 64, 64, false,
+     launch_lean_dw_or<64, 64, 64, launch_lean_dw_64x64x64_w4x1, launch_db<128, 128, 32, 2, 2, false>>},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -363,6 +383,8 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // kVariants).
 constexpr int kVec = 24;       // lean_128x128x32_w2x2
 constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below 160 tiles)
+constexpr int kAny = 37;       // lean_dw_128x128x32_w2x2: 4-byte loads, any alignment
+constexpr int kAny64 = 38;     // lean_dw_64x64x64_w4x1
 constexpr int kNumCUs = 256;   // MI355X
 
 // Fill of the last wave of blocks: with t tiles spread over the CUs, the
@@ -372,21 +394,25 @@ double wave_fill(long tiles) {
     return rounds > 0 ? (double)tiles / (double)(rounds * kNumCUs) : 0.0;
 }
 
-// Automatic choice: 32-bit access unless the operands allow 128-bit access.
-// Then the lean kernel on 128x128x32 tiles or on 64x64x64 tiles: the
-// smaller tile when the 128x128 grid has fewer than 160 tiles (it then also
-// splits K below 160 of its own tiles), or when its last wave of tiles is
+// Tile choice of the automatic dispatch: the 64x64 tile when the 128x128
+// grid has fewer than 160 tiles, or when the last wave of 64x64 tiles is
 // fuller by more than the 3% that the smaller tile costs in throughput at
 // full occupancy.  Measured (bench.py --sweep): 64x64x64 ahead at 768^3 to
-// 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3 and short K.  No HIP
-// call.
-int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
-                 const float *C, int ldc) {
-    if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return SGEMM_VARIANT_DB128_SCALAR;
+// 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3 and short K.
+bool prefer_64(int M, int N) {
     const long t128 = ceil_div(M, 128) * ceil_div(N, 128);
     const long t64 = ceil_div(M, 64) * ceil_div(N, 64);
-    if (t128 < 160) return kVec64;
-    return wave_fill(t64) * 0.97 > wave_fill(t128) ? kVec64 : kVec;
+    return t128 < 160 || wave_fill(t64) * 0.97 > wave_fill(t128);
+}
+
+// Automatic choice: the lean kernel with 16-byte loads when the operands
+// allow them (the 64x64x64 form splits K below 160 of its tiles), else the
+// lean kernel with 4-byte loads; the tile by prefer_64().  No HIP call.
+int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
+                 const float *C, int ldc) {
+    const bool small = prefer_64(M, N);
+    if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return small ? kAny64 : kAny;
+    return small ? kVec64 : kVec;
 }
 
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,

@@ -24,6 +24,24 @@ __device__ __forceinline__ int buffer_range(long bytes) {
     return (int)(bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes));
 }
 
+// One direct load per lane into LDS: 16 or 4 bytes from the buffer at
+// voffset + soffset to the LDS address of `dst` plus 16 or 4 bytes per lane.
+// (The size must be a literal at the call, hence one function per size.)
+typedef __attribute__((address_space(3))) void *lds_addr_t;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voffset, soffset, 0, 0);
+}
+template <bool DW>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
+    if constexpr (DW)
+        dma4(r, dst, voffset, soffset);
+    else
+        dma16(r, dst, voffset, soffset);
+}
+
 // s_waitcnt with vmcnt 0 and the other counters at their maximum
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -107,8 +125,14 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 // 31-bit buffer range (BM * lda + K and K * ldb below 2^29 elements).
 //
 // EDGE = false: M, N and K are whole numbers of tiles.
+// DW = false: 16-byte loads (A, B, C 16-byte aligned, leading dimensions
+// multiples of 4).  DW = true: 4-byte loads of single floats into the same
+// LDS layout and 32-bit C access, for any alignment; four times the load
+// instructions, and every edge below is exact to the element, so N and K
+// need not be multiples of 4.
+//
 // EDGE = true: any M and N, and any K of at least BK, with K and N multiples
-// of 4.  The hardware range check of buffer loads does the edges without a
+// of 4 unless DW.  The hardware range check of buffer loads does the edges without a
 // branch in the K loop (it compares the per-lane offset with the
 // descriptor's range; the scalar offset is not part of the check):
 //   - A's descriptor ends at the last element of A, so rows at or past M are
@@ -130,15 +154,18 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 // depend on arrival order), resets the counter and runs the epilogue.  No
 // block waits for another.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT, bool DW>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lean_kernel(Args p) {
-    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, true, EDGE>;
+    // DW: 4-byte loads and 32-bit C access (any alignment), else 16-byte ones
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, !DW, EDGE>;
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int KH = T::KH;
     static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
-    constexpr int NA = BM * BK / 4 / T::NT;
-    constexpr int NB = BK * BN / 4 / T::NT;
+    constexpr int EW = DW ? 1 : 4;                          // floats per lane per load
+    constexpr int LSTEP = 64 * EW;                          // floats of LDS per load instruction
+    constexpr int NA = BM * BK / EW / T::NT;
+    constexpr int NB = BK * BN / EW / T::NT;
     constexpr int NM = T::MI * T::NJ * 16;
     constexpr int NR = T::MI + 4 * T::NJ;
     constexpr int LS = KH == 4 ? 2 : 1;                     // sections carrying the loads
@@ -154,19 +181,33 @@ sgemm_lean_kernel(Args p) {
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // loop-invariant per-lane byte offsets of the direct loads
+    // Loop-invariant per-lane byte offsets of the direct loads.  Load i of a
+    // lane fills LDS unit u = (i * NWAVES + wave) * 64 + lane of the stage (a
+    // 16-byte chunk, or with DW one float of chunk u / 4); the A offset is
+    // that of the logical (row, k) the swizzled layout keeps there.
+    auto a_coords = [&](int i, int &m, int &k) {
+        const int u = (i * NWAVES + wave) * 64 + lane;
+        int c;
+        ALayout<BK>::inverse(DW ? u / 4 : u, m, c);
+        k = 4 * c + (DW ? u % 4 : 0);
+    };
+    auto b_coords = [&](int i, int &r, int &col) {
+        const int g = ((i * NWAVES + wave) * 64 + lane) * EW;     // float index in the B stage
+        r = g / BN;
+        col = g % BN;
+    };
     unsigned offA[NA], offB[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        int m, c;
-        ALayout<BK>::inverse((i * NWAVES + wave) * 64 + lane, m, c);
-        offA[i] = 4u * (unsigned)(m * (int)p.lda + 4 * c);
+        int m, k;
+        a_coords(i, m, k);
+        offA[i] = 4u * (unsigned)(m * (int)p.lda + k);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const int q = (i * NWAVES + wave) * 64 + lane;
-        const int col = 4 * (q % T::B_CPR);
-        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)((q / T::B_CPR) * (int)p.ldb + col);
+        int r, col;
+        b_coords(i, r, col);
+        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)(r * (int)p.ldb + col);
     }
     // K remainder taken first (EDGE only): tile 0 covers k in [0, kr), full
     // tiles follow from k = kr.
@@ -199,11 +240,10 @@ sgemm_lean_kernel(Args p) {
     auto issue_one = [&](int t, float *stage, int i) {
         const unsigned tf = (unsigned)max(t - tail, 0);
         if (i < NA)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)(stage + (i * NWAVES + wave) * 256), 16,
-                                                     (int)offA[i], (int)(tf * stepA), 0, 0);
+            dma<DW>(rsA, (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP), (int)offA[i], (int)(tf * stepA));
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * 256),
-                                                     16, (int)offB[i - NA], (int)(tf * stepB), 0, 0);
+            dma<DW>(rsB, (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP), (int)offB[i - NA],
+                    (int)(tf * stepB));
     };
     // Loads of the K remainder tile, on descriptors based at k = 0.
     auto issue_remainder = [&](float *stage) {
@@ -213,18 +253,17 @@ sgemm_lean_kernel(Args p) {
             (void *)(p.B + n0), (short)0, buffer_range(endB), 0x00020000);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            int m, c;
-            ALayout<BK>::inverse((i * NWAVES + wave) * 64 + lane, m, c);
-            const unsigned off = 4 * c < kr ? offA[i] : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA0, (lds_ptr)(stage + (i * NWAVES + wave) * 256), 16, (int)off,
-                                                     0, 0, 0);
+            int m, k;
+            a_coords(i, m, k);
+            const unsigned off = k < kr ? offA[i] : kOutOfRange;
+            dma<DW>(rA0, (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP), (int)off, 0);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int q = (i * NWAVES + wave) * 64 + lane;
-            const unsigned off = q / T::B_CPR < kr ? offB[i] : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB0, (lds_ptr)(stage + BM * BK + (i * NWAVES + wave) * 256), 16,
-                                                     (int)off, 0, 0, 0);
+            int r, col;
+            b_coords(i, r, col);
+            const unsigned off = r < kr ? offB[i] : kOutOfRange;
+            dma<DW>(rB0, (lds_ptr)(stage + BM * BK + (i * NWAVES + wave) * LSTEP), (int)off, 0);
         }
     };
 
@@ -294,13 +333,13 @@ sgemm_lean_kernel(Args p) {
 }
 
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW = false>
 void launch_lean(const Args &a0, int splits, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits), block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT>), grid, block, 0, stream, a)
+    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW>), grid, block, 0, stream, a)
     if (edge) {
         if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
         else SGEMM_LAUNCH(false, true);
@@ -321,6 +360,11 @@ void launch_lean_64x64x32_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 6
 void launch_lean_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false>(a, 1, s); }
 void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t s) { launch_lean<64, 128, 32, 2, 2, false>(a, 1, s); }
 void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t s) { launch_lean<128, 64, 32, 4, 1, false>(a, 1, s); }
+// 4-byte loads, 32-bit C access: any alignment and leading dimensions
+void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t s) {
+    launch_lean<128, 128, 32, 2, 2, false, true>(a, 1, s);
+}
+void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false, true>(a, 1, s); }
 // Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
 // splits * tiles * BM * BN floats and `tiles` zeroed counters.
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t s) {

@@ -74,12 +74,14 @@ extern "C" {
 
 /*
  * sgemm: C = alpha*A*B + beta*C (see above).  Picks the kernel variant from
- * the alignment class: 32-bit access (variant SGEMM_VARIANT_DB128_SCALAR)
- * unless the operands allow 128-bit access; then the lean direct-to-LDS
- * kernel on 128x128x32 block tiles (with its guarded fallback for shapes it
- * does not take), splitting K when the tile grid has fewer than 160 tiles
- * and K holds at least eight 32-deep tiles.  beta == 0 selects an epilogue
- * that never reads C.  Returns SGEMM_STATUS_*.
+ * the alignment class and the shape: the lean direct-to-LDS kernel with
+ * 16-byte loads when the operands allow 128-bit access, else with 4-byte
+ * loads (any alignment); on 64x64x64 block tiles when a 128x128 grid would
+ * have fewer than 160 tiles or a less full last wave over the 256 compute
+ * units, else on 128x128x32 tiles.  The 16-byte 64x64x64 form splits K when
+ * its own grid has fewer than 160 tiles.  Shapes a lean kernel does not
+ * take go to a guarded kernel.  beta == 0 selects an epilogue that never
+ * reads C.  Returns SGEMM_STATUS_*.
  */
 int sgemm(int M, int N, int K, float alpha,
           const float *A, int lda,

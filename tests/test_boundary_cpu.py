@@ -180,14 +180,18 @@ def test_split_factors():
 
 
 def test_variant_selection_by_alignment():
+    """Operands that do not allow 128-bit access take the lean kernel with
+    4-byte loads, on the tile the aligned case would use."""
     sel = capi.sgemm_select_variant
     assert _needs_vec(sel(64, 64, 64, AL, 64, AL, 64, 0.0, AL, 64))
-    assert sel(64, 64, 64, MIS, 64, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
-    assert sel(64, 64, 64, AL, 64, MIS, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
-    assert sel(64, 64, 64, AL, 64, AL, 64, 0.0, MIS, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
-    assert sel(64, 64, 64, AL, 66, AL, 64, 0.0, AL, 64) == capi.SGEMM_VARIANT_DB128_SCALAR
+    for args in [(MIS, 64, AL, 64, AL, 64), (AL, 64, MIS, 64, AL, 64), (AL, 64, AL, 64, MIS, 64),
+                 (AL, 66, AL, 64, AL, 64)]:
+        a, lda, b, ldb, c, ldc = args
+        assert _name(sel(64, 64, 64, a, lda, b, ldb, 0.0, c, ldc)) == "lean_dw_64x64x64_w4x1"
+    assert _name(sel(4096, 4096, 4095, AL, 4095, AL, 4096, 0.0, AL, 4096)) == "lean_dw_128x128x32_w2x2"
+    assert _name(sel(3072, 3072, 3071, AL, 3071, AL, 3072, 0.0, AL, 3072)) == "lean_dw_64x64x64_w4x1"
     # the ragged workload's leading dimensions (2047, 4999) are not multiples of 4
-    assert sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999) == capi.SGEMM_VARIANT_DB128_SCALAR
+    assert not _needs_vec(sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999))
     assert sel(-1, 4, 4, AL, 4, AL, 4, 0.0, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM
 
 

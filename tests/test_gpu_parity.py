@@ -104,17 +104,26 @@ def test_variant_shapes(variant, shape, ab):
     check_close(dC.cpu().numpy(), ref, f"variant {variant} {shape} {ab}")
 
 
-@pytest.mark.parametrize("variant", [capi.SGEMM_VARIANT_SIMPLE, capi.SGEMM_VARIANT_DB128_SCALAR])
-def test_unaligned_views(variant):
-    """Odd leading dimensions and base pointers 4 bytes off 16-byte alignment."""
+ANY_ALIGN_VARIANTS = [v for v in ALL_VARIANTS if capi.sgemm_variant_info(v)[4] == 0]
+UNALIGNED_SHAPES = [(203, 157, 301), (130, 67, 77), (1, 3, 129), (300, 129, 64), (256, 256, 256),
+                    (129, 131, 1001)]
+
+
+@pytest.mark.parametrize("variant", ANY_ALIGN_VARIANTS)
+@pytest.mark.parametrize("shape", UNALIGNED_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_unaligned_views(variant, shape):
+    """Odd leading dimensions and base pointers 4 bytes off 16-byte alignment,
+    with K and N not multiples of 4 (the 4-byte direct-load kernels' exact
+    edges) and NaN in every padding element."""
     torch = torch_cuda()
-    M, N, K = 203, 157, 301
+    M, N, K = shape
     A, B, Cin = make_problem(M, N, K, 31, dist="normal", with_c=True)
     dA, _ = padded_device(A, K + 3, torch, offset=1)
     dB, _ = padded_device(B, N + 5, torch, offset=3)
     dC, bufC = padded_device(Cin, N + 1, torch, offset=1)
-    assert capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K + 3, dB.data_ptr(), N + 5, 0.75,
-                                     dC.data_ptr(), N + 1) == capi.SGEMM_VARIANT_DB128_SCALAR
+    auto = capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K + 3, dB.data_ptr(), N + 5, 0.75,
+                                     dC.data_ptr(), N + 1)
+    assert capi.sgemm_variant_info(auto)[4] == 0
     sgemm(dA, dB, dC, alpha=1.25, beta=0.75, variant=variant)
     torch.cuda.synchronize()
     ref = oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=0.75)
