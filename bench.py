@@ -13,7 +13,8 @@ from HIP events recorded on the stream the kernel is launched on.  Prints
 one JSON line.
 
 --sweep times the given variant ids (comma separated; -1 = the automatic
-choice, "mm" = torch.mm in FP32 for context) on problems of the given sizes
+choice, "mm" = torch.mm in FP32 for context, "op:TN" and the like = sgemm_op
+with the operands stored transposed as named) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike, and prints one JSON line per (size, variant) with the
 median kernel time.  It is the evidence behind the automatic tile choice.
@@ -92,6 +93,18 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
         rows = r1
         if dt < target_seconds / 8:
             step *= 2
+    # the same oracle on one thread, over a small leading slab (about a tenth
+    # of the time budget), for the per-core rate
+    oracle.set_threads(1)
+    one_spent, one_rows = 0.0, 0
+    while one_spent < target_seconds / 10 and one_rows < w.M:
+        r_end = min(one_rows + 8, w.M)
+        t0 = time.perf_counter()
+        oracle.sgemm_ref(A[one_rows:r_end], B, alpha=w.alpha, beta=w.beta)
+        one_spent += time.perf_counter() - t0
+        one_rows = r_end
+    oracle.set_threads(threads)
+    one_rate = 2.0 * one_rows * w.N * w.K / one_spent / 1e9 if one_spent > 0 else None
     return {
         "value": flop / spent / 1e12,
         "unit": "TFLOP/s",
@@ -100,9 +113,24 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
         "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, {flop / 1e9:.1f} GFLOP) of the same "
                   f"problem, fp64 oracle, {spent:.1f} s",
         "seconds": spent,
+        "single_thread_gflops": one_rate,
+        "single_thread_sample": f"rows 0..{one_rows - 1}, {one_spent:.2f} s",
+        "cpu_model": cpu_model(),
+        "nproc": os.cpu_count(),
         "parity_on_sample_max_err_over_tol": max_ratio,
         "parity_on_sample_ok": bool(max_ratio <= 1.0),
     }
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def parse_shape(text):
@@ -120,7 +148,7 @@ def sweep(variants, sizes, rounds):
 
     import torch
 
-    from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm
+    from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm, sgemm_op
     from fp32_sgemm_tuning_amd.inputs import make_problem
     torch.backends.cuda.matmul.allow_tf32 = False
     capi.load()
@@ -131,9 +159,18 @@ def sweep(variants, sizes, rounds):
         flop = 2 * M * N * K
         reps = max(5, min(200, int(2e11 / max(flop, 1))))
 
+        stored = {}
+        for v in variants:
+            if isinstance(v, str) and v.startswith("op:"):
+                ta, tb = v[3] == "T", v[4] == "T"
+                stored[v] = (dA.t().contiguous() if ta else dA, dB.t().contiguous() if tb else dB, ta, tb)
+
         def run(v):
             if v == "mm":
                 torch.mm(dA, dB, out=dC)
+            elif v in stored:
+                sa, sb, ta, tb = stored[v]
+                sgemm_op(sa, sb, dC, trans_a=ta, trans_b=tb)
             else:
                 sgemm(dA, dB, dC, variant=None if v == -1 else v)
         usable = []
@@ -162,6 +199,8 @@ def sweep(variants, sizes, rounds):
             ms = statistics.median(times[v])
             if v == "mm":
                 name = "torch.mm fp32"
+            elif v in stored:
+                name = "sgemm_op " + v[3:5]
             elif v == -1:
                 name = "auto:" + capi.sgemm_variant_name(capi.sgemm_select_variant(
                     M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dC.data_ptr(), N))
@@ -193,7 +232,7 @@ def main():
         sys.exit(2)
 
     if args.sweep is not None:
-        variants = [v if v == "mm" else int(v) for v in args.sweep.split(",")]
+        variants = [v if v == "mm" or v.startswith("op:") else int(v) for v in args.sweep.split(",")]
         sweep(variants, [parse_shape(x) for x in args.sweep_sizes.split(",")], args.rounds)
         return
 

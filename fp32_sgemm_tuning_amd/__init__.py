@@ -7,7 +7,7 @@ HIP stream.  PyTorch only supplies device memory and streams.
 """
 from . import capi
 
-__all__ = ["sgemm", "SgemmError", "capi", "variant_names"]
+__all__ = ["sgemm", "sgemm_op", "SgemmError", "capi", "variant_names"]
 
 
 class SgemmError(RuntimeError):
@@ -72,3 +72,65 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
 
 def variant_names():
     return [capi.sgemm_variant_name(v) for v in range(capi.sgemm_num_variants())]
+
+
+def _mat(t, name):
+    """(rows, cols, ld) of a row-major matrix view, or of each matrix of a
+    3-D batch view (then also the batch stride)."""
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() == 2:
+        return t.shape[0], t.shape[1], _ld(t, name), 0
+    if t.dim() == 3:
+        rows, cols = t.shape[1], t.shape[2]
+        if cols > 1 and t.stride(2) != 1:
+            raise ValueError(f"{name} must have unit column stride (row-major)")
+        ld = t.stride(1) if rows > 1 or t.stride(1) >= max(cols, 1) else max(cols, 1)
+        return rows, cols, ld, t.stride(0) if t.shape[0] > 1 else 0
+    raise ValueError(f"{name} must be 2-D or 3-D")
+
+
+def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C with op(X) = X or X^T, row-major;
+    returns C.
+
+    A and B are the stored matrices: with trans_a, A is [K,M]; with trans_b,
+    B is [N,K].  3-D tensors ([batch, rows, cols], any batch stride, one of A
+    and B may have batch 1 to be shared) run as one strided batch.
+    """
+    import torch
+    batched = A.dim() == 3 or B.dim() == 3 or (C is not None and C.dim() == 3)
+    ra, ca, lda, sa = _mat(A, "A")
+    rb, cb, ldb, sb = _mat(B, "B")
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
+    batch = max(A.shape[0] if A.dim() == 3 else 1, B.shape[0] if B.dim() == 3 else 1)
+    for t, name in ((A, "A"), (B, "B")):
+        if t.dim() == 3 and t.shape[0] not in (1, batch):
+            raise ValueError(f"{name} has batch {t.shape[0]}, expected 1 or {batch}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((batch, M, N) if batched else (M, N), dtype=torch.float32, device=A.device)
+    rc, cc, ldc, sc = _mat(C, "C")
+    if (rc, cc) != (M, N) or (C.dim() == 3 and C.shape[0] != batch):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(batch, M, N) if batched else (M, N)}")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    op_a = capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N
+    op_b = capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N
+    with torch.cuda.device(A.device):
+        if batched:
+            st = capi.sgemm_strided_batched(op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda, sa,
+                                            B.data_ptr(), ldb, sb, float(beta), C.data_ptr(), ldc, sc, batch,
+                                            s.cuda_stream)
+        else:
+            st = capi.sgemm_op(op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                               float(beta), C.data_ptr(), ldc, s.cuda_stream)
+    if st != capi.SGEMM_STATUS_OK:
+        raise SgemmError(st)
+    return C

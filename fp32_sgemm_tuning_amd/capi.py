@@ -15,6 +15,10 @@ SGEMM_STATUS_NULL_POINTER = -2
 SGEMM_STATUS_HIP_ERROR = -3
 SGEMM_STATUS_INVALID_VARIANT = -4
 SGEMM_STATUS_UNSUPPORTED = -5
+SGEMM_STATUS_INVALID_OP = -6
+
+SGEMM_OP_N = 0
+SGEMM_OP_T = 1
 
 SGEMM_VARIANT_AUTO = -1
 SGEMM_VARIANT_SIMPLE = 0
@@ -24,7 +28,8 @@ SGEMM_VARIANT_DB128_SCALAR = 2
 # Every symbol include/sgemm.h declares.
 EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
-           "sgemm_last_hip_error", "sgemm_version")
+           "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
+           "sgemm_cm_strided_batched")
 
 _lib = None
 
@@ -66,6 +71,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     lib.sgemm_variant_info.argtypes = [i, ip, ip, ip, ip]
     lib.sgemm_variant_info.restype = i
+    ll = ctypes.c_longlong
+    op_args = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
+    batched_args = [i, i, i, i, i, f, vp, i, ll, vp, i, ll, f, vp, i, ll, i, vp]
+    for name, args in (("sgemm_op", op_args), ("sgemm_cm", op_args),
+                       ("sgemm_strided_batched", batched_args), ("sgemm_cm_strided_batched", batched_args)):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = i
     lib.sgemm_split_factor.argtypes = [i, i, i, i]
     lib.sgemm_split_factor.restype = i
     lib.sgemm_strerror.argtypes = [i]
@@ -105,6 +117,24 @@ def sgemm_variant_info(variant):
     v = [ctypes.c_int(0) for _ in range(4)]
     st = load().sgemm_variant_info(variant, *[ctypes.byref(x) for x in v])
     return (st,) + tuple(x.value for x in v)
+
+
+def sgemm_op(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    return load().sgemm_op(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_cm(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    return load().sgemm_cm(op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch, stream):
+    return load().sgemm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc,
+                                        batch, stream)
+
+
+def sgemm_cm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch, stream):
+    return load().sgemm_cm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc,
+                                           batch, stream)
 
 
 def sgemm_split_factor(variant, M, N, K):

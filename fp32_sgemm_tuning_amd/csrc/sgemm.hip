@@ -37,6 +37,7 @@ void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
+void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
@@ -290,10 +291,20 @@ void launch_lean_dw_or(const Args &a, hipStream_t stream) {
         FALLBACK(a, stream);
 }
 
-void launch_simple(const Args &a0, hipStream_t stream) {
+void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
-    hipLaunchKernelGGL(sgemm_simple_kernel, dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch);
+    if (ta && tb)
+        hipLaunchKernelGGL((sgemm_simple_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    else if (ta)
+        hipLaunchKernelGGL((sgemm_simple_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    else if (tb)
+        hipLaunchKernelGGL((sgemm_simple_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_simple_kernel<false, false>), grid, dim3(256), 0, stream, a);
 }
+
+void launch_simple(const Args &a, hipStream_t stream) { launch_simple_general(a, false, false, 1, stream); }
 
 struct VariantDesc {
     const char *name;
@@ -386,6 +397,7 @@ constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below
 constexpr int kAny = 37;       // lean_dw_128x128x32_w2x2: 4-byte loads, any alignment
 constexpr int kAny64 = 38;     // lean_dw_64x64x64_w4x1
 constexpr int kNumCUs = 256;   // MI355X
+constexpr int kMaxBatch = 65535;  // problems per strided batch (launch grid z extent)
 
 // Fill of the last wave of blocks: with t tiles spread over the CUs, the
 // busiest CU runs ceil(t / 256) tiles while the average is t / 256.
@@ -399,9 +411,10 @@ double wave_fill(long tiles) {
 // fuller by more than the 3% that the smaller tile costs in throughput at
 // full occupancy.  Measured (bench.py --sweep): 64x64x64 ahead at 768^3 to
 // 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3 and short K.
-bool prefer_64(int M, int N) {
-    const long t128 = ceil_div(M, 128) * ceil_div(N, 128);
-    const long t64 = ceil_div(M, 64) * ceil_div(N, 64);
+// (`batch` problems of one strided batch count as batch times the tiles)
+bool prefer_64(int M, int N, long batch = 1) {
+    const long t128 = ceil_div(M, 128) * ceil_div(N, 128) * batch;
+    const long t64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
     return t128 < 160 || wave_fill(t64) * 0.97 > wave_fill(t128);
 }
 
@@ -447,6 +460,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.splits = 1;
     a.ws = nullptr;
     a.counters = nullptr;
+    a.strideA = a.strideB = a.strideC = 0;
     if (d.split_k) {
         const int splits = choose_splits(M, N, K, d.bm, d.bn, d.bk);
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -467,6 +481,72 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     d.launch(a, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip_error(e, "kernel launch");
+    return SGEMM_STATUS_OK;
+}
+
+// Transposed operands and strided batches (row-major).  op_a / op_b are
+// SGEMM_OP_N or SGEMM_OP_T; A is M x K (stored K x M when transposed), B is
+// K x N (stored N x K when transposed).  An untransposed single problem takes
+// run() and its automatic choice.  Otherwise: the lean kernel (16-byte loads
+// for untransposed aligned operands, else 4-byte loads) on the tile
+// prefer_64() picks for batch x tiles, without split-K; shapes it does not
+// take go to the plain kernel.
+int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
+                const float *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch,
+                void *stream) {
+    if ((op_a != SGEMM_OP_N && op_a != SGEMM_OP_T) || (op_b != SGEMM_OP_N && op_b != SGEMM_OP_T))
+        return SGEMM_STATUS_INVALID_OP;
+    const bool ta = op_a == SGEMM_OP_T, tb = op_b == SGEMM_OP_T;
+    if (M < 0 || N < 0 || K < 0 || batch < 0 || batch > kMaxBatch) return SGEMM_STATUS_INVALID_DIM;
+    const int need_lda = ta ? (M > 1 ? M : 1) : (K > 1 ? K : 1);
+    const int need_ldb = tb ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
+    if (lda < need_lda || ldb < need_ldb || ldc < (N > 1 ? N : 1)) return SGEMM_STATUS_INVALID_DIM;
+    if (batch > 1 && (sA < 0 || sB < 0 || (M > 0 && N > 0 && sC < (long long)(M - 1) * ldc + N)))
+        return SGEMM_STATUS_INVALID_DIM;
+    if (M == 0 || N == 0 || batch == 0) return SGEMM_STATUS_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
+    if (!ta && !tb && batch == 1)
+        return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
+
+    Args a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = a.tiles_n = 0;   // set by each launcher from its tile
+    a.group_m = knobs().group_m;
+    a.xcd_remap = knobs().xcd_remap;
+    a.splits = 1;
+    a.ws = nullptr;
+    a.counters = nullptr;
+    a.strideA = batch > 1 ? (long)sA : 0;
+    a.strideB = batch > 1 ? (long)sB : 0;
+    a.strideC = batch > 1 ? (long)sC : 0;
+
+    const bool tile64 = prefer_64(M, N, batch);
+    const int bm = tile64 ? 64 : 128, bn = bm, bk = tile64 ? 64 : 32;
+    const bool strides4 = batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0);
+    const bool vec = !ta && !tb && strides4 && vec_ok(K, A, lda, B, ldb, beta, C, ldc) && K % 4 == 0 && N % 4 == 0;
+    const long lim = 0x7fffffffL;
+    const long spanA = ta ? (long)K * lda + bm : (long)(bm - 1) * lda + K;
+    const long spanB = tb ? (long)bn * ldb + K : (long)K * ldb + bn;
+    const bool lean = K >= bk && 4L * spanA < lim && 4L * spanB < lim;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (lean)
+        launch_lean_general(a, tile64, !vec, ta, tb, batch, s);
+    else
+        launch_simple_general(a, ta, tb, batch, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
@@ -510,6 +590,34 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec) {
     return SGEMM_STATUS_OK;
 }
 
+int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream) {
+    return run_general(op_a, op_b, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, stream);
+}
+
+int sgemm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda,
+                          long long stride_a, const float *B, int ldb, long long stride_b, float beta, float *C,
+                          int ldc, long long stride_c, int batch, void *stream) {
+    return run_general(op_a, op_b, M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b, beta, C, ldc, stride_c, batch,
+                       stream);
+}
+
+// Column-major (BLAS) calls: a column-major matrix is the row-major storage
+// of its transpose, so C = op(A) op(B) in column-major storage is the
+// row-major product C^T = op(B)^T op(A)^T: the operands trade places, and so
+// do M and N and the two ops.
+int sgemm_cm(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream) {
+    return run_general(op_b, op_a, N, M, K, alpha, B, ldb, 0, A, lda, 0, beta, C, ldc, 0, 1, stream);
+}
+
+int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda,
+                             long long stride_a, const float *B, int ldb, long long stride_b, float beta, float *C,
+                             int ldc, long long stride_c, int batch, void *stream) {
+    return run_general(op_b, op_a, N, M, K, alpha, B, ldb, stride_b, A, lda, stride_a, beta, C, ldc, stride_c, batch,
+                       stream);
+}
+
 int sgemm_split_factor(int variant, int M, int N, int K) {
     if (variant < 0 || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
     if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
@@ -526,6 +634,7 @@ const char *sgemm_strerror(int status) {
         case SGEMM_STATUS_HIP_ERROR: return "HIP runtime error";
         case SGEMM_STATUS_INVALID_VARIANT: return "unknown kernel variant";
         case SGEMM_STATUS_UNSUPPORTED: return "variant needs 16-byte aligned pointers and leading dimensions";
+        case SGEMM_STATUS_INVALID_OP: return "operation code is neither SGEMM_OP_N nor SGEMM_OP_T";
         default: return "unknown status";
     }
 }

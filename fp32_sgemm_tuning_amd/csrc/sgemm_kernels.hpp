@@ -43,7 +43,18 @@ struct Args {
     int splits;
     float *ws;
     unsigned *counters;
+    // strided batch (lean and plain kernels): problem z = blockIdx.z uses
+    // A + z * strideA, B + z * strideB, C + z * strideC (elements)
+    long strideA, strideB, strideC;
 };
+
+// Move the operand pointers to problem blockIdx.z of a strided batch.
+__device__ __forceinline__ void batch_offset(Args &p) {
+    const long z = blockIdx.z;
+    p.A += z * p.strideA;
+    p.B += z * p.strideB;
+    p.C += z * p.strideC;
+}
 
 // Launch arguments for a kernel with block tile bm x bn.  Every launcher
 // takes its tile counts from its own tile through this, so a launcher handed
@@ -90,10 +101,15 @@ __device__ __forceinline__ void tile_coords(const Args &p, int &tm, int &tn) {
 // global load a guarded 32-bit load with zero fill, every store guarded.  The
 // shape of "Matmul I", section 6 (load, barrier, multiply, barrier), with the
 // per-thread multiply-add replaced by MFMA.  Four waves in a 2x2 grid, each
-// owning a 32x32 sub-tile (2x2 MFMA tiles).
+// owning a 32x32 sub-tile (2x2 MFMA tiles).  TA / TB: A is stored as A^T
+// ([K][M], element (i,k) at A[k*lda + i]) / B as B^T ([N][K], element (k,j)
+// at B[j*ldb + k]).  Strided batches by blockIdx.z.  It is also the fallback
+// of the lean kernels for transposed or batched problems they do not take.
 // ---------------------------------------------------------------------------
-static __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
     constexpr int BM = 64, BN = 64, BK = 16;
+    batch_offset(p);
     __shared__ float As[BM][BK + 1];
     __shared__ float Bs[BK][BN + 1];
 
@@ -112,12 +128,12 @@ static __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
         for (int e = tid; e < BM * BK; e += 256) {
             const int r = e / BK, c = e % BK;
             const int gi = m0 + r, gk = k0 + c;
-            As[r][c] = (gi < p.M && gk < p.K) ? p.A[(long)gi * p.lda + gk] : 0.0f;
+            As[r][c] = (gi < p.M && gk < p.K) ? p.A[TA ? (long)gk * p.lda + gi : (long)gi * p.lda + gk] : 0.0f;
         }
         for (int e = tid; e < BK * BN; e += 256) {
             const int r = e / BN, c = e % BN;
             const int gk = k0 + r, gj = n0 + c;
-            Bs[r][c] = (gk < p.K && gj < p.N) ? p.B[(long)gk * p.ldb + gj] : 0.0f;
+            Bs[r][c] = (gk < p.K && gj < p.N) ? p.B[TB ? (long)gj * p.ldb + gk : (long)gk * p.ldb + gj] : 0.0f;
         }
         __syncthreads();
         for (int kk = 0; kk < BK; kk += 4) {

@@ -121,30 +121,40 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 //     and a scalar offset that advances one tile per iteration;
 //   - the tile loop is unrolled by the two LDS stages, so every fragment read
 //     address is a loop-invariant register plus an immediate.
-// Every byte offset inside A's row block and B's column block must fit the
-// 31-bit buffer range (BM * lda + K and K * ldb below 2^29 elements).
+// Every byte offset inside the block's part of A and B must fit the 31-bit
+// buffer range (BM * lda + K and K * ldb, or for transposed operands
+// K * lda + BM and BN * ldb + K, below 2^29 elements).
 //
-// EDGE = false: M, N and K are whole numbers of tiles.
 // DW = false: 16-byte loads (A, B, C 16-byte aligned, leading dimensions
 // multiples of 4).  DW = true: 4-byte loads of single floats into the same
 // LDS layout and 32-bit C access, for any alignment; four times the load
 // instructions, and every edge below is exact to the element, so N and K
 // need not be multiples of 4.
 //
-// EDGE = true: any M and N, and any K of at least BK, with K and N multiples
-// of 4 unless DW.  The hardware range check of buffer loads does the edges without a
-// branch in the K loop (it compares the per-lane offset with the
-// descriptor's range; the scalar offset is not part of the check):
-//   - A's descriptor ends at the last element of A, so rows at or past M are
-//     out of range;
-//   - B chunks at or past column N get an offset beyond every range;
+// TA / TB (DW only): A stored transposed ([K][M], element (m, k) at
+// k * lda + m) / B stored transposed ([N][K], element (k, n) at n * ldb + k).
+// Each lane's 4-byte load picks the element that the unchanged LDS layout
+// keeps at its position, so fragments, MFMAs and epilogue stay the same; the
+// loads of one instruction then come from up to 32 rows of the stored
+// operand instead of one.
+//
+// EDGE = false: M, N and K are whole numbers of tiles.  EDGE = true: any M
+// and N, and any K of at least BK, with K and N multiples of 4 unless DW.
+// The hardware range check of buffer loads does the edges without a branch
+// in the K loop (it compares the per-lane offset with the descriptor's
+// range; the scalar offset is not part of the check):
+//   - each descriptor ends at its operand's last element;
+//   - elements of rows past M or columns past N get an offset beyond every
+//     range (set once, before the K loop);
 //   - a K remainder kr = K % BK is taken as the first tile, k in [0, kr), whose
-//     chunks at k >= kr get that offset too, and the full tiles follow from
+//     elements at k >= kr get that offset too, and the full tiles follow from
 //     k = kr on descriptors based there.
 // Out-of-range loads access no memory and deposit zeros, which is what the
 // K remainder needs (A's padding past column K may hold anything).  Rows past
 // M and columns past N only reach accumulators that the guarded epilogue
 // does not store.
+//
+// Strided batches: problem blockIdx.z, on pointers moved by the strides.
 //
 // SPLIT = true: split-K.  gridDim.y = S blocks share each output tile; block
 // y takes K tiles [y * T / S, (y + 1) * T / S) of the T tiles (the remainder
@@ -154,9 +164,12 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 // depend on arrival order), resets the counter and runs the epilogue.  No
 // block waits for another.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT, bool DW>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT, bool DW, bool TA,
+          bool TB>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lean_kernel(Args p) {
+    static_assert(DW || (!TA && !TB), "transposed operands need the 4-byte loads");
+    batch_offset(p);
     // DW: 4-byte loads and 32-bit C access (any alignment), else 16-byte ones
     using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, !DW, EDGE>;
     constexpr int NWAVES = WAVES_M * WAVES_N;
@@ -196,18 +209,24 @@ sgemm_lean_kernel(Args p) {
         r = g / BN;
         col = g % BN;
     };
+    // Element (m, k) of the A tile is at m * lda + k from the tile's corner,
+    // or k * lda + m when A is stored transposed (TA); likewise (k, n) of B at
+    // k * ldb + n, or n * ldb + k (TB).  Rows past M and columns past N get
+    // an offset beyond every range (EDGE).
     unsigned offA[NA], offB[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         int m, k;
         a_coords(i, m, k);
-        offA[i] = 4u * (unsigned)(m * (int)p.lda + k);
+        const int e = TA ? k * (int)p.lda + m : m * (int)p.lda + k;
+        offA[i] = (EDGE && m0 + m >= p.M) ? kOutOfRange : 4u * (unsigned)e;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         int r, col;
         b_coords(i, r, col);
-        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)(r * (int)p.ldb + col);
+        const int e = TB ? col * (int)p.ldb + r : r * (int)p.ldb + col;
+        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)e;
     }
     // K remainder taken first (EDGE only): tile 0 covers k in [0, kr), full
     // tiles follow from k = kr.
@@ -226,13 +245,18 @@ sgemm_lean_kernel(Args p) {
     // and first column of B at k = kr to the last element of each operand
     // (clamped to [0, 2^31 - 1]; the offsets in use stay below the cap); the
     // per-tile advance goes in the scalar offset of each load.
-    const long endA = 4L * ((long)(p.M - 1 - m0) * p.lda + p.K);
-    const long endB = 4L * ((long)(p.K - 1) * p.ldb + p.N - n0);
+    // (block corner at k = 0, the k stride in the stored operand, the byte
+    // distance from that corner to the operand's last element)
+    const float *cornerA = TA ? p.A + m0 : p.A + (long)m0 * p.lda;
+    const float *cornerB = TB ? p.B + (long)n0 * p.ldb : p.B + n0;
+    const long kstrideA = TA ? p.lda : 1, kstrideB = TB ? 1 : p.ldb;
+    const long endA = TA ? 4L * ((long)(p.K - 1) * p.lda + p.M - m0) : 4L * ((long)(p.M - 1 - m0) * p.lda + p.K);
+    const long endB = TB ? 4L * ((long)(p.N - 1 - n0) * p.ldb + p.K) : 4L * ((long)(p.K - 1) * p.ldb + p.N - n0);
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.A + (long)m0 * p.lda + kr), (short)0, buffer_range(endA - 4L * kr), 0x00020000);
+        (void *)(cornerA + kr * kstrideA), (short)0, buffer_range(endA - 4L * kr * kstrideA), 0x00020000);
     const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.B + (long)kr * p.ldb + n0), (short)0, buffer_range(endB - 4L * kr * p.ldb), 0x00020000);
-    const unsigned stepA = 4u * BK, stepB = 4u * BK * (unsigned)p.ldb;
+        (void *)(cornerB + kr * kstrideB), (short)0, buffer_range(endB - 4L * kr * kstrideB), 0x00020000);
+    const unsigned stepA = 4u * BK * (unsigned)kstrideA, stepB = 4u * BK * (unsigned)kstrideB;
 
     // Loads of tile t >= tail (a full tile).  (The explicit int conversions
     // matter: with the array element passed as is, the host pass drops the
@@ -247,10 +271,10 @@ sgemm_lean_kernel(Args p) {
     };
     // Loads of the K remainder tile, on descriptors based at k = 0.
     auto issue_remainder = [&](float *stage) {
-        const __amdgpu_buffer_rsrc_t rA0 = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.A + (long)m0 * p.lda), (short)0, buffer_range(endA), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.B + n0), (short)0, buffer_range(endB), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rA0 =
+            __builtin_amdgcn_make_buffer_rsrc((void *)cornerA, (short)0, buffer_range(endA), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rB0 =
+            __builtin_amdgcn_make_buffer_rsrc((void *)cornerB, (short)0, buffer_range(endB), 0x00020000);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             int m, k;
@@ -333,13 +357,16 @@ sgemm_lean_kernel(Args p) {
 }
 
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW = false>
-void launch_lean(const Args &a0, int splits, hipStream_t stream) {
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW = false, bool TA = false,
+          bool TB = false>
+void launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) {
     const Args a = tiled(a0, BM, BN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits), block(64 * WAVES_M * WAVES_N);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits, (unsigned)batch);
+    const dim3 block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW>), grid, block, 0, stream, a)
+    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW, TA, TB>), grid, block, 0, \
+                       stream, a)
     if (edge) {
         if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
         else SGEMM_LAUNCH(false, true);
@@ -365,6 +392,28 @@ void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t s) {
     launch_lean<128, 128, 32, 2, 2, false, true>(a, 1, s);
 }
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false, true>(a, 1, s); }
+// Transposed operands and strided batches: the 16-byte form for untransposed
+// operands (the caller has checked its alignment), else the 4-byte form, on
+// 64x64x64 tiles (tile64) or 128x128x32 tiles.
+template <int BM, int BN, int BK, int WM, int WN>
+void launch_lean_ops(const Args &a, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
+    if (!dw)
+        launch_lean<BM, BN, BK, WM, WN, false, false, false, false>(a, 1, s, batch);
+    else if (ta && tb)
+        launch_lean<BM, BN, BK, WM, WN, false, true, true, true>(a, 1, s, batch);
+    else if (ta)
+        launch_lean<BM, BN, BK, WM, WN, false, true, true, false>(a, 1, s, batch);
+    else if (tb)
+        launch_lean<BM, BN, BK, WM, WN, false, true, false, true>(a, 1, s, batch);
+    else
+        launch_lean<BM, BN, BK, WM, WN, false, true, false, false>(a, 1, s, batch);
+}
+void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
+    if (tile64)
+        launch_lean_ops<64, 64, 64, 4, 1>(a, dw, ta, tb, batch, s);
+    else
+        launch_lean_ops<128, 128, 32, 2, 2>(a, dw, ta, tb, batch, s);
+}
 // Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
 // splits * tiles * BM * BN floats and `tiles` zeroed counters.
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t s) {

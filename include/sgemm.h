@@ -58,6 +58,11 @@ extern "C" {
 #define SGEMM_STATUS_HIP_ERROR (-3)         /* the HIP runtime reported an error; see sgemm_last_hip_error() */
 #define SGEMM_STATUS_INVALID_VARIANT (-4)   /* sgemm_ex: no such variant */
 #define SGEMM_STATUS_UNSUPPORTED (-5)       /* sgemm_ex: variant needs 16-byte alignment the arguments lack */
+#define SGEMM_STATUS_INVALID_OP (-6)        /* an operation code other than SGEMM_OP_N / SGEMM_OP_T */
+
+/* Operation codes of the sgemm_op family. */
+#define SGEMM_OP_N 0                        /* use the stored matrix as is */
+#define SGEMM_OP_T 1                        /* use the transpose of the stored matrix */
 
 /* Variant ids for sgemm_ex(). */
 #define SGEMM_VARIANT_AUTO (-1)             /* what sgemm() picks */
@@ -123,6 +128,58 @@ const char *sgemm_variant_name(int variant);
  * be NULL.  Returns SGEMM_STATUS_OK or SGEMM_STATUS_INVALID_VARIANT.
  */
 int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
+
+/*
+ * sgemm_op: C = alpha * op(A) * op(B) + beta * C, row-major, with
+ * op(X) = X (SGEMM_OP_N) or X^T (SGEMM_OP_T).  op(A) is M x K and op(B) is
+ * K x N: with op_a = SGEMM_OP_T, A is stored K x M (element (i,k) of op(A)
+ * at A[k*lda + i], lda >= max(1,M)); with op_b = SGEMM_OP_T, B is stored
+ * N x K (element (k,j) of op(B) at B[j*ldb + k], ldb >= max(1,K)).  The
+ * untransposed forms have the layout of sgemm().  The operation is the same
+ * dot-product definition as sgemm() with the operands read through the
+ * transpose ("Matmul I: tiling and shared memory", section 1); the pages
+ * stop at packed untransposed operands and name the column-major BLAS
+ * convention only in passing.  sgemm_op(N, N, ...) is sgemm().  Transposed
+ * operands are read with 4-byte loads (any alignment).  Returns
+ * SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for another op code.
+ */
+int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream);
+
+/*
+ * sgemm_strided_batched: `batch` independent sgemm_op problems of one shape;
+ * problem z uses A + z*stride_a, B + z*stride_b and C + z*stride_c (in
+ * elements).  0 <= batch <= 65535.  stride_a and stride_b may be 0 (one
+ * operand shared by all problems); the C problems must not overlap:
+ * stride_c >= (M-1)*ldc + N when batch > 1.  One kernel launch for the whole
+ * batch (no split-K).  batch == 0 is a no-op.  Returns SGEMM_STATUS_*.
+ */
+int sgemm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha,
+                          const float *A, int lda, long long stride_a,
+                          const float *B, int ldb, long long stride_b,
+                          float beta, float *C, int ldc, long long stride_c,
+                          int batch, void *stream);
+
+/*
+ * sgemm_cm, sgemm_cm_strided_batched: the same operations on column-major
+ * matrices (the BLAS convention): element (i,j) of an r x c matrix X at
+ * X[i + j*ld], ld >= max(1,r); op(A) is M x K, op(B) is K x N, C is M x N
+ * with ldc >= max(1,M).  A column-major matrix is the row-major storage of
+ * its transpose, so these run the row-major product C^T = op(B)^T op(A)^T.
+ */
+int sgemm_cm(int op_a, int op_b, int M, int N, int K, float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc,
+             void *stream);
+int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long stride_a,
+                             const float *B, int ldb, long long stride_b,
+                             float beta, float *C, int ldc, long long stride_c,
+                             int batch, void *stream);
 
 /*
  * sgemm_split_factor: the number of workgroups per output tile along K

@@ -61,7 +61,7 @@ def test_version_and_variants(lib):
     assert capi.sgemm_last_hip_error() == ""
 
 
-@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5])
+@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5, -6])
 def test_strerror_known(status):
     s = capi.sgemm_strerror(status)
     assert s and s != "unknown status"
@@ -212,3 +212,55 @@ def test_single_hip_runtime_in_process():
     n, path, torch_dir = r.stdout.split("\n")[:3]
     assert n == "1", r.stdout
     assert os.path.realpath(path).startswith(os.path.realpath(torch_dir)), (path, torch_dir)
+
+
+def _op(fn, op_a, op_b, M, N, K, lda, ldb, ldc, A=AL, B=AL, C=AL, batch=None, strides=(0, 0, 0)):
+    if batch is None:
+        return fn(op_a, op_b, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, None)
+    sa, sb, sc = strides
+    return fn(op_a, op_b, M, N, K, 1.0, A, lda, sa, B, ldb, sb, 0.0, C, ldc, sc, batch, None)
+
+
+N_, T_ = capi.SGEMM_OP_N, capi.SGEMM_OP_T
+
+
+@pytest.mark.parametrize("op_a,op_b,lda,ldb,ok", [
+    # row-major: lda >= K (or M when A is transposed), ldb >= N (or K)
+    (N_, N_, 7, 5, True), (N_, N_, 6, 5, False), (N_, N_, 7, 4, False),
+    (T_, N_, 3, 5, True), (T_, N_, 2, 5, False),
+    (N_, T_, 7, 7, True), (N_, T_, 7, 6, False),
+    (T_, T_, 3, 7, True),
+])
+def test_op_leading_dimension_checks(op_a, op_b, lda, ldb, ok):
+    """M = 3, N = 5, K = 7: the required leading dimensions follow the stored
+    shape of each operand.  Invalid calls return before any HIP call; the
+    valid ones are not run here (no GPU), only the invalid ones are."""
+    if not ok:
+        assert _op(capi.sgemm_op, op_a, op_b, 3, 5, 7, lda, ldb, 5) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+def test_op_codes_and_batches():
+    assert _op(capi.sgemm_op, 2, N_, 3, 5, 7, 7, 5, 5) == capi.SGEMM_STATUS_INVALID_OP
+    assert _op(capi.sgemm_op, N_, -1, 3, 5, 7, 7, 5, 5) == capi.SGEMM_STATUS_INVALID_OP
+    sb = capi.sgemm_strided_batched
+    # empty batches and empty extents are no-ops, even with NULL pointers
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=0, A=None, B=None, C=None) == capi.SGEMM_STATUS_OK
+    assert _op(sb, T_, N_, 0, 5, 7, 1, 5, 5, batch=3, A=None, C=None) == capi.SGEMM_STATUS_OK
+    # negative batch, too large a batch, overlapping C problems, negative strides
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=-1) == capi.SGEMM_STATUS_INVALID_DIM
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=65536) == capi.SGEMM_STATUS_INVALID_DIM
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=2, strides=(21, 35, 14)) == capi.SGEMM_STATUS_INVALID_DIM
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=2, strides=(-21, 35, 15)) == capi.SGEMM_STATUS_INVALID_DIM
+    assert _op(sb, N_, N_, 3, 5, 7, 7, 5, 5, batch=2, strides=(21, 35, 15), C=None) == \
+        capi.SGEMM_STATUS_NULL_POINTER
+
+
+@pytest.mark.parametrize("op_a,op_b,lda,ldb,ldc,ok", [
+    # column-major: lda >= M (or K when transposed), ldb >= K (or N), ldc >= M
+    (N_, N_, 3, 7, 3, True), (N_, N_, 2, 7, 3, False), (N_, N_, 3, 6, 3, False), (N_, N_, 3, 7, 2, False),
+    (T_, N_, 7, 7, 3, True), (T_, N_, 6, 7, 3, False),
+    (N_, T_, 3, 5, 3, True), (N_, T_, 3, 4, 3, False),
+])
+def test_column_major_leading_dimension_checks(op_a, op_b, lda, ldb, ldc, ok):
+    if not ok:
+        assert _op(capi.sgemm_cm, op_a, op_b, 3, 5, 7, lda, ldb, ldc) == capi.SGEMM_STATUS_INVALID_DIM

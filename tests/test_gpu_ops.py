@@ -1,0 +1,154 @@
+"""GPU parity of the transposed, column-major and strided-batched entry
+points (sgemm_op, sgemm_cm, sgemm_strided_batched, sgemm_cm_strided_batched)
+against the oracle.  The oracle takes op(A) and op(B) as plain row-major
+arrays; the transposed and column-major storages are built from them on the
+host, inside buffers whose padding holds NaN."""
+import numpy as np
+import pytest
+
+import oracle
+from fp32_sgemm_tuning_amd import capi, sgemm_op
+from fp32_sgemm_tuning_amd.inputs import make_problem
+from gpu_util import check_close, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+N_, T_ = capi.SGEMM_OP_N, capi.SGEMM_OP_T
+OPS = [(N_, N_), (T_, N_), (N_, T_), (T_, T_)]
+OP_IDS = ["NN", "TN", "NT", "TT"]
+SHAPES = [(1, 1, 1), (7, 5, 3), (64, 64, 64), (130, 67, 77), (256, 384, 96), (300, 260, 1028),
+          (129, 131, 1001), (1024, 1024, 1024), (517, 999, 333)]
+
+
+def _stored(x, transposed, pad, torch, offset=0):
+    """Device buffer holding x (or x^T when transposed) row-major with `pad`
+    extra NaN columns per row; returns (device view of the stored matrix, ld)."""
+    s = np.ascontiguousarray(x.T if transposed else x)
+    rows, cols = s.shape
+    ld = cols + pad
+    buf = torch.full((offset + rows * ld + 8,), float("nan"), dtype=torch.float32, device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(torch.from_numpy(s).to("cuda"))
+    return view, max(ld, 1)
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+@pytest.mark.parametrize("ab", [(1.0, 0.0), (-0.75, 1.5)], ids=["b0", "b1"])
+def test_row_major_ops(ops, shape, ab):
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    alpha, beta = ab
+    A, B, Cin = make_problem(M, N, K, seed=M + 2 * N + 3 * K + op_a + 2 * op_b, dist="normal", with_c=True)
+    dA, lda = _stored(A, op_a == T_, 3, torch, offset=1)
+    dB, ldb = _stored(B, op_b == T_, 5, torch, offset=2)
+    dC, ldc = _stored(Cin, False, 4, torch)
+    if beta == 0.0:
+        dC.fill_(float("nan"))
+    st = capi.sgemm_op(op_a, op_b, M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                       dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=alpha, beta=beta),
+                f"row-major op {ops} {shape}")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", [(7, 5, 3), (130, 67, 77), (300, 260, 1028), (1024, 768, 512)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_column_major_ops(ops, shape):
+    """BLAS convention: X (r x c) stored column-major is X^T stored row-major."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    A, B, Cin = make_problem(M, N, K, seed=7 * M + N + K, dist="normal", with_c=True)
+    # column-major storage of op(A) = A:  A^T row-major; of op(A) = A^T (A
+    # stored K x M column-major): A row-major.
+    dA, lda = _stored(A, op_a == N_, 2, torch)
+    dB, ldb = _stored(B, op_b == N_, 1, torch)
+    dC, ldc = _stored(Cin, True, 3, torch)
+    st = capi.sgemm_cm(op_a, op_b, M, N, K, 0.5, dA.data_ptr(), lda, dB.data_ptr(), ldb, -2.0,
+                       dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    check_close(dC.cpu().numpy().T, oracle.sgemm_ref(A, B, Cin, alpha=0.5, beta=-2.0),
+                f"column-major op {ops} {shape}")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape,batch", [((64, 64, 64), 5), ((130, 67, 77), 3), ((256, 256, 512), 4),
+                                         ((1, 1, 1), 2), ((33, 100, 200), 7)],
+                         ids=["64x5", "130x67x77x3", "256x4", "1x2", "33x100x200x7"])
+def test_strided_batched(ops, shape, batch):
+    """Each problem of a strided batch equals the oracle on its own inputs;
+    problem strides include padding between matrices."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    probs = [make_problem(M, N, K, seed=100 + z, dist="normal", with_c=True) for z in range(batch)]
+    sa = (K * M if op_a == T_ else M * K) + 17
+    sb = (N * K if op_b == T_ else K * N) + 9
+    sc = M * N + 5
+    ra, ca = (K, M) if op_a == T_ else (M, K)
+    rb, cb = (N, K) if op_b == T_ else (K, N)
+    bufA = torch.full((batch * sa,), float("nan"), device="cuda")
+    bufB = torch.full((batch * sb,), float("nan"), device="cuda")
+    bufC = torch.full((batch * sc,), float("nan"), device="cuda")
+    for z, (A, B, Cin) in enumerate(probs):
+        bufA[z * sa:z * sa + ra * ca].copy_(torch.from_numpy(np.ascontiguousarray(A.T if op_a == T_ else A)).flatten())
+        bufB[z * sb:z * sb + rb * cb].copy_(torch.from_numpy(np.ascontiguousarray(B.T if op_b == T_ else B)).flatten())
+        bufC[z * sc:z * sc + M * N].copy_(torch.from_numpy(Cin).flatten())
+    st = capi.sgemm_strided_batched(op_a, op_b, M, N, K, 1.25, bufA.data_ptr(), ca, sa, bufB.data_ptr(), cb, sb,
+                                    0.5, bufC.data_ptr(), N, sc, batch, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    host = bufC.cpu().numpy()
+    for z, (A, B, Cin) in enumerate(probs):
+        check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=0.5),
+                    f"batch {ops} {shape} problem {z}")
+        assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
+
+
+def test_batched_shared_operand_and_column_major():
+    """stride 0 shares B across the batch; the column-major batched entry
+    equals the row-major one on transposed storage."""
+    torch = torch_cuda()
+    M, N, K, batch = 96, 80, 144, 6
+    As = [make_problem(M, N, K, seed=300 + z, dist="normal")[0] for z in range(batch)]
+    B = make_problem(M, N, K, seed=299, dist="normal")[1]
+    dA = torch.from_numpy(np.stack(As)).cuda()
+    dB = torch.from_numpy(B).cuda()[None]
+    C = sgemm_op(dA, dB)                       # [batch, M, N], B shared (batch 1)
+    # Row-major C is column-major C^T = B^T A^T (N x M), whose column-major
+    # operands are B (stored as row-major B, ld N) and A (row-major, ld K).
+    Ccm = torch.full((batch, M, N), float("nan"), device="cuda")
+    st = capi.sgemm_cm_strided_batched(N_, N_, N, M, K, 1.0, dB.data_ptr(), N, 0, dA.data_ptr(), K, M * K,
+                                       0.0, Ccm.data_ptr(), N, M * N, batch, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK
+    torch.cuda.synchronize()
+    for z in range(batch):
+        ref = oracle.sgemm_ref(As[z], B)
+        check_close(C[z].cpu().numpy(), ref, f"shared B, problem {z}")
+        check_close(Ccm[z].cpu().numpy(), ref, f"column-major batch, problem {z}")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+def test_large_transposed_sampled(ops):
+    """A 2048^3 product through each op pair (the 128x128 or 64x64 lean tile
+    in 4-byte mode), compared on the 4096-entry sample and bit-identical on a
+    repeat."""
+    torch = torch_cuda()
+    from fp32_sgemm_tuning_amd.inputs import sample_indices
+    op_a, op_b = ops
+    n = 2048
+    A, B, _ = make_problem(n, n, n, 11)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T if op_a == T_ else A)).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T if op_b == T_ else B)).cuda()
+    c1 = sgemm_op(dA, dB, trans_a=op_a == T_, trans_b=op_b == T_)
+    c2 = sgemm_op(dA, dB, trans_a=op_a == T_, trans_b=op_b == T_)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    I, J = sample_indices(n, n, 11)
+    got = c1.cpu().numpy()[I, J]
+    check_close(got, oracle.sgemm_ref_sampled(A, B, I, J), f"2048^3 {ops}")
