@@ -273,7 +273,22 @@ struct ALayout<64> {
 // registers, their store into an LDS stage, MFMA fragment reads, the MFMAs
 // of one K tile and the epilogue.  Block tile BM x BN, K step BK, WAVES_M x
 // WAVES_N waves of 64 lanes, each owning a WM x WN register tile.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD>
+//
+// TA / TB (lean kernels only): the operand is stored transposed and kept in
+// LDS in its stored orientation, loaded with the same 16-byte runs as the
+// untransposed operands.
+//   - TA: the A stage is [BK][BM], m contiguous (the geometry of the B
+//     stage).  A lane's ds_read_b128 at k holds four consecutive rows
+//     4*(lane%16) + {0..3} of the 64-row wave tile; element ir feeds the
+//     MFMA of row group ir, whose local row rho is real row 4*rho + ir.  The
+//     four reads of a 16-deep half are the four k steps, so the count of
+//     reads and MFMAs is the untransposed one.  Needs 64-row wave tiles.
+//   - TB: the B stage is [BN][BK], k contiguous, in the swizzled A layout
+//     (row n instead of m), read like A: the read for column group ic holds
+//     four k steps of row n = 64*nj + 16*ic + lane%16, so MFMA column c of
+//     group ic is real column 16*ic + c.  A lane's four C values of a row are
+//     then 16 columns apart and the epilogue stores them one by one.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC, bool GUARD, bool TA = false, bool TB = false>
 struct TileOps {
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int WM = BM / WAVES_M;
@@ -289,6 +304,7 @@ struct TileOps {
     static_assert(BK == 16 || BK == 32 || BK == 64, "BK");
     static_assert(BM % 32 == 0, "A layout pairs 16-row slabs");
     static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "load split");
+    static_assert(!TA || MI == 4, "transposed A stage needs 64-row wave tiles");
 
     struct Staging {
         f32x4 a[A_PER];
@@ -369,19 +385,34 @@ struct TileOps {
     // MFMA fragments of the 16-deep half h of the stage.
     static __device__ __forceinline__ void read_frags(const float *stage, int wm, int wn, int lane, int h,
                                                       Frags &f) {
-        const float *As = stage;
-        const float *Bs = stage + BM * BK;
-        const int lrow = lane & 15;
-        const int lq = lane >> 4;
+        if constexpr (TA || TB) {
+            read_all(stage, wm, wn, lane, h, f, IntSeq<0>{});
+        } else {
+            const float *As = stage;
+            const float *Bs = stage + BM * BK;
+            const int lrow = lane & 15;
+            const int lq = lane >> 4;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            f.a[mi] = *reinterpret_cast<const f32x4 *>(As + ALayout<BK>::offset(wm * WM + mi * 16 + lrow, 4 * h + lq));
+            for (int mi = 0; mi < MI; ++mi)
+                f.a[mi] =
+                    *reinterpret_cast<const f32x4 *>(As + ALayout<BK>::offset(wm * WM + mi * 16 + lrow, 4 * h + lq));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int nj = 0; nj < NJ; ++nj)
-                f.b[j][nj] = *reinterpret_cast<const f32x4 *>(Bs + (16 * h + 4 * lq + j) * BN + wn * WN + nj * 64 +
-                                                              4 * lrow);
+                for (int nj = 0; nj < NJ; ++nj)
+                    f.b[j][nj] = *reinterpret_cast<const f32x4 *>(Bs + (16 * h + 4 * lq + j) * BN + wn * WN + nj * 64 +
+                                                                  4 * lrow);
+        }
+    }
+    template <int R>
+    struct IntSeq {};
+    template <int R>
+    static __device__ __forceinline__ void read_all(const float *stage, int wm, int wn, int lane, int h, Frags &f,
+                                                    IntSeq<R>) {
+        if constexpr (R < MI + 4 * NJ) {
+            read_one<R>(stage, wm, wn, lane, h, f);
+            read_all(stage, wm, wn, lane, h, f, IntSeq<R + 1>{});
+        }
     }
 
     // Single items, for kernels that place every instruction explicitly.
@@ -391,15 +422,28 @@ struct TileOps {
     template <int Q>
     static __device__ __forceinline__ void mma_one(f32x4 (&acc)[MI][NJ][4], const Frags &f) {
         constexpr int i = Q % 4, nj = (Q / 4) % NJ, mi = (Q / (4 * NJ)) % MI, j = Q / (4 * NJ * MI);
-        acc[mi][nj][i] = mfma_16x16x4(f.a[mi][j], f.b[j][nj][i], acc[mi][nj][i]);
+        // TA: f.a[j] holds the four row groups of k step j; TB: f.b[i][nj]
+        // holds the four k steps of column group i
+        const float a = TA ? f.a[j][mi] : f.a[mi][j];
+        const float b = TB ? f.b[i][nj][j] : f.b[j][nj][i];
+        acc[mi][nj][i] = mfma_16x16x4(a, b, acc[mi][nj][i]);
     }
-    // fragment read number r: A slabs first, then B (j, nj)
+    // fragment read number r: A (slabs, or with TA k steps) first, then B
+    // ((j, nj), or with TB (column group, nj))
     template <int R>
     static __device__ __forceinline__ void read_one(const float *stage, int wm, int wn, int lane, int h, Frags &f) {
         const int lrow = lane & 15;
         const int lq = lane >> 4;
         if constexpr (R < MI) {
-            f.a[R] = *reinterpret_cast<const f32x4 *>(stage + ALayout<BK>::offset(wm * WM + R * 16 + lrow, 4 * h + lq));
+            if constexpr (TA)
+                f.a[R] = *reinterpret_cast<const f32x4 *>(stage + (16 * h + 4 * lq + R) * BM + wm * WM + 4 * lrow);
+            else
+                f.a[R] =
+                    *reinterpret_cast<const f32x4 *>(stage + ALayout<BK>::offset(wm * WM + R * 16 + lrow, 4 * h + lq));
+        } else if constexpr (TB) {
+            constexpr int ic = (R - MI) / NJ, nj = (R - MI) % NJ;
+            f.b[ic][nj] = *reinterpret_cast<const f32x4 *>(
+                stage + BM * BK + ALayout<BK>::offset(wn * WN + nj * 64 + 16 * ic + lrow, 4 * h + lq));
         } else {
             constexpr int j = (R - MI) / NJ, nj = (R - MI) % NJ;
             f.b[j][nj] = *reinterpret_cast<const f32x4 *>(stage + BM * BK + (16 * h + 4 * lq + j) * BN + wn * WN +
@@ -407,8 +451,10 @@ struct TileOps {
         }
     }
 
-    // The 16 k of one fragment set: MI x NJ x 4 column groups x 4 k steps.
+    // The 16 k of one fragment set: MI x NJ x 4 column groups x 4 k steps
+    // (untransposed stages only).
     static __device__ __forceinline__ void mma(f32x4 (&acc)[MI][NJ][4], const Frags &f) {
+        static_assert(!TA && !TB, "transposed stages use mma_one");
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -433,7 +479,23 @@ struct TileOps {
             for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + r;
+                    // TA: MFMA row rho = 4*(lane/16) + r of row group mi is
+                    // real row 4*rho + mi
+                    const int row = m0 + wm * WM + (TA ? 16 * (lane >> 4) + 4 * r + mi : mi * 16 + 4 * (lane >> 4) + r);
+                    if constexpr (TB) {
+                        // column group i is real column 16*i + lane%16
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int col = n0 + wn * WN + nj * 64 + 16 * i + (lane & 15);
+                            if (!GUARD || (row < p.M && col < p.N)) {
+                                float *dst = p.C + (long)row * p.ldc + col;
+                                float o = alpha * acc[mi][nj][i][r];
+                                if (!BETA0) o += beta * *dst;
+                                *dst = o;
+                            }
+                        }
+                        continue;
+                    }
                     const int col = n0 + wn * WN + nj * 64 + 4 * (lane & 15);
                     f32x4 v = {acc[mi][nj][0][r], acc[mi][nj][1][r], acc[mi][nj][2][r], acc[mi][nj][3][r]};
                     v *= alpha;

@@ -131,12 +131,14 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 // instructions, and every edge below is exact to the element, so N and K
 // need not be multiples of 4.
 //
-// TA / TB (DW only): A stored transposed ([K][M], element (m, k) at
-// k * lda + m) / B stored transposed ([N][K], element (k, n) at n * ldb + k).
-// Each lane's 4-byte load picks the element that the unchanged LDS layout
-// keeps at its position, so fragments, MFMAs and epilogue stay the same; the
-// loads of one instruction then come from up to 32 rows of the stored
-// operand instead of one.
+// TA / TB: A stored transposed ([K][M], element (m, k) at k * lda + m) / B
+// stored transposed ([N][K], element (k, n) at n * ldb + k).  With 16-byte
+// loads the operand keeps its stored orientation in LDS (TileOps describes
+// the fragment reads; TA needs 64-row wave tiles, M a multiple of 4 for A's
+// edge chunks, TB needs K a multiple of 4).  With 4-byte loads each lane
+// picks the element that the untransposed LDS layout keeps at its position,
+// so fragments, MFMAs and epilogue stay untransposed; the loads of one
+// instruction then come from up to 32 rows of the stored operand.
 //
 // EDGE = false: M, N and K are whole numbers of tiles.  EDGE = true: any M
 // and N, and any K of at least BK, with K and N multiples of 4 unless DW.
@@ -168,10 +170,13 @@ template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDG
           bool TB>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lean_kernel(Args p) {
-    static_assert(DW || (!TA && !TB), "transposed operands need the 4-byte loads");
     batch_offset(p);
+    // Transposed operands with 16-byte loads keep their stored orientation in
+    // LDS (see TileOps); with 4-byte loads they are gathered into the
+    // untransposed layout.
+    constexpr bool LTA = TA && !DW, LTB = TB && !DW;
     // DW: 4-byte loads and 32-bit C access (any alignment), else 16-byte ones
-    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, !DW, EDGE>;
+    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, !DW, EDGE, LTA, LTB>;
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int KH = T::KH;
     static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
@@ -200,14 +205,27 @@ sgemm_lean_kernel(Args p) {
     // that of the logical (row, k) the swizzled layout keeps there.
     auto a_coords = [&](int i, int &m, int &k) {
         const int u = (i * NWAVES + wave) * 64 + lane;
-        int c;
-        ALayout<BK>::inverse(DW ? u / 4 : u, m, c);
-        k = 4 * c + (DW ? u % 4 : 0);
+        if constexpr (LTA) {            // [BK][BM] stage
+            const int g = u * EW;
+            k = g / BM;
+            m = g % BM;
+        } else {
+            int c;
+            ALayout<BK>::inverse(DW ? u / 4 : u, m, c);
+            k = 4 * c + (DW ? u % 4 : 0);
+        }
     };
     auto b_coords = [&](int i, int &r, int &col) {
-        const int g = ((i * NWAVES + wave) * 64 + lane) * EW;     // float index in the B stage
-        r = g / BN;
-        col = g % BN;
+        const int u = (i * NWAVES + wave) * 64 + lane;
+        if constexpr (LTB) {            // [BN][BK] stage in the swizzled layout
+            int c;
+            ALayout<BK>::inverse(u, col, c);
+            r = 4 * c;
+        } else {
+            const int g = u * EW;       // float index in the B stage
+            r = g / BN;
+            col = g % BN;
+        }
     };
     // Element (m, k) of the A tile is at m * lda + k from the tile's corner,
     // or k * lda + m when A is stored transposed (TA); likewise (k, n) of B at
@@ -392,14 +410,22 @@ void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t s) {
     launch_lean<128, 128, 32, 2, 2, false, true>(a, 1, s);
 }
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false, true>(a, 1, s); }
-// Transposed operands and strided batches: the 16-byte form for untransposed
-// operands (the caller has checked its alignment), else the 4-byte form, on
+// Transposed operands and strided batches: the 16-byte form when the caller
+// has checked the operands' alignment (dw false), else the 4-byte form, on
 // 64x64x64 tiles (tile64) or 128x128x32 tiles.
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, bool TA16>
 void launch_lean_ops(const Args &a, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
-    if (!dw)
+    if (!dw) {
+        if constexpr (TA16) {
+            if (ta && tb)
+                return launch_lean<BM, BN, BK, WM, WN, false, false, true, true>(a, 1, s, batch);
+            if (ta)
+                return launch_lean<BM, BN, BK, WM, WN, false, false, true, false>(a, 1, s, batch);
+        }
+        if (tb)
+            return launch_lean<BM, BN, BK, WM, WN, false, false, false, true>(a, 1, s, batch);
         launch_lean<BM, BN, BK, WM, WN, false, false, false, false>(a, 1, s, batch);
-    else if (ta && tb)
+    } else if (ta && tb)
         launch_lean<BM, BN, BK, WM, WN, false, true, true, true>(a, 1, s, batch);
     else if (ta)
         launch_lean<BM, BN, BK, WM, WN, false, true, true, false>(a, 1, s, batch);
@@ -408,11 +434,12 @@ void launch_lean_ops(const Args &a, bool dw, bool ta, bool tb, int batch, hipStr
     else
         launch_lean<BM, BN, BK, WM, WN, false, true, false, false>(a, 1, s, batch);
 }
+// (16-byte loads of a transposed A need 64-row wave tiles: 128x128x32 only)
 void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
     if (tile64)
-        launch_lean_ops<64, 64, 64, 4, 1>(a, dw, ta, tb, batch, s);
+        launch_lean_ops<64, 64, 64, 4, 1, false>(a, dw, ta, tb, batch, s);
     else
-        launch_lean_ops<128, 128, 32, 2, 2>(a, dw, ta, tb, batch, s);
+        launch_lean_ops<128, 128, 32, 2, 2, true>(a, dw, ta, tb, batch, s);
 }
 // Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
 // splits * tiles * BM * BN floats and `tiles` zeroed counters.

@@ -152,3 +152,45 @@ def test_large_transposed_sampled(ops):
     I, J = sample_indices(n, n, 11)
     got = c1.cpu().numpy()[I, J]
     check_close(got, oracle.sgemm_ref_sampled(A, B, I, J), f"2048^3 {ops}")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", [(1940, 2044, 132), (2048, 2048, 96)], ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_transposed_16byte_stages(ops, shape):
+    """Grids of 256 128x128 tiles take the 128x128x32 lean tile, where aligned
+    transposed operands keep their stored orientation in LDS (16-byte loads,
+    row-group and column-group fragment reads); edges in M, N and a K
+    remainder, NaN padding, beta != 0."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    A, B, Cin = make_problem(M, N, K, seed=M + N + K + 5 * op_a + 7 * op_b, dist="normal", with_c=True)
+    dA, lda = _stored(A, op_a == T_, 4, torch)
+    dB, ldb = _stored(B, op_b == T_, 8, torch)
+    dC, ldc = _stored(Cin, False, 4, torch)
+    st = capi.sgemm_op(op_a, op_b, M, N, K, 1.5, dA.data_ptr(), lda, dB.data_ptr(), ldb, -0.5,
+                       dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.5, beta=-0.5), f"16-byte op {ops} {shape}")
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (200, 300, 260), (64, 64, 64), (3072, 512, 128)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_transposed_aligned_small(ops, shape):
+    """Aligned operands (leading dimensions multiples of 4) on grids that
+    pick the 64x64 tile: the 16-byte B^T stage there, the 4-byte gather for
+    a transposed A (or the 128x128 tile when its grid is large enough)."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    A, B, Cin = make_problem(M, N, K, seed=2 * M + N + K + op_a + op_b, dist="normal", with_c=True)
+    dA, lda = _stored(A, op_a == T_, 4, torch)
+    dB, ldb = _stored(B, op_b == T_, 4, torch)
+    dC, ldc = _stored(Cin, False, 4, torch)
+    st = capi.sgemm_op(op_a, op_b, M, N, K, 1.0, dA.data_ptr(), lda, dB.data_ptr(), ldb, 0.25,
+                       dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.0, beta=0.25), f"aligned op {ops} {shape}")
