@@ -39,7 +39,8 @@ METRIC = "SGEMM TFLOP/s (2MNK/t) at M=N=K=4096 FP32; % of MI355X FP32 matrix pea
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_sq4096.txt")
 
 
-KERNEL_SOURCES = ("sgemm.hip", "sgemm_kernels.hpp", "sgemm_lean.hip")
+KERNEL_SOURCES = ("sgemm.hip", "sgemm_kernels.hpp", "sgemm_lean.hpp", "sgemm_lean.hip", "sgemm_lean_split.hip",
+                  "sgemm_lean_ops.hip")
 
 
 def kernel_source_hash():

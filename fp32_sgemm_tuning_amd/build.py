@@ -20,16 +20,20 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgemm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-# (source, extra flags): each translation unit is compiled on its own, then
-# linked into one shared library.  sgemm_lean.hip keeps MFMA results in
-# ordinary VGPRs; that flag is per translation unit and would make the
-# shared header's 256-accumulator kernels spill.
+# (source, extra flags): each translation unit is compiled on its own (in
+# parallel), then linked into one shared library.  The sgemm_lean*.hip units
+# keep MFMA results in ordinary VGPRs; that flag is per translation unit and
+# would make the shared header's 256-accumulator kernels spill.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 UNITS = [
     ("sgemm.hip", []),
-    ("sgemm_lean.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("sgemm_lean.hip", VGPR_FORM),
+    ("sgemm_lean_split.hip", VGPR_FORM),
+    ("sgemm_lean_ops.hip", VGPR_FORM),
 ]
 SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS]
-DEPS = SOURCES + [os.path.join(CSRC, "sgemm_kernels.hpp"), os.path.join(INCLUDE, "sgemm.h")]
+DEPS = SOURCES + [os.path.join(CSRC, h) for h in ("sgemm_kernels.hpp", "sgemm_lean.hpp")] + \
+    [os.path.join(INCLUDE, "sgemm.h")]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

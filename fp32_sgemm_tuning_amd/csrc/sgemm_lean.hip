@@ -1,399 +1,8 @@
-// Lean direct-to-LDS SGEMM kernel, in a translation unit of its own.
-//
-// This file is compiled with MFMA results kept in ordinary VGPRs
-// (-mllvm -amdgpu-mfma-vgpr-form).  With the default accumulation registers
-// the two-stage unrolled loop below gets accumulator copies between the
-// unrolled halves and fragment round trips through the accumulation file,
-// one VALU copy for every five MFMAs; in VGPR form the K loop is MFMAs, LDS
-// reads, direct loads and a few scalar instructions only.  The flag applies
-// to a whole translation unit, and kernels of the shared header that hold
-// 256 accumulators per lane do not fit 256 VGPRs, hence the separate file.
-// Only wave tiles of 64x64 or 64x128 outputs are instantiated here.
-#include <hip/hip_runtime.h>
-
-#include "sgemm_kernels.hpp"
+// Lean kernels: untransposed single problems (16-byte and 4-byte loads).
+// (Built with MFMA results in VGPRs; see sgemm_lean.hpp.)
+#include "sgemm_lean.hpp"
 
 namespace sgemm_mi355x {
-
-// A buffer offset past every descriptor's range (ranges are below 2^31).
-constexpr unsigned kOutOfRange = 0x80000000u;
-
-// Byte range of a buffer descriptor: the distance to the operand's end,
-// clamped to [0, 2^31 - 1] (an empty range makes every load out of range).
-__device__ __forceinline__ int buffer_range(long bytes) {
-    return (int)(bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes));
-}
-
-// One direct load per lane into LDS: 16 or 4 bytes from the buffer at
-// voffset + soffset to the LDS address of `dst` plus 16 or 4 bytes per lane.
-// (The size must be a literal at the call, hence one function per size.)
-typedef __attribute__((address_space(3))) void *lds_addr_t;
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, soffset, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voffset, soffset, 0, 0);
-}
-template <bool DW>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, int voffset, int soffset) {
-    if constexpr (DW)
-        dma4(r, dst, voffset, soffset);
-    else
-        dma16(r, dst, voffset, soffset);
-}
-
-// s_waitcnt with vmcnt 0 and the other counters at their maximum
-// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Split-K hand-off of one output tile.  Every block stores its partial
-// accumulators to workspace slot blockIdx.y of the tile (chunk-major: chunk c
-// of thread t at c * NT + t, so each store and load instruction covers one
-// contiguous run) and takes a ticket from the tile's counter.  Returns false
-// for all blocks but the last; the last one reads the other partials, leaves
-// their sum in split order in acc and resets the counter for the next call.
-//
-// Every XCD has its own L2, so the partials move at device scope: the
-// stores and loads carry the device-scope cache policy (sc1, the encoding
-// the compiler uses for relaxed agent-scope atomics), each block waits for
-// its stores to complete before the barrier that precedes its ticket, and
-// the ticket is a device-scope atomic.  No cache-wide write-back or
-// invalidate is needed, so other blocks keep their cached A and B.
-template <class T>
-__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, f32x4 (&acc)[T::MI][T::NJ][4]) {
-    constexpr int TILE = T::NT * T::MI * T::NJ * 16;   // floats per partial tile (BM x BN)
-    constexpr int kDeviceScope = 16;                    // cache policy bits: sc1
-    const int S = gridDim.y, y = blockIdx.y;
-    const __amdgpu_buffer_rsrc_t slab = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.ws + (long)tile_id * S * TILE), (short)0, S * TILE * 4, 0x00020000);
-#pragma unroll
-    for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(acc[mi][nj][i], slab,
-                                                       (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16, y * TILE * 4,
-                                                       kDeviceScope);
-    wait_vmcnt0();
-    __syncthreads();
-    __shared__ unsigned ticket;
-    if (tid == 0) ticket = atomicAdd(p.counters + tile_id, 1u);
-    __syncthreads();
-    if (ticket != (unsigned)(S - 1)) return false;
-    f32x4 sum[T::MI][T::NJ][4];
-    for (int s = 0; s < S; ++s) {
-#pragma unroll
-        for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 x = s == y ? acc[mi][nj][i]
-                                           : __builtin_amdgcn_raw_buffer_load_b128(
-                                                 slab, (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16,
-                                                 s * TILE * 4, kDeviceScope);
-                    sum[mi][nj][i] = s == 0 ? x : sum[mi][nj][i] + x;
-                }
-    }
-#pragma unroll
-    for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = sum[mi][nj][i];
-    if (tid == 0) atomicExch(p.counters + tile_id, 0u);
-    return true;
-}
-
-// ---------------------------------------------------------------------------
-// Lean direct-to-LDS kernel: the section schedule of sgemm_dtl_kernel with
-// the per-tile address arithmetic taken out of the K loop.
-//
-// In the K loop of the direct-to-LDS kernel about a quarter of the issued
-// instructions besides the MFMAs were address arithmetic: reading the wave
-// index back into a scalar for M0, 64-bit adds advancing every load address
-// per tile, and ORs placing the runtime stage base into every LDS read
-// address.  Here
-//   - the wave index is wave-uniform (a scalar), so M0 is scalar arithmetic;
-//   - the direct loads are buffer loads (buffer_load_dwordx4 ... lds): a
-//     wave-uniform descriptor, a loop-invariant 32-bit per-lane byte offset
-//     and a scalar offset that advances one tile per iteration;
-//   - the tile loop is unrolled by the two LDS stages, so every fragment read
-//     address is a loop-invariant register plus an immediate.
-// Every byte offset inside the block's part of A and B must fit the 31-bit
-// buffer range (BM * lda + K and K * ldb, or for transposed operands
-// K * lda + BM and BN * ldb + K, below 2^29 elements).
-//
-// DW = false: 16-byte loads (A, B, C 16-byte aligned, leading dimensions
-// multiples of 4).  DW = true: 4-byte loads of single floats into the same
-// LDS layout and 32-bit C access, for any alignment; four times the load
-// instructions, and every edge below is exact to the element, so N and K
-// need not be multiples of 4.
-//
-// TA / TB: A stored transposed ([K][M], element (m, k) at k * lda + m) / B
-// stored transposed ([N][K], element (k, n) at n * ldb + k).  With 16-byte
-// loads the operand keeps its stored orientation in LDS (TileOps describes
-// the fragment reads; TA needs 64-row wave tiles, M a multiple of 4 for A's
-// edge chunks, TB needs K a multiple of 4).  With 4-byte loads each lane
-// picks the element that the untransposed LDS layout keeps at its position,
-// so fragments, MFMAs and epilogue stay untransposed; the loads of one
-// instruction then come from up to 32 rows of the stored operand.
-//
-// EDGE = false: M, N and K are whole numbers of tiles.  EDGE = true: any M
-// and N, and any K of at least BK, with K and N multiples of 4 unless DW.
-// The hardware range check of buffer loads does the edges without a branch
-// in the K loop (it compares the per-lane offset with the descriptor's
-// range; the scalar offset is not part of the check):
-//   - each descriptor ends at its operand's last element;
-//   - elements of rows past M or columns past N get an offset beyond every
-//     range (set once, before the K loop);
-//   - a K remainder kr = K % BK is taken as the first tile, k in [0, kr), whose
-//     elements at k >= kr get that offset too, and the full tiles follow from
-//     k = kr on descriptors based there.
-// Out-of-range loads access no memory and deposit zeros, which is what the
-// K remainder needs (A's padding past column K may hold anything).  Rows past
-// M and columns past N only reach accumulators that the guarded epilogue
-// does not store.
-//
-// Strided batches: problem blockIdx.z, on pointers moved by the strides.
-//
-// SPLIT = true: split-K.  gridDim.y = S blocks share each output tile; block
-// y takes K tiles [y * T / S, (y + 1) * T / S) of the T tiles (the remainder
-// tile, if any, goes to y = 0), writes its partial tile to the workspace and
-// counts itself in on the tile's counter.  The block that arrives last adds
-// the S partials in the fixed order y = 0 .. S-1 (so the result does not
-// depend on arrival order), resets the counter and runs the epilogue.  No
-// block waits for another.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool BETA0, bool EDGE, bool SPLIT, bool DW, bool TA,
-          bool TB>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
-sgemm_lean_kernel(Args p) {
-    batch_offset(p);
-    // Transposed operands with 16-byte loads keep their stored orientation in
-    // LDS (see TileOps); with 4-byte loads they are gathered into the
-    // untransposed layout.
-    constexpr bool LTA = TA && !DW, LTB = TB && !DW;
-    // DW: 4-byte loads and 32-bit C access (any alignment), else 16-byte ones
-    using T = TileOps<BM, BN, BK, WAVES_M, WAVES_N, !DW, EDGE, LTA, LTB>;
-    constexpr int NWAVES = WAVES_M * WAVES_N;
-    constexpr int KH = T::KH;
-    static_assert(KH == 2 || KH == 4, "BK must be 32 or 64");
-    constexpr int EW = DW ? 1 : 4;                          // floats per lane per load
-    constexpr int LSTEP = 64 * EW;                          // floats of LDS per load instruction
-    constexpr int NA = BM * BK / EW / T::NT;
-    constexpr int NB = BK * BN / EW / T::NT;
-    constexpr int NM = T::MI * T::NJ * 16;
-    constexpr int NR = T::MI + 4 * T::NJ;
-    constexpr int LS = KH == 4 ? 2 : 1;                     // sections carrying the loads
-    constexpr int PER = (NA + NB + LS - 1) / LS;
-    __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
-    typedef __attribute__((address_space(3))) void *lds_ptr;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    int tm, tn;
-    tile_coords(p, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    // Loop-invariant per-lane byte offsets of the direct loads.  Load i of a
-    // lane fills LDS unit u = (i * NWAVES + wave) * 64 + lane of the stage (a
-    // 16-byte chunk, or with DW one float of chunk u / 4); the A offset is
-    // that of the logical (row, k) the swizzled layout keeps there.
-    auto a_coords = [&](int i, int &m, int &k) {
-        const int u = (i * NWAVES + wave) * 64 + lane;
-        if constexpr (LTA) {            // [BK][BM] stage
-            const int g = u * EW;
-            k = g / BM;
-            m = g % BM;
-        } else {
-            int c;
-            ALayout<BK>::inverse(DW ? u / 4 : u, m, c);
-            k = 4 * c + (DW ? u % 4 : 0);
-        }
-    };
-    auto b_coords = [&](int i, int &r, int &col) {
-        const int u = (i * NWAVES + wave) * 64 + lane;
-        if constexpr (LTB) {            // [BN][BK] stage in the swizzled layout
-            int c;
-            ALayout<BK>::inverse(u, col, c);
-            r = 4 * c;
-        } else {
-            const int g = u * EW;       // float index in the B stage
-            r = g / BN;
-            col = g % BN;
-        }
-    };
-    // Element (m, k) of the A tile is at m * lda + k from the tile's corner,
-    // or k * lda + m when A is stored transposed (TA); likewise (k, n) of B at
-    // k * ldb + n, or n * ldb + k (TB).  Rows past M and columns past N get
-    // an offset beyond every range (EDGE).
-    unsigned offA[NA], offB[NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-        int m, k;
-        a_coords(i, m, k);
-        const int e = TA ? k * (int)p.lda + m : m * (int)p.lda + k;
-        offA[i] = (EDGE && m0 + m >= p.M) ? kOutOfRange : 4u * (unsigned)e;
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        int r, col;
-        b_coords(i, r, col);
-        const int e = TB ? col * (int)p.ldb + r : r * (int)p.ldb + col;
-        offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)e;
-    }
-    // K remainder taken first (EDGE only): tile 0 covers k in [0, kr), full
-    // tiles follow from k = kr.
-    const int kr = EDGE ? p.K % BK : 0;
-    const int tail = kr != 0;
-    const int ntiles = p.K / BK + tail;
-    // K tiles of this block: all of them, or this split's share
-    int t_begin = 0, t_end = ntiles;
-    if constexpr (SPLIT) {
-        const int S = gridDim.y, y = blockIdx.y;
-        t_begin = (int)((long)ntiles * y / S);
-        t_end = (int)((long)ntiles * (y + 1) / S);
-    }
-
-    // Buffer descriptors for the full tiles, from the block's first row of A
-    // and first column of B at k = kr to the last element of each operand
-    // (clamped to [0, 2^31 - 1]; the offsets in use stay below the cap); the
-    // per-tile advance goes in the scalar offset of each load.
-    // (block corner at k = 0, the k stride in the stored operand, the byte
-    // distance from that corner to the operand's last element)
-    const float *cornerA = TA ? p.A + m0 : p.A + (long)m0 * p.lda;
-    const float *cornerB = TB ? p.B + (long)n0 * p.ldb : p.B + n0;
-    const long kstrideA = TA ? p.lda : 1, kstrideB = TB ? 1 : p.ldb;
-    const long endA = TA ? 4L * ((long)(p.K - 1) * p.lda + p.M - m0) : 4L * ((long)(p.M - 1 - m0) * p.lda + p.K);
-    const long endB = TB ? 4L * ((long)(p.N - 1 - n0) * p.ldb + p.K) : 4L * ((long)(p.K - 1) * p.ldb + p.N - n0);
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cornerA + kr * kstrideA), (short)0, buffer_range(endA - 4L * kr * kstrideA), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cornerB + kr * kstrideB), (short)0, buffer_range(endB - 4L * kr * kstrideB), 0x00020000);
-    const unsigned stepA = 4u * BK * (unsigned)kstrideA, stepB = 4u * BK * (unsigned)kstrideB;
-
-    // Loads of tile t >= tail (a full tile).  (The explicit int conversions
-    // matter: with the array element passed as is, the host pass drops the
-    // kernel and its launch stub.)
-    auto issue_one = [&](int t, float *stage, int i) {
-        const unsigned tf = (unsigned)max(t - tail, 0);
-        if (i < NA)
-            dma<DW>(rsA, (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP), (int)offA[i], (int)(tf * stepA));
-        else
-            dma<DW>(rsB, (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP), (int)offB[i - NA],
-                    (int)(tf * stepB));
-    };
-    // Loads of the K remainder tile, on descriptors based at k = 0.
-    auto issue_remainder = [&](float *stage) {
-        const __amdgpu_buffer_rsrc_t rA0 =
-            __builtin_amdgcn_make_buffer_rsrc((void *)cornerA, (short)0, buffer_range(endA), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rB0 =
-            __builtin_amdgcn_make_buffer_rsrc((void *)cornerB, (short)0, buffer_range(endB), 0x00020000);
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            int m, k;
-            a_coords(i, m, k);
-            const unsigned off = k < kr ? offA[i] : kOutOfRange;
-            dma<DW>(rA0, (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP), (int)off, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            int r, col;
-            b_coords(i, r, col);
-            const unsigned off = r < kr ? offB[i] : kOutOfRange;
-            dma<DW>(rB0, (lds_ptr)(stage + BM * BK + (i * NWAVES + wave) * LSTEP), (int)off, 0);
-        }
-    };
-
-    f32x4 acc[T::MI][T::NJ][4];
-#pragma unroll
-    for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    typename T::Frags F[2];
-
-    // one K tile held in stage SC (compile time); loads of tile t+1 go to
-    // the other stage
-    auto tile = [&](int t, auto sc) {
-        constexpr int SC = decltype(sc)::value;
-        constexpr int SN = 1 - SC;
-        const float *cs = lds + SC * T::STAGE;
-        float *ns = lds + SN * T::STAGE;
-        const int t_next = min(t + 1, t_end - 1);
-        auto section = [&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            constexpr int g_lo = h * PER < NA + NB ? h * PER : NA + NB;
-            constexpr int g_hi = (h + 1) * PER < NA + NB ? (h + 1) * PER : NA + NB;
-            emit_spread<NM, NR, NM * 3 / 4, (h < LS) ? g_hi - g_lo : 0>(
-                [&](auto q) { T::template mma_one<decltype(q)::value>(acc, F[h & 1]); },
-                [&](auto r) { T::template read_one<decltype(r)::value>(cs, wm, wn, lane, h + 1, F[(h + 1) & 1]); },
-                [&](auto g) { issue_one(t_next, ns, g_lo + decltype(g)::value); });
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        section(IntC<0>{});
-        if constexpr (KH == 4) {
-            section(IntC<1>{});
-            section(IntC<2>{});
-        }
-        wait_vmcnt0();
-        __syncthreads();
-        emit_spread<NM, NR, NR, 0>(
-            [&](auto q) { T::template mma_one<decltype(q)::value>(acc, F[(KH - 1) & 1]); },
-            [&](auto r) { T::template read_one<decltype(r)::value>(ns, wm, wn, lane, 0, F[0]); },
-            [&](auto) {});
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    if (t_end > t_begin) {
-        if (tail && t_begin == 0) {
-            issue_remainder(lds);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NA + NB; ++i) issue_one(t_begin, lds, i);
-        }
-        wait_vmcnt0();
-        __syncthreads();
-        T::read_frags(lds, wm, wn, lane, 0, F[0]);
-        int t = t_begin;
-        for (; t + 1 < t_end; t += 2) {
-            tile(t, IntC<0>{});
-            tile(t + 1, IntC<1>{});
-        }
-        if (t < t_end) tile(t, IntC<0>{});
-    }
-    if constexpr (SPLIT) {
-        if (!split_reduce<T>(p, tm * p.tiles_n + tn, tid, acc)) return;
-    }
-    T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
-}
-
-
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW = false, bool TA = false,
-          bool TB = false>
-void launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) {
-    const Args a = tiled(a0, BM, BN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits, (unsigned)batch);
-    const dim3 block(64 * WAVES_M * WAVES_N);
-    const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
-#define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW, TA, TB>), grid, block, 0, \
-                       stream, a)
-    if (edge) {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(false, true);
-    } else {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, false);
-        else SGEMM_LAUNCH(false, false);
-    }
-#undef SGEMM_LAUNCH
-}
 
 // Launchers called from the C ABI's translation unit.
 void launch_lean_128x128x64_w2x2(const Args &a, hipStream_t s) { launch_lean<128, 128, 64, 2, 2, false>(a, 1, s); }
@@ -410,53 +19,5 @@ void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t s) {
     launch_lean<128, 128, 32, 2, 2, false, true>(a, 1, s);
 }
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t s) { launch_lean<64, 64, 64, 4, 1, false, true>(a, 1, s); }
-// Transposed operands and strided batches: the 16-byte form when the caller
-// has checked the operands' alignment (dw false), else the 4-byte form, on
-// 64x64x64 tiles (tile64) or 128x128x32 tiles.
-template <int BM, int BN, int BK, int WM, int WN, bool TA16>
-void launch_lean_ops(const Args &a, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
-    if (!dw) {
-        if constexpr (TA16) {
-            if (ta && tb)
-                return launch_lean<BM, BN, BK, WM, WN, false, false, true, true>(a, 1, s, batch);
-            if (ta)
-                return launch_lean<BM, BN, BK, WM, WN, false, false, true, false>(a, 1, s, batch);
-        }
-        if (tb)
-            return launch_lean<BM, BN, BK, WM, WN, false, false, false, true>(a, 1, s, batch);
-        launch_lean<BM, BN, BK, WM, WN, false, false, false, false>(a, 1, s, batch);
-    } else if (ta && tb)
-        launch_lean<BM, BN, BK, WM, WN, false, true, true, true>(a, 1, s, batch);
-    else if (ta)
-        launch_lean<BM, BN, BK, WM, WN, false, true, true, false>(a, 1, s, batch);
-    else if (tb)
-        launch_lean<BM, BN, BK, WM, WN, false, true, false, true>(a, 1, s, batch);
-    else
-        launch_lean<BM, BN, BK, WM, WN, false, true, false, false>(a, 1, s, batch);
-}
-// (16-byte loads of a transposed A need 64-row wave tiles: 128x128x32 only)
-void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t s) {
-    if (tile64)
-        launch_lean_ops<64, 64, 64, 4, 1, false>(a, dw, ta, tb, batch, s);
-    else
-        launch_lean_ops<128, 128, 32, 2, 2, true>(a, dw, ta, tb, batch, s);
-}
-// Split-K over `splits` >= 2 blocks per tile; a.ws and a.counters must hold
-// splits * tiles * BM * BN floats and `tiles` zeroed counters.
-void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t s) {
-    launch_lean<128, 128, 32, 2, 2, true>(a, splits, s);
-}
-void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t s) {
-    launch_lean<64, 64, 32, 4, 1, true>(a, splits, s);
-}
-void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t s) {
-    launch_lean<64, 64, 64, 4, 1, true>(a, splits, s);
-}
-void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t s) {
-    launch_lean<64, 128, 32, 2, 2, true>(a, splits, s);
-}
-void launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t s) {
-    launch_lean<128, 64, 32, 4, 1, true>(a, splits, s);
-}
 
 }  // namespace sgemm_mi355x
