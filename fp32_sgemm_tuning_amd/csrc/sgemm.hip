@@ -264,15 +264,23 @@ void launch_split_or_plain(const Args &a, hipStream_t stream) {
         PLAIN(a, stream);
 }
 
+// Whether the byte offsets within one K tile of the lean kernel's part of A
+// and B fit the buffer descriptors' 31-bit range (the operands themselves
+// may be larger: every tile gets its own descriptor base).
+bool lean_fits(int bm, int bn, int bk, long lda, long ldb, bool ta, bool tb) {
+    const long lim = 0x7fffffffL;
+    const long spanA = ta ? (long)bk * lda + bm : (long)bm * lda + bk;
+    const long spanB = tb ? (long)bn * ldb + bk : (long)bk * ldb + bn;
+    return 4L * spanA < lim && 4L * spanB < lim;
+}
+
 // The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
-// be whole tiles) and byte offsets within A's row block and B's column block
-// below 2^31 (the buffer descriptors' range); other shapes go to FALLBACK, a
-// guarded kernel.
+// be whole tiles) and offsets within a tile that fit the descriptors' range;
+// other shapes go to FALLBACK, a guarded kernel.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_or(const Args &a, hipStream_t stream) {
     const bool shape = a.K >= BK && !(a.K % 4) && !(a.N % 4);
-    const long lim = 0x7fffffffL;
-    const bool fits = 4L * ((long)(BM - 1) * a.lda + a.K) < lim && 4L * ((long)a.K * a.ldb + BN) < lim;
+    const bool fits = lean_fits(BM, BN, BK, a.lda, a.ldb, false, false);
     if (shape && fits)
         LEAN(a, stream);
     else
@@ -280,12 +288,10 @@ void launch_lean_or(const Args &a, hipStream_t stream) {
 }
 
 // The lean kernel with 4-byte loads takes any alignment and any K >= BK, with
-// byte offsets below 2^31 as above; other shapes go to FALLBACK.
+// offsets within a tile that fit as above; other shapes go to FALLBACK.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_dw_or(const Args &a, hipStream_t stream) {
-    const long lim = 0x7fffffffL;
-    const bool fits = 4L * ((long)(BM - 1) * a.lda + a.K) < lim && 4L * ((long)a.K * a.ldb + BN) < lim;
-    if (a.K >= BK && fits)
+    if (a.K >= BK && lean_fits(BM, BN, BK, a.lda, a.ldb, false, false))
         LEAN(a, stream);
     else
         FALLBACK(a, stream);
@@ -545,10 +551,7 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     if (tile64 && ta && aligned && ceil_div(M, 128) * ceil_div(N, 128) * batch >= 160) tile64 = false;
     const bool vec = aligned && !(tile64 && ta);
     const int bm = tile64 ? 64 : 128, bn = bm, bk = tile64 ? 64 : 32;
-    const long lim = 0x7fffffffL;
-    const long spanA = ta ? (long)K * lda + bm : (long)(bm - 1) * lda + K;
-    const long spanB = tb ? (long)bn * ldb + K : (long)K * ldb + bn;
-    const bool lean = K >= bk && 4L * spanA < lim && 4L * spanB < lim;
+    const bool lean = K >= bk && lean_fits(bm, bn, bk, lda, ldb, ta, tb);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();

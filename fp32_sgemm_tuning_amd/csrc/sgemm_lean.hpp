@@ -22,12 +22,6 @@ namespace sgemm_mi355x {
 // A buffer offset past every descriptor's range (ranges are below 2^31).
 constexpr unsigned kOutOfRange = 0x80000000u;
 
-// Byte range of a buffer descriptor: the distance to the operand's end,
-// clamped to [0, 2^31 - 1] (an empty range makes every load out of range).
-__device__ __forceinline__ int buffer_range(long bytes) {
-    return (int)(bytes < 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffffL : bytes));
-}
-
 // One direct load per lane into LDS: 16 or 4 bytes from the buffer at
 // voffset + soffset to the LDS address of `dst` plus 16 or 4 bytes per lane.
 // (The size must be a literal at the call, hence one function per size.)
@@ -125,9 +119,10 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 //     and a scalar offset that advances one tile per iteration;
 //   - the tile loop is unrolled by the two LDS stages, so every fragment read
 //     address is a loop-invariant register plus an immediate.
-// Every byte offset inside the block's part of A and B must fit the 31-bit
-// buffer range (BM * lda + K and K * ldb, or for transposed operands
-// K * lda + BM and BN * ldb + K, below 2^29 elements).
+// The byte offsets within one K tile of the block's part of A and B must
+// fit the 31-bit buffer range (BM * lda and BK * ldb, or for transposed
+// operands BK * lda and BN * ldb, below 2^29 elements); the operands
+// themselves may be of any size.
 //
 // DW = false: 16-byte loads (A, B, C 16-byte aligned, leading dimensions
 // multiples of 4).  DW = true: 4-byte loads of single floats into the same
@@ -148,13 +143,14 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 // and N, and any K of at least BK, with K and N multiples of 4 unless DW.
 // The hardware range check of buffer loads does the edges without a branch
 // in the K loop (it compares the per-lane offset with the descriptor's
-// range; the scalar offset is not part of the check):
-//   - each descriptor ends at its operand's last element;
+// range):
+//   - each descriptor covers the block's part of one K tile, which lies
+//     inside its operand;
 //   - elements of rows past M or columns past N get an offset beyond every
 //     range (set once, before the K loop);
 //   - a K remainder kr = K % BK is taken as the first tile, k in [0, kr), whose
 //     elements at k >= kr get that offset too, and the full tiles follow from
-//     k = kr on descriptors based there.
+//     k = kr.
 // Out-of-range loads access no memory and deposit zeros, which is what the
 // K remainder needs (A's padding past column K may hold anything).  Rows past
 // M and columns past N only reach accumulators that the guarded epilogue
@@ -263,40 +259,40 @@ sgemm_lean_kernel(Args p) {
         t_end = (int)((long)ntiles * (y + 1) / S);
     }
 
-    // Buffer descriptors for the full tiles, from the block's first row of A
-    // and first column of B at k = kr to the last element of each operand
-    // (clamped to [0, 2^31 - 1]; the offsets in use stay below the cap); the
-    // per-tile advance goes in the scalar offset of each load.
-    // (block corner at k = 0, the k stride in the stored operand, the byte
-    // distance from that corner to the operand's last element)
+    // Buffer descriptors.  Block corner at k = 0 in each stored operand and
+    // its k stride.  Every K tile is loaded through descriptors based at that
+    // tile (a 64-bit scalar base, a few scalar instructions per tile), so only
+    // the offsets within one tile need to fit the 31-bit range and the
+    // operands may be of any size.  The range of each descriptor is the extent
+    // of the block's part of one tile (rows up to M, columns up to N, BK deep),
+    // so every in-range load stays inside the operand, and the out-of-range
+    // offset lies beyond it.
     const float *cornerA = TA ? p.A + m0 : p.A + (long)m0 * p.lda;
     const float *cornerB = TB ? p.B + (long)n0 * p.ldb : p.B + n0;
     const long kstrideA = TA ? p.lda : 1, kstrideB = TB ? 1 : p.ldb;
-    const long endA = TA ? 4L * ((long)(p.K - 1) * p.lda + p.M - m0) : 4L * ((long)(p.M - 1 - m0) * p.lda + p.K);
-    const long endB = TB ? 4L * ((long)(p.N - 1 - n0) * p.ldb + p.K) : 4L * ((long)(p.K - 1) * p.ldb + p.N - n0);
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cornerA + kr * kstrideA), (short)0, buffer_range(endA - 4L * kr * kstrideA), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cornerB + kr * kstrideB), (short)0, buffer_range(endB - 4L * kr * kstrideB), 0x00020000);
-    const unsigned stepA = 4u * BK * (unsigned)kstrideA, stepB = 4u * BK * (unsigned)kstrideB;
+    const long rowsA = min(BM, p.M - m0), colsB = min(BN, p.N - n0);
+    const int rangeA = (int)(TA ? 4L * ((long)(BK - 1) * p.lda + rowsA) : 4L * ((rowsA - 1) * p.lda + BK));
+    const int rangeB = (int)(TB ? 4L * ((colsB - 1) * p.ldb + BK) : 4L * ((long)(BK - 1) * p.ldb + colsB));
+    auto tile_rsrc = [](const float *corner, long kstride, long kfirst, int range) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(corner + kfirst * kstride), (short)0, range, 0x00020000);
+    };
 
-    // Loads of tile t >= tail (a full tile).  (The explicit int conversions
-    // matter: with the array element passed as is, the host pass drops the
-    // kernel and its launch stub.)
+    // Loads of tile t >= tail (a full tile, k from kr + (t - tail) * BK).
+    // (The explicit int conversions matter: with the array element passed as
+    // is, the host pass drops the kernel and its launch stub.)
     auto issue_one = [&](int t, float *stage, int i) {
-        const unsigned tf = (unsigned)max(t - tail, 0);
+        const long kfirst = kr + (long)max(t - tail, 0) * BK;
         if (i < NA)
-            dma<DW>(rsA, (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP), (int)offA[i], (int)(tf * stepA));
+            dma<DW>(tile_rsrc(cornerA, kstrideA, kfirst, rangeA), (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP),
+                    (int)offA[i], 0);
         else
-            dma<DW>(rsB, (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP), (int)offB[i - NA],
-                    (int)(tf * stepB));
+            dma<DW>(tile_rsrc(cornerB, kstrideB, kfirst, rangeB),
+                    (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP), (int)offB[i - NA], 0);
     };
     // Loads of the K remainder tile, on descriptors based at k = 0.
     auto issue_remainder = [&](float *stage) {
-        const __amdgpu_buffer_rsrc_t rA0 =
-            __builtin_amdgcn_make_buffer_rsrc((void *)cornerA, (short)0, buffer_range(endA), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rB0 =
-            __builtin_amdgcn_make_buffer_rsrc((void *)cornerB, (short)0, buffer_range(endB), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rA0 = tile_rsrc(cornerA, kstrideA, 0, rangeA);
+        const __amdgpu_buffer_rsrc_t rB0 = tile_rsrc(cornerB, kstrideB, 0, rangeB);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             int m, k;

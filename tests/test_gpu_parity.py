@@ -241,3 +241,18 @@ def test_split_k_variants_forced(variant, shape):
     check_close(c1.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=0.5, beta=-1.5),
                 f"{capi.sgemm_variant_name(variant)} {shape}")
     assert torch.equal(c1, c2)
+
+
+def test_operand_over_2gib():
+    """B of 65536 x 8192 floats (2 GiB): the lean kernel gives every K tile
+    its own descriptor base, so operands past the 31-bit buffer range stay on
+    it; sampled against the oracle, corners included."""
+    torch = torch_cuda()
+    M, N, K = 128, 8192, 65536
+    A, B, _ = make_problem(M, N, K, 21)
+    assert B.nbytes >= 2 ** 31
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    C = sgemm(dA, dB)
+    torch.cuda.synchronize()
+    I, J = sample_indices(M, N, 21, n=512)
+    check_close(C.cpu().numpy()[I, J], oracle.sgemm_ref_sampled(A, B, I, J), "2 GiB operand")
