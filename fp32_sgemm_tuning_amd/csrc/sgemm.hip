@@ -540,16 +540,11 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
 
     // 16-byte loads: aligned operands with leading dimensions and strides
     // that are multiples of 4, and the edge chunks of each stored operand
-    // whole (its contiguous extent a multiple of 4).  A transposed A takes
-    // them only on the 128x128x32 tile; the 4-byte gather it needs on the
-    // 64x64 tile costs about twice as much, so the larger tile is kept for
-    // it whenever its grid has at least 160 tiles.
+    // whole (its contiguous extent a multiple of 4).
     const bool strides4 = batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0);
-    const bool aligned = strides4 && vec_ok(K, A, lda, B, ldb, beta, C, ldc) && (ta ? M : K) % 4 == 0 &&
-                         (tb ? K : N) % 4 == 0;
-    bool tile64 = prefer_64(M, N, batch);
-    if (tile64 && ta && aligned && ceil_div(M, 128) * ceil_div(N, 128) * batch >= 160) tile64 = false;
-    const bool vec = aligned && !(tile64 && ta);
+    const bool vec = strides4 && vec_ok(K, A, lda, B, ldb, beta, C, ldc) && (ta ? M : K) % 4 == 0 &&
+                     (tb ? K : N) % 4 == 0;
+    const bool tile64 = prefer_64(M, N, batch);
     const int bm = tile64 ? 64 : 128, bn = bm, bk = tile64 ? 64 : 32;
     const bool lean = K >= bk && lean_fits(bm, bn, bk, lda, ldb, ta, tb);
 

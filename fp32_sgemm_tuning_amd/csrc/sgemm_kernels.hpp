@@ -277,12 +277,17 @@ struct ALayout<64> {
 // TA / TB (lean kernels only): the operand is stored transposed and kept in
 // LDS in its stored orientation, loaded with the same 16-byte runs as the
 // untransposed operands.
-//   - TA: the A stage is [BK][BM], m contiguous (the geometry of the B
-//     stage).  A lane's ds_read_b128 at k holds four consecutive rows
-//     4*(lane%16) + {0..3} of the 64-row wave tile; element ir feeds the
-//     MFMA of row group ir, whose local row rho is real row 4*rho + ir.  The
-//     four reads of a 16-deep half are the four k steps, so the count of
-//     reads and MFMAs is the untransposed one.  Needs 64-row wave tiles.
+//   - TA with 64-row wave tiles: the A stage is [BK][BM], m contiguous (the
+//     geometry of the B stage).  A lane's ds_read_b128 at k holds four
+//     consecutive rows 4*(lane%16) + {0..3} of the wave tile; element ir
+//     feeds the MFMA of row group ir, whose local row rho is real row
+//     4*rho + ir.  The four reads of a 16-deep half are the four k steps, so
+//     the count of reads and MFMAs is the untransposed one.
+//   - TA with smaller wave tiles: the same [BK][BM] stage with the 16-byte
+//     chunks of row k XOR-swizzled by ta_swz(k), read one float per lane
+//     (ds_read_b32) in the untransposed fragment order: four reads per 16-row
+//     slab and half instead of one.  The four k rows a wave reads at once
+//     (k = 4*(lane/16) + j) land on four disjoint chunk groups.
 //   - TB: the B stage is [BN][BK], k contiguous, in the swizzled A layout
 //     (row n instead of m), read like A: the read for column group ic holds
 //     four k steps of row n = 64*nj + 16*ic + lane%16, so MFMA column c of
@@ -304,7 +309,11 @@ struct TileOps {
     static_assert(BK == 16 || BK == 32 || BK == 64, "BK");
     static_assert(BM % 32 == 0, "A layout pairs 16-row slabs");
     static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "load split");
-    static_assert(!TA || MI == 4, "transposed A stage needs 64-row wave tiles");
+    static constexpr bool TA_RG = TA && MI == 4;       // row-group reads of the transposed A stage
+    static constexpr bool TA_W = TA && MI != 4;        // word reads of the swizzled transposed A stage
+    static constexpr int NREAD_A = TA_W ? 4 * MI : MI; // A fragment reads per 16-deep half
+    // chunk swizzle of row k of the word-read transposed A stage
+    static __host__ __device__ constexpr int ta_swz(int k) { return 4 * ((k >> 2) & 3); }
 
     struct Staging {
         f32x4 a[A_PER];
@@ -409,7 +418,7 @@ struct TileOps {
     template <int R>
     static __device__ __forceinline__ void read_all(const float *stage, int wm, int wn, int lane, int h, Frags &f,
                                                     IntSeq<R>) {
-        if constexpr (R < MI + 4 * NJ) {
+        if constexpr (R < NREAD) {
             read_one<R>(stage, wm, wn, lane, h, f);
             read_all(stage, wm, wn, lane, h, f, IntSeq<R + 1>{});
         }
@@ -417,14 +426,14 @@ struct TileOps {
 
     // Single items, for kernels that place every instruction explicitly.
     static constexpr int NMFMA = MI * NJ * 16;     // MFMAs per fragment set
-    static constexpr int NREAD = MI + 4 * NJ;      // fragment reads per set
+    static constexpr int NREAD = NREAD_A + 4 * NJ; // fragment reads per set
     // MFMA number q: q = ((j * MI + mi) * NJ + nj) * 4 + i
     template <int Q>
     static __device__ __forceinline__ void mma_one(f32x4 (&acc)[MI][NJ][4], const Frags &f) {
         constexpr int i = Q % 4, nj = (Q / 4) % NJ, mi = (Q / (4 * NJ)) % MI, j = Q / (4 * NJ * MI);
         // TA: f.a[j] holds the four row groups of k step j; TB: f.b[i][nj]
         // holds the four k steps of column group i
-        const float a = TA ? f.a[j][mi] : f.a[mi][j];
+        const float a = TA_RG ? f.a[j][mi] : f.a[mi][j];
         const float b = TB ? f.b[i][nj][j] : f.b[j][nj][i];
         acc[mi][nj][i] = mfma_16x16x4(a, b, acc[mi][nj][i]);
     }
@@ -434,18 +443,24 @@ struct TileOps {
     static __device__ __forceinline__ void read_one(const float *stage, int wm, int wn, int lane, int h, Frags &f) {
         const int lrow = lane & 15;
         const int lq = lane >> 4;
-        if constexpr (R < MI) {
-            if constexpr (TA)
+        if constexpr (R < NREAD_A) {
+            if constexpr (TA_RG) {
                 f.a[R] = *reinterpret_cast<const f32x4 *>(stage + (16 * h + 4 * lq + R) * BM + wm * WM + 4 * lrow);
-            else
+            } else if constexpr (TA_W) {
+                constexpr int mi = R / 4, j = R % 4;
+                const int k = 16 * h + 4 * lq + j;
+                const int m = wm * WM + mi * 16 + lrow;
+                f.a[mi][j] = stage[k * BM + 4 * ((m >> 2) ^ ta_swz(k)) + (m & 3)];
+            } else {
                 f.a[R] =
                     *reinterpret_cast<const f32x4 *>(stage + ALayout<BK>::offset(wm * WM + R * 16 + lrow, 4 * h + lq));
+            }
         } else if constexpr (TB) {
-            constexpr int ic = (R - MI) / NJ, nj = (R - MI) % NJ;
+            constexpr int ic = (R - NREAD_A) / NJ, nj = (R - NREAD_A) % NJ;
             f.b[ic][nj] = *reinterpret_cast<const f32x4 *>(
                 stage + BM * BK + ALayout<BK>::offset(wn * WN + nj * 64 + 16 * ic + lrow, 4 * h + lq));
         } else {
-            constexpr int j = (R - MI) / NJ, nj = (R - MI) % NJ;
+            constexpr int j = (R - NREAD_A) / NJ, nj = (R - NREAD_A) % NJ;
             f.b[j][nj] = *reinterpret_cast<const f32x4 *>(stage + BM * BK + (16 * h + 4 * lq + j) * BN + wn * WN +
                                                           nj * 64 + 4 * lrow);
         }
@@ -481,7 +496,8 @@ struct TileOps {
                 for (int r = 0; r < 4; ++r) {
                     // TA: MFMA row rho = 4*(lane/16) + r of row group mi is
                     // real row 4*rho + mi
-                    const int row = m0 + wm * WM + (TA ? 16 * (lane >> 4) + 4 * r + mi : mi * 16 + 4 * (lane >> 4) + r);
+                    const int row =
+                        m0 + wm * WM + (TA_RG ? 16 * (lane >> 4) + 4 * r + mi : mi * 16 + 4 * (lane >> 4) + r);
                     if constexpr (TB) {
                         // column group i is real column 16*i + lane%16
 #pragma unroll

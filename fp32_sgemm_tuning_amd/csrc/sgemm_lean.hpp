@@ -185,7 +185,7 @@ sgemm_lean_kernel(Args p) {
     constexpr int NA = BM * BK / EW / T::NT;
     constexpr int NB = BK * BN / EW / T::NT;
     constexpr int NM = T::MI * T::NJ * 16;
-    constexpr int NR = T::MI + 4 * T::NJ;
+    constexpr int NR = T::NREAD;
     constexpr int LS = KH == 4 ? 2 : 1;                     // sections carrying the loads
     constexpr int PER = (NA + NB + LS - 1) / LS;
     __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
@@ -205,10 +205,10 @@ sgemm_lean_kernel(Args p) {
     // that of the logical (row, k) the swizzled layout keeps there.
     auto a_coords = [&](int i, int &m, int &k) {
         const int u = (i * NWAVES + wave) * 64 + lane;
-        if constexpr (LTA) {            // [BK][BM] stage
-            const int g = u * EW;
-            k = g / BM;
-            m = g % BM;
+        if constexpr (LTA) {            // [BK][BM] stage (chunks swizzled for word reads)
+            k = u / (BM / 4);
+            const int slot = u % (BM / 4);
+            m = 4 * (T::TA_W ? slot ^ T::ta_swz(k) : slot);
         } else {
             int c;
             ALayout<BK>::inverse(DW ? u / 4 : u, m, c);
