@@ -14,7 +14,10 @@ one JSON line.
 
 --sweep times the given variant ids (comma separated; -1 = the automatic
 choice, "mm" = torch.mm in FP32 for context, "op:TN" and the like = sgemm_op
-with the operands stored transposed as named) on problems of the given sizes
+with the operands stored transposed as named, "lowp:bf16" / "lowp:f16" =
+sgemm_lowp on the same values in that 16-bit type ("lowp:bf16:V" forces
+sgemm_lowp_ex variant V), "mm:bf16" / "mm:f16" =
+torch.mm in that type, 16-bit output, for context) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike, and prints one JSON line per (size, variant) with the
 median kernel time.  It is the evidence behind the automatic tile choice.
@@ -40,7 +43,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_sq4096.txt")
 
 
 KERNEL_SOURCES = ("sgemm.hip", "sgemm_kernels.hpp", "sgemm_lean.hpp", "sgemm_lean.hip", "sgemm_lean_split.hip",
-                  "sgemm_lean_ops.hip")
+                  "sgemm_lean_ops.hip", "sgemm_lowp.hip")
 
 
 def kernel_source_hash():
@@ -149,7 +152,7 @@ def sweep(variants, sizes, rounds):
 
     import torch
 
-    from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm, sgemm_op
+    from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm, sgemm_lowp, sgemm_op
     from fp32_sgemm_tuning_amd.inputs import make_problem
     torch.backends.cuda.matmul.allow_tf32 = False
     capi.load()
@@ -160,15 +163,42 @@ def sweep(variants, sizes, rounds):
         flop = 2 * M * N * K
         reps = max(5, min(200, int(2e11 / max(flop, 1))))
 
-        stored = {}
+        stored, half = {}, {}
         for v in variants:
             if isinstance(v, str) and v.startswith("op:"):
                 ta, tb = v[3] == "T", v[4] == "T"
                 stored[v] = (dA.t().contiguous() if ta else dA, dB.t().contiguous() if tb else dB, ta, tb)
+            if isinstance(v, str) and v.split(":")[0] in ("lowp", "mm") and ":" in v:
+                t = {"bf16": torch.bfloat16, "f16": torch.float16}[v.split(":")[1]]
+                half[v] = (dA.to(t), dB.to(t), torch.empty((M, N), dtype=t, device="cuda"))
+
+        def label(v):
+            if v == "mm":
+                return "torch.mm fp32"
+            if v in stored:
+                return "sgemm_op " + v[3:5]
+            if v in half:
+                if v.startswith("lowp"):
+                    parts = v.split(":")
+                    var = int(parts[2]) if len(parts) > 2 else capi.sgemm_lowp_select_variant(
+                        M, N, K, half[v][0].data_ptr(), K, half[v][1].data_ptr(), N)
+                    return f"sgemm_lowp {parts[1]} {capi.sgemm_lowp_variant_name(var)}"
+                return "torch.mm " + v.split(":")[1]
+            if v == -1:
+                return "auto:" + capi.sgemm_variant_name(capi.sgemm_select_variant(
+                    M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dC.data_ptr(), N))
+            return capi.sgemm_variant_name(v)
 
         def run(v):
             if v == "mm":
                 torch.mm(dA, dB, out=dC)
+            elif v in half:
+                a16, b16, c16 = half[v]
+                if v.startswith("lowp"):
+                    parts = v.split(":")
+                    sgemm_lowp(a16, b16, dC, variant=int(parts[2]) if len(parts) > 2 else None)
+                else:
+                    torch.mm(a16, b16, out=c16)
             elif v in stored:
                 sa, sb, ta, tb = stored[v]
                 sgemm_op(sa, sb, dC, trans_a=ta, trans_b=tb)
@@ -181,7 +211,7 @@ def sweep(variants, sizes, rounds):
                     run(v)
                 usable.append(v)
             except SgemmError as e:      # e.g. a 128-bit variant on unaligned rows
-                print(json.dumps({"sweep": capi.sgemm_variant_name(v), "variant": v, "shape": f"{M}x{N}x{K}",
+                print(json.dumps({"sweep": label(v), "variant": v, "shape": f"{M}x{N}x{K}",
                                   "skipped": str(e)}), flush=True)
         torch.cuda.synchronize()
         times = {v: [] for v in usable}
@@ -198,16 +228,7 @@ def sweep(variants, sizes, rounds):
                 times[v] += [a.elapsed_time(b) for a, b in evs]
         for v in usable:
             ms = statistics.median(times[v])
-            if v == "mm":
-                name = "torch.mm fp32"
-            elif v in stored:
-                name = "sgemm_op " + v[3:5]
-            elif v == -1:
-                name = "auto:" + capi.sgemm_variant_name(capi.sgemm_select_variant(
-                    M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dC.data_ptr(), N))
-            else:
-                name = capi.sgemm_variant_name(v)
-            print(json.dumps({"sweep": name, "variant": v, "shape": f"{M}x{N}x{K}", "median_ms": round(ms, 5),
+            print(json.dumps({"sweep": label(v), "variant": v, "shape": f"{M}x{N}x{K}", "median_ms": round(ms, 5),
                               "tflops": round(flop / ms / 1e9, 2)}), flush=True)
 
 
@@ -233,7 +254,7 @@ def main():
         sys.exit(2)
 
     if args.sweep is not None:
-        variants = [v if v == "mm" or v.startswith("op:") else int(v) for v in args.sweep.split(",")]
+        variants = [v if v == "mm" or ":" in v else int(v) for v in args.sweep.split(",")]
         sweep(variants, [parse_shape(x) for x in args.sweep_sizes.split(",")], args.rounds)
         return
 

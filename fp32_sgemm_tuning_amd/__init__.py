@@ -7,7 +7,7 @@ HIP stream.  PyTorch only supplies device memory and streams.
 """
 from . import capi
 
-__all__ = ["sgemm", "sgemm_op", "SgemmError", "capi", "variant_names"]
+__all__ = ["sgemm", "sgemm_op", "sgemm_lowp", "SgemmError", "capi", "variant_names"]
 
 
 class SgemmError(RuntimeError):
@@ -19,10 +19,10 @@ class SgemmError(RuntimeError):
         self.status = status
 
 
-def _ld(t, name):
+def _ld(t, name, dtypes=None):
     import torch
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
+    if t.dtype not in (dtypes or (torch.float32,)):
+        raise TypeError(f"{name} must be " + " or ".join(str(d).replace("torch.", "") for d in (dtypes or (torch.float32,))))
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
     if t.device.type != "cuda":
@@ -131,6 +131,38 @@ def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, st
         else:
             st = capi.sgemm_op(op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
                                float(beta), C.data_ptr(), ldc, s.cuda_stream)
+    if st != capi.SGEMM_STATUS_OK:
+        raise SgemmError(st)
+    return C
+
+
+def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
+    """C = alpha * A @ B + beta * C with bfloat16 or float16 A [M,K] and B
+    [K,N] (one type for both, unit column stride) and FP32 accumulation; C
+    is float32 [M,N] (allocated when None, then beta must be 0); returns C.
+    ``variant`` forces a kernel variant (tests and sweeps)."""
+    import torch
+    codes = {torch.bfloat16: capi.SGEMM_DTYPE_BF16, torch.float16: capi.SGEMM_DTYPE_F16}
+    lda = _ld(A, "A", tuple(codes))
+    ldb = _ld(B, "B", tuple(codes))
+    if B.dtype != A.dtype:
+        raise TypeError(f"A is {A.dtype} but B is {B.dtype}")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
+    ldc = _ld(C, "C")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                float(beta), C.data_ptr(), ldc, s.cuda_stream)
+        st = capi.sgemm_lowp(*args) if variant is None else capi.sgemm_lowp_ex(*args, int(variant))
     if st != capi.SGEMM_STATUS_OK:
         raise SgemmError(st)
     return C

@@ -16,6 +16,10 @@ SGEMM_STATUS_HIP_ERROR = -3
 SGEMM_STATUS_INVALID_VARIANT = -4
 SGEMM_STATUS_UNSUPPORTED = -5
 SGEMM_STATUS_INVALID_OP = -6
+SGEMM_STATUS_INVALID_DTYPE = -7
+
+SGEMM_DTYPE_BF16 = 1
+SGEMM_DTYPE_F16 = 2
 
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
@@ -29,7 +33,8 @@ SGEMM_VARIANT_DB128_SCALAR = 2
 EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
-           "sgemm_cm_strided_batched")
+           "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
+           "sgemm_lowp_variant_name")
 
 _lib = None
 
@@ -78,6 +83,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                        ("sgemm_strided_batched", batched_args), ("sgemm_cm_strided_batched", batched_args)):
         getattr(lib, name).argtypes = args
         getattr(lib, name).restype = i
+    lib.sgemm_lowp.argtypes = [i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
+    lib.sgemm_lowp.restype = i
+    lib.sgemm_lowp_ex.argtypes = [i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, i]
+    lib.sgemm_lowp_ex.restype = i
+    lib.sgemm_lowp_select_variant.argtypes = [i, i, i, vp, i, vp, i]
+    lib.sgemm_lowp_select_variant.restype = i
+    lib.sgemm_lowp_variant_name.argtypes = [i]
+    lib.sgemm_lowp_variant_name.restype = cp
     lib.sgemm_split_factor.argtypes = [i, i, i, i]
     lib.sgemm_split_factor.restype = i
     lib.sgemm_strerror.argtypes = [i]
@@ -135,6 +148,31 @@ def sgemm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, be
 def sgemm_cm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch, stream):
     return load().sgemm_cm_strided_batched(op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc,
                                            batch, stream)
+
+
+def sgemm_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    return load().sgemm_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_lowp_ex(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant):
+    return load().sgemm_lowp_ex(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
+
+
+def sgemm_lowp_select_variant(M, N, K, A, lda, B, ldb):
+    return load().sgemm_lowp_select_variant(M, N, K, A, lda, B, ldb)
+
+
+def sgemm_lowp_variant_name(variant):
+    s = load().sgemm_lowp_variant_name(variant)
+    return None if s is None else s.decode()
+
+
+def lowp_variants():
+    """Every sgemm_lowp_ex variant id."""
+    n = 0
+    while sgemm_lowp_variant_name(n) is not None:
+        n += 1
+    return list(range(n))
 
 
 def sgemm_split_factor(variant, M, N, K):

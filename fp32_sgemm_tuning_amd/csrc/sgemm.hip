@@ -38,6 +38,7 @@ void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
+void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
@@ -312,6 +313,16 @@ void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStrea
 
 void launch_simple(const Args &a, hipStream_t stream) { launch_simple_general(a, false, false, 1, stream); }
 
+// The plain kernel on 16-bit inputs (each element widened to FP32 on load).
+void launch_simple_lowp(const Args &a0, bool f16, hipStream_t stream) {
+    const Args a = tiled(a0, 64, 64);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+    if (f16)
+        hipLaunchKernelGGL((sgemm_simple_kernel<false, false, kF16>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_simple_kernel<false, false, kBF16>), grid, dim3(256), 0, stream, a);
+}
+
 struct VariantDesc {
     const char *name;
     int bm, bn, bk;
@@ -559,9 +570,126 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     return SGEMM_STATUS_OK;
 }
 
+// 16-bit inputs, FP32 accumulation and output.  Variant 0 is the plain
+// kernel (any shape); the others are the direct-to-LDS kernel on a block
+// tile and a number of LDS stages (`tile` of launch_lowp_tile = id - 1).
+struct LowpVariant {
+    const char *name;
+    int bm, bn, bk;
+};
+const LowpVariant kLowpVariants[] = {
+    {"lowp_simple_64x64", 64, 64, 16},
+    {"lowp_128x128x64_s2", 128, 128, 64},
+    {"lowp_256x128x64_s3", 256, 128, 64},
+    {"lowp_256x256x32_s4", 256, 256, 32},
+    {"lowp_256x256x32_s5", 256, 256, 32},
+};
+constexpr int kNumLowpVariants = (int)(sizeof(kLowpVariants) / sizeof(kLowpVariants[0]));
+
+// Whether the direct-to-LDS kernel of a bm x bn tile takes the operands: its
+// loads are 16-byte chunks of 8 elements (aligned rows, N and K multiples of
+// 8), K >= 64 keeps every K tile inside the operands (the remainder tile is
+// taken first), and the buffer ranges of one block tile's part of a K tile
+// fit in 31 bits.
+bool lowp_fast_ok(const LowpVariant &v, int N, int K, const void *A, int lda, const void *B, int ldb) {
+    const long lim = 0x7fffffffL;
+    return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && N % 8 == 0 && K % 8 == 0 && K >= v.bk &&
+           2L * ((long)v.bm * lda + v.bk) < lim && 2L * ((long)v.bk * ldb + v.bn) < lim;
+}
+
+// Automatic choice among the 128x128 two-stage (two workgroups per compute
+// unit), 256x128 three-stage and 256x256 five-stage kernels (one per compute
+// unit): the least predicted time, waves of workgroups x tile area x
+// workgroups per wave / the kernel's measured large-problem rate (1.05, 1.2
+// and 1.3 PFLOP/s on MI355X).  Shapes none of them takes run the plain
+// kernel.
+int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
+    struct Cand {
+        int id, slots;
+        double rate;
+    };
+    const Cand cands[] = {{1, 512, 1.05}, {2, 256, 1.2}, {4, 256, 1.3}};
+    int best = 0;
+    double best_t = 0.0;
+    for (const Cand &c : cands) {
+        const LowpVariant &v = kLowpVariants[c.id];
+        if (!lowp_fast_ok(v, N, K, A, lda, B, ldb)) continue;
+        const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
+        const double t = (double)ceil_div(tiles, c.slots) * v.bm * v.bn * c.slots / c.rate;
+        if (best == 0 || t < best_t) {
+            best = c.id;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+int run_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+             float beta, float *C, int ldc, void *stream, int variant) {
+    if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_STATUS_INVALID_DTYPE;
+    const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
+    const int st = check_args(M, N, K, Af, lda, Bf, ldb, C, ldc);
+    if (st != SGEMM_STATUS_OK) return st;
+    if (variant < SGEMM_VARIANT_AUTO || variant >= kNumLowpVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    if (M == 0 || N == 0) return SGEMM_STATUS_OK;
+    if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
+    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb);
+    const LowpVariant &v = kLowpVariants[variant];
+    if (variant > 0 && !lowp_fast_ok(v, N, K, A, lda, B, ldb)) return SGEMM_STATUS_UNSUPPORTED;
+    Args a;
+    a.A = Af;
+    a.B = Bf;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = a.tiles_n = 0;   // set by each launcher from its tile
+    a.group_m = knobs().group_m;
+    a.xcd_remap = knobs().xcd_remap;
+    a.splits = 1;
+    a.ws = nullptr;
+    a.counters = nullptr;
+    a.strideA = a.strideB = a.strideC = 0;
+    const bool f16 = dtype == SGEMM_DTYPE_F16;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (variant > 0)
+        launch_lowp_tile(a, f16, variant - 1, s);
+    else
+        launch_simple_lowp(a, f16, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip_error(e, "kernel launch");
+    return SGEMM_STATUS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sgemm_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+               float beta, float *C, int ldc, void *stream) {
+    return run_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
+}
+
+int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+                  float beta, float *C, int ldc, void *stream, int variant) {
+    return run_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+int sgemm_lowp_select_variant(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    return lowp_auto(M, N, K, A, lda, B, ldb);
+}
+
+const char *sgemm_lowp_variant_name(int variant) {
+    return variant >= 0 && variant < kNumLowpVariants ? kLowpVariants[variant].name : nullptr;
+}
+
 
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, void *stream) {
@@ -642,6 +770,7 @@ const char *sgemm_strerror(int status) {
         case SGEMM_STATUS_INVALID_VARIANT: return "unknown kernel variant";
         case SGEMM_STATUS_UNSUPPORTED: return "variant needs 16-byte aligned pointers and leading dimensions";
         case SGEMM_STATUS_INVALID_OP: return "operation code is neither SGEMM_OP_N nor SGEMM_OP_T";
+        case SGEMM_STATUS_INVALID_DTYPE: return "input type is neither SGEMM_DTYPE_BF16 nor SGEMM_DTYPE_F16";
         default: return "unknown status";
     }
 }

@@ -28,6 +28,8 @@ namespace sgemm_mi355x {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Args {
+    // (the 16-bit-input kernels keep 16-bit elements behind A and B, with lda
+    // and ldb counted in those elements)
     const float *A;
     const float *B;
     float *C;
@@ -79,7 +81,8 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
 // the logical ids are then walked in groups of `group_m` tile rows, column
 // by column inside a group, so tiles that run together share rows of A and
 // columns of B.
-__device__ __forceinline__ void tile_coords(const Args &p, int &tm, int &tn) {
+template <class P>
+__device__ __forceinline__ void tile_coords(const P &p, int &tm, int &tn) {
     int bid = blockIdx.x;
     const int nwg = gridDim.x;
     if (p.xcd_remap) {
@@ -103,10 +106,29 @@ __device__ __forceinline__ void tile_coords(const Args &p, int &tm, int &tn) {
 // per-thread multiply-add replaced by MFMA.  Four waves in a 2x2 grid, each
 // owning a 32x32 sub-tile (2x2 MFMA tiles).  TA / TB: A is stored as A^T
 // ([K][M], element (i,k) at A[k*lda + i]) / B as B^T ([N][K], element (k,j)
-// at B[j*ldb + k]).  Strided batches by blockIdx.z.  It is also the fallback
-// of the lean kernels for transposed or batched problems they do not take.
+// at B[j*ldb + k]).  Strided batches by blockIdx.z.  E: the element type of
+// A and B (FP32, or BF16 / FP16 widened exactly to FP32 on load).  It is
+// also the fallback of the lean kernels for transposed or batched problems
+// and of the 16-bit-input kernel for shapes they do not take.
 // ---------------------------------------------------------------------------
-template <bool TA, bool TB>
+// Element types of the inputs A and B.
+enum ElemType { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Element e of an input array of element type E, widened to FP32 (exact for
+// the 16-bit formats).
+template <int E>
+__device__ __forceinline__ float load_elem(const float *base, long e) {
+    if constexpr (E == kF32) {
+        return base[e];
+    } else if constexpr (E == kBF16) {
+        const unsigned short bits = reinterpret_cast<const unsigned short *>(base)[e];
+        return __uint_as_float((unsigned)bits << 16);
+    } else {
+        return (float)reinterpret_cast<const _Float16 *>(base)[e];
+    }
+}
+
+template <bool TA, bool TB, int E = kF32>
 __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
     constexpr int BM = 64, BN = 64, BK = 16;
     batch_offset(p);
@@ -128,12 +150,14 @@ __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
         for (int e = tid; e < BM * BK; e += 256) {
             const int r = e / BK, c = e % BK;
             const int gi = m0 + r, gk = k0 + c;
-            As[r][c] = (gi < p.M && gk < p.K) ? p.A[TA ? (long)gk * p.lda + gi : (long)gi * p.lda + gk] : 0.0f;
+            As[r][c] = (gi < p.M && gk < p.K) ? load_elem<E>(p.A, TA ? (long)gk * p.lda + gi : (long)gi * p.lda + gk)
+                                              : 0.0f;
         }
         for (int e = tid; e < BK * BN; e += 256) {
             const int r = e / BN, c = e % BN;
             const int gk = k0 + r, gj = n0 + c;
-            Bs[r][c] = (gk < p.K && gj < p.N) ? p.B[TB ? (long)gj * p.ldb + gk : (long)gk * p.ldb + gj] : 0.0f;
+            Bs[r][c] = (gk < p.K && gj < p.N) ? load_elem<E>(p.B, TB ? (long)gj * p.ldb + gk : (long)gk * p.ldb + gj)
+                                              : 0.0f;
         }
         __syncthreads();
         for (int kk = 0; kk < BK; kk += 4) {

@@ -1,0 +1,417 @@
+// GEMM with BF16 or FP16 inputs and FP32 accumulation and output:
+// C = alpha * A * B + beta * C, A [M,K] and B [K,N] row-major 16-bit, C
+// [M,N] row-major FP32.  (Built with MFMA results in VGPRs; see
+// sgemm_lean.hpp.)
+//
+// The kernel is the lean direct-to-LDS design on 16-bit data, with
+// v_mfma_f32_16x16x32_{bf16,f16} (16x16 outputs, 32 k per instruction).
+// Lane layout of that instruction (checked on gfx950 with a probe): lane l
+// supplies A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7, and
+// receives D[4*(l/16) + r][l%16], r = 0..3.
+//
+//   - A stage: rows of the K tile.  BK = 64 gives 128-byte rows in the
+//     swizzled layout of the FP32 kernels (16-byte chunk c of row m at
+//     c ^ ((m/2) % 8)); BK = 32 gives 64-byte rows, two 16-row slabs per
+//     128-byte LDS row (the FP32 kernels' BK = 16 layout).  One ds_read_b128
+//     at chunk 4s + l/16 of row m is the A fragment of k step s.
+//   - B stays in its stored orientation, [k][n] with n contiguous, and is
+//     read with the LDS transpose read ds_read_b64_tr_b16.  Within each group
+//     of 16 lanes it hands lane i element e of the 8-byte row that source lane
+//     4e + i/4 points at, taken at element i%4.  So when the 16 lanes of group
+//     g point at rows k0 + 8g + {0..3} and column runs n0 + 4*{0..3}, lane i
+//     receives B[k0 + 8g + e][n0 + i], e = 0..3: two such reads (rows +0 and
+//     +4) make the B fragment of one 16-column block.  The 32-byte units of a
+//     B row are XOR-swizzled (lowp_b_slot) so that the reads are free of bank
+//     conflicts.
+//   - The product is formed transposed (B fragment first), so each lane holds
+//     four consecutive columns of one C row: 16-byte C stores.
+//   - NSTAGE LDS stages: the loads of K tile t + NSTAGE are issued while tile
+//     t is multiplied, so NSTAGE - 1 tiles are in flight; one barrier per
+//     tile, placed behind the first MFMAs of a step.
+//   - Loads, edges, K remainder and per-tile descriptors as in the lean FP32
+//     kernel, on 16-byte chunks of 8 elements: N and K must be multiples of 8
+//     and the operands' rows 16-byte aligned; other shapes take the plain
+//     kernel with 16-bit loads.
+#include "sgemm_lean.hpp"
+
+namespace sgemm_mi355x {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_ptr;
+
+// f(IntC<I>{}) for I = 0 .. N-1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+}
+
+// Slot of 16-byte chunk c in row k of the B stage: the 32-byte units of a
+// row are XORed with (k % 4) + 4 * ((k / 8) % 2).  A transposed read takes
+// four rows k..k+3 per group of 16 lanes, and the hardware pairs the groups
+// {0,1} and {2,3} of a wave, whose rows differ by 8: measured free of bank
+// conflicts on gfx950 (the XOR with k % 4 alone measured two-way conflicts).
+__host__ __device__ constexpr int lowp_b_slot(int c, int k) {
+    return 2 * ((c >> 1) ^ ((k & 3) | (((k >> 3) & 1) << 2))) + (c & 1);
+}
+
+// 16-byte direct load of one chunk per lane into LDS at lds_base + 16 *
+// lane, through the buffer descriptor {base, range} (raw, stride 0: an
+// offset at or past `range` loads zeros and touches no memory).  Written as
+// inline assembly on purpose: the compiler's wait insertion treats every
+// LDS transpose read issued after a direct-to-LDS load it knows of as a
+// possible reader of that load and waits for all loads in flight first,
+// which would serialise the K pipeline.  Ordering is explicit instead: the
+// stage a load writes is read only after a wait on vmcnt and a barrier.
+__device__ __forceinline__ void dma16_lowp(const char *base, int range, unsigned lds_base, int voffset) {
+    // every operand but the lane offset is wave-uniform; readfirstlane keeps
+    // it in scalar registers where the compiler cannot prove that by itself
+    const unsigned long b = reinterpret_cast<unsigned long>(base);
+    const i32x4 rsrc = {__builtin_amdgcn_readfirstlane((int)(unsigned)b),
+                        __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xffffu)),
+                        __builtin_amdgcn_readfirstlane(range), 0x00020000};
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane((int)lds_base))
+                 : "memory", "m0");
+}
+
+// Number of N items placed at or before slot q when spread evenly over the
+// SPAN slots from FIRST on (all of them from the last slot on).
+constexpr int spread_upto(int q, int N, int FIRST, int SPAN) {
+    return q < FIRST ? 0 : (q >= FIRST + SPAN - 1 || (q - FIRST) * N / SPAN + 1 > N ? N : (q - FIRST) * N / SPAN + 1);
+}
+
+// s_waitcnt with vmcnt <= N, lgkmcnt 0 and expcnt at its maximum (gfx9
+// encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+
+// BM x BN block tile, WAVES_M x WAVES_N waves, NSTAGE LDS stages of one
+// BK-deep K tile each (BK = 64: two k steps per tile, A rows of 128 bytes;
+// BK = 32: one k step, A rows of 64 bytes in the paired-slab layout).
+// VECC: C rows 16-byte aligned (128-bit C access).
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NSTAGE, bool BETA0, bool EDGE, bool F16, bool VECC>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+sgemm_lowp_kernel(Args p) {
+    static_assert(BK == 32 || BK == 64, "K tile");
+    using AL = ALayout<BK / 2>;                             // A stage layout (its unit is 4 bytes)
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int NWAVES = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int MI = WM / 16, NB = WN / 16;               // 16x16 blocks per wave
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+    constexpr int NA = A_BYTES / 16 / NT, NBL = B_BYTES / 16 / NT;
+    constexpr int L = NA + NBL;                             // 16-byte loads per lane per K tile
+    constexpr int BROW = BN * 2;                            // bytes per B stage row
+    constexpr int BCH = BN / 8;                             // 16-byte chunks per B stage row
+    constexpr int NM = MI * NB;                             // MFMAs per k step
+    constexpr int QSYNC = NM / 4 > NB ? NM / 4 : NB;        // MFMAs of a step ahead of the barrier
+    static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "wave tile");
+    static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "load split");
+    static_assert(BN % 128 == 0, "the B swizzle needs eight 32-byte units per row");
+    static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const char *Ab = reinterpret_cast<const char *>(p.A);
+    const char *Bb = reinterpret_cast<const char *>(p.B);
+
+    // direct-load coordinates of load i of this lane: 16-byte chunk u of the
+    // stage; A: (row m, chunk c = 8 elements of k); B: (row k, chunk c of n)
+    auto a_coords = [&](int i, int &m, int &c) { AL::inverse((i * NWAVES + wave) * 64 + lane, m, c); };
+    auto b_coords = [&](int i, int &k, int &c) {
+        const int u = (i * NWAVES + wave) * 64 + lane;
+        k = u / BCH;
+        c = lowp_b_slot(u % BCH, k);                        // the swizzle is its own inverse
+    };
+    unsigned offA[NA], offB[NBL];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        int m, c;
+        a_coords(i, m, c);
+        offA[i] = (EDGE && m0 + m >= p.M) ? kOutOfRange : 2u * (unsigned)(m * (int)p.lda + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        int k, c;
+        b_coords(i, k, c);
+        offB[i] = (EDGE && n0 + 8 * c >= p.N) ? kOutOfRange : 2u * (unsigned)(k * (int)p.ldb + 8 * c);
+    }
+
+    const int kr = EDGE ? p.K % BK : 0;                     // K remainder, taken first
+    const int tail = kr != 0;
+    const int ntiles = p.K / BK + tail;
+    const long rowsA = min(BM, p.M - m0), colsB = min(BN, p.N - n0);
+    const int rangeA = (int)(2L * ((rowsA - 1) * p.lda + BK));
+    const int rangeB = (int)(2L * ((long)(BK - 1) * p.ldb + colsB));
+    const char *cornerA = Ab + 2L * m0 * p.lda, *cornerB = Bb + 2L * n0;
+    // LDS byte address of a point in the stages (wave-uniform)
+    const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>((lds_addr_t)lds);
+    // LDS address of this wave's 1 KiB of load g in stage `st` (A loads
+    // first, then B)
+    auto dst = [&](int st, int g) {
+        return lds0 + (unsigned)(st * STAGE + (g < NA ? 0 : A_BYTES) + ((g < NA ? g : g - NA) * NWAVES + wave) * 1024);
+    };
+    // load g of K tile t into stage `st`.  Tiles past the last get an empty
+    // range: their loads touch no memory and write zeros, so every tile
+    // issues the same number of loads and the vmcnt waits stay constant.
+    auto issue_one = [&](int t, int st, int g) {
+        const bool live = t < ntiles;
+        const long kfirst = kr + (long)max(t - tail, 0) * BK;
+        if (g < NA)
+            dma16_lowp(cornerA + 2 * kfirst, live ? rangeA : 0, dst(st, g), (int)offA[g]);
+        else
+            dma16_lowp(cornerB + 2 * kfirst * p.ldb, live ? rangeB : 0, dst(st, g), (int)offB[g - NA]);
+    };
+    auto issue_remainder = [&]() {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            int m, c;
+            a_coords(i, m, c);
+            dma16_lowp(cornerA, rangeA, dst(0, i), (int)(8 * c < kr ? offA[i] : kOutOfRange));
+        }
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            int k, c;
+            b_coords(i, k, c);
+            dma16_lowp(cornerB, rangeB, dst(0, NA + i), (int)(k < kr ? offB[i] : kOutOfRange));
+        }
+    };
+
+    // Fragments of one k step (32 k): A per 16-row slab, B per 16-column
+    // block.  The B fragments are double-buffered (every MFMA of a step uses
+    // all of them).  The A fragments are not: the MFMAs run slab by slab and
+    // slab mi's fragment for the next step is read right after its last
+    // MFMA of this step, which keeps the 256x256 tile within 256 VGPRs.
+    const int lrow = lane & 15, lg = lane >> 4;
+    i32x4 fa[MI];
+    i32x4 fb[2][NB];
+    auto read_a = [&](int mi, const char *stage, int s) {
+        const int m = wm * WM + mi * 16 + lrow;
+        fa[mi] = *reinterpret_cast<const i32x4 *>(stage + 4 * AL::offset(m, 4 * s + lg));
+    };
+    // B read r of k step s: block r/2, its transposed 8-byte read r%2
+    auto read_b = [&](int r, const char *stage, int s, i32x4 *f) {
+        const int nb = r / 2, half = r % 2;
+        const int k = 32 * s + 8 * lg + 4 * half + (lrow >> 2);
+        const int n = wn * WN + 16 * nb + 4 * (lrow & 3);
+        const int c = n >> 3;
+        const char *addr = stage + A_BYTES + k * BROW + 16 * lowp_b_slot(c, k) + 8 * ((n >> 2) & 1);
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(addr));
+        const i32x2 w = __builtin_bit_cast(i32x2, v);
+        f[nb][2 * half] = w[0];
+        f[nb][2 * half + 1] = w[1];
+    };
+
+    // The product is formed transposed: the B fragment is the instruction's
+    // first operand and the A fragment its second, so block (mi, nb) holds
+    // C^T and lane l receives C[row l%16][columns 4*(l/16) .. +3].
+    f32x4 acc[MI][NB];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One k step: MFMA q = (slab q / NB, block q % NB) from fa and fb[BC].
+    // After MFMA QB-1 (QB a multiple of NB; before MFMA 0 when QB is 0) the
+    // `sync` hook runs; every read of the step comes after it.  After a
+    // slab's last MFMA (and the hook) its A fragment of step `s` of stage
+    // `rs` is read; the B reads of that step
+    // go into fb[1 - BC], spread from the hook to 3/4 of the step; the G
+    // direct loads are spread from the hook to the end.
+    auto step = [&](auto bc, const char *rs, int s, auto qb, auto gcount, auto &&sync, auto &&issue) {
+        constexpr int BC = decltype(bc)::value;
+        constexpr int QB = decltype(qb)::value;
+        constexpr int G = decltype(gcount)::value;
+        constexpr int FIRST = QB > 0 ? QB - 1 : 0;
+        constexpr int RSPAN = NM * 3 / 4 - FIRST, GSPAN = NM - FIRST;
+        static_assert(QB <= NM && RSPAN > 0, "the reads need MFMAs after the hook");
+        if constexpr (QB == 0) {
+            sync();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<0, NM>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            acc[q / NB][q % NB] = mfma_16x16x32<F16>(fb[BC][q % NB], fa[q / NB], acc[q / NB][q % NB]);
+            if constexpr (q == QB - 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                sync();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // slab mi is read after its last MFMA, and not before the hook
+            if constexpr (q == QB - 1)
+                static_for<0, QB / NB>([&](auto mc) { read_a(decltype(mc)::value, rs, s); });
+            if constexpr (q % NB == NB - 1 && q >= QB) read_a(q / NB, rs, s);
+            static_for<spread_upto(q - 1, 2 * NB, FIRST, RSPAN), spread_upto(q, 2 * NB, FIRST, RSPAN)>(
+                [&](auto r) { read_b(decltype(r)::value, rs, s, fb[1 - BC]); });
+            static_for<spread_upto(q - 1, G, FIRST, GSPAN), spread_upto(q, G, FIRST, GSPAN)>(
+                [&](auto g) { issue(decltype(g)::value); });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // Wait until tile t+1 has landed (the loads of the NSTAGE-2 tiles after
+    // it may stay in flight) and this wave's reads are done, then the
+    // barrier: every wave's part of tile t+1 is in LDS and no wave still
+    // reads the stage the next loads overwrite.
+    auto sync_tile = [&]() {
+        wait_vm_lgkm0<(NSTAGE - 2) * L>();
+        __builtin_amdgcn_s_barrier();
+    };
+    // BK = 64: one K tile in stage SC.  Step 0 reads step 1 of the same
+    // stage.  Step 1 runs its first MFMAs, syncs, then reads step 0 of tile
+    // t+1 and loads tile t+NSTAGE into SC.  BK = 32: the one step of tile t
+    // (B fragments in fb[P]) runs its first MFMAs, syncs, loads tile
+    // t+NSTAGE into SC and reads tile t+1.  The MFMAs before the barrier
+    // keep the matrix unit busy while the waves meet.
+    auto tile = [&](int t, auto sc, auto pc) {
+        constexpr int SC = decltype(sc)::value;
+        constexpr int SN = (SC + 1) % NSTAGE;
+        const char *cs = lds + SC * STAGE;
+        const char *ns = lds + SN * STAGE;
+        auto none = [&](int) {};
+        if constexpr (BK == 64) {
+            step(IntC<0>{}, cs, 1, IntC<0>{}, IntC<0>{}, [&]() {}, none);
+            step(IntC<1>{}, ns, 0, IntC<QSYNC>{}, IntC<L>{}, sync_tile, [&](int g) { issue_one(t + NSTAGE, SC, g); });
+        } else {
+            step(pc, ns, 0, IntC<QSYNC>{}, IntC<0>{},
+                 [&]() {
+                     sync_tile();
+#pragma unroll
+                     for (int g = 0; g < L; ++g) issue_one(t + NSTAGE, SC, g);
+                 },
+                 none);
+        }
+    };
+
+    if (ntiles > 0) {
+        if (tail) {
+            issue_remainder();
+        } else {
+#pragma unroll
+            for (int g = 0; g < L; ++g) issue_one(0, 0, g);
+        }
+        static_for<1, NSTAGE>([&](auto sc) {
+#pragma unroll
+            for (int g = 0; g < L; ++g) issue_one(decltype(sc)::value, decltype(sc)::value, g);
+        });
+        wait_vm_lgkm0<(NSTAGE - 1) * L>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) read_a(mi, lds, 0);
+#pragma unroll
+        for (int r = 0; r < 2 * NB; ++r) read_b(r, lds, 0, fb[0]);
+        // unrolled so that the stage (and for BK = 32 the B buffer) of
+        // every tile is a compile-time constant
+        constexpr int U = (BK == 32 && NSTAGE % 2) ? 2 * NSTAGE : NSTAGE;
+        for (int t0 = 0; t0 < ntiles; t0 += U) {
+            static_for<0, U>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                const int t = t0 + u;
+                if (t < ntiles) tile(t, IntC<u % NSTAGE>{}, IntC<u % 2>{});
+            });
+        }
+        // drain: the loads of the tiles past the last write zeros into LDS
+        // and must land before the workgroup ends
+        wait_vmcnt0();
+    }
+
+    // C = alpha * acc (+ beta * C): block (mi, nb) holds row l%16 and
+    // columns 4*(l/16) .. +3 of its 16x16 output block
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = m0 + wm * WM + mi * 16 + lrow;
+            const int col = n0 + wn * WN + nb * 16 + 4 * lg;
+            if (EDGE && row >= p.M) continue;
+            float *dst = p.C + (long)row * p.ldc + col;
+            if constexpr (VECC) {
+                // N is a multiple of 8 here, so a vector starting below N ends below N
+                if (EDGE && col >= p.N) continue;
+                f32x4 o = acc[mi][nb] * alpha;
+                if (!BETA0) o += *reinterpret_cast<const f32x4 *>(dst) * beta;
+                *reinterpret_cast<f32x4 *>(dst) = o;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (EDGE && col + r >= p.N) continue;
+                    float o = alpha * acc[mi][nb][r];
+                    if (!BETA0) o += beta * dst[r];
+                    dst[r] = o;
+                }
+            }
+        }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16>
+void launch_lowp(const Args &a0, hipStream_t stream) {
+    const Args a = tiled(a0, BM, BN);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
+    const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
+    const bool vecc = (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && a.ldc % 4 == 0;
+#define SGEMM_LAUNCH(Z, E, V) \
+    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, Z, E, F16, V>), grid, block, 0, stream, a)
+#define SGEMM_LAUNCH_V(Z, E)              \
+    do {                                  \
+        if (vecc) SGEMM_LAUNCH(Z, E, true); \
+        else SGEMM_LAUNCH(Z, E, false);   \
+    } while (0)
+    if (edge) {
+        if (a.beta == 0.0f) SGEMM_LAUNCH_V(true, true);
+        else SGEMM_LAUNCH_V(false, true);
+    } else {
+        if (a.beta == 0.0f) SGEMM_LAUNCH_V(true, false);
+        else SGEMM_LAUNCH_V(false, false);
+    }
+#undef SGEMM_LAUNCH_V
+#undef SGEMM_LAUNCH
+}
+
+// Launcher called from the C ABI's translation unit; `tile` picks the block
+// tile, K tile, waves and number of stages (the table of variants in the C
+// ABI's translation unit lists them in this order).
+void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
+#define SGEMM_T(BM, BN, BK, WM, WN, NS)                                    \
+    do {                                                                  \
+        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true>(a, s);        \
+        else launch_lowp<BM, BN, BK, WM, WN, NS, false>(a, s);           \
+    } while (0)
+    switch (tile) {
+        case 1: SGEMM_T(256, 128, 64, 2, 4, 3); break;
+        case 2: SGEMM_T(256, 256, 32, 2, 4, 4); break;
+        case 3: SGEMM_T(256, 256, 32, 2, 4, 5); break;
+        default: SGEMM_T(128, 128, 64, 2, 2, 2); break;
+    }
+#undef SGEMM_T
+}
+
+}  // namespace sgemm_mi355x

@@ -96,3 +96,23 @@ def sample_indices(M, N, seed, n=4096):
 def small_int_matrix(rng, shape, lo, hi):
     """Integers in [lo, hi] stored as float32 (exact)."""
     return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def to_16bit_values(x, dtype):
+    """float32 array -> float32 array whose every entry is a value of the
+    16-bit type `dtype` ("bf16": the low 16 bits of each float32 cleared;
+    "f16": numpy's float16 conversion).  A choice of input values, not part of
+    the GEMM: both sides then see the same 16-bit numbers."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def make_problem_16bit(M, N, K, seed, dtype, dist="uniform", with_c=False):
+    """make_problem() with A and B made 16-bit values (to_16bit_values); C_in
+    stays float32.  All three are float32 arrays."""
+    A, B, C = make_problem(M, N, K, seed, dist, with_c)
+    return to_16bit_values(A, dtype), to_16bit_values(B, dtype), C

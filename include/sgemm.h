@@ -60,6 +60,12 @@ extern "C" {
 #define SGEMM_STATUS_UNSUPPORTED (-5)       /* sgemm_ex: variant needs 16-byte alignment the arguments lack */
 #define SGEMM_STATUS_INVALID_OP (-6)        /* an operation code other than SGEMM_OP_N / SGEMM_OP_T */
 
+#define SGEMM_STATUS_INVALID_DTYPE (-7)     /* sgemm_lowp: an input type other than SGEMM_DTYPE_BF16 / _F16 */
+
+/* Input element types of sgemm_lowp. */
+#define SGEMM_DTYPE_BF16 1                  /* bfloat16: 1 sign, 8 exponent, 7 fraction bits */
+#define SGEMM_DTYPE_F16 2                   /* IEEE binary16 */
+
 /* Operation codes of the sgemm_op family. */
 #define SGEMM_OP_N 0                        /* use the stored matrix as is */
 #define SGEMM_OP_T 1                        /* use the transpose of the stored matrix */
@@ -180,6 +186,54 @@ int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alph
                              const float *B, int ldb, long long stride_b,
                              float beta, float *C, int ldc, long long stride_c,
                              int batch, void *stream);
+
+/*
+ * sgemm_lowp: C = alpha * A * B + beta * C with 16-bit inputs and FP32
+ * accumulation and output.  A [M,K] and B [K,N] are row-major arrays of
+ * `dtype` elements (SGEMM_DTYPE_BF16 or SGEMM_DTYPE_F16; lda and ldb count
+ * elements), C [M,N] is row-major FP32.  The product of two 16-bit values is
+ * exact in FP32, so the result is that of sgemm() on the inputs widened to
+ * FP32, up to summation order.  The pages name 16-bit inputs on matrix
+ * units with FP32 accumulation as the step past FP32 ("gpu_matmul",
+ * Conclusion & Next Steps; "The Final Kernel: Retuning Against the
+ * Pipeline", What Could Be Improved, And What It Would Take).
+ *
+ * Fast path: A and B 16-byte aligned, lda, ldb, N and K multiples of 8 and
+ * K >= 32.  It runs the matrix instructions v_mfma_f32_16x16x32_bf16 / _f16
+ * on 128x128, 256x128 or 256x256 block tiles, picked from the shape, with
+ * 16-byte C access when C is 16-byte aligned and ldc a multiple of 4.  Any
+ * other shape runs a plain kernel that widens each element on load.  No
+ * split-K, no workspace.  Argument checks, layout rules and status codes as
+ * for sgemm(), plus SGEMM_STATUS_INVALID_DTYPE, which is checked first.
+ */
+int sgemm_lowp(int dtype, int M, int N, int K, float alpha,
+               const void *A, int lda,
+               const void *B, int ldb,
+               float beta, float *C, int ldc,
+               void *stream);
+
+/*
+ * sgemm_lowp_ex: sgemm_lowp() with the kernel variant forced, for tests and
+ * tile sweeps: SGEMM_VARIANT_AUTO (-1) behaves like sgemm_lowp(), 0 is the
+ * plain kernel (any shape), 1 .. n-1 the matrix-instruction kernel on a block
+ * tile and stage count that sgemm_lowp_variant_name() names.  Returns
+ * SGEMM_STATUS_INVALID_VARIANT for an unknown id and SGEMM_STATUS_UNSUPPORTED
+ * when a variant other than 0 is forced on operands outside its fast path.
+ */
+int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
+                  const void *A, int lda,
+                  const void *B, int ldb,
+                  float beta, float *C, int ldc,
+                  void *stream, int variant);
+
+/* The variant sgemm_lowp() would run for these arguments (no launch; the
+ * pointers are only inspected for alignment), or SGEMM_STATUS_INVALID_DIM. */
+int sgemm_lowp_select_variant(int M, int N, int K,
+                              const void *A, int lda,
+                              const void *B, int ldb);
+
+/* Static name of a sgemm_lowp_ex() variant, or NULL for an unknown id. */
+const char *sgemm_lowp_variant_name(int variant);
 
 /*
  * sgemm_split_factor: the number of workgroups per output tile along K

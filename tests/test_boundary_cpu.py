@@ -61,7 +61,7 @@ def test_version_and_variants(lib):
     assert capi.sgemm_last_hip_error() == ""
 
 
-@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5, -6])
+@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5, -6, -7])
 def test_strerror_known(status):
     s = capi.sgemm_strerror(status)
     assert s and s != "unknown status"
@@ -264,3 +264,65 @@ def test_op_codes_and_batches():
 def test_column_major_leading_dimension_checks(op_a, op_b, lda, ldb, ldc, ok):
     if not ok:
         assert _op(capi.sgemm_cm, op_a, op_b, 3, 5, 7, lda, ldb, ldc) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+def test_lowp_argument_checks():
+    """The 16-bit-input entry point: type code first, then the checks of sgemm()."""
+    f = capi.sgemm_lowp
+    bf, hf = capi.SGEMM_DTYPE_BF16, capi.SGEMM_DTYPE_F16
+    for bad in (0, 3, -1):
+        assert f(bad, 8, 8, 8, 1.0, AL, 8, AL, 8, 0.0, AL, 8, None) == capi.SGEMM_STATUS_INVALID_DTYPE
+    assert f(bf, -1, 8, 8, 1.0, AL, 8, AL, 8, 0.0, AL, 8, None) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(bf, 8, 8, 8, 1.0, AL, 7, AL, 8, 0.0, AL, 8, None) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(hf, 8, 8, 8, 1.0, AL, 8, AL, 7, 0.0, AL, 8, None) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(hf, 8, 8, 8, 1.0, AL, 8, AL, 8, 0.0, AL, 7, None) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(bf, 8, 8, 8, 1.0, None, 8, AL, 8, 0.0, AL, 8, None) == capi.SGEMM_STATUS_NULL_POINTER
+    assert f(bf, 8, 8, 8, 1.0, AL, 8, AL, 8, 0.0, None, 8, None) == capi.SGEMM_STATUS_NULL_POINTER
+    # empty extents: OK without launching, even with NULL pointers
+    assert f(hf, 0, 8, 8, 1.0, None, 8, None, 8, 0.0, None, 8, None) == capi.SGEMM_STATUS_OK
+    assert f(bf, 8, 0, 8, 1.0, None, 8, None, 1, 0.0, None, 1, None) == capi.SGEMM_STATUS_OK
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_16bit_inputs_are_16bit_values(dtype):
+    """The 16-bit-input problems hold values that the 16-bit type represents
+    exactly (a round trip through torch's conversion changes nothing)."""
+    import numpy as np
+    import torch
+    from fp32_sgemm_tuning_amd.inputs import make_problem, make_problem_16bit
+    A, B, C = make_problem_16bit(33, 17, 65, seed=1, dtype=dtype, dist="normal", with_c=True)
+    t = torch.bfloat16 if dtype == "bf16" else torch.float16
+    for x in (A, B):
+        assert x.dtype == np.float32
+        assert np.array_equal(torch.from_numpy(x).to(t).float().numpy(), x)
+    A32, B32, C32 = make_problem(33, 17, 65, seed=1, dist="normal", with_c=True)
+    assert np.array_equal(C, C32)
+    # the 16-bit values are the FP32 draws to within the type's precision
+    rel = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
+    assert np.all(np.abs(A - A32) <= rel * np.abs(A32) + 2.0 ** -24)
+
+
+def test_lowp_variants_and_selection():
+    """Forced 16-bit variants: unknown ids and operands outside a variant's
+    fast path are refused before anything is enqueued; the automatic choice
+    takes the plain kernel for shapes the fast kernels do not take."""
+    bf = capi.SGEMM_DTYPE_BF16
+    ids = capi.lowp_variants()
+    assert len(ids) >= 2 and capi.sgemm_lowp_variant_name(0).startswith("lowp_simple")
+    assert capi.sgemm_lowp_variant_name(len(ids)) is None and capi.sgemm_lowp_variant_name(-1) is None
+    ex = capi.sgemm_lowp_ex
+    assert ex(bf, 64, 64, 64, 1.0, AL, 64, AL, 64, 0.0, AL, 64, None, len(ids)) == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert ex(bf, 64, 64, 64, 1.0, AL, 64, AL, 64, 0.0, AL, 64, None, -2) == capi.SGEMM_STATUS_INVALID_VARIANT
+    for v in ids[1:]:
+        # K below one K tile, K or N not a multiple of 8, misaligned A, odd lda
+        for M, N, K, A, lda, ldb in ((64, 64, 16, AL, 16, 64), (64, 64, 100, AL, 100, 64), (64, 60, 64, AL, 64, 60),
+                                     (64, 64, 64, AL + 2, 64, 64), (64, 64, 64, AL, 68, 64)):
+            assert ex(bf, M, N, K, 1.0, A, lda, AL, ldb, 0.0, AL, N, None, v) == capi.SGEMM_STATUS_UNSUPPORTED
+    sel = capi.sgemm_lowp_select_variant
+    assert sel(64, 64, 16, AL, 16, AL, 64) == 0
+    assert capi.sgemm_lowp_variant_name(sel(64, 64, 32, AL, 32, AL, 64)).endswith(
+        ("x32_s4", "x32_s5", "simple_64x64"))
+    assert sel(3001, 4999, 2047, AL, 2047, AL, 4999) == 0
+    assert sel(4096, 4096, 4096, AL, 4096, AL, 4096) > 0
+    assert sel(4096, 4096, 4096, AL + 2, 4096, AL, 4096) == 0
+    assert sel(-1, 4, 4, AL, 4, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM

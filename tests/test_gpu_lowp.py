@@ -1,0 +1,190 @@
+"""GPU parity of the 16-bit-input entry point (sgemm_lowp: BF16 or FP16 A
+and B, FP32 accumulation and C) against the fp64 CPU oracle.
+
+Every product of two 16-bit values is exact in FP32, so the operation is the
+FP32 GEMM of the same values widened: the oracle receives those values as
+float32 arrays and the parity bar is the FP32 one, |C - C_ref| <= 1e-3 +
+1e-4 |C_ref| elementwise.  The inputs are drawn as for the FP32 workloads and
+made 16-bit values by the input module (bf16: low 16 bits cleared; f16:
+rounded); the device copies are those exact values.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp32_sgemm_tuning_amd import capi, sgemm_lowp
+from fp32_sgemm_tuning_amd.inputs import make_problem_16bit, sample_indices
+from gpu_util import check_close, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["bf16", "f16"]
+
+
+def _tdtype(torch, dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float16
+
+
+def _dev16(x, dtype, torch, ld=None, offset=0, fill=float("nan")):
+    """Device 16-bit copy of the float32 array x (whose values are 16-bit
+    values), inside a buffer with leading dimension ld (padding = fill),
+    starting `offset` elements into the allocation."""
+    rows, cols = x.shape
+    ld = cols if ld is None else ld
+    t16 = torch.from_numpy(np.ascontiguousarray(x)).to(_tdtype(torch, dtype))
+    assert np.array_equal(t16.float().numpy(), x), "input values are not 16-bit values"
+    buf = torch.full((offset + rows * ld + 16,), fill, dtype=_tdtype(torch, dtype), device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(t16.to("cuda"))
+    return view, buf
+
+
+# (M, N, K): fast path (16-byte aligned, lda/ldb/N/K multiples of 8, K >= 64)
+# with whole tiles, odd and even K-tile counts, ragged M and N edges and a K
+# remainder tile taken first; then shapes that take the plain kernel.
+FAST_SHAPES = [
+    (128, 128, 64), (128, 128, 128), (256, 256, 192), (256, 384, 512),
+    (200, 136, 256), (1, 8, 64), (129, 264, 72), (300, 520, 1000), (777, 1032, 136),
+]
+PLAIN_SHAPES = [(1, 1, 1), (7, 5, 3), (64, 64, 56), (130, 131, 129), (3001, 4999, 2047)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", FAST_SHAPES + PLAIN_SHAPES)
+def test_lowp_shapes(dtype, shape):
+    torch = torch_cuda()
+    M, N, K = shape
+    print(f"[lowp] {dtype} {M}x{N}x{K}", flush=True)
+    A, B, Cin = make_problem_16bit(M, N, K, seed=M + 7 * N + 13 * K, dtype=dtype, dist="normal", with_c=True)
+    dA, _ = _dev16(A, dtype, torch)
+    dB, _ = _dev16(B, dtype, torch)
+    for alpha, beta in ((1.0, 0.0), (1.5, -0.5)):
+        dC = torch.from_numpy(Cin).to("cuda") if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+        sgemm_lowp(dA, dB, dC, alpha=alpha, beta=beta)
+        torch.cuda.synchronize()
+        ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+        check_close(dC.cpu().numpy(), ref, f"{dtype} {shape} alpha={alpha} beta={beta}")
+
+
+try:
+    LOWP_VARIANTS = capi.lowp_variants()
+except capi.LibraryMissing:      # collection without a built library
+    LOWP_VARIANTS = [0, 1]
+
+VARIANT_SHAPES = [(256, 256, 128), (300, 520, 1000), (129, 264, 72), (512, 384, 192), (1, 8, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("variant", LOWP_VARIANTS)
+def test_lowp_variants(dtype, variant):
+    """Every kernel variant, forced, on whole and ragged tiles, odd and even
+    K-tile counts (the multi-stage pipelines' wrap-around) and a K
+    remainder."""
+    torch = torch_cuda()
+    for M, N, K in VARIANT_SHAPES:
+        print(f"[lowp] {dtype} variant {variant} {M}x{N}x{K}", flush=True)
+        A, B, Cin = make_problem_16bit(M, N, K, seed=3 * M + N + K, dtype=dtype, dist="normal", with_c=True)
+        dA, _ = _dev16(A, dtype, torch)
+        dB, _ = _dev16(B, dtype, torch)
+        dC = torch.from_numpy(Cin).to("cuda")
+        sgemm_lowp(dA, dB, dC, alpha=-1.25, beta=0.5, variant=variant)
+        torch.cuda.synchronize()
+        check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=-1.25, beta=0.5),
+                    f"{dtype} variant {variant} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lowp_unaligned_c(dtype):
+    """C rows that are not 16-byte aligned take 32-bit C access."""
+    torch = torch_cuda()
+    M, N, K = 130, 136, 128
+    A, B, Cin = make_problem_16bit(M, N, K, seed=17, dtype=dtype, with_c=True)
+    dA, _ = _dev16(A, dtype, torch)
+    dB, _ = _dev16(B, dtype, torch)
+    for ldc, off in ((N + 1, 0), (N, 1)):
+        buf = torch.full((off + M * ldc + 8,), float("nan"), device="cuda")
+        dC = buf[off:off + M * ldc].view(M, ldc)[:, :N]
+        dC.copy_(torch.from_numpy(Cin))
+        sgemm_lowp(dA, dB, dC, alpha=2.0, beta=-1.0)
+        torch.cuda.synchronize()
+        check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=2.0, beta=-1.0), f"ldc={ldc} off={off}")
+        pad = buf[off:off + M * ldc].view(M, ldc)[:, N:]
+        assert torch.isnan(pad).all(), "a column past N was written"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lowp_padded_rows_and_misalignment(dtype):
+    """Leading dimensions beyond the row length, NaN in every padding
+    element (never read), and operands that start off a 16-byte boundary or
+    have leading dimensions that are not multiples of 8 (plain kernel)."""
+    torch = torch_cuda()
+    M, N, K = 200, 264, 200
+    A, B, Cin = make_problem_16bit(M, N, K, seed=11, dtype=dtype, with_c=True)
+    ref = oracle.sgemm_ref(A, B, Cin, alpha=0.75, beta=1.25)
+    for lda, ldb, off in ((208, 272, 0), (K + 3, N + 5, 0), (208, 272, 1), (K, N, 3)):
+        print(f"[lowp] {dtype} {M}x{N}x{K} lda={lda} ldb={ldb} offset={off}", flush=True)
+        dA, _ = _dev16(A, dtype, torch, ld=lda, offset=off)
+        dB, _ = _dev16(B, dtype, torch, ld=ldb, offset=off)
+        dC = torch.from_numpy(Cin).to("cuda")
+        sgemm_lowp(dA, dB, dC, alpha=0.75, beta=1.25)
+        torch.cuda.synchronize()
+        check_close(dC.cpu().numpy(), ref, f"{dtype} lda={lda} ldb={ldb} offset={off}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lowp_sq4096_sampled(dtype):
+    """The 4096^3 square product with 16-bit inputs, checked on a seeded
+    sample of outputs plus the corners and on the first and last 128-row
+    tile rows in full."""
+    torch = torch_cuda()
+    M = N = K = 4096
+    print(f"[lowp] {dtype} 4096^3 (sampled)", flush=True)
+    A, B, _ = make_problem_16bit(M, N, K, seed=2, dtype=dtype)
+    dA, _ = _dev16(A, dtype, torch)
+    dB, _ = _dev16(B, dtype, torch)
+    I, J = sample_indices(M, N, 2)
+    ref = oracle.sgemm_ref_sampled(A, B, I, J)
+    for v in LOWP_VARIANTS[1:]:
+        print(f"[lowp] {dtype} 4096^3 variant {v}", flush=True)
+        check_close(sgemm_lowp(dA, dB, variant=v).cpu().numpy()[I, J], ref, f"{dtype} 4096^3 variant {v} sample")
+    C = sgemm_lowp(dA, dB).cpu().numpy()
+    check_close(C[I, J], ref, f"{dtype} 4096^3 sample")
+    for r0 in (0, M - 128):
+        sl = slice(r0, r0 + 128)
+        check_close(C[sl], oracle.sgemm_ref(np.ascontiguousarray(A[sl]), B), f"{dtype} 4096^3 rows {r0}..")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lowp_special_values(dtype):
+    """K == 0 (C = beta*C), empty M, and exact small-integer products that
+    any summation order gives bit for bit."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    C0 = torch.full((5, 8), 3.0, device="cuda")
+    st = capi.sgemm_lowp(capi.SGEMM_DTYPE_BF16 if dtype == "bf16" else capi.SGEMM_DTYPE_F16, 5, 8, 0, 1.0,
+                         C0.data_ptr(), 1, C0.data_ptr(), 8, -2.0, C0.data_ptr(), 8,
+                         torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == capi.SGEMM_STATUS_OK
+    assert torch.equal(C0, torch.full((5, 8), -6.0, device="cuda"))
+    empty = sgemm_lowp(torch.empty((0, 64), dtype=t, device="cuda"), torch.empty((64, 8), dtype=t, device="cuda"))
+    assert empty.shape == (0, 8)
+    rng = np.random.default_rng(5)
+    M, N, K = 256, 128, 320
+    A = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    B = rng.integers(-8, 9, size=(K, N)).astype(np.float32)
+    C = sgemm_lowp(torch.from_numpy(A).to(t).cuda(), torch.from_numpy(B).to(t).cuda()).cpu().numpy()
+    assert np.array_equal(C.astype(np.float64), oracle.sgemm_ref(A, B))
+
+
+def test_lowp_rejects_mixed_types():
+    torch = torch_cuda()
+    a = torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError):
+        sgemm_lowp(a, a.half())
+    with pytest.raises(TypeError):
+        sgemm_lowp(a.float(), a.float())
+    assert capi.sgemm_lowp(9, 8, 8, 8, 1.0, a.data_ptr(), 8, a.data_ptr(), 8, 0.0, a.data_ptr(), 8, None) == \
+        capi.SGEMM_STATUS_INVALID_DTYPE
+    with pytest.raises(ValueError):
+        sgemm_lowp(a, torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda"))
