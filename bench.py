@@ -42,13 +42,15 @@ METRIC = "SGEMM TFLOP/s (2MNK/t) at M=N=K=4096 FP32; % of MI355X FP32 matrix pea
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_sq4096.txt")
 
 
-KERNEL_SOURCES = ("sgemm.hip", "sgemm_kernels.hpp", "sgemm_lean.hpp", "sgemm_lean.hip", "sgemm_lean_split.hip",
-                  "sgemm_lean_ops.hip", "sgemm_lowp.hip")
+# The translation unit the timed 4096^3 kernel (the lean 128x128x32 kernel)
+# is compiled from, with the headers it includes.
+KERNEL_SOURCES = ("sgemm_kernels.hpp", "sgemm_lean.hpp", "sgemm_lean.hip")
 
 
 def kernel_source_hash():
-    """Hash of the library's device and launch sources: a counter record taken
-    on other kernel code no longer describes the kernel that runs."""
+    """Hash of the timed kernel's sources: a counter record taken on other
+    kernel code no longer describes the kernel that runs (the record also
+    names the variant, so a change of the automatic choice voids it too)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc", name), "rb") as f:
