@@ -582,7 +582,7 @@ const LowpVariant kLowpVariants[] = {
     {"lowp_128x128x64_s2", 128, 128, 64},
     {"lowp_256x128x64_s3", 256, 128, 64},
     {"lowp_256x256x32_s4", 256, 256, 32},
-    {"lowp_256x256x32_s5", 256, 256, 32},
+    {"lowp_256x256x32_s4_alt", 256, 256, 32},
 };
 constexpr int kNumLowpVariants = (int)(sizeof(kLowpVariants) / sizeof(kLowpVariants[0]));
 
@@ -597,25 +597,27 @@ bool lowp_fast_ok(const LowpVariant &v, int N, int K, const void *A, int lda, co
            2L * ((long)v.bm * lda + v.bk) < lim && 2L * ((long)v.bk * ldb + v.bn) < lim;
 }
 
-// Automatic choice among the 128x128 two-stage (two workgroups per compute
-// unit), 256x128 three-stage and 256x256 five-stage kernels (one per compute
-// unit): the least predicted time, waves of workgroups x tile area x
-// workgroups per wave / the kernel's measured large-problem rate (1.05, 1.2
-// and 1.3 PFLOP/s on MI355X).  Shapes none of them takes run the plain
-// kernel.
+// Automatic choice among the 128x128 two-stage kernel (up to two workgroups
+// per compute unit), the 256x128 three-stage kernel and the 256x256
+// four-stage kernel with the alternating schedule (one workgroup per compute
+// unit): the least predicted time, waves of workgroups x tile area / the
+// rate of one workgroup (TFLOP/s measured on MI355X: 2.07 for the 128x128
+// kernel with two per compute unit, 2.25 alone, 4.2 and 5.0 for the larger
+// tiles).  Shapes none of them takes run the plain kernel.
 int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
     struct Cand {
         int id, slots;
-        double rate;
+        double rate, rate_alone;
     };
-    const Cand cands[] = {{1, 512, 1.05}, {2, 256, 1.2}, {4, 256, 1.3}};
+    const Cand cands[] = {{1, 512, 2.07, 2.25}, {2, 256, 4.2, 4.2}, {4, 256, 5.0, 5.0}};
     int best = 0;
     double best_t = 0.0;
     for (const Cand &c : cands) {
         const LowpVariant &v = kLowpVariants[c.id];
         if (!lowp_fast_ok(v, N, K, A, lda, B, ldb)) continue;
         const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
-        const double t = (double)ceil_div(tiles, c.slots) * v.bm * v.bn * c.slots / c.rate;
+        const double rate = tiles <= 256 ? c.rate_alone : c.rate;
+        const double t = (double)ceil_div(tiles, c.slots) * v.bm * v.bn / rate;
         if (best == 0 || t < best_t) {
             best = c.id;
             best_t = t;

@@ -28,6 +28,10 @@
 //   - NSTAGE LDS stages: the loads of K tile t + NSTAGE are issued while tile
 //     t is multiplied, so NSTAGE - 1 tiles are in flight; one barrier per
 //     tile, placed behind the first MFMAs of a step.
+//   - PP (alternating schedule, eight waves): the waves split into two groups
+//     of four, one wave of each per SIMD, that alternate fragment reads and
+//     MFMAs half a tile apart, so that on every SIMD one wave multiplies
+//     while the other reads.
 //   - Loads, edges, K remainder and per-tile descriptors as in the lean FP32
 //     kernel, on 16-byte chunks of 8 elements: N and K must be multiples of 8
 //     and the operands' rows 16-byte aligned; other shapes take the plain
@@ -110,10 +114,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // BK-deep K tile each (BK = 64: two k steps per tile, A rows of 128 bytes;
 // BK = 32: one k step, A rows of 64 bytes in the paired-slab layout).
 // VECC: C rows 16-byte aligned (128-bit C access).
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NSTAGE, bool BETA0, bool EDGE, bool F16, bool VECC>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NSTAGE, bool PP, bool BETA0, bool EDGE, bool F16,
+          bool VECC>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lowp_kernel(Args p) {
     static_assert(BK == 32 || BK == 64, "K tile");
+    static_assert(!PP || WAVES_M * WAVES_N == 8, "the alternating schedule runs 8 waves");
     using AL = ALayout<BK / 2>;                             // A stage layout (its unit is 4 bytes)
     constexpr int NT = 64 * WAVES_M * WAVES_N;
     constexpr int NWAVES = WAVES_M * WAVES_N;
@@ -212,10 +218,11 @@ sgemm_lowp_kernel(Args p) {
     const int lrow = lane & 15, lg = lane >> 4;
     i32x4 fa[MI];
     i32x4 fb[2][NB];
-    auto read_a = [&](int mi, const char *stage, int s) {
+    auto read_a_into = [&](int mi, const char *stage, int s, i32x4 *f) {
         const int m = wm * WM + mi * 16 + lrow;
-        fa[mi] = *reinterpret_cast<const i32x4 *>(stage + 4 * AL::offset(m, 4 * s + lg));
+        f[mi] = *reinterpret_cast<const i32x4 *>(stage + 4 * AL::offset(m, 4 * s + lg));
     };
+    auto read_a = [&](int mi, const char *stage, int s) { read_a_into(mi, stage, s, fa); };
     // B read r of k step s: block r/2, its transposed 8-byte read r%2
     auto read_b = [&](int r, const char *stage, int s, i32x4 *f) {
         const int nb = r / 2, half = r % 2;
@@ -310,7 +317,74 @@ sgemm_lowp_kernel(Args p) {
         }
     };
 
-    if (ntiles > 0) {
+    if constexpr (PP) {
+        if (ntiles > 0) {
+            // Alternating schedule: waves 0-3 and 4-7 share the four SIMDs,
+            // one of each per SIMD.  Each wave alternates a memory phase
+            // (fragment reads of tile t from LDS, the loads of tile
+            // t+NSTAGE-1) and a compute phase (the MFMAs of tile t), and the
+            // second group runs one phase behind the first, so that on every
+            // SIMD one wave multiplies while the other reads.  Every phase
+            // ends with a barrier of all eight waves.
+            const int group = wave >> 2;
+            if (tail) {
+                issue_remainder();
+            } else {
+#pragma unroll
+                for (int g = 0; g < L; ++g) issue_one(0, 0, g);
+            }
+            static_for<1, NSTAGE - 1>([&](auto sc) {
+#pragma unroll
+                for (int g = 0; g < L; ++g) issue_one(decltype(sc)::value, decltype(sc)::value, g);
+            });
+            wait_vm_lgkm0<(NSTAGE - 2) * L>();
+            __builtin_amdgcn_s_barrier();
+            if (group) __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int KS = BK / 32;                     // k steps per tile
+            i32x4 pa[KS][MI], pb[KS][NB];
+            auto pp_tile = [&](int t, auto sc) {
+                constexpr int SC = decltype(sc)::value;
+                const char *cs = lds + SC * STAGE;
+                // memory phase: fragments of tile t, loads of tile
+                // t+NSTAGE-1 into the stage tile t-1 had (free: both groups
+                // read it before the last barrier and waited for the reads)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi) read_a_into(mi, cs, ks, pa[ks]);
+#pragma unroll
+                    for (int r = 0; r < 2 * NB; ++r) read_b(r, cs, ks, pb[ks]);
+                }
+#pragma unroll
+                for (int g = 0; g < L; ++g) issue_one(t + NSTAGE - 1, (SC + NSTAGE - 1) % NSTAGE, g);
+                __builtin_amdgcn_sched_barrier(0);
+                // the next phase of the other group reads tile t (group 0)
+                // or tile t+1 (group 1): this wave's loads of it have landed
+                if (group) wait_vm_lgkm0<(NSTAGE - 2) * L>();
+                else wait_vm_lgkm0<(NSTAGE - 1) * L>();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                // compute phase
+                static_for<0, KS * NM>([&](auto qc) {
+                    constexpr int ks = decltype(qc)::value / NM, q = decltype(qc)::value % NM;
+                    acc[q / NB][q % NB] = mfma_16x16x32<F16>(pb[ks][q % NB], pa[ks][q / NB], acc[q / NB][q % NB]);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vm_lgkm0<(NSTAGE - 2) * L>();
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
+                static_for<0, NSTAGE>([&](auto uc) {
+                    const int t = t0 + decltype(uc)::value;
+                    if (t < ntiles) pp_tile(t, uc);
+                });
+            }
+            if (!group) __builtin_amdgcn_s_barrier();
+            wait_vmcnt0();
+        }
+    } else if (ntiles > 0) {
         if (tail) {
             issue_remainder();
         } else {
@@ -372,14 +446,14 @@ sgemm_lowp_kernel(Args p) {
         }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16>
+template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP = false>
 void launch_lowp(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool vecc = (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && a.ldc % 4 == 0;
 #define SGEMM_LAUNCH(Z, E, V) \
-    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, Z, E, F16, V>), grid, block, 0, stream, a)
+    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, V>), grid, block, 0, stream, a)
 #define SGEMM_LAUNCH_V(Z, E)              \
     do {                                  \
         if (vecc) SGEMM_LAUNCH(Z, E, true); \
@@ -400,16 +474,16 @@ void launch_lowp(const Args &a0, hipStream_t stream) {
 // tile, K tile, waves and number of stages (the table of variants in the C
 // ABI's translation unit lists them in this order).
 void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
-#define SGEMM_T(BM, BN, BK, WM, WN, NS)                                    \
+#define SGEMM_T(BM, BN, BK, WM, WN, NS, PP)                                \
     do {                                                                  \
-        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true>(a, s);        \
-        else launch_lowp<BM, BN, BK, WM, WN, NS, false>(a, s);           \
+        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP>(a, s);    \
+        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP>(a, s);       \
     } while (0)
     switch (tile) {
-        case 1: SGEMM_T(256, 128, 64, 2, 4, 3); break;
-        case 2: SGEMM_T(256, 256, 32, 2, 4, 4); break;
-        case 3: SGEMM_T(256, 256, 32, 2, 4, 5); break;
-        default: SGEMM_T(128, 128, 64, 2, 2, 2); break;
+        case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false); break;
+        case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false); break;
+        case 3: SGEMM_T(256, 256, 32, 2, 4, 4, true); break;
+        default: SGEMM_T(128, 128, 64, 2, 2, 2, false); break;
     }
 #undef SGEMM_T
 }
