@@ -34,7 +34,7 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
            "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
-           "sgemm_lowp_variant_name")
+           "sgemm_lowp_variant_name", "sgemm_lowp_split_factor")
 
 _lib = None
 
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_lowp_ex.restype = i
     lib.sgemm_lowp_select_variant.argtypes = [i, i, i, vp, i, vp, i]
     lib.sgemm_lowp_select_variant.restype = i
+    lib.sgemm_lowp_split_factor.argtypes = [i, i, i, i]
+    lib.sgemm_lowp_split_factor.restype = i
     lib.sgemm_lowp_variant_name.argtypes = [i]
     lib.sgemm_lowp_variant_name.restype = cp
     lib.sgemm_split_factor.argtypes = [i, i, i, i]
@@ -165,6 +167,10 @@ def sgemm_lowp_select_variant(M, N, K, A, lda, B, ldb):
 def sgemm_lowp_variant_name(variant):
     s = load().sgemm_lowp_variant_name(variant)
     return None if s is None else s.decode()
+
+
+def sgemm_lowp_split_factor(variant, M, N, K):
+    return load().sgemm_lowp_split_factor(variant, M, N, K)
 
 
 def lowp_variants():

@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -186,7 +187,7 @@ typedef void (*Launcher)(const Args &, hipStream_t);
 // four waves, so the limits below count blocks alike for all of them.
 constexpr long kSplitMaxBlocks = 512;                    // splits x tiles (two blocks per CU)
 constexpr long kSplitMaxTiles = 4096;                    // tiles with counters
-constexpr size_t kSplitPartialBytes = 32u << 20;         // 512 partial tiles of 128x128
+constexpr size_t kSplitPartialBytes = 64u << 20;         // 1024 partial tiles of 128x128, 256 of 256x256
 constexpr size_t kSplitWorkspaceBytes = kSplitPartialBytes + kSplitMaxTiles * sizeof(unsigned);
 
 // Split factor for an M x N x K problem on bm x bn x bk tiles (1 = no
@@ -251,6 +252,24 @@ int get_workspace(hipStream_t stream, Workspace &out) {
     }
     cache[key] = w;
     out = w;
+    return SGEMM_STATUS_OK;
+}
+
+// Split K `splits` ways (when above one) with the stream's workspace: sets
+// a.splits, a.ws and a.counters.  A stream under graph capture cannot
+// allocate or clear memory, so K is split only outside capture.
+int attach_workspace(Args &a, int splits, void *stream) {
+    if (splits <= 1) return SGEMM_STATUS_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    const bool capturing = hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+                           cap != hipStreamCaptureStatusNone;
+    if (capturing) return SGEMM_STATUS_OK;
+    Workspace w;
+    const int ws = get_workspace(reinterpret_cast<hipStream_t>(stream), w);
+    if (ws != SGEMM_STATUS_OK) return ws;
+    a.splits = splits;
+    a.ws = w.partials;
+    a.counters = w.counters;
     return SGEMM_STATUS_OK;
 }
 
@@ -479,20 +498,8 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
     if (d.split_k) {
-        const int splits = choose_splits(M, N, K, d.bm, d.bn, d.bk);
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        // A stream under graph capture cannot allocate or clear memory, so
-        // K is split only outside capture.
-        const bool capturing = hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
-                               cap != hipStreamCaptureStatusNone;
-        if (splits > 1 && !capturing) {
-            Workspace w;
-            const int ws = get_workspace(reinterpret_cast<hipStream_t>(stream), w);
-            if (ws != SGEMM_STATUS_OK) return ws;
-            a.splits = splits;
-            a.ws = w.partials;
-            a.counters = w.counters;
-        }
+        const int ws = attach_workspace(a, choose_splits(M, N, K, d.bm, d.bn, d.bk), stream);
+        if (ws != SGEMM_STATUS_OK) return ws;
     }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -597,29 +604,61 @@ bool lowp_fast_ok(const LowpVariant &v, int N, int K, const void *A, int lda, co
            2L * ((long)v.bm * lda + v.bk) < lim && 2L * ((long)v.bk * ldb + v.bn) < lim;
 }
 
+// The largest split-K factor the 128x128 16-bit kernel (the one built with
+// split-K) may use: the tile grid must fill less than 3/4 of its 512
+// workgroup slots (two per compute unit), each split keeps at least eight K
+// tiles, and the partial tiles fit the workspace.  1 for other variants.
+int lowp_max_splits(int variant, int M, int N, int K) {
+    if (variant != 1) return 1;
+    const LowpVariant &v = kLowpVariants[variant];
+    const long slots = 512;
+    const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
+    if (tiles * 4 >= slots * 3 || tiles > kSplitMaxTiles) return 1;
+    long s = slots / tiles;
+    s = std::min(s, ceil_div(K, v.bk) / 8);
+    s = std::min(s, 16L);
+    s = std::min(s, (long)(kSplitPartialBytes / ((size_t)v.bm * v.bn * sizeof(float) * tiles)));
+    return s < 1 ? 1 : (int)s;
+}
+
+// Predicted time (us) of a 16-bit variant with split factor s: waves of
+// workgroups x (a workgroup's share of the product / its rate + 3 us of
+// pipeline fill and epilogue), plus for s > 1 the partial tiles (written and
+// read back, 2 s x M x N x 4 bytes at 5 TB/s) and 2 us.  Rates of one
+// workgroup (TFLOP/s measured on MI355X): 2.07 for the 128x128 kernel with
+// two per compute unit, 2.25 alone, 4.2 for the 256x128 kernel and 5.0 for
+// the alternating 256x256 kernel.
+double lowp_predict_us(int variant, int s, int M, int N, int K) {
+    const LowpVariant &v = kLowpVariants[variant];
+    const bool two_per_cu = variant == 1;
+    const long blocks = ceil_div(M, v.bm) * ceil_div(N, v.bn) * s;
+    const double rate = variant == 1 ? (blocks <= 256 ? 2.25 : 2.07) : variant == 2 ? 4.2 : 5.0;
+    const long waves = ceil_div(blocks, two_per_cu ? 512 : 256);
+    double t = (double)waves * (2.0 * v.bm * v.bn * ((double)K / s) / (rate * 1e6) + 3.0);
+    if (s > 1) t += 2.0 * s * (double)M * N * 4 / 5e6 + 2.0;
+    return t;
+}
+
+// The split factor of a variant: the better of no split and the largest
+// allowed split by the prediction above.
+int lowp_splits(int variant, int M, int N, int K) {
+    const int s = lowp_max_splits(variant, M, N, K);
+    return s > 1 && lowp_predict_us(variant, s, M, N, K) < lowp_predict_us(variant, 1, M, N, K) ? s : 1;
+}
+
 // Automatic choice among the 128x128 two-stage kernel (up to two workgroups
-// per compute unit), the 256x128 three-stage kernel and the 256x256
-// four-stage kernel with the alternating schedule (one workgroup per compute
-// unit): the least predicted time, waves of workgroups x tile area / the
-// rate of one workgroup (TFLOP/s measured on MI355X: 2.07 for the 128x128
-// kernel with two per compute unit, 2.25 alone, 4.2 and 5.0 for the larger
-// tiles).  Shapes none of them takes run the plain kernel.
+// per compute unit, split-K), the 256x128 three-stage kernel and the
+// 256x256 four-stage kernel with the alternating schedule (one workgroup per
+// compute unit): the least predicted time.  Shapes none of them takes run
+// the plain kernel.
 int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
-    struct Cand {
-        int id, slots;
-        double rate, rate_alone;
-    };
-    const Cand cands[] = {{1, 512, 2.07, 2.25}, {2, 256, 4.2, 4.2}, {4, 256, 5.0, 5.0}};
     int best = 0;
     double best_t = 0.0;
-    for (const Cand &c : cands) {
-        const LowpVariant &v = kLowpVariants[c.id];
-        if (!lowp_fast_ok(v, N, K, A, lda, B, ldb)) continue;
-        const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
-        const double rate = tiles <= 256 ? c.rate_alone : c.rate;
-        const double t = (double)ceil_div(tiles, c.slots) * v.bm * v.bn / rate;
+    for (int id : {1, 2, 4}) {
+        if (!lowp_fast_ok(kLowpVariants[id], N, K, A, lda, B, ldb)) continue;
+        const double t = lowp_predict_us(id, lowp_splits(id, M, N, K), M, N, K);
         if (best == 0 || t < best_t) {
-            best = c.id;
+            best = id;
             best_t = t;
         }
     }
@@ -657,6 +696,8 @@ int run_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
+    const int ws = attach_workspace(a, lowp_splits(variant, M, N, K), stream);
+    if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -686,6 +727,12 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha, const void *A, in
 int sgemm_lowp_select_variant(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
     if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
     return lowp_auto(M, N, K, A, lda, B, ldb);
+}
+
+int sgemm_lowp_split_factor(int variant, int M, int N, int K) {
+    if (variant < 0 || variant >= kNumLowpVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    return lowp_splits(variant, M, N, K);
 }
 
 const char *sgemm_lowp_variant_name(int variant) {

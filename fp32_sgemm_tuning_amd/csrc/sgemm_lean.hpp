@@ -45,10 +45,11 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, lds_addr_t dst, in
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Split-K hand-off of one output tile.  Every block stores its partial
-// accumulators to workspace slot blockIdx.y of the tile (chunk-major: chunk c
-// of thread t at c * NT + t, so each store and load instruction covers one
-// contiguous run) and takes a ticket from the tile's counter.  Returns false
-// for all blocks but the last; the last one reads the other partials, leaves
+// accumulators (NACC 16-byte chunks per thread, acc(c) for chunk c) to
+// workspace slot blockIdx.y of the tile (chunk-major: chunk c of thread t at
+// c * NT + t, so each store and load instruction covers one contiguous run)
+// and takes a ticket from the tile's counter.  Returns false
+// for all blocks but the last; the last one reads all partials back, leaves
 // their sum in split order in acc and resets the counter for the next call.
 //
 // Every XCD has its own L2, so the partials move at device scope: the
@@ -57,51 +58,41 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // its stores to complete before the barrier that precedes its ticket, and
 // the ticket is a device-scope atomic.  No cache-wide write-back or
 // invalidate is needed, so other blocks keep their cached A and B.
-template <class T>
-__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, f32x4 (&acc)[T::MI][T::NJ][4]) {
-    constexpr int TILE = T::NT * T::MI * T::NJ * 16;   // floats per partial tile (BM x BN)
+template <int NT, int NACC, class Ref>
+__device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int tid, Ref &&acc) {
+    constexpr int TILE = NT * NACC * 4;                 // floats per partial tile
     constexpr int kDeviceScope = 16;                    // cache policy bits: sc1
     const int S = gridDim.y, y = blockIdx.y;
     const __amdgpu_buffer_rsrc_t slab = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.ws + (long)tile_id * S * TILE), (short)0, S * TILE * 4, 0x00020000);
 #pragma unroll
-    for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(acc[mi][nj][i], slab,
-                                                       (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16, y * TILE * 4,
-                                                       kDeviceScope);
+    for (int c = 0; c < NACC; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(acc(c), slab, (c * NT + tid) * 16, y * TILE * 4, kDeviceScope);
     wait_vmcnt0();
     __syncthreads();
     __shared__ unsigned ticket;
     if (tid == 0) ticket = atomicAdd(p.counters + tile_id, 1u);
     __syncthreads();
     if (ticket != (unsigned)(S - 1)) return false;
-    f32x4 sum[T::MI][T::NJ][4];
+    // every partial, this block's own included, is read back in split
+    // order, so the sum needs no registers beyond the accumulators
     for (int s = 0; s < S; ++s) {
 #pragma unroll
-        for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 x = s == y ? acc[mi][nj][i]
-                                           : __builtin_amdgcn_raw_buffer_load_b128(
-                                                 slab, (((mi * T::NJ + nj) * 4 + i) * T::NT + tid) * 16,
-                                                 s * TILE * 4, kDeviceScope);
-                    sum[mi][nj][i] = s == 0 ? x : sum[mi][nj][i] + x;
-                }
+        for (int c = 0; c < NACC; ++c) {
+            const f32x4 x =
+                __builtin_amdgcn_raw_buffer_load_b128(slab, (c * NT + tid) * 16, s * TILE * 4, kDeviceScope);
+            acc(c) = s == 0 ? x : acc(c) + x;
+        }
     }
-#pragma unroll
-    for (int mi = 0; mi < T::MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < T::NJ; ++nj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mi][nj][i] = sum[mi][nj][i];
     if (tid == 0) atomicExch(p.counters + tile_id, 0u);
     return true;
+}
+
+// The same for the FP32 lean kernels' accumulator layout.
+template <class T>
+__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, f32x4 (&acc)[T::MI][T::NJ][4]) {
+    return split_reduce_n<T::NT, T::MI * T::NJ * 4>(
+        p, tile_id, tid, [&](int c) -> f32x4 & { return acc[c / (T::NJ * 4)][(c / 4) % T::NJ][c % 4]; });
 }
 
 // ---------------------------------------------------------------------------

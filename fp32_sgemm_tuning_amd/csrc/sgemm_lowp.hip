@@ -113,9 +113,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // BM x BN block tile, WAVES_M x WAVES_N waves, NSTAGE LDS stages of one
 // BK-deep K tile each (BK = 64: two k steps per tile, A rows of 128 bytes;
 // BK = 32: one k step, A rows of 64 bytes in the paired-slab layout).
-// VECC: C rows 16-byte aligned (128-bit C access).
+// SPLIT: split-K, gridDim.y blocks per output tile, each on a contiguous
+// share of the K tiles (the remainder tile with the first), combined by
+// split_reduce_n as in the FP32 lean kernel.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NSTAGE, bool PP, bool BETA0, bool EDGE, bool F16,
-          bool VECC>
+          bool SPLIT>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lowp_kernel(Args p) {
     static_assert(BK == 32 || BK == 64, "K tile");
@@ -172,7 +174,15 @@ sgemm_lowp_kernel(Args p) {
 
     const int kr = EDGE ? p.K % BK : 0;                     // K remainder, taken first
     const int tail = kr != 0;
-    const int ntiles = p.K / BK + tail;
+    // K tiles of this block: all of them, or this split's share; ntiles
+    // counts this block's tiles, t_first is the first one's index
+    int t_first = 0, ntiles = p.K / BK + tail;
+    if constexpr (SPLIT) {
+        const int S = gridDim.y, y = blockIdx.y, total = ntiles;
+        t_first = (int)((long)total * y / S);
+        ntiles = (int)((long)total * (y + 1) / S) - t_first;
+    }
+    const bool remainder_first = tail && t_first == 0;
     const long rowsA = min(BM, p.M - m0), colsB = min(BN, p.N - n0);
     const int rangeA = (int)(2L * ((rowsA - 1) * p.lda + BK));
     const int rangeB = (int)(2L * ((long)(BK - 1) * p.ldb + colsB));
@@ -189,7 +199,7 @@ sgemm_lowp_kernel(Args p) {
     // issues the same number of loads and the vmcnt waits stay constant.
     auto issue_one = [&](int t, int st, int g) {
         const bool live = t < ntiles;
-        const long kfirst = kr + (long)max(t - tail, 0) * BK;
+        const long kfirst = kr + (long)max(t_first + t - tail, 0) * BK;
         if (g < NA)
             dma16_lowp(cornerA + 2 * kfirst, live ? rangeA : 0, dst(st, g), (int)offA[g]);
         else
@@ -327,7 +337,7 @@ sgemm_lowp_kernel(Args p) {
             // SIMD one wave multiplies while the other reads.  Every phase
             // ends with a barrier of all eight waves.
             const int group = wave >> 2;
-            if (tail) {
+            if (remainder_first) {
                 issue_remainder();
             } else {
 #pragma unroll
@@ -385,7 +395,7 @@ sgemm_lowp_kernel(Args p) {
             wait_vmcnt0();
         }
     } else if (ntiles > 0) {
-        if (tail) {
+        if (remainder_first) {
             issue_remainder();
         } else {
 #pragma unroll
@@ -417,9 +427,17 @@ sgemm_lowp_kernel(Args p) {
         wait_vmcnt0();
     }
 
+    if constexpr (SPLIT) {
+        if (!split_reduce_n<NT, MI * NB>(p, tm * p.tiles_n + tn, tid,
+                                         [&](int c) -> f32x4 & { return acc[c / NB][c % NB]; }))
+            return;
+    }
+
     // C = alpha * acc (+ beta * C): block (mi, nb) holds row l%16 and
-    // columns 4*(l/16) .. +3 of its 16x16 output block
+    // columns 4*(l/16) .. +3 of its 16x16 output block; 16-byte accesses
+    // when C's rows are 16-byte aligned
     const float alpha = p.alpha, beta = p.beta;
+    const bool vecc = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc & 3) == 0;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -428,7 +446,7 @@ sgemm_lowp_kernel(Args p) {
             const int col = n0 + wn * WN + nb * 16 + 4 * lg;
             if (EDGE && row >= p.M) continue;
             float *dst = p.C + (long)row * p.ldc + col;
-            if constexpr (VECC) {
+            if (vecc) {
                 // N is a multiple of 8 here, so a vector starting below N ends below N
                 if (EDGE && col >= p.N) continue;
                 f32x4 o = acc[mi][nb] * alpha;
@@ -446,44 +464,42 @@ sgemm_lowp_kernel(Args p) {
         }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP = false>
+template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT>
 void launch_lowp(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(SPLIT ? a.splits : 1)), block(64 * WM * WN);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
-    const bool vecc = (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && a.ldc % 4 == 0;
-#define SGEMM_LAUNCH(Z, E, V) \
-    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, V>), grid, block, 0, stream, a)
-#define SGEMM_LAUNCH_V(Z, E)              \
-    do {                                  \
-        if (vecc) SGEMM_LAUNCH(Z, E, true); \
-        else SGEMM_LAUNCH(Z, E, false);   \
-    } while (0)
+#define SGEMM_LAUNCH(Z, E) \
+    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT>), grid, block, 0, stream, a)
     if (edge) {
-        if (a.beta == 0.0f) SGEMM_LAUNCH_V(true, true);
-        else SGEMM_LAUNCH_V(false, true);
+        if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
+        else SGEMM_LAUNCH(false, true);
     } else {
-        if (a.beta == 0.0f) SGEMM_LAUNCH_V(true, false);
-        else SGEMM_LAUNCH_V(false, false);
+        if (a.beta == 0.0f) SGEMM_LAUNCH(true, false);
+        else SGEMM_LAUNCH(false, false);
     }
-#undef SGEMM_LAUNCH_V
 #undef SGEMM_LAUNCH
 }
 
 // Launcher called from the C ABI's translation unit; `tile` picks the block
 // tile, K tile, waves and number of stages (the table of variants in the C
-// ABI's translation unit lists them in this order).
+// ABI's translation unit lists them in this order).  a.splits > 1 runs the
+// split-K form (built for the 128x128 kernel).
 void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
-#define SGEMM_T(BM, BN, BK, WM, WN, NS, PP)                                \
-    do {                                                                  \
-        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP>(a, s);    \
-        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP>(a, s);       \
+#define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                  \
+    do {                                                                         \
+        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s);       \
+        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP, SP>(a, s);          \
     } while (0)
+    const bool split = a.splits > 1;
     switch (tile) {
-        case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false); break;
-        case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false); break;
-        case 3: SGEMM_T(256, 256, 32, 2, 4, 4, true); break;
-        default: SGEMM_T(128, 128, 64, 2, 2, 2, false); break;
+        case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false, false); break;
+        case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false, false); break;
+        case 3: SGEMM_T(256, 256, 32, 2, 4, 4, true, false); break;
+        default:
+            if (split) SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
+            else SGEMM_T(128, 128, 64, 2, 2, 2, false, false);
+            break;
     }
 #undef SGEMM_T
 }

@@ -31,7 +31,7 @@
  * Workspace.  Small tile grids split K over several workgroups per output
  * tile (split-K).  Those calls use a workspace that the library allocates
  * with hipMalloc on the first such call for each (device, stream) pair and
- * keeps until the process ends: 32 MiB of partial tiles and 256 tile
+ * keeps until the process ends: 64 MiB of partial tiles and 4096 tile
  * counters, the counters cleared once on the stream before first use and
  * left cleared by every call.  Calls on one stream share the workspace in
  * stream order; calls on different streams use different workspaces.  The
@@ -202,9 +202,11 @@ int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alph
  * K >= 32.  It runs the matrix instructions v_mfma_f32_16x16x32_bf16 / _f16
  * on 128x128, 256x128 or 256x256 block tiles, picked from the shape, with
  * 16-byte C access when C is 16-byte aligned and ldc a multiple of 4.  Any
- * other shape runs a plain kernel that widens each element on load.  No
- * split-K, no workspace.  Argument checks, layout rules and status codes as
- * for sgemm(), plus SGEMM_STATUS_INVALID_DTYPE, which is checked first.
+ * other shape runs a plain kernel that widens each element on load.  Small
+ * tile grids split K and use the workspace described above (same rules:
+ * allocated on first use per (device, stream), no split under graph
+ * capture, deterministic).  Argument checks, layout rules and status codes
+ * as for sgemm(), plus SGEMM_STATUS_INVALID_DTYPE, which is checked first.
  */
 int sgemm_lowp(int dtype, int M, int N, int K, float alpha,
                const void *A, int lda,
@@ -231,6 +233,11 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
 int sgemm_lowp_select_variant(int M, int N, int K,
                               const void *A, int lda,
                               const void *B, int ldb);
+
+/* Split-K factor (1 = no split) that sgemm_lowp_ex() with this variant would
+ * use for an M x N x K problem outside graph capture; no HIP call.  Returns
+ * the factor, SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM. */
+int sgemm_lowp_split_factor(int variant, int M, int N, int K);
 
 /* Static name of a sgemm_lowp_ex() variant, or NULL for an unknown id. */
 const char *sgemm_lowp_variant_name(int variant);

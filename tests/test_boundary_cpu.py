@@ -326,3 +326,25 @@ def test_lowp_variants_and_selection():
     assert sel(4096, 4096, 4096, AL, 4096, AL, 4096) > 0
     assert sel(4096, 4096, 4096, AL + 2, 4096, AL, 4096) == 0
     assert sel(-1, 4, 4, AL, 4, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+def test_lowp_split_factors():
+    """16-bit split-K: only the 128x128 kernel splits; small grids with long K
+    split, full grids and short K do not; the factor respects the slots and
+    the 64 MiB workspace."""
+    f = capi.sgemm_lowp_split_factor
+    names = {capi.sgemm_lowp_variant_name(v): v for v in capi.lowp_variants()}
+    v128, valt, v256x128 = names["lowp_128x128x64_s2"], names["lowp_256x256x32_s4_alt"], names["lowp_256x128x64_s3"]
+    assert f(v128, 2048, 2048, 8192) == 2          # 256 tiles in 512 slots, long K
+    assert f(v128, 1024, 1024, 8192) == 8
+    assert f(v128, 4096, 4096, 4096) == 1          # a full grid
+    assert f(v128, 512, 512, 256) == 1             # 4 K tiles: too short to split
+    for v in (valt, v256x128):                     # no split-K form
+        assert f(v, 2048, 2048, 8192) == 1 and f(v, 256, 256, 65536) == 1
+    for M, N, K in ((2048, 2048, 8192), (512, 512, 65536), (256, 256, 4096), (1000, 3000, 5000), (64, 64, 1 << 20)):
+        s = f(v128, M, N, K)
+        tiles = -(-M // 128) * -(-N // 128)
+        assert 1 <= s <= 16
+        assert s == 1 or (s * tiles <= 512 and s * tiles * 128 * 128 * 4 <= 64 << 20 and -(-K // 64) >= 8 * s)
+    assert f(len(names), 8, 8, 8) == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert f(v128, -1, 8, 8) == capi.SGEMM_STATUS_INVALID_DIM

@@ -188,3 +188,56 @@ def test_lowp_rejects_mixed_types():
         capi.SGEMM_STATUS_INVALID_DTYPE
     with pytest.raises(ValueError):
         sgemm_lowp(a, torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_lowp_operand_over_2gib():
+    """B of 131072 x 8192 BF16 values (2 GiB): every K tile gets its own
+    descriptor base, so the fast kernels take operands past the 31-bit
+    buffer range; the automatic choice and the alternating 256x256 kernel,
+    sampled against the oracle, corners included."""
+    torch = torch_cuda()
+    M, N, K = 256, 8192, 131072
+    A, B, _ = make_problem_16bit(M, N, K, seed=23, dtype="bf16")
+    assert B.size * 2 >= 2 ** 31
+    dA = torch.from_numpy(A).to(torch.bfloat16).cuda()
+    dB = torch.from_numpy(B).to(torch.bfloat16).cuda()
+    I, J = sample_indices(M, N, 23, n=512)
+    ref = oracle.sgemm_ref_sampled(A, B, I, J)
+    del B
+    for v in (None, capi.SGEMM_VARIANT_AUTO, 4):
+        print(f"[lowp] 2 GiB operand variant {v}", flush=True)
+        C = sgemm_lowp(dA, dB, variant=v)
+        torch.cuda.synchronize()
+        check_close(C.cpu().numpy()[I, J], ref, f"2 GiB operand, variant {v}")
+
+
+SPLIT_SHAPES = [(2048, 2048, 2048), (512, 768, 8192), (300, 520, 4104), (1000, 1000, 3000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lowp_split_k(dtype):
+    """Split-K on small grids with long K (the 128x128 kernel, forced, and the
+    automatic choice; the alternating kernel on the same shapes): parity with the oracle,
+    bit-identical repeats (the partials are added in a fixed order) and a
+    factor above one where the shape calls for it."""
+    torch = torch_cuda()
+    names = {capi.sgemm_lowp_variant_name(v): v for v in capi.lowp_variants()}
+    for M, N, K in SPLIT_SHAPES:
+        A, B, Cin = make_problem_16bit(M, N, K, seed=M + N + K, dtype=dtype, dist="normal", with_c=True)
+        dA, _ = _dev16(A, dtype, torch)
+        dB, _ = _dev16(B, dtype, torch)
+        ref = oracle.sgemm_ref(A, B, Cin, alpha=0.5, beta=1.5)
+        for v in (None, names["lowp_128x128x64_s2"], names["lowp_256x256x32_s4_alt"]):
+            s = capi.sgemm_lowp_split_factor(v if v is not None else capi.sgemm_lowp_select_variant(
+                M, N, K, dA.data_ptr(), K, dB.data_ptr(), N), M, N, K)
+            print(f"[lowp] split {dtype} {M}x{N}x{K} variant {v} factor {s}", flush=True)
+            outs = []
+            for _ in range(2):
+                dC = torch.from_numpy(Cin).to("cuda")
+                sgemm_lowp(dA, dB, dC, alpha=0.5, beta=1.5, variant=v)
+                torch.cuda.synchronize()
+                outs.append(dC.cpu().numpy())
+            check_close(outs[0], ref, f"{dtype} {M}x{N}x{K} variant {v} split {s}")
+            assert np.array_equal(outs[0], outs[1]), "split-K result changed between calls"
+    assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 512, 768, 8192) > 1
+    assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 1000, 1000, 3000) > 1
