@@ -443,15 +443,17 @@ double wave_fill(long tiles) {
 }
 
 // Tile choice of the automatic dispatch: the 64x64 tile when the 128x128
-// grid has fewer than 160 tiles, or when the last wave of 64x64 tiles is
-// fuller by more than the 3% that the smaller tile costs in throughput at
-// full occupancy.  Measured (bench.py --sweep): 64x64x64 ahead at 768^3 to
-// 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3 and short K.
-// (`batch` problems of one strided batch count as batch times the tiles)
+// grid has at most 256 tiles (both kernels run two workgroups per compute
+// unit, so such a grid leaves half the slots empty), or when the last wave
+// of 64x64 tiles is fuller by more than the 3% that the smaller tile costs
+// in throughput at full occupancy.  Measured (bench.py --sweep): 64x64x64
+// ahead at 768^3 to 3584^3 and 5120^3, 128x128x32 ahead at 4096^3, 8192^3
+// and short K.  (`batch` problems of one strided batch count as batch times
+// the tiles)
 bool prefer_64(int M, int N, long batch = 1) {
     const long t128 = ceil_div(M, 128) * ceil_div(N, 128) * batch;
     const long t64 = ceil_div(M, 64) * ceil_div(N, 64) * batch;
-    return t128 < 160 || wave_fill(t64) * 0.97 > wave_fill(t128);
+    return t128 <= kNumCUs || wave_fill(t64) * 0.97 > wave_fill(t128);
 }
 
 // Automatic choice: the lean kernel with 16-byte loads when the operands

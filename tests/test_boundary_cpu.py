@@ -132,8 +132,10 @@ def _name(v):
     ((1024, 1024, 64), "lean_64x64x64_w4x1_splitk"),
     ((1024, 1024, 1024), "lean_64x64x64_w4x1_splitk"),
     ((1536, 1536, 1536), "lean_64x64x64_w4x1_splitk"),
+    # 128x128 grid of at most 256 tiles: half the two-per-CU slots
+    ((2048, 2048, 2048), "lean_64x64x64_w4x1_splitk"),
+    ((2000, 2000, 500), "lean_64x64x64_w4x1_splitk"),
     # last wave of 128x128 tiles fuller than that of 64x64 tiles less 3%
-    ((2048, 2048, 2048), "lean_128x128x32_w2x2"),
     ((4096, 4096, 4096), "lean_128x128x32_w2x2"),
     ((8192, 8192, 8192), "lean_128x128x32_w2x2"),
     ((4096, 4000, 100), "lean_128x128x32_w2x2"),
@@ -144,8 +146,8 @@ def _name(v):
     ((1920, 1536, 1024), "lean_64x64x64_w4x1_splitk"),
 ])
 def test_variant_selection_by_shape(shape, expected):
-    """Aligned operands take a lean variant chosen by the fill of the last
-    wave of tiles over the 256 CUs."""
+    """Aligned operands take a lean variant chosen by the size of the grid and
+    the fill of the last wave of tiles over the 256 CUs."""
     M, N, K = shape
     v = capi.sgemm_select_variant(M, N, K, AL, K, AL, N, 0.0, AL, N)
     assert _name(v) == expected, (shape, _name(v))
