@@ -34,7 +34,7 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
            "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
-           "sgemm_lowp_variant_name", "sgemm_lowp_split_factor")
+           "sgemm_lowp_variant_name", "sgemm_lowp_split_factor", "sgemm_tail_split")
 
 _lib = None
 
@@ -93,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_lowp_split_factor.restype = i
     lib.sgemm_lowp_variant_name.argtypes = [i]
     lib.sgemm_lowp_variant_name.restype = cp
+    lib.sgemm_tail_split.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.sgemm_tail_split.restype = i
     lib.sgemm_split_factor.argtypes = [i, i, i, i]
     lib.sgemm_split_factor.restype = i
     lib.sgemm_strerror.argtypes = [i]
@@ -179,6 +181,13 @@ def lowp_variants():
     while sgemm_lowp_variant_name(n) is not None:
         n += 1
     return list(range(n))
+
+
+def sgemm_tail_split(variant, M, N, K):
+    """(S, tiles of the second launch) of the last-wave split; S == 1: one launch."""
+    t = ctypes.c_int(0)
+    s = load().sgemm_tail_split(variant, M, N, K, ctypes.byref(t))
+    return s, t.value
 
 
 def sgemm_split_factor(variant, M, N, K):

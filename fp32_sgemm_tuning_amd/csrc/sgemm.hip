@@ -273,6 +273,16 @@ int attach_workspace(Args &a, int splits, void *stream) {
     return SGEMM_STATUS_OK;
 }
 
+// Wave quantization: a grid of whole waves plus a last wave less than a
+// quarter full runs as two launches, the whole waves as they are and the
+// last wave with K split S ways, so that the last wave's few tiles spread
+// over the whole chip.  Workgroup slots: two per compute unit (both lean
+// default tiles).  S: up to the slots over the tiles left, at least two K
+// tiles per split, at most 16, within the workspace; 1 = one launch.
+constexpr long kTailSlots = 2 * 256;
+struct VariantDesc;
+int choose_tail_splits(const VariantDesc &d, const Args &a);
+
 // A split-capable variant: split-K when a.splits > 1, else the plain lean
 // kernel of the same tile.
 typedef void (*SplitLauncher)(const Args &, int, hipStream_t);
@@ -294,17 +304,27 @@ bool lean_fits(int bm, int bn, int bk, long lda, long ldb, bool ta, bool tb) {
     return 4L * spanA < lim && 4L * spanB < lim;
 }
 
+// Whether the lean kernel of a bm x bn x bk tile takes the operands of an
+// untransposed problem (else launch_lean_or runs its guarded fallback).
+bool lean_takes(int bm, int bn, int bk, const Args &a) {
+    return a.K >= bk && !(a.K % 4) && !(a.N % 4) && lean_fits(bm, bn, bk, a.lda, a.ldb, false, false);
+}
+
 // The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
 // be whole tiles) and offsets within a tile that fit the descriptors' range;
 // other shapes go to FALLBACK, a guarded kernel.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_or(const Args &a, hipStream_t stream) {
-    const bool shape = a.K >= BK && !(a.K % 4) && !(a.N % 4);
-    const bool fits = lean_fits(BM, BN, BK, a.lda, a.ldb, false, false);
-    if (shape && fits)
+    // (a launch over part of the grid, a.tile_count > 0, is made only for
+    // operands the lean kernel takes; the fallback always covers the whole
+    // grid)
+    if (lean_takes(BM, BN, BK, a)) {
         LEAN(a, stream);
-    else
-        FALLBACK(a, stream);
+    } else {
+        Args whole = a;
+        whole.tile_base = whole.tile_count = 0;
+        FALLBACK(whole, stream);
+    }
 }
 
 // The lean kernel with 4-byte loads takes any alignment and any K >= BK, with
@@ -426,6 +446,18 @@ const VariantDesc kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
+int choose_tail_splits(const VariantDesc &d, const Args &a) {
+    if (!lean_takes(d.bm, d.bn, d.bk, a)) return 1;
+    const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
+    const long rem = tiles % kTailSlots;
+    if (tiles < kTailSlots || rem == 0 || rem * 4 > kTailSlots || rem > kSplitMaxTiles) return 1;
+    long s = kTailSlots / rem;
+    s = std::min(s, ceil_div(a.K, d.bk) / 2);
+    s = std::min(s, 16L);
+    s = std::min(s, (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem)));
+    return s < 2 ? 1 : (int)s;
+}
+
 // Variants the automatic choice uses for 128-bit operands (indices into
 // kVariants).
 constexpr int kVec = 24;       // lean_128x128x32_w2x2
@@ -496,6 +528,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.group_m = knobs().group_m;
     a.xcd_remap = knobs().xcd_remap;
     a.splits = 1;
+    a.tile_base = a.tile_count = 0;
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
@@ -506,7 +539,22 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    d.launch(a, s);
+    const int tail_splits = d.split_k && a.splits == 1 ? choose_tail_splits(d, a) : 1;
+    if (tail_splits > 1) {
+        // Whole waves of tiles first, then the last, partly filled wave with
+        // K split: two launches on the stream, over disjoint tiles of C.
+        const long tiles = tiles_m * tiles_n, rem = tiles % kTailSlots;
+        Args head = a, tail = a;
+        head.tile_count = (int)(tiles - rem);
+        tail.tile_base = (int)(tiles - rem);
+        tail.tile_count = (int)rem;
+        const int ws = attach_workspace(tail, tail_splits, stream);
+        if (ws != SGEMM_STATUS_OK) return ws;
+        d.launch(head, s);
+        d.launch(tail, s);
+    } else {
+        d.launch(a, s);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
@@ -552,6 +600,7 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     a.group_m = knobs().group_m;
     a.xcd_remap = knobs().xcd_remap;
     a.splits = 1;
+    a.tile_base = a.tile_count = 0;
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = batch > 1 ? (long)sA : 0;
@@ -695,6 +744,7 @@ int run_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda
     a.group_m = knobs().group_m;
     a.xcd_remap = knobs().xcd_remap;
     a.splits = 1;
+    a.tile_base = a.tile_count = 0;
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
@@ -810,6 +860,24 @@ int sgemm_split_factor(int variant, int M, int N, int K) {
     const VariantDesc &d = kVariants[variant];
     if (!d.split_k || M == 0 || N == 0) return 1;
     return choose_splits(M, N, K, d.bm, d.bn, d.bk);
+}
+
+int sgemm_tail_split(int variant, int M, int N, int K, int *tail_tiles) {
+    if (tail_tiles) *tail_tiles = 0;
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    const VariantDesc &d = kVariants[variant];
+    if (!d.split_k || M == 0 || N == 0 || choose_splits(M, N, K, d.bm, d.bn, d.bk) > 1) return 1;
+    // the lean kernel's operand checks with packed leading dimensions
+    Args a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.lda = K > 1 ? K : 1;
+    a.ldb = N > 1 ? N : 1;
+    const int s = choose_tail_splits(d, a);
+    if (s > 1 && tail_tiles) *tail_tiles = (int)((ceil_div(M, d.bm) * ceil_div(N, d.bn)) % kTailSlots);
+    return s;
 }
 
 const char *sgemm_strerror(int status) {

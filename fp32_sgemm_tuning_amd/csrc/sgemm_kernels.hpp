@@ -37,6 +37,10 @@ struct Args {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;   // block tiles along M and N
+    // the launch covers tiles tile_base .. tile_base + gridDim.x - 1 of the
+    // raster order below; tile_count (host side, lean launchers only) is
+    // that grid size, 0 meaning the whole grid (then tile_base is 0)
+    int tile_base, tile_count;
     int group_m;            // tile rows per raster group (>= 1)
     int xcd_remap;          // 1: give each XCD a contiguous run of tiles
     // split-K only: blocks per tile along K (the launch's gridDim.y), partial
@@ -81,14 +85,19 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
 // the logical ids are then walked in groups of `group_m` tile rows, column
 // by column inside a group, so tiles that run together share rows of A and
 // columns of B.
+// Returns the workgroup's index in the launch after the XCD remap (a
+// permutation of 0 .. gridDim.x - 1), which split-K uses for its workspace
+// slot; the raster position is that index plus p.tile_base.
 template <class P>
-__device__ __forceinline__ void tile_coords(const P &p, int &tm, int &tn) {
+__device__ __forceinline__ int tile_coords(const P &p, int &tm, int &tn) {
     int bid = blockIdx.x;
     const int nwg = gridDim.x;
     if (p.xcd_remap) {
         const int per = nwg >> 3;            // full rounds over the 8 XCDs
         if (bid < (per << 3)) bid = (bid & 7) * per + (bid >> 3);
     }
+    const int local = bid;
+    bid += p.tile_base;
     const int gm = p.group_m;
     const int group_size = gm * p.tiles_n;
     const int g = bid / group_size;
@@ -97,6 +106,7 @@ __device__ __forceinline__ void tile_coords(const P &p, int &tm, int &tn) {
     const int in_group = bid - g * group_size;
     tm = first_m + in_group % rows;
     tn = in_group / rows;
+    return local;
 }
 
 // ---------------------------------------------------------------------------

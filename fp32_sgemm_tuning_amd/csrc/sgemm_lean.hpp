@@ -187,7 +187,7 @@ sgemm_lean_kernel(Args p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     int tm, tn;
-    tile_coords(p, tm, tn);
+    const int slot = tile_coords(p, tm, tn);          // split-K workspace slot
     const int m0 = tm * BM, n0 = tn * BN;
 
     // Loop-invariant per-lane byte offsets of the direct loads.  Load i of a
@@ -360,7 +360,7 @@ sgemm_lean_kernel(Args p) {
         if (t < t_end) tile(t, IntC<0>{});
     }
     if constexpr (SPLIT) {
-        if (!split_reduce<T>(p, tm * p.tiles_n + tn, tid, acc)) return;
+        if (!split_reduce<T>(p, slot, tid, acc)) return;
     }
     T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
 }
@@ -370,7 +370,9 @@ template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW 
           bool TB = false>
 void launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) {
     const Args a = tiled(a0, BM, BN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits, (unsigned)batch);
+    // a.tile_count > 0: this launch covers tiles a.tile_base .. + tile_count - 1
+    const int tiles = a0.tile_count > 0 ? a0.tile_count : a.tiles_m * a.tiles_n;
+    const dim3 grid((unsigned)tiles, (unsigned)splits, (unsigned)batch);
     const dim3 block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \

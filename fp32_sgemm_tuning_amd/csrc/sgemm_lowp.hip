@@ -145,7 +145,7 @@ sgemm_lowp_kernel(Args p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     int tm, tn;
-    tile_coords(p, tm, tn);
+    const int slot = tile_coords(p, tm, tn);          // split-K workspace slot
     const int m0 = tm * BM, n0 = tn * BN;
     const char *Ab = reinterpret_cast<const char *>(p.A);
     const char *Bb = reinterpret_cast<const char *>(p.B);
@@ -428,7 +428,7 @@ sgemm_lowp_kernel(Args p) {
     }
 
     if constexpr (SPLIT) {
-        if (!split_reduce_n<NT, MI * NB>(p, tm * p.tiles_n + tn, tid,
+        if (!split_reduce_n<NT, MI * NB>(p, slot, tid,
                                          [&](int c) -> f32x4 & { return acc[c / NB][c % NB]; }))
             return;
     }

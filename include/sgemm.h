@@ -25,7 +25,8 @@
  *
  * Ownership and execution.  The caller owns A, B and C.  A call validates
  * its arguments, enqueues one kernel on `stream` (a hipStream_t; NULL is the
- * null stream) and returns without synchronising.  Calls are thread-safe
+ * null stream; two kernels when the last wave of tiles is split, see
+ * sgemm_tail_split) and returns without synchronising.  Calls are thread-safe
  * and deterministic: the same inputs give the same bits.
  *
  * Workspace.  Small tile grids split K over several workgroups per output
@@ -252,6 +253,19 @@ const char *sgemm_lowp_variant_name(int variant);
  * (negative sizes).
  */
 int sgemm_split_factor(int variant, int M, int N, int K);
+
+/*
+ * sgemm_tail_split: the split of the last wave that sgemm_ex() with this
+ * variant would make for an M x N x K problem with packed leading dimensions
+ * outside graph capture (no HIP call).  A split-capable variant whose grid
+ * is whole waves of tiles (two workgroups per compute unit) plus a last wave
+ * at most a quarter full, and that does not split K already, runs as two
+ * launches on the stream: the whole waves, then the last wave's tiles with K
+ * split S ways.  Returns S (1: a single launch) and, if tail_tiles is not
+ * NULL, stores the number of tiles in the second launch (0 when S is 1);
+ * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM on bad arguments.
+ */
+int sgemm_tail_split(int variant, int M, int N, int K, int *tail_tiles);
 
 /* Static text for a status code. */
 const char *sgemm_strerror(int status);

@@ -350,3 +350,26 @@ def test_lowp_split_factors():
         assert s == 1 or (s * tiles <= 512 and s * tiles * 128 * 128 * 4 <= 64 << 20 and -(-K // 64) >= 8 * s)
     assert f(len(names), 8, 8, 8) == capi.SGEMM_STATUS_INVALID_VARIANT
     assert f(v128, -1, 8, 8) == capi.SGEMM_STATUS_INVALID_DIM
+
+
+def test_tail_split_plan():
+    """A grid of whole waves (512 workgroup slots) plus a last wave at most a
+    quarter full runs as two launches, the last wave's tiles with K split."""
+    names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
+    v64, v128 = names["lean_64x64x64_w4x1_splitk"], names["lean_128x128x32_w2x2_splitk"]
+    t = capi.sgemm_tail_split
+    assert t(v64, 1536, 1536, 1536) == (8, 64)      # 576 tiles = 512 + 64
+    assert t(v64, 1550, 1572, 1000) == (4, 113)     # 625 tiles, 16 K tiles
+    assert t(v64, 1550, 1570, 1000) == (1, 0)       # N not a multiple of 4: no lean kernel
+    assert t(v128, 2944, 2944, 256) == (4, 17)      # 529 tiles, 8 K tiles
+    assert t(v64, 2048, 2048, 2048) == (1, 0)       # whole waves
+    assert t(v128, 4096, 4096, 4096) == (1, 0)
+    assert t(v64, 1664, 1664, 1664) == (1, 0)       # 676 tiles: last wave a third full
+    assert t(v64, 512, 512, 4096) == (1, 0)         # a small grid splits K as a whole instead
+    assert t(v64, 1536, 1536, 64) == (1, 0)         # one K tile
+    assert t(names["lean_64x64x64_w4x1"], 1536, 1536, 1536) == (1, 0)   # no split-K form
+    assert t(len(names), 8, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_VARIANT
+    assert t(v64, -1, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_DIM
+    # the automatic choice at 1536^3 is the split-capable 64x64 kernel
+    assert capi.sgemm_variant_name(capi.sgemm_select_variant(1536, 1536, 1536, AL, 1536, AL, 1536, 0.0, AL,
+                                                              1536)) == "lean_64x64x64_w4x1_splitk"

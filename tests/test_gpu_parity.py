@@ -256,3 +256,37 @@ def test_operand_over_2gib():
     torch.cuda.synchronize()
     I, J = sample_indices(M, N, 21, n=512)
     check_close(C.cpu().numpy()[I, J], oracle.sgemm_ref_sampled(A, B, I, J), "2 GiB operand")
+
+
+TAIL_CASES = [
+    # (M, N, K, variant name): the grid is whole waves plus a last wave at
+    # most a quarter full, which runs as a second launch with K split
+    (1536, 1536, 1536, None),
+    (1550, 1572, 1000, "lean_64x64x64_w4x1_splitk"),
+    (2944, 2944, 256, "lean_128x128x32_w2x2_splitk"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,name", TAIL_CASES)
+def test_last_wave_split(M, N, K, name):
+    """Two launches over disjoint tiles of C, the second split-K: parity with
+    the oracle for beta = 0 over NaN C and for beta != 0, and bit-identical
+    repeats."""
+    torch = torch_cuda()
+    names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
+    v = None if name is None else names[name]
+    plan = capi.sgemm_tail_split(v if v is not None else names["lean_64x64x64_w4x1_splitk"], M, N, K)
+    print(f"[tail] {M}x{N}x{K} {name} plan {plan}", flush=True)
+    assert plan[0] > 1
+    A, B, Cin = make_problem(M, N, K, 31, dist="normal", with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    for alpha, beta in ((1.0, 0.0), (0.75, -1.25)):
+        ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+        outs = []
+        for _ in range(2):
+            dC = to_dev(Cin, torch) if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+            sgemm(dA, dB, dC, alpha=alpha, beta=beta, variant=v)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().numpy())
+        check_close(outs[0], ref, f"{M}x{N}x{K} {name} beta={beta}")
+        assert np.array_equal(outs[0], outs[1])
