@@ -641,6 +641,7 @@ const LowpVariant kLowpVariants[] = {
     {"lowp_256x128x64_s3", 256, 128, 64},
     {"lowp_256x256x32_s4", 256, 256, 32},
     {"lowp_256x256x32_s4_alt", 256, 256, 32},
+    {"lowp_128x128x64_s4_alt", 128, 128, 64},
 };
 constexpr int kNumLowpVariants = (int)(sizeof(kLowpVariants) / sizeof(kLowpVariants[0]));
 
@@ -676,14 +677,18 @@ int lowp_max_splits(int variant, int M, int N, int K) {
 // workgroups x (a workgroup's share of the product / its rate + 3 us of
 // pipeline fill and epilogue), plus for s > 1 the partial tiles (written and
 // read back, 2 s x M x N x 4 bytes at 5 TB/s) and 2 us.  Rates of one
-// workgroup (TFLOP/s measured on MI355X): 2.07 for the 128x128 kernel with
-// two per compute unit, 2.25 alone, 4.2 for the 256x128 kernel and 5.0 for
-// the alternating 256x256 kernel.
+// workgroup (TFLOP/s measured on MI355X): 2.07 for the 128x128 two-stage
+// kernel with two per compute unit, 2.25 alone, 4.2 for the 256x128 kernel,
+// 5.0 for the alternating 256x256 kernel and 3.3 for the alternating
+// 128x128 kernel.
 double lowp_predict_us(int variant, int s, int M, int N, int K) {
     const LowpVariant &v = kLowpVariants[variant];
     const bool two_per_cu = variant == 1;
     const long blocks = ceil_div(M, v.bm) * ceil_div(N, v.bn) * s;
-    const double rate = variant == 1 ? (blocks <= 256 ? 2.25 : 2.07) : variant == 2 ? 4.2 : 5.0;
+    const double rate = variant == 1   ? (blocks <= 256 ? 2.25 : 2.07)
+                        : variant == 2 ? 4.2
+                        : variant == 5 ? 3.3
+                                       : 5.0;
     const long waves = ceil_div(blocks, two_per_cu ? 512 : 256);
     double t = (double)waves * (2.0 * v.bm * v.bn * ((double)K / s) / (rate * 1e6) + 3.0);
     if (s > 1) t += 2.0 * s * (double)M * N * 4 / 5e6 + 2.0;
@@ -699,13 +704,13 @@ int lowp_splits(int variant, int M, int N, int K) {
 
 // Automatic choice among the 128x128 two-stage kernel (up to two workgroups
 // per compute unit, split-K), the 256x128 three-stage kernel and the
-// 256x256 four-stage kernel with the alternating schedule (one workgroup per
-// compute unit): the least predicted time.  Shapes none of them takes run
-// the plain kernel.
+// 256x256 and 128x128 four-stage kernels with the alternating schedule (one
+// workgroup per compute unit): the least predicted time.  Shapes none of
+// them takes run the plain kernel.
 int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
     int best = 0;
     double best_t = 0.0;
-    for (int id : {1, 2, 4}) {
+    for (int id : {1, 2, 4, 5}) {
         if (!lowp_fast_ok(kLowpVariants[id], N, K, A, lda, B, ldb)) continue;
         const double t = lowp_predict_us(id, lowp_splits(id, M, N, K), M, N, K);
         if (best == 0 || t < best_t) {

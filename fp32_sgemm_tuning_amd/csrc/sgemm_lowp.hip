@@ -496,6 +496,7 @@ void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
         case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false, false); break;
         case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false, false); break;
         case 3: SGEMM_T(256, 256, 32, 2, 4, 4, true, false); break;
+        case 4: SGEMM_T(128, 128, 64, 2, 4, 4, true, false); break;
         default:
             if (split) SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
             else SGEMM_T(128, 128, 64, 2, 2, 2, false, false);
