@@ -57,6 +57,7 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
     if tuple(C.shape) != (M, N):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
     lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
+    _same_device(A, B, C)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
             float(beta), C.data_ptr(), ldc, s.cuda_stream)
@@ -68,6 +69,12 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
     if st != capi.SGEMM_STATUS_OK:
         raise SgemmError(st)
     return C
+
+
+def _same_device(*tensors):
+    devs = {t.device for t in tensors}
+    if len(devs) != 1:
+        raise ValueError(f"A, B and C must be on one device, got {sorted(str(d) for d in devs)}")
 
 
 def variant_names():
@@ -118,6 +125,7 @@ def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, st
             raise ValueError("beta != 0 needs C")
         C = torch.empty((batch, M, N) if batched else (M, N), dtype=torch.float32, device=A.device)
     rc, cc, ldc, sc = _mat(C, "C")
+    _same_device(A, B, C)
     if (rc, cc) != (M, N) or (C.dim() == 3 and C.shape[0] != batch):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(batch, M, N) if batched else (M, N)}")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
@@ -158,6 +166,7 @@ def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
     if tuple(C.shape) != (M, N):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
     ldc = _ld(C, "C")
+    _same_device(A, B, C)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
         args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
