@@ -250,7 +250,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU per process; --gpus {args.gpus} is not supported "
               "(row-slab sharding across GPUs is described in the design notes but not built)",
               file=sys.stderr)
         sys.exit(2)
