@@ -16,7 +16,8 @@ one JSON line.
 choice, "mm" = torch.mm in FP32 for context, "op:TN" and the like = sgemm_op
 with the operands stored transposed as named, "lowp:bf16" / "lowp:f16" =
 sgemm_lowp on the same values in that 16-bit type ("lowp:bf16:V" forces
-sgemm_lowp_ex variant V), "mm:bf16" / "mm:f16" =
+sgemm_lowp_ex variant V, "lowp:bf16:op:TN" and the like run sgemm_lowp_op
+with the operands stored transposed as named), "mm:bf16" / "mm:f16" =
 torch.mm in that type, 16-bit output, for context) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike, and prints one JSON line per (size, variant) with the
@@ -171,8 +172,13 @@ def sweep(variants, sizes, rounds):
                 ta, tb = v[3] == "T", v[4] == "T"
                 stored[v] = (dA.t().contiguous() if ta else dA, dB.t().contiguous() if tb else dB, ta, tb)
             if isinstance(v, str) and v.split(":")[0] in ("lowp", "mm") and ":" in v:
-                t = {"bf16": torch.bfloat16, "f16": torch.float16}[v.split(":")[1]]
-                half[v] = (dA.to(t), dB.to(t), torch.empty((M, N), dtype=t, device="cuda"))
+                parts = v.split(":")
+                t = {"bf16": torch.bfloat16, "f16": torch.float16}[parts[1]]
+                a16, b16 = dA.to(t), dB.to(t)
+                if len(parts) > 3 and parts[2] == "op":
+                    a16 = a16.t().contiguous() if parts[3][0] == "T" else a16
+                    b16 = b16.t().contiguous() if parts[3][1] == "T" else b16
+                half[v] = (a16, b16, torch.empty((M, N), dtype=t, device="cuda"))
 
         def label(v):
             if v == "mm":
@@ -182,6 +188,8 @@ def sweep(variants, sizes, rounds):
             if v in half:
                 if v.startswith("lowp"):
                     parts = v.split(":")
+                    if len(parts) > 3 and parts[2] == "op":
+                        return f"sgemm_lowp_op {parts[1]} {parts[3]}"
                     var = int(parts[2]) if len(parts) > 2 else capi.sgemm_lowp_select_variant(
                         M, N, K, half[v][0].data_ptr(), K, half[v][1].data_ptr(), N)
                     return f"sgemm_lowp {parts[1]} {capi.sgemm_lowp_variant_name(var)}"
@@ -198,7 +206,10 @@ def sweep(variants, sizes, rounds):
                 a16, b16, c16 = half[v]
                 if v.startswith("lowp"):
                     parts = v.split(":")
-                    sgemm_lowp(a16, b16, dC, variant=int(parts[2]) if len(parts) > 2 else None)
+                    if len(parts) > 3 and parts[2] == "op":
+                        sgemm_lowp(a16, b16, dC, trans_a=parts[3][0] == "T", trans_b=parts[3][1] == "T")
+                    else:
+                        sgemm_lowp(a16, b16, dC, variant=int(parts[2]) if len(parts) > 2 else None)
                 else:
                     torch.mm(a16, b16, out=c16)
             elif v in stored:

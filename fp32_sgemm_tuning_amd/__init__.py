@@ -144,21 +144,22 @@ def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, st
     return C
 
 
-def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
-    """C = alpha * A @ B + beta * C with bfloat16 or float16 A [M,K] and B
-    [K,N] (one type for both, unit column stride) and FP32 accumulation; C
-    is float32 [M,N] (allocated when None, then beta must be 0); returns C.
-    ``variant`` forces a kernel variant (tests and sweeps)."""
+def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None, trans_a=False, trans_b=False):
+    """C = alpha * op(A) @ op(B) + beta * C with bfloat16 or float16 A and B
+    (one type for both, unit column stride) and FP32 accumulation; C is
+    float32 [M,N] (allocated when None, then beta must be 0); returns C.
+    op(X) = X, or X^T with trans_a / trans_b (then A is stored [K,M], B
+    [N,K]).  ``variant`` forces a kernel variant (tests and sweeps)."""
     import torch
     codes = {torch.bfloat16: capi.SGEMM_DTYPE_BF16, torch.float16: capi.SGEMM_DTYPE_F16}
     lda = _ld(A, "A", tuple(codes))
     ldb = _ld(B, "B", tuple(codes))
     if B.dtype != A.dtype:
         raise TypeError(f"A is {A.dtype} but B is {B.dtype}")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
     if K2 != K:
-        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+        raise ValueError(f"inner dimensions differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
@@ -169,9 +170,15 @@ def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
     _same_device(A, B, C)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
-                float(beta), C.data_ptr(), ldc, s.cuda_stream)
-        st = capi.sgemm_lowp(*args) if variant is None else capi.sgemm_lowp_ex(*args, int(variant))
+        if trans_a or trans_b:
+            st = capi.sgemm_lowp_op(codes[A.dtype], capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N,
+                                    capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N, M, N, K, float(alpha),
+                                    A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
+                                    s.cuda_stream, capi.SGEMM_VARIANT_AUTO if variant is None else int(variant))
+        else:
+            args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                    float(beta), C.data_ptr(), ldc, s.cuda_stream)
+            st = capi.sgemm_lowp(*args) if variant is None else capi.sgemm_lowp_ex(*args, int(variant))
     if st != capi.SGEMM_STATUS_OK:
         raise SgemmError(st)
     return C

@@ -39,7 +39,7 @@ void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
-void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t stream);
+void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
@@ -353,13 +353,19 @@ void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStrea
 void launch_simple(const Args &a, hipStream_t stream) { launch_simple_general(a, false, false, 1, stream); }
 
 // The plain kernel on 16-bit inputs (each element widened to FP32 on load).
-void launch_simple_lowp(const Args &a0, bool f16, hipStream_t stream) {
+void launch_simple_lowp(const Args &a0, bool f16, bool ta, bool tb, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
-    if (f16)
-        hipLaunchKernelGGL((sgemm_simple_kernel<false, false, kF16>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_simple_kernel<false, false, kBF16>), grid, dim3(256), 0, stream, a);
+#define SGEMM_S(A, B)                                                                                         \
+    do {                                                                                                      \
+        if (f16) hipLaunchKernelGGL((sgemm_simple_kernel<A, B, kF16>), grid, dim3(256), 0, stream, a);        \
+        else hipLaunchKernelGGL((sgemm_simple_kernel<A, B, kBF16>), grid, dim3(256), 0, stream, a);           \
+    } while (0)
+    if (ta && tb) SGEMM_S(true, true);
+    else if (ta) SGEMM_S(true, false);
+    else if (tb) SGEMM_S(false, true);
+    else SGEMM_S(false, false);
+#undef SGEMM_S
 }
 
 struct VariantDesc {
@@ -645,15 +651,23 @@ const LowpVariant kLowpVariants[] = {
 };
 constexpr int kNumLowpVariants = (int)(sizeof(kLowpVariants) / sizeof(kLowpVariants[0]));
 
+// Variants built for transposed operands: the two alternating kernels.
+bool lowp_takes_ops(int variant) { return variant == 4 || variant == 5; }
+
 // Whether the direct-to-LDS kernel of a bm x bn tile takes the operands: its
 // loads are 16-byte chunks of 8 elements (aligned rows, N and K multiples of
 // 8), K >= 64 keeps every K tile inside the operands (the remainder tile is
 // taken first), and the buffer ranges of one block tile's part of a K tile
 // fit in 31 bits.
-bool lowp_fast_ok(const LowpVariant &v, int N, int K, const void *A, int lda, const void *B, int ldb) {
+// (ta / tb: A or B stored transposed.  A stored operand's contiguous extent,
+// K for A and N for B, or M for A^T and K for B^T, must be whole chunks.)
+bool lowp_fast_ok(const LowpVariant &v, int M, int N, int K, const void *A, int lda, const void *B, int ldb,
+                  bool ta = false, bool tb = false) {
     const long lim = 0x7fffffffL;
-    return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && N % 8 == 0 && K % 8 == 0 && K >= v.bk &&
-           2L * ((long)v.bm * lda + v.bk) < lim && 2L * ((long)v.bk * ldb + v.bn) < lim;
+    const long spanA = ta ? (long)v.bk * lda + v.bm : (long)v.bm * lda + v.bk;
+    const long spanB = tb ? (long)v.bn * ldb + v.bk : (long)v.bk * ldb + v.bn;
+    return aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && (ta ? M : K) % 8 == 0 &&
+           (tb ? K : N) % 8 == 0 && K >= v.bk && 2L * spanA < lim && 2L * spanB < lim;
 }
 
 // The largest split-K factor the 128x128 16-bit kernel (the one built with
@@ -707,11 +721,15 @@ int lowp_splits(int variant, int M, int N, int K) {
 // 256x256 and 128x128 four-stage kernels with the alternating schedule (one
 // workgroup per compute unit): the least predicted time.  Shapes none of
 // them takes run the plain kernel.
-int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {
+// (transposed operands: the two alternating kernels, which are the ones
+// built for them)
+int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb, bool ta = false,
+              bool tb = false) {
     int best = 0;
     double best_t = 0.0;
     for (int id : {1, 2, 4, 5}) {
-        if (!lowp_fast_ok(kLowpVariants[id], N, K, A, lda, B, ldb)) continue;
+        if ((ta || tb) && !lowp_takes_ops(id)) continue;
+        if (!lowp_fast_ok(kLowpVariants[id], M, N, K, A, lda, B, ldb, ta, tb)) continue;
         const double t = lowp_predict_us(id, lowp_splits(id, M, N, K), M, N, K);
         if (best == 0 || t < best_t) {
             best = id;
@@ -721,18 +739,25 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
     return best;
 }
 
-int run_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
-             float beta, float *C, int ldc, void *stream, int variant) {
+int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
+             const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
     if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_STATUS_INVALID_DTYPE;
-    const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
-    const int st = check_args(M, N, K, Af, lda, Bf, ldb, C, ldc);
-    if (st != SGEMM_STATUS_OK) return st;
+    if ((op_a != SGEMM_OP_N && op_a != SGEMM_OP_T) || (op_b != SGEMM_OP_N && op_b != SGEMM_OP_T))
+        return SGEMM_STATUS_INVALID_OP;
+    const bool ta = op_a == SGEMM_OP_T, tb = op_b == SGEMM_OP_T;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_DIM;
+    const int need_lda = ta ? (M > 1 ? M : 1) : (K > 1 ? K : 1);
+    const int need_ldb = tb ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
+    if (lda < need_lda || ldb < need_ldb || ldc < (N > 1 ? N : 1)) return SGEMM_STATUS_INVALID_DIM;
     if (variant < SGEMM_VARIANT_AUTO || variant >= kNumLowpVariants) return SGEMM_STATUS_INVALID_VARIANT;
     if (M == 0 || N == 0) return SGEMM_STATUS_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
+    const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
     if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
-    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb);
+    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb);
     const LowpVariant &v = kLowpVariants[variant];
-    if (variant > 0 && !lowp_fast_ok(v, N, K, A, lda, B, ldb)) return SGEMM_STATUS_UNSUPPORTED;
+    if (variant > 0 && ((ta || tb) && !lowp_takes_ops(variant))) return SGEMM_STATUS_UNSUPPORTED;
+    if (variant > 0 && !lowp_fast_ok(v, M, N, K, A, lda, B, ldb, ta, tb)) return SGEMM_STATUS_UNSUPPORTED;
     Args a;
     a.A = Af;
     a.B = Bf;
@@ -753,15 +778,15 @@ int run_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
-    const int ws = attach_workspace(a, lowp_splits(variant, M, N, K), stream);
+    const int ws = attach_workspace(a, ta || tb ? 1 : lowp_splits(variant, M, N, K), stream);
     if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (variant > 0)
-        launch_lowp_tile(a, f16, variant - 1, s);
+        launch_lowp_tile(a, f16, variant - 1, ta, tb, s);
     else
-        launch_simple_lowp(a, f16, s);
+        launch_simple_lowp(a, f16, ta, tb, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
@@ -773,12 +798,18 @@ extern "C" {
 
 int sgemm_lowp(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
                float beta, float *C, int ldc, void *stream) {
-    return run_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
+    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                    SGEMM_VARIANT_AUTO);
 }
 
 int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
                   float beta, float *C, int ldc, void *stream, int variant) {
-    return run_lowp(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
+                  const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
+    return run_lowp(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
 }
 
 int sgemm_lowp_select_variant(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {

@@ -116,8 +116,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // SPLIT: split-K, gridDim.y blocks per output tile, each on a contiguous
 // share of the K tiles (the remainder tile with the first), combined by
 // split_reduce_n as in the FP32 lean kernel.
+// TA / TB: A stored as A^T ([K][M], element (i,k) at A[k*lda + i]) / B as
+// B^T ([N][K], element (k,j) at B[j*ldb + k]).  Each operand keeps its
+// stored orientation in LDS: an operand stored k-contiguous (A, or B^T) sits
+// in the A-stage layout and is read with ds_read_b128; one stored
+// m- or n-contiguous (B, or A^T) sits in the swizzled [k][x] layout and is
+// read with the transpose read.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NSTAGE, bool PP, bool BETA0, bool EDGE, bool F16,
-          bool SPLIT>
+          bool SPLIT, bool TA = false, bool TB = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 sgemm_lowp_kernel(Args p) {
     static_assert(BK == 32 || BK == 64, "K tile");
@@ -130,13 +136,15 @@ sgemm_lowp_kernel(Args p) {
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
     constexpr int NA = A_BYTES / 16 / NT, NBL = B_BYTES / 16 / NT;
     constexpr int L = NA + NBL;                             // 16-byte loads per lane per K tile
-    constexpr int BROW = BN * 2;                            // bytes per B stage row
-    constexpr int BCH = BN / 8;                             // 16-byte chunks per B stage row
+    constexpr int AROW = BM * 2, ACH = BM / 8;              // [k][m] A stage (TA): bytes, chunks per row
+    constexpr int BROW = BN * 2, BCH = BN / 8;              // [k][n] B stage (!TB): bytes, chunks per row
+    constexpr int NRB = TB ? NB : 2 * NB;                   // B fragment reads per k step
     constexpr int NM = MI * NB;                             // MFMAs per k step
     constexpr int QSYNC = NM / 4 > NB ? NM / 4 : NB;        // MFMAs of a step ahead of the barrier
     static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "wave tile");
     static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "load split");
-    static_assert(BN % 128 == 0, "the B swizzle needs eight 32-byte units per row");
+    static_assert((TB || BN % 128 == 0) && (!TA || BM % 128 == 0),
+                  "the [k][x] swizzle needs eight 32-byte units per row");
     static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
 
@@ -150,26 +158,36 @@ sgemm_lowp_kernel(Args p) {
     const char *Ab = reinterpret_cast<const char *>(p.A);
     const char *Bb = reinterpret_cast<const char *>(p.B);
 
-    // direct-load coordinates of load i of this lane: 16-byte chunk u of the
-    // stage; A: (row m, chunk c = 8 elements of k); B: (row k, chunk c of n)
-    auto a_coords = [&](int i, int &m, int &c) { AL::inverse((i * NWAVES + wave) * 64 + lane, m, c); };
-    auto b_coords = [&](int i, int &k, int &c) {
+    // Direct-load coordinates of load i of this lane, 16-byte chunk u of the
+    // operand's stage: a k-contiguous stage gives (row x, chunk c = 8
+    // elements of k), a [k][x] stage (row k, chunk c = 8 elements of x).
+    // k8: the chunk's first k (compared with kr for the K remainder tile).
+    auto coords = [&](bool kcontig, int xch, int i, int &x, int &c, int &k8) {
         const int u = (i * NWAVES + wave) * 64 + lane;
-        k = u / BCH;
-        c = lowp_b_slot(u % BCH, k);                        // the swizzle is its own inverse
+        if (kcontig) {
+            AL::inverse(u, x, c);
+            k8 = 8 * c;                                     // first k of the chunk
+        } else {
+            const int k = u / xch;
+            c = lowp_b_slot(u % xch, k);                    // the swizzle is its own inverse
+            x = 8 * c;                                      // first x of the chunk
+            k8 = k;
+        }
     };
     unsigned offA[NA], offB[NBL];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        int m, c;
-        a_coords(i, m, c);
-        offA[i] = (EDGE && m0 + m >= p.M) ? kOutOfRange : 2u * (unsigned)(m * (int)p.lda + 8 * c);
+        int x, c, k;
+        coords(!TA, ACH, i, x, c, k);
+        const bool out = EDGE && m0 + x >= p.M;
+        offA[i] = out ? kOutOfRange : 2u * (unsigned)(TA ? k * (int)p.lda + 8 * c : x * (int)p.lda + 8 * c);
     }
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
-        int k, c;
-        b_coords(i, k, c);
-        offB[i] = (EDGE && n0 + 8 * c >= p.N) ? kOutOfRange : 2u * (unsigned)(k * (int)p.ldb + 8 * c);
+        int x, c, k;
+        coords(TB, BCH, i, x, c, k);
+        const bool out = EDGE && n0 + x >= p.N;
+        offB[i] = out ? kOutOfRange : 2u * (unsigned)(TB ? x * (int)p.ldb + 8 * c : k * (int)p.ldb + 8 * c);
     }
 
     const int kr = EDGE ? p.K % BK : 0;                     // K remainder, taken first
@@ -183,10 +201,14 @@ sgemm_lowp_kernel(Args p) {
         ntiles = (int)((long)total * (y + 1) / S) - t_first;
     }
     const bool remainder_first = tail && t_first == 0;
+    // Per-tile descriptors: the block's part of one K tile of each stored
+    // operand (rows up to M or N, BK deep), based at that tile.
     const long rowsA = min(BM, p.M - m0), colsB = min(BN, p.N - n0);
-    const int rangeA = (int)(2L * ((rowsA - 1) * p.lda + BK));
-    const int rangeB = (int)(2L * ((long)(BK - 1) * p.ldb + colsB));
-    const char *cornerA = Ab + 2L * m0 * p.lda, *cornerB = Bb + 2L * n0;
+    const int rangeA = (int)(TA ? 2L * ((long)(BK - 1) * p.lda + rowsA) : 2L * ((rowsA - 1) * p.lda + BK));
+    const int rangeB = (int)(TB ? 2L * ((colsB - 1) * p.ldb + BK) : 2L * ((long)(BK - 1) * p.ldb + colsB));
+    const char *cornerA = TA ? Ab + 2L * m0 : Ab + 2L * m0 * p.lda;
+    const char *cornerB = TB ? Bb + 2L * n0 * p.ldb : Bb + 2L * n0;
+    const long kstrideA = TA ? p.lda : 1, kstrideB = TB ? 1 : p.ldb;
     // LDS byte address of a point in the stages (wave-uniform)
     const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>((lds_addr_t)lds);
     // LDS address of this wave's 1 KiB of load g in stage `st` (A loads
@@ -201,21 +223,21 @@ sgemm_lowp_kernel(Args p) {
         const bool live = t < ntiles;
         const long kfirst = kr + (long)max(t_first + t - tail, 0) * BK;
         if (g < NA)
-            dma16_lowp(cornerA + 2 * kfirst, live ? rangeA : 0, dst(st, g), (int)offA[g]);
+            dma16_lowp(cornerA + 2 * kfirst * kstrideA, live ? rangeA : 0, dst(st, g), (int)offA[g]);
         else
-            dma16_lowp(cornerB + 2 * kfirst * p.ldb, live ? rangeB : 0, dst(st, g), (int)offB[g - NA]);
+            dma16_lowp(cornerB + 2 * kfirst * kstrideB, live ? rangeB : 0, dst(st, g), (int)offB[g - NA]);
     };
     auto issue_remainder = [&]() {
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            int m, c;
-            a_coords(i, m, c);
-            dma16_lowp(cornerA, rangeA, dst(0, i), (int)(8 * c < kr ? offA[i] : kOutOfRange));
+            int x, c, k;
+            coords(!TA, ACH, i, x, c, k);
+            dma16_lowp(cornerA, rangeA, dst(0, i), (int)(k < kr ? offA[i] : kOutOfRange));
         }
 #pragma unroll
         for (int i = 0; i < NBL; ++i) {
-            int k, c;
-            b_coords(i, k, c);
+            int x, c, k;
+            coords(TB, BCH, i, x, c, k);
             dma16_lowp(cornerB, rangeB, dst(0, NA + i), (int)(k < kr ? offB[i] : kOutOfRange));
         }
     };
@@ -228,22 +250,46 @@ sgemm_lowp_kernel(Args p) {
     const int lrow = lane & 15, lg = lane >> 4;
     i32x4 fa[MI];
     i32x4 fb[2][NB];
+    // the two transposed 8-byte reads of one 16-wide block of a [k][x] stage
+    // (row length ROW bytes) at x0: lane l gets x0 + l%16, k = 32s + 8(l/16) + e
+    auto read_tr = [&](const char *base, int rowbytes, int x0, int s, i32x4 &f) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int k = 32 * s + 8 * lg + 4 * half + (lrow >> 2);
+            const int x = x0 + 4 * (lrow & 3);
+            const char *addr = base + k * rowbytes + 16 * lowp_b_slot(x >> 3, k) + 8 * ((x >> 2) & 1);
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(addr));
+            const i32x2 w = __builtin_bit_cast(i32x2, v);
+            f[2 * half] = w[0];
+            f[2 * half + 1] = w[1];
+        }
+    };
     auto read_a_into = [&](int mi, const char *stage, int s, i32x4 *f) {
-        const int m = wm * WM + mi * 16 + lrow;
-        f[mi] = *reinterpret_cast<const i32x4 *>(stage + 4 * AL::offset(m, 4 * s + lg));
+        if constexpr (TA) {
+            read_tr(stage, AROW, wm * WM + mi * 16, s, f[mi]);
+        } else {
+            const int m = wm * WM + mi * 16 + lrow;
+            f[mi] = *reinterpret_cast<const i32x4 *>(stage + 4 * AL::offset(m, 4 * s + lg));
+        }
     };
     auto read_a = [&](int mi, const char *stage, int s) { read_a_into(mi, stage, s, fa); };
-    // B read r of k step s: block r/2, its transposed 8-byte read r%2
+    // B read r of k step s: from a [k][n] stage, block r/2 and its
+    // transposed 8-byte read r%2; from an [n][k] stage (TB), block r
     auto read_b = [&](int r, const char *stage, int s, i32x4 *f) {
-        const int nb = r / 2, half = r % 2;
-        const int k = 32 * s + 8 * lg + 4 * half + (lrow >> 2);
-        const int n = wn * WN + 16 * nb + 4 * (lrow & 3);
-        const int c = n >> 3;
-        const char *addr = stage + A_BYTES + k * BROW + 16 * lowp_b_slot(c, k) + 8 * ((n >> 2) & 1);
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(addr));
-        const i32x2 w = __builtin_bit_cast(i32x2, v);
-        f[nb][2 * half] = w[0];
-        f[nb][2 * half + 1] = w[1];
+        if constexpr (TB) {
+            const int n = wn * WN + 16 * r + lrow;
+            f[r] = *reinterpret_cast<const i32x4 *>(stage + A_BYTES + 4 * AL::offset(n, 4 * s + lg));
+        } else {
+            const int nb = r / 2, half = r % 2;
+            const int k = 32 * s + 8 * lg + 4 * half + (lrow >> 2);
+            const int n = wn * WN + 16 * nb + 4 * (lrow & 3);
+            const int c = n >> 3;
+            const char *addr = stage + A_BYTES + k * BROW + 16 * lowp_b_slot(c, k) + 8 * ((n >> 2) & 1);
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(addr));
+            const i32x2 w = __builtin_bit_cast(i32x2, v);
+            f[nb][2 * half] = w[0];
+            f[nb][2 * half + 1] = w[1];
+        }
     };
 
     // The product is formed transposed: the B fragment is the instruction's
@@ -285,7 +331,7 @@ sgemm_lowp_kernel(Args p) {
             if constexpr (q == QB - 1)
                 static_for<0, QB / NB>([&](auto mc) { read_a(decltype(mc)::value, rs, s); });
             if constexpr (q % NB == NB - 1 && q >= QB) read_a(q / NB, rs, s);
-            static_for<spread_upto(q - 1, 2 * NB, FIRST, RSPAN), spread_upto(q, 2 * NB, FIRST, RSPAN)>(
+            static_for<spread_upto(q - 1, NRB, FIRST, RSPAN), spread_upto(q, NRB, FIRST, RSPAN)>(
                 [&](auto r) { read_b(decltype(r)::value, rs, s, fb[1 - BC]); });
             static_for<spread_upto(q - 1, G, FIRST, GSPAN), spread_upto(q, G, FIRST, GSPAN)>(
                 [&](auto g) { issue(decltype(g)::value); });
@@ -364,7 +410,7 @@ sgemm_lowp_kernel(Args p) {
 #pragma unroll
                     for (int mi = 0; mi < MI; ++mi) read_a_into(mi, cs, ks, pa[ks]);
 #pragma unroll
-                    for (int r = 0; r < 2 * NB; ++r) read_b(r, cs, ks, pb[ks]);
+                    for (int r = 0; r < NRB; ++r) read_b(r, cs, ks, pb[ks]);
                 }
 #pragma unroll
                 for (int g = 0; g < L; ++g) issue_one(t + NSTAGE - 1, (SC + NSTAGE - 1) % NSTAGE, g);
@@ -411,7 +457,7 @@ sgemm_lowp_kernel(Args p) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) read_a(mi, lds, 0);
 #pragma unroll
-        for (int r = 0; r < 2 * NB; ++r) read_b(r, lds, 0, fb[0]);
+        for (int r = 0; r < NRB; ++r) read_b(r, lds, 0, fb[0]);
         // unrolled so that the stage (and for BK = 32 the B buffer) of
         // every tile is a compile-time constant
         constexpr int U = (BK == 32 && NSTAGE % 2) ? 2 * NSTAGE : NSTAGE;
@@ -464,13 +510,15 @@ sgemm_lowp_kernel(Args p) {
         }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT>
+template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT, bool TA = false,
+          bool TB = false>
 void launch_lowp(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(SPLIT ? a.splits : 1)), block(64 * WM * WN);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
-#define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT>), grid, block, 0, stream, a)
+#define SGEMM_LAUNCH(Z, E)                                                                                        \
+    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT, TA, TB>), grid, block, \
+                       0, stream, a)
     if (edge) {
         if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
         else SGEMM_LAUNCH(false, true);
@@ -481,11 +529,30 @@ void launch_lowp(const Args &a0, hipStream_t stream) {
 #undef SGEMM_LAUNCH
 }
 
+// One alternating kernel with each of the four operand orientations.
+template <int BM, int BN, int BK, int NS>
+void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, hipStream_t s) {
+#define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, false, A, B>(a, s)
+    if (f16) {
+        if (ta && tb) SGEMM_O(true, true, true);
+        else if (ta) SGEMM_O(true, true, false);
+        else if (tb) SGEMM_O(true, false, true);
+        else SGEMM_O(true, false, false);
+    } else {
+        if (ta && tb) SGEMM_O(false, true, true);
+        else if (ta) SGEMM_O(false, true, false);
+        else if (tb) SGEMM_O(false, false, true);
+        else SGEMM_O(false, false, false);
+    }
+#undef SGEMM_O
+}
+
 // Launcher called from the C ABI's translation unit; `tile` picks the block
 // tile, K tile, waves and number of stages (the table of variants in the C
 // ABI's translation unit lists them in this order).  a.splits > 1 runs the
-// split-K form (built for the 128x128 kernel).
-void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
+// split-K form (built for the 128x128 two-stage kernel); ta / tb (transposed
+// operands) are built for the two alternating kernels.
+void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, hipStream_t s) {
 #define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                  \
     do {                                                                         \
         if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s);       \
@@ -495,8 +562,8 @@ void launch_lowp_tile(const Args &a, bool f16, int tile, hipStream_t s) {
     switch (tile) {
         case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false, false); break;
         case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false, false); break;
-        case 3: SGEMM_T(256, 256, 32, 2, 4, 4, true, false); break;
-        case 4: SGEMM_T(128, 128, 64, 2, 4, 4, true, false); break;
+        case 3: launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, s); break;
+        case 4: launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, s); break;
         default:
             if (split) SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
             else SGEMM_T(128, 128, 64, 2, 2, 2, false, false);

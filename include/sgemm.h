@@ -229,6 +229,23 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
                   float beta, float *C, int ldc,
                   void *stream, int variant);
 
+/*
+ * sgemm_lowp_op: sgemm_lowp() with op(A) and op(B) as in sgemm_op(): with
+ * op_a = SGEMM_OP_T, A is stored K x M (lda >= max(1,M)); with op_b =
+ * SGEMM_OP_T, B is stored N x K (ldb >= max(1,K)); leading dimensions count
+ * elements.  `variant` as in sgemm_lowp_ex() (SGEMM_VARIANT_AUTO for the
+ * automatic choice); transposed operands run on the alternating-schedule
+ * variants or the plain kernel, with each operand kept in LDS in its stored
+ * orientation (16-byte chunks along its contiguous extent, which must be a
+ * multiple of 8 elements for the fast path).  No split-K.  Returns
+ * SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for another op code.
+ */
+int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
+                  const void *A, int lda,
+                  const void *B, int ldb,
+                  float beta, float *C, int ldc,
+                  void *stream, int variant);
+
 /* The variant sgemm_lowp() would run for these arguments (no launch; the
  * pointers are only inspected for alignment), or SGEMM_STATUS_INVALID_DIM. */
 int sgemm_lowp_select_variant(int M, int N, int K,

@@ -373,3 +373,24 @@ def test_tail_split_plan():
     # the automatic choice at 1536^3 is the split-capable 64x64 kernel
     assert capi.sgemm_variant_name(capi.sgemm_select_variant(1536, 1536, 1536, AL, 1536, AL, 1536, 0.0, AL,
                                                               1536)) == "lean_64x64x64_w4x1_splitk"
+
+
+def test_lowp_op_argument_checks():
+    """Transposed 16-bit operands: op codes, the leading dimensions of the
+    stored operands, and variants not built for transposes."""
+    f = capi.sgemm_lowp_op
+    bf, T, N_ = capi.SGEMM_DTYPE_BF16, capi.SGEMM_OP_T, capi.SGEMM_OP_N
+    auto = capi.SGEMM_VARIANT_AUTO
+    assert f(bf, 2, N_, 8, 8, 8, 1.0, AL, 8, AL, 8, 0.0, AL, 8, None, auto) == capi.SGEMM_STATUS_INVALID_OP
+    assert f(9, T, N_, 8, 8, 8, 1.0, AL, 8, AL, 8, 0.0, AL, 8, None, auto) == capi.SGEMM_STATUS_INVALID_DTYPE
+    # A stored K x M: lda >= M; B stored N x K: ldb >= K
+    assert f(bf, T, N_, 16, 8, 4, 1.0, AL, 15, AL, 8, 0.0, AL, 8, None, auto) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(bf, N_, T, 8, 8, 16, 1.0, AL, 16, AL, 15, 0.0, AL, 8, None, auto) == capi.SGEMM_STATUS_INVALID_DIM
+    assert f(bf, T, T, 8, 8, 8, 1.0, None, 8, AL, 8, 0.0, AL, 8, None, auto) == capi.SGEMM_STATUS_NULL_POINTER
+    assert f(bf, T, T, 0, 8, 8, 1.0, None, 1, None, 8, 0.0, None, 8, None, auto) == capi.SGEMM_STATUS_OK
+    names = {capi.sgemm_lowp_variant_name(v): v for v in capi.lowp_variants()}
+    for n in ("lowp_128x128x64_s2", "lowp_256x128x64_s3", "lowp_256x256x32_s4"):
+        assert f(bf, T, N_, 256, 256, 256, 1.0, AL, 256, AL, 256, 0.0, AL, 256, None, names[n]) == \
+            capi.SGEMM_STATUS_UNSUPPORTED
+    assert f(bf, T, N_, 256, 256, 256, 1.0, AL, 256, AL, 256, 0.0, AL, 256, None, len(names)) == \
+        capi.SGEMM_STATUS_INVALID_VARIANT

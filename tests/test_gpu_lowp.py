@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from fp32_sgemm_tuning_amd import capi, sgemm_lowp
+from fp32_sgemm_tuning_amd import SgemmError, capi, sgemm_lowp
 from fp32_sgemm_tuning_amd.inputs import make_problem_16bit, sample_indices
 from gpu_util import check_close, torch_cuda
 
@@ -241,3 +241,53 @@ def test_lowp_split_k(dtype):
             assert np.array_equal(outs[0], outs[1]), "split-K result changed between calls"
     assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 512, 768, 8192) > 1
     assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 1000, 1000, 3000) > 1
+
+
+OP_SHAPES = [(256, 512, 192), (304, 520, 1000), (129, 264, 72), (512, 256, 4104), (300, 200, 130)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans_a,trans_b", [(True, False), (False, True), (True, True)])
+def test_lowp_transposed_operands(dtype, trans_a, trans_b):
+    """op(A) / op(B) with the operands stored transposed (A as K x M, B as
+    N x K), on the automatic choice and on each variant built for them (the
+    two alternating kernels and the plain kernel); NaN in every padding
+    element of the stored operands; whole and ragged tiles, K remainders,
+    and shapes whose contiguous extents are not multiples of 8 (plain
+    kernel)."""
+    torch = torch_cuda()
+    names = {capi.sgemm_lowp_variant_name(v): v for v in capi.lowp_variants()}
+    forced = [None, names["lowp_256x256x32_s4_alt"], names["lowp_128x128x64_s4_alt"], names["lowp_simple_64x64"]]
+    for M, N, K in OP_SHAPES:
+        A, B, Cin = make_problem_16bit(M, N, K, seed=5 * M + N + 3 * K, dtype=dtype, dist="normal", with_c=True)
+        sa = np.ascontiguousarray(A.T) if trans_a else A           # stored operands
+        sb = np.ascontiguousarray(B.T) if trans_b else B
+        lda = sa.shape[1] + (8 if sa.shape[1] % 8 == 0 else 3)
+        ldb = sb.shape[1] + (8 if sb.shape[1] % 8 == 0 else 5)
+        dA, _ = _dev16(sa, dtype, torch, ld=lda)
+        dB, _ = _dev16(sb, dtype, torch, ld=ldb)
+        ref = oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=-0.5)
+        for v in forced:
+            print(f"[lowp] op {dtype} ta={trans_a} tb={trans_b} {M}x{N}x{K} variant {v}", flush=True)
+            dC = torch.from_numpy(Cin).to("cuda")
+            try:
+                sgemm_lowp(dA, dB, dC, alpha=1.25, beta=-0.5, variant=v, trans_a=trans_a, trans_b=trans_b)
+            except SgemmError as e:
+                # a fast variant forced on operands outside its fast path
+                assert v not in (None, names["lowp_simple_64x64"]) and e.status == capi.SGEMM_STATUS_UNSUPPORTED
+                continue
+            torch.cuda.synchronize()
+            check_close(dC.cpu().numpy(), ref, f"{dtype} ta={trans_a} tb={trans_b} {M}x{N}x{K} variant {v}")
+
+
+@pytest.mark.parametrize("trans_a,trans_b", [(True, False), (False, True), (True, True)])
+def test_lowp_transposed_sq4096_sampled(trans_a, trans_b):
+    torch = torch_cuda()
+    M = N = K = 4096
+    print(f"[lowp] op bf16 4096^3 ta={trans_a} tb={trans_b} (sampled)", flush=True)
+    A, B, _ = make_problem_16bit(M, N, K, seed=2, dtype="bf16")
+    dA = torch.from_numpy(np.ascontiguousarray(A.T) if trans_a else A).to(torch.bfloat16).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T) if trans_b else B).to(torch.bfloat16).cuda()
+    C = sgemm_lowp(dA, dB, trans_a=trans_a, trans_b=trans_b).cpu().numpy()
+    I, J = sample_indices(M, N, 2)
+    check_close(C[I, J], oracle.sgemm_ref_sampled(A, B, I, J), f"4096^3 ta={trans_a} tb={trans_b} sample")
