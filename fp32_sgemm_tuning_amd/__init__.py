@@ -81,16 +81,16 @@ def variant_names():
     return [capi.sgemm_variant_name(v) for v in range(capi.sgemm_num_variants())]
 
 
-def _mat(t, name):
+def _mat(t, name, dtypes=None):
     """(rows, cols, ld) of a row-major matrix view, or of each matrix of a
     3-D batch view (then also the batch stride)."""
     import torch
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
+    if t.dtype not in (dtypes or (torch.float32,)):
+        raise TypeError(f"{name} has type {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() == 2:
-        return t.shape[0], t.shape[1], _ld(t, name), 0
+        return t.shape[0], t.shape[1], _ld(t, name, dtypes), 0
     if t.dim() == 3:
         rows, cols = t.shape[1], t.shape[2]
         if cols > 1 and t.stride(2) != 1:
@@ -147,34 +147,46 @@ def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, st
 def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None, trans_a=False, trans_b=False):
     """C = alpha * op(A) @ op(B) + beta * C with bfloat16 or float16 A and B
     (one type for both, unit column stride) and FP32 accumulation; C is
-    float32 [M,N] (allocated when None, then beta must be 0); returns C.
-    op(X) = X, or X^T with trans_a / trans_b (then A is stored [K,M], B
-    [N,K]).  ``variant`` forces a kernel variant (tests and sweeps)."""
+    float32 (allocated when None, then beta must be 0); returns C.  op(X) =
+    X, or X^T with trans_a / trans_b (then A is stored [K,M], B [N,K]).  3-D
+    tensors ([batch, rows, cols], any batch stride, one of A and B may have
+    batch 1 to be shared) run as one strided batch.  ``variant`` forces a
+    kernel variant of a single untransposed problem (tests and sweeps)."""
     import torch
     codes = {torch.bfloat16: capi.SGEMM_DTYPE_BF16, torch.float16: capi.SGEMM_DTYPE_F16}
-    lda = _ld(A, "A", tuple(codes))
-    ldb = _ld(B, "B", tuple(codes))
+    batched = A.dim() == 3 or B.dim() == 3 or (C is not None and C.dim() == 3)
+    ra, ca, lda, sa = _mat(A, "A", tuple(codes))
+    rb, cb, ldb, sb = _mat(B, "B", tuple(codes))
     if B.dtype != A.dtype:
         raise TypeError(f"A is {A.dtype} but B is {B.dtype}")
-    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
-    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
     if K2 != K:
         raise ValueError(f"inner dimensions differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
+    batch = max(A.shape[0] if A.dim() == 3 else 1, B.shape[0] if B.dim() == 3 else 1)
+    for t, name in ((A, "A"), (B, "B")):
+        if t.dim() == 3 and t.shape[0] not in (1, batch):
+            raise ValueError(f"{name} has batch {t.shape[0]}, expected 1 or {batch}")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    if tuple(C.shape) != (M, N):
-        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
-    ldc = _ld(C, "C")
+        C = torch.empty((batch, M, N) if batched else (M, N), dtype=torch.float32, device=A.device)
+    rc, cc, ldc, sc = _mat(C, "C")
+    if (rc, cc) != (M, N) or (C.dim() == 3 and C.shape[0] != batch):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(batch, M, N) if batched else (M, N)}")
     _same_device(A, B, C)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    op_a = capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N
+    op_b = capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N
     with torch.cuda.device(A.device):
-        if trans_a or trans_b:
-            st = capi.sgemm_lowp_op(codes[A.dtype], capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N,
-                                    capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N, M, N, K, float(alpha),
-                                    A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
-                                    s.cuda_stream, capi.SGEMM_VARIANT_AUTO if variant is None else int(variant))
+        if batched:
+            st = capi.sgemm_lowp_strided_batched(codes[A.dtype], op_a, op_b, M, N, K, float(alpha), A.data_ptr(),
+                                                 lda, sa, B.data_ptr(), ldb, sb, float(beta), C.data_ptr(), ldc, sc,
+                                                 batch, s.cuda_stream)
+        elif trans_a or trans_b:
+            st = capi.sgemm_lowp_op(codes[A.dtype], op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda,
+                                    B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, s.cuda_stream,
+                                    capi.SGEMM_VARIANT_AUTO if variant is None else int(variant))
         else:
             args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
                     float(beta), C.data_ptr(), ldc, s.cuda_stream)

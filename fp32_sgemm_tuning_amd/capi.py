@@ -34,7 +34,8 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_variant_info", "sgemm_split_factor", "sgemm_strerror",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
            "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
-           "sgemm_lowp_variant_name", "sgemm_lowp_split_factor", "sgemm_tail_split", "sgemm_lowp_op")
+           "sgemm_lowp_variant_name", "sgemm_lowp_split_factor", "sgemm_tail_split", "sgemm_lowp_op",
+           "sgemm_lowp_strided_batched")
 
 _lib = None
 
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_lowp_ex.restype = i
     lib.sgemm_lowp_op.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, i]
     lib.sgemm_lowp_op.restype = i
+    lib.sgemm_lowp_strided_batched.argtypes = [i, i, i, i, i, i, f, vp, i, ll, vp, i, ll, f, vp, i, ll, i, vp]
+    lib.sgemm_lowp_strided_batched.restype = i
     lib.sgemm_lowp_select_variant.argtypes = [i, i, i, vp, i, vp, i]
     lib.sgemm_lowp_select_variant.restype = i
     lib.sgemm_lowp_split_factor.argtypes = [i, i, i, i]
@@ -166,6 +169,12 @@ def sgemm_lowp_ex(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, v
 
 def sgemm_lowp_op(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant):
     return load().sgemm_lowp_op(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
+
+
+def sgemm_lowp_strided_batched(dtype, op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch,
+                               stream):
+    return load().sgemm_lowp_strided_batched(dtype, op_a, op_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C,
+                                             ldc, sc, batch, stream)
 
 
 def sgemm_lowp_select_variant(M, N, K, A, lda, B, ldb):

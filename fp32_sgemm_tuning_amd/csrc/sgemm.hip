@@ -39,7 +39,7 @@ void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
 void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
-void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, hipStream_t stream);
+void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
@@ -353,9 +353,9 @@ void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStrea
 void launch_simple(const Args &a, hipStream_t stream) { launch_simple_general(a, false, false, 1, stream); }
 
 // The plain kernel on 16-bit inputs (each element widened to FP32 on load).
-void launch_simple_lowp(const Args &a0, bool f16, bool ta, bool tb, hipStream_t stream) {
+void launch_simple_lowp(const Args &a0, bool f16, bool ta, bool tb, int batch, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch);
 #define SGEMM_S(A, B)                                                                                         \
     do {                                                                                                      \
         if (f16) hipLaunchKernelGGL((sgemm_simple_kernel<A, B, kF16>), grid, dim3(256), 0, stream, a);        \
@@ -695,10 +695,10 @@ int lowp_max_splits(int variant, int M, int N, int K) {
 // kernel with two per compute unit, 2.25 alone, 4.2 for the 256x128 kernel,
 // 5.0 for the alternating 256x256 kernel and 3.3 for the alternating
 // 128x128 kernel.
-double lowp_predict_us(int variant, int s, int M, int N, int K) {
+double lowp_predict_us(int variant, int s, int M, int N, int K, long batch = 1) {
     const LowpVariant &v = kLowpVariants[variant];
     const bool two_per_cu = variant == 1;
-    const long blocks = ceil_div(M, v.bm) * ceil_div(N, v.bn) * s;
+    const long blocks = ceil_div(M, v.bm) * ceil_div(N, v.bn) * s * batch;
     const double rate = variant == 1   ? (blocks <= 256 ? 2.25 : 2.07)
                         : variant == 2 ? 4.2
                         : variant == 5 ? 3.3
@@ -724,13 +724,14 @@ int lowp_splits(int variant, int M, int N, int K) {
 // (transposed operands: the two alternating kernels, which are the ones
 // built for them)
 int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ldb, bool ta = false,
-              bool tb = false) {
+              bool tb = false, long batch = 1) {
     int best = 0;
     double best_t = 0.0;
     for (int id : {1, 2, 4, 5}) {
         if ((ta || tb) && !lowp_takes_ops(id)) continue;
         if (!lowp_fast_ok(kLowpVariants[id], M, N, K, A, lda, B, ldb, ta, tb)) continue;
-        const double t = lowp_predict_us(id, lowp_splits(id, M, N, K), M, N, K);
+        const int s = ta || tb || batch > 1 ? 1 : lowp_splits(id, M, N, K);
+        const double t = lowp_predict_us(id, s, M, N, K, batch);
         if (best == 0 || t < best_t) {
             best = id;
             best_t = t;
@@ -740,7 +741,8 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
 }
 
 int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
-             const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
+             const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant,
+             long long sA = 0, long long sB = 0, long long sC = 0, int batch = 1) {
     if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_STATUS_INVALID_DTYPE;
     if ((op_a != SGEMM_OP_N && op_a != SGEMM_OP_T) || (op_b != SGEMM_OP_N && op_b != SGEMM_OP_T))
         return SGEMM_STATUS_INVALID_OP;
@@ -749,12 +751,15 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     const int need_lda = ta ? (M > 1 ? M : 1) : (K > 1 ? K : 1);
     const int need_ldb = tb ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
     if (lda < need_lda || ldb < need_ldb || ldc < (N > 1 ? N : 1)) return SGEMM_STATUS_INVALID_DIM;
+    if (batch < 0 || batch > kMaxBatch) return SGEMM_STATUS_INVALID_DIM;
+    if (batch > 1 && (sA < 0 || sB < 0 || (M > 0 && N > 0 && sC < (long long)(M - 1) * ldc + N)))
+        return SGEMM_STATUS_INVALID_DIM;
     if (variant < SGEMM_VARIANT_AUTO || variant >= kNumLowpVariants) return SGEMM_STATUS_INVALID_VARIANT;
-    if (M == 0 || N == 0) return SGEMM_STATUS_OK;
+    if (M == 0 || N == 0 || batch == 0) return SGEMM_STATUS_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
     const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
     if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
-    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb);
+    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch);
     const LowpVariant &v = kLowpVariants[variant];
     if (variant > 0 && ((ta || tb) && !lowp_takes_ops(variant))) return SGEMM_STATUS_UNSUPPORTED;
     if (variant > 0 && !lowp_fast_ok(v, M, N, K, A, lda, B, ldb, ta, tb)) return SGEMM_STATUS_UNSUPPORTED;
@@ -777,16 +782,18 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     a.tile_base = a.tile_count = 0;
     a.ws = nullptr;
     a.counters = nullptr;
-    a.strideA = a.strideB = a.strideC = 0;
-    const int ws = attach_workspace(a, ta || tb ? 1 : lowp_splits(variant, M, N, K), stream);
+    a.strideA = batch > 1 ? (long)sA : 0;
+    a.strideB = batch > 1 ? (long)sB : 0;
+    a.strideC = batch > 1 ? (long)sC : 0;
+    const int ws = attach_workspace(a, ta || tb || batch > 1 ? 1 : lowp_splits(variant, M, N, K), stream);
     if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (variant > 0)
-        launch_lowp_tile(a, f16, variant - 1, ta, tb, s);
+        launch_lowp_tile(a, f16, variant - 1, ta, tb, batch, s);
     else
-        launch_simple_lowp(a, f16, ta, tb, s);
+        launch_simple_lowp(a, f16, ta, tb, batch, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
@@ -810,6 +817,13 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha, const void *A, in
 int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
                   const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
     return run_lowp(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A,
+                               int lda, long long stride_a, const void *B, int ldb, long long stride_b, float beta,
+                               float *C, int ldc, long long stride_c, int batch, void *stream) {
+    return run_lowp(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO,
+                    stride_a, stride_b, stride_c, batch);
 }
 
 int sgemm_lowp_select_variant(int M, int N, int K, const void *A, int lda, const void *B, int ldb) {

@@ -54,11 +54,13 @@ struct Args {
     long strideA, strideB, strideC;
 };
 
-// Move the operand pointers to problem blockIdx.z of a strided batch.
+// Move the operand pointers to problem blockIdx.z of a strided batch
+// (ESIZE: bytes per element of A and B; C is FP32).
+template <int ESIZE = 4>
 __device__ __forceinline__ void batch_offset(Args &p) {
     const long z = blockIdx.z;
-    p.A += z * p.strideA;
-    p.B += z * p.strideB;
+    p.A = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.A) + ESIZE * z * p.strideA);
+    p.B = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.B) + ESIZE * z * p.strideB);
     p.C += z * p.strideC;
 }
 
@@ -141,7 +143,7 @@ __device__ __forceinline__ float load_elem(const float *base, long e) {
 template <bool TA, bool TB, int E = kF32>
 __global__ void __launch_bounds__(256) sgemm_simple_kernel(Args p) {
     constexpr int BM = 64, BN = 64, BK = 16;
-    batch_offset(p);
+    batch_offset<E == kF32 ? 4 : 2>(p);
     __shared__ float As[BM][BK + 1];
     __shared__ float Bs[BK][BN + 1];
 

@@ -148,6 +148,7 @@ sgemm_lowp_kernel(Args p) {
     static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
 
+    batch_offset<2>(p);                                     // problem blockIdx.z of a strided batch
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -512,9 +513,10 @@ sgemm_lowp_kernel(Args p) {
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT, bool TA = false,
           bool TB = false>
-void launch_lowp(const Args &a0, hipStream_t stream) {
+void launch_lowp(const Args &a0, hipStream_t stream, int batch = 1) {
     const Args a = tiled(a0, BM, BN);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(SPLIT ? a.splits : 1)), block(64 * WM * WN);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(SPLIT ? a.splits : 1), (unsigned)batch);
+    const dim3 block(64 * WM * WN);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E)                                                                                        \
     hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT, TA, TB>), grid, block, \
@@ -531,8 +533,8 @@ void launch_lowp(const Args &a0, hipStream_t stream) {
 
 // One alternating kernel with each of the four operand orientations.
 template <int BM, int BN, int BK, int NS>
-void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, hipStream_t s) {
-#define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, false, A, B>(a, s)
+void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int batch, hipStream_t s) {
+#define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, false, A, B>(a, s, batch)
     if (f16) {
         if (ta && tb) SGEMM_O(true, true, true);
         else if (ta) SGEMM_O(true, true, false);
@@ -551,19 +553,20 @@ void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, hipStream_t s
 // tile, K tile, waves and number of stages (the table of variants in the C
 // ABI's translation unit lists them in this order).  a.splits > 1 runs the
 // split-K form (built for the 128x128 two-stage kernel); ta / tb (transposed
-// operands) are built for the two alternating kernels.
-void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, hipStream_t s) {
+// operands) are built for the two alternating kernels; batch problems on
+// gridDim.z.
+void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t s) {
 #define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                  \
     do {                                                                         \
-        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s);       \
-        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP, SP>(a, s);          \
+        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s, batch); \
+        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP, SP>(a, s, batch);    \
     } while (0)
     const bool split = a.splits > 1;
     switch (tile) {
         case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false, false); break;
         case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false, false); break;
-        case 3: launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, s); break;
-        case 4: launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, s); break;
+        case 3: launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, batch, s); break;
+        case 4: launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, batch, s); break;
         default:
             if (split) SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
             else SGEMM_T(128, 128, 64, 2, 2, 2, false, false);

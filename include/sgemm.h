@@ -246,6 +246,20 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
                   float beta, float *C, int ldc,
                   void *stream, int variant);
 
+/*
+ * sgemm_lowp_strided_batched: `batch` independent sgemm_lowp_op() problems of
+ * one shape, problem z on A + z*stride_a, B + z*stride_b (in 16-bit
+ * elements) and C + z*stride_c (in floats); the rules of
+ * sgemm_strided_batched() (0 <= batch <= 65535, strides of A and B may be 0,
+ * C problems must not overlap, one launch, no split-K) and the automatic
+ * variant choice over batch x tiles.  Returns SGEMM_STATUS_*.
+ */
+int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
+                               const void *A, int lda, long long stride_a,
+                               const void *B, int ldb, long long stride_b,
+                               float beta, float *C, int ldc, long long stride_c,
+                               int batch, void *stream);
+
 /* The variant sgemm_lowp() would run for these arguments (no launch; the
  * pointers are only inspected for alignment), or SGEMM_STATUS_INVALID_DIM. */
 int sgemm_lowp_select_variant(int M, int N, int K,

@@ -291,3 +291,39 @@ def test_lowp_transposed_sq4096_sampled(trans_a, trans_b):
     C = sgemm_lowp(dA, dB, trans_a=trans_a, trans_b=trans_b).cpu().numpy()
     I, J = sample_indices(M, N, 2)
     check_close(C[I, J], oracle.sgemm_ref_sampled(A, B, I, J), f"4096^3 ta={trans_a} tb={trans_b} sample")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans_a,trans_b,shared_b", [(False, False, False), (False, False, True), (True, False, False),
+                                                       (False, True, True), (True, True, False)])
+def test_lowp_strided_batched(dtype, trans_a, trans_b, shared_b):
+    """Strided batches of 16-bit problems (one launch, blockIdx.z), batch
+    strides with gaps between the problems, B shared by all problems
+    (stride 0), transposed operands; every problem against the oracle.
+    Shapes: one on the fast kernels, one on the plain kernel."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    batch = 3
+    for M, N, K in ((256, 264, 136), (130, 70, 50)):
+        print(f"[lowp] batched {dtype} ta={trans_a} tb={trans_b} shared_b={shared_b} {M}x{N}x{K}", flush=True)
+        probs = [make_problem_16bit(M, N, K, seed=100 + z, dtype=dtype, dist="normal", with_c=True) for z in range(batch)]
+        if shared_b:
+            probs = [(a, probs[0][1], c) for a, _, c in probs]
+        sa = [np.ascontiguousarray(a.T) if trans_a else a for a, _, _ in probs]
+        sb = [np.ascontiguousarray(b.T) if trans_b else b for _, b, _ in probs]
+        # batch strides with a gap of 8 elements after each problem
+        def stack(xs):
+            r, c = xs[0].shape
+            buf = torch.full((len(xs), r * c + 8), float("nan"), dtype=t, device="cuda")
+            view = buf[:, :r * c].view(len(xs), r, c)
+            for z, x in enumerate(xs):
+                view[z].copy_(torch.from_numpy(x).to(t))
+            return view
+        dA = stack(sa)
+        dB = stack(sb[:1]) if shared_b else stack(sb)
+        dC = torch.from_numpy(np.stack([c for _, _, c in probs])).cuda()
+        sgemm_lowp(dA, dB, dC, alpha=0.5, beta=2.0, trans_a=trans_a, trans_b=trans_b)
+        torch.cuda.synchronize()
+        C = dC.cpu().numpy()
+        for z, (a, b, c) in enumerate(probs):
+            check_close(C[z], oracle.sgemm_ref(a, b, c, alpha=0.5, beta=2.0), f"problem {z}")
