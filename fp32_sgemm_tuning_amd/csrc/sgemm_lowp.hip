@@ -66,8 +66,9 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
                                                        c, 0, 0, 0);
 }
 
-// Slot of 16-byte chunk c in row k of the B stage: the 32-byte units of a
-// row are XORed with (k % 4) + 4 * ((k / 8) % 2).  A transposed read takes
+// Slot of 16-byte chunk c in row k of a [k][x] stage (B, or A stored
+// transposed): the 32-byte units of a row are XORed with (k % 4) +
+// 4 * ((k / 8) % 2).  A transposed read takes
 // four rows k..k+3 per group of 16 lanes, and the hardware pairs the groups
 // {0,1} and {2,3} of a wave, whose rows differ by 8: measured free of bank
 // conflicts on gfx950 (the XOR with k % 4 alone measured two-way conflicts).
