@@ -41,6 +41,7 @@ void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
 void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
 void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t stream);
 void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
+void launch_lean_splitk_dw_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
 void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
@@ -273,7 +274,7 @@ int attach_workspace(Args &a, int splits, void *stream) {
     return SGEMM_STATUS_OK;
 }
 
-// Wave quantization: a grid of whole waves plus a last wave less than a
+// Wave quantization: a grid of whole waves plus a last wave at most a
 // quarter full runs as two launches, the whole waves as they are and the
 // last wave with K split S ways, so that the last wave's few tiles spread
 // over the whole chip.  Workgroup slots: two per compute unit (both lean
@@ -309,6 +310,10 @@ bool lean_fits(int bm, int bn, int bk, long lda, long ldb, bool ta, bool tb) {
 bool lean_takes(int bm, int bn, int bk, const Args &a) {
     return a.K >= bk && !(a.K % 4) && !(a.N % 4) && lean_fits(bm, bn, bk, a.lda, a.ldb, false, false);
 }
+// The same for the lean kernel with 4-byte loads (any K, N and alignment).
+bool lean_dw_takes(int bm, int bn, int bk, const Args &a) {
+    return a.K >= bk && lean_fits(bm, bn, bk, a.lda, a.ldb, false, false);
+}
 
 // The lean kernel takes K >= BK, K and N multiples of 4 (M, N and K need not
 // be whole tiles) and offsets within a tile that fit the descriptors' range;
@@ -331,10 +336,13 @@ void launch_lean_or(const Args &a, hipStream_t stream) {
 // offsets within a tile that fit as above; other shapes go to FALLBACK.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
 void launch_lean_dw_or(const Args &a, hipStream_t stream) {
-    if (a.K >= BK && lean_fits(BM, BN, BK, a.lda, a.ldb, false, false))
+    if (lean_dw_takes(BM, BN, BK, a)) {
         LEAN(a, stream);
-    else
-        FALLBACK(a, stream);
+    } else {
+        Args whole = a;                      // the fallback covers the whole grid
+        whole.tile_base = whole.tile_count = 0;
+        FALLBACK(whole, stream);
+    }
 }
 
 void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStream_t stream) {
@@ -374,6 +382,7 @@ struct VariantDesc {
     bool needs_vec;
     Launcher launch;
     bool split_k = false;   // may split K (needs the workspace)
+    bool dw = false;        // lean kernel with 4-byte loads (any alignment)
 };
 
 // Ids 0..2 are the stable ones named in sgemm.h; the rest are tile shapes
@@ -449,16 +458,21 @@ const VariantDesc kVariants[] = {
      launch_lean_dw_or<128, 128, 32, launch_lean_dw_128x128x32_w2x2, launch_db<128, 128, 32, 2, 2, false>>},
     {"lean_dw_64x64x64_w4x1", 64, 64, 64, false,
      launch_lean_dw_or<64, 64, 64, launch_lean_dw_64x64x64_w4x1, launch_db<128, 128, 32, 2, 2, false>>},
+    {"lean_dw_64x64x64_w4x1_splitk", 64, 64, 64, false,
+     launch_lean_dw_or<64, 64, 64,
+                       launch_split_or_plain<launch_lean_splitk_dw_64x64x64_w4x1, launch_lean_dw_64x64x64_w4x1>,
+                       launch_db<128, 128, 32, 2, 2, false>>,
+     true, true},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 int choose_tail_splits(const VariantDesc &d, const Args &a) {
-    if (!lean_takes(d.bm, d.bn, d.bk, a)) return 1;
+    if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
     const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
     const long rem = tiles % kTailSlots;
-    if (tiles < kTailSlots || rem == 0 || rem * 4 > kTailSlots || rem > kSplitMaxTiles) return 1;
+    if (tiles < kTailSlots || rem == 0 || rem * 3 > kTailSlots || rem > kSplitMaxTiles) return 1;
     long s = kTailSlots / rem;
-    s = std::min(s, ceil_div(a.K, d.bk) / 2);
+    s = std::min(s, ceil_div(a.K, d.bk) / 3);
     s = std::min(s, 16L);
     s = std::min(s, (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem)));
     return s < 2 ? 1 : (int)s;
@@ -469,7 +483,7 @@ int choose_tail_splits(const VariantDesc &d, const Args &a) {
 constexpr int kVec = 24;       // lean_128x128x32_w2x2
 constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below 160 tiles)
 constexpr int kAny = 37;       // lean_dw_128x128x32_w2x2: 4-byte loads, any alignment
-constexpr int kAny64 = 38;     // lean_dw_64x64x64_w4x1
+constexpr int kAny64 = 39;     // lean_dw_64x64x64_w4x1_splitk
 constexpr int kNumCUs = 256;   // MI355X
 constexpr int kMaxBatch = 65535;  // problems per strided batch (launch grid z extent)
 

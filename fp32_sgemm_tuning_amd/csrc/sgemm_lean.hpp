@@ -51,6 +51,12 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // and takes a ticket from the tile's counter.  Returns false
 // for all blocks but the last; the last one reads all partials back, leaves
 // their sum in split order in acc and resets the counter for the next call.
+// The ticket is shared through word 0 of the kernel's own LDS buffer
+// (`ticket`), free by then: the barrier below follows every wave's last LDS
+// read and its last direct-to-LDS load.  A second LDS object would cost the
+// whole K loop: the compiler then no longer tells the direct-to-LDS writes
+// apart from the fragment reads and waits for every load to land before the
+// next LDS read.
 //
 // Every XCD has its own L2, so the partials move at device scope: the
 // stores and loads carry the device-scope cache policy (sc1, the encoding
@@ -59,7 +65,7 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // the ticket is a device-scope atomic.  No cache-wide write-back or
 // invalidate is needed, so other blocks keep their cached A and B.
 template <int NT, int NACC, class Ref>
-__device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int tid, Ref &&acc) {
+__device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int tid, unsigned *ticket, Ref &&acc) {
     constexpr int TILE = NT * NACC * 4;                 // floats per partial tile
     constexpr int kDeviceScope = 16;                    // cache policy bits: sc1
     const int S = gridDim.y, y = blockIdx.y;
@@ -70,10 +76,9 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
         __builtin_amdgcn_raw_buffer_store_b128(acc(c), slab, (c * NT + tid) * 16, y * TILE * 4, kDeviceScope);
     wait_vmcnt0();
     __syncthreads();
-    __shared__ unsigned ticket;
-    if (tid == 0) ticket = atomicAdd(p.counters + tile_id, 1u);
+    if (tid == 0) *ticket = atomicAdd(p.counters + tile_id, 1u);
     __syncthreads();
-    if (ticket != (unsigned)(S - 1)) return false;
+    if (*ticket != (unsigned)(S - 1)) return false;
     // every partial, this block's own included, is read back in split
     // order, so the sum needs no registers beyond the accumulators
     for (int s = 0; s < S; ++s) {
@@ -90,9 +95,10 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
 
 // The same for the FP32 lean kernels' accumulator layout.
 template <class T>
-__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, f32x4 (&acc)[T::MI][T::NJ][4]) {
+__device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid, unsigned *ticket,
+                                             f32x4 (&acc)[T::MI][T::NJ][4]) {
     return split_reduce_n<T::NT, T::MI * T::NJ * 4>(
-        p, tile_id, tid, [&](int c) -> f32x4 & { return acc[c / (T::NJ * 4)][(c / 4) % T::NJ][c % 4]; });
+        p, tile_id, tid, ticket, [&](int c) -> f32x4 & { return acc[c / (T::NJ * 4)][(c / 4) % T::NJ][c % 4]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +366,7 @@ sgemm_lean_kernel(Args p) {
         if (t < t_end) tile(t, IntC<0>{});
     }
     if constexpr (SPLIT) {
-        if (!split_reduce<T>(p, slot, tid, acc)) return;
+        if (!split_reduce<T>(p, slot, tid, reinterpret_cast<unsigned *>(lds), acc)) return;
     }
     T::template epilogue<BETA0>(p, m0, n0, wm, wn, lane, acc);
 }

@@ -21,5 +21,9 @@ void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t s)
 void launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t s) {
     launch_lean<128, 64, 32, 4, 1, true>(a, splits, s);
 }
+// 4-byte loads (any alignment)
+void launch_lean_splitk_dw_64x64x64_w4x1(const Args &a, int splits, hipStream_t s) {
+    launch_lean<64, 64, 64, 4, 1, true, true>(a, splits, s);
+}
 
 }  // namespace sgemm_mi355x

@@ -476,7 +476,7 @@ sgemm_lowp_kernel(Args p) {
     }
 
     if constexpr (SPLIT) {
-        if (!split_reduce_n<NT, MI * NB>(p, slot, tid,
+        if (!split_reduce_n<NT, MI * NB>(p, slot, tid, reinterpret_cast<unsigned *>(lds),
                                          [&](int c) -> f32x4 & { return acc[c / NB][c % NB]; }))
             return;
     }

@@ -189,9 +189,9 @@ def test_variant_selection_by_alignment():
     for args in [(MIS, 64, AL, 64, AL, 64), (AL, 64, MIS, 64, AL, 64), (AL, 64, AL, 64, MIS, 64),
                  (AL, 66, AL, 64, AL, 64)]:
         a, lda, b, ldb, c, ldc = args
-        assert _name(sel(64, 64, 64, a, lda, b, ldb, 0.0, c, ldc)) == "lean_dw_64x64x64_w4x1"
+        assert _name(sel(64, 64, 64, a, lda, b, ldb, 0.0, c, ldc)) == "lean_dw_64x64x64_w4x1_splitk"
     assert _name(sel(4096, 4096, 4095, AL, 4095, AL, 4096, 0.0, AL, 4096)) == "lean_dw_128x128x32_w2x2"
-    assert _name(sel(3072, 3072, 3071, AL, 3071, AL, 3072, 0.0, AL, 3072)) == "lean_dw_64x64x64_w4x1"
+    assert _name(sel(3072, 3072, 3071, AL, 3071, AL, 3072, 0.0, AL, 3072)) == "lean_dw_64x64x64_w4x1_splitk"
     # the ragged workload's leading dimensions (2047, 4999) are not multiples of 4
     assert not _needs_vec(sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999))
     assert sel(-1, 4, 4, AL, 4, AL, 4, 0.0, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM
@@ -354,20 +354,27 @@ def test_lowp_split_factors():
 
 def test_tail_split_plan():
     """A grid of whole waves (512 workgroup slots) plus a last wave at most a
-    quarter full runs as two launches, the last wave's tiles with K split."""
+    third full runs as two launches, the last wave's tiles with K split (at
+    least three K tiles per split); the any-alignment 64x64 kernel too."""
     names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
     v64, v128 = names["lean_64x64x64_w4x1_splitk"], names["lean_128x128x32_w2x2_splitk"]
     t = capi.sgemm_tail_split
     assert t(v64, 1536, 1536, 1536) == (8, 64)      # 576 tiles = 512 + 64
     assert t(v64, 1550, 1572, 1000) == (4, 113)     # 625 tiles, 16 K tiles
     assert t(v64, 1550, 1570, 1000) == (1, 0)       # N not a multiple of 4: no lean kernel
-    assert t(v128, 2944, 2944, 256) == (4, 17)      # 529 tiles, 8 K tiles
+    assert t(v128, 2944, 2944, 256) == (2, 17)      # 529 tiles, 8 K tiles
     assert t(v64, 2048, 2048, 2048) == (1, 0)       # whole waves
     assert t(v128, 4096, 4096, 4096) == (1, 0)
-    assert t(v64, 1664, 1664, 1664) == (1, 0)       # 676 tiles: last wave a third full
+    assert t(v64, 1664, 1664, 1664) == (3, 164)     # 676 tiles: last wave under a third full
+    assert t(v64, 1792, 1792, 1792) == (1, 0)       # 784 tiles: last wave over half full
+    assert t(v64, 2944, 2944, 128) == (1, 0)        # 2116 tiles, 2 K tiles
     assert t(v64, 512, 512, 4096) == (1, 0)         # a small grid splits K as a whole instead
     assert t(v64, 1536, 1536, 64) == (1, 0)         # one K tile
     assert t(names["lean_64x64x64_w4x1"], 1536, 1536, 1536) == (1, 0)   # no split-K form
+    vdw = names["lean_dw_64x64x64_w4x1_splitk"]
+    assert t(vdw, 1535, 1537, 1535) == (5, 88)      # 600 tiles = 1 wave + 88
+    assert t(vdw, 3001, 4999, 2047) == (3, 129)     # 3713 tiles = 7 waves + 129
+    assert t(vdw, 1536, 1536, 1535) == (8, 64)      # K not a multiple of 4: the 4-byte kernel takes it
     assert t(len(names), 8, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_VARIANT
     assert t(v64, -1, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_DIM
     # the automatic choice at 1536^3 is the split-capable 64x64 kernel
