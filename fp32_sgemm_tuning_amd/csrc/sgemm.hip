@@ -185,36 +185,63 @@ typedef void (*Launcher)(const Args &, hipStream_t);
 // compute unit leaves CUs idle while each busy CU walks all of K; splitting
 // K over S blocks per tile multiplies the parallelism by S at the price of
 // writing and re-reading S partial tiles.  Every split-capable lean tile has
-// four waves, so the limits below count blocks alike for all of them.
-constexpr long kSplitMaxBlocks = 512;                    // splits x tiles (two blocks per CU)
+// four waves and 64 KiB of LDS (two blocks per CU), so the model below
+// counts blocks alike for all of them.
+constexpr long kNumCUs = 256;                            // MI355X
+constexpr long kTailSlots = 2 * kNumCUs;                 // resident lean blocks: two per CU
 constexpr long kSplitMaxTiles = 4096;                    // tiles with counters
 constexpr size_t kSplitPartialBytes = 64u << 20;         // 1024 partial tiles of 128x128, 256 of 256x256
 constexpr size_t kSplitWorkspaceBytes = kSplitPartialBytes + kSplitMaxTiles * sizeof(unsigned);
 
 // Split factor for an M x N x K problem on bm x bn x bk tiles (1 = no
-// split): up to 512 blocks in all, at least four K tiles per split, at most
-// 16 splits, only while the tile grid has fewer than 160 tiles (measured on
-// 128x128 tiles: 144 tiles gain from three splits, 180 tiles lose with two
-// or four).  SGEMM_SPLITK forces a factor (clamped to the same limits and
-// to the workspace) for sweeps.
+// split), for grids of fewer than one full wave of resident blocks (larger
+// grids are left to the last-wave split).  Cost model, in K-tile steps of
+// one block on a CU of its own (2 * bm * bn * bk flops at 1/256 of the
+// 157.3 TFLOP/s peak):
+//   - the busiest CU: a CU runs its blocks at about the same aggregate rate
+//     whether it holds one or two, so ceil(tiles * S / 256) blocks of
+//     ceil(kt / S) steps and about half a step of pipeline fill each;
+//   - a floor set by the operand traffic of the whole grid, which every S
+//     moves alike: 0.15 * tiles * kt * (bm + bn) / (bm * bn) steps;
+//   - the partials, written and read back once each (8 * S * bm * bn bytes
+//     per tile at about 5 TB/s): 0.49 * S * tiles / bk steps.
+// The cost is the larger of the first two plus the third.  S is the factor
+// of least cost, with at least four K tiles per split, at most 16, within
+// the workspace, taken when it costs at most 95% of no split.  The floor's
+// and the fill's constants are fitted to measured sweeps (19 shapes from
+// 16 to 484 tiles of 64x64, S = 1 to 16): the factor chosen is the fastest
+// measured one, or within 6% of it, on every shape.  SGEMM_SPLITK forces a
+// factor (clamped to the K tiles and the workspace) for sweeps.
+double split_cost(long tiles, long kt, long s, int bm, int bn, int bk) {
+    const double busiest = (double)ceil_div(tiles * s, kNumCUs) * ((double)ceil_div(kt, s) + 0.5);
+    const double floor = 0.15 * (double)(tiles * kt) * (double)(bm + bn) / ((double)bm * bn);
+    const double partials = s > 1 ? 0.49 * (double)(s * tiles) / bk : 0.0;
+    return (busiest > floor ? busiest : floor) + partials;
+}
+
 int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
     const long tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const long kt = ceil_div(K, bk);
     const long fit = (long)(kSplitPartialBytes / ((size_t)bm * bn * sizeof(float)));
     if (tiles > kSplitMaxTiles || kt < 2) return 1;
-    long s;
     if (knobs().splitk > 0) {
-        s = knobs().splitk;
+        long s = knobs().splitk;
         if (s * tiles > fit) s = fit / tiles;
-    } else {
-        if (tiles >= 160) return 1;
-        s = kSplitMaxBlocks / tiles;
-        if (s > kt / 4) s = kt / 4;
-        if (s > 16) s = 16;
-        if (s * tiles > kSplitMaxBlocks) s = kSplitMaxBlocks / tiles;
+        if (s > kt) s = kt;
+        return s < 1 ? 1 : (int)s;
     }
-    if (s > kt) s = kt;
-    return s < 1 ? 1 : (int)s;
+    if (tiles >= kTailSlots) return 1;
+    const double base = split_cost(tiles, kt, 1, bm, bn, bk);
+    long best = 1;
+    double best_cost = base;
+    for (long s = 2; s <= 16 && s <= kt / 4 && s * tiles <= fit; ++s) {
+        const double cost = split_cost(tiles, kt, s, bm, bn, bk);
+        if (cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return best_cost <= 0.95 * base ? (int)best : 1;
 }
 
 // One split-K workspace per (device, stream), allocated on first use and
@@ -277,10 +304,9 @@ int attach_workspace(Args &a, int splits, void *stream) {
 // Wave quantization: a grid of whole waves plus a last wave at most a
 // quarter full runs as two launches, the whole waves as they are and the
 // last wave with K split S ways, so that the last wave's few tiles spread
-// over the whole chip.  Workgroup slots: two per compute unit (both lean
-// default tiles).  S: up to the slots over the tiles left, at least two K
-// tiles per split, at most 16, within the workspace; 1 = one launch.
-constexpr long kTailSlots = 2 * 256;
+// over the whole chip.  Workgroup slots: two per compute unit (kTailSlots).
+// S: up to the slots over the tiles left, at least three K tiles per split,
+// at most 16, within the workspace; 1 = one launch.
 struct VariantDesc;
 int choose_tail_splits(const VariantDesc &d, const Args &a);
 
@@ -470,7 +496,7 @@ int choose_tail_splits(const VariantDesc &d, const Args &a) {
     if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
     const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
     const long rem = tiles % kTailSlots;
-    if (tiles < kTailSlots || rem == 0 || rem * 3 > kTailSlots || rem > kSplitMaxTiles) return 1;
+    if (tiles < kTailSlots || rem == 0 || rem * 4 > kTailSlots || rem > kSplitMaxTiles) return 1;
     long s = kTailSlots / rem;
     s = std::min(s, ceil_div(a.K, d.bk) / 3);
     s = std::min(s, 16L);
@@ -484,7 +510,6 @@ constexpr int kVec = 24;       // lean_128x128x32_w2x2
 constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below 160 tiles)
 constexpr int kAny = 37;       // lean_dw_128x128x32_w2x2: 4-byte loads, any alignment
 constexpr int kAny64 = 39;     // lean_dw_64x64x64_w4x1_splitk
-constexpr int kNumCUs = 256;   // MI355X
 constexpr int kMaxBatch = 65535;  // problems per strided batch (launch grid z extent)
 
 // Fill of the last wave of blocks: with t tiles spread over the CUs, the

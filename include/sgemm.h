@@ -89,11 +89,13 @@ extern "C" {
  * the alignment class and the shape: the lean direct-to-LDS kernel with
  * 16-byte loads when the operands allow 128-bit access, else with 4-byte
  * loads (any alignment); on 64x64x64 block tiles when a 128x128 grid would
- * have fewer than 160 tiles or a less full last wave over the 256 compute
- * units, else on 128x128x32 tiles.  The 16-byte 64x64x64 form splits K when
- * its own grid has fewer than 160 tiles.  Shapes a lean kernel does not
- * take go to a guarded kernel.  beta == 0 selects an epilogue that never
- * reads C.  Returns SGEMM_STATUS_*.
+ * have at most 256 tiles or a less full last wave over the 256 compute
+ * units, else on 128x128x32 tiles.  The 64x64x64 forms split K when their
+ * own grid is under one wave of resident blocks (512 tiles) and splitting
+ * saves time by the library's cost model (see sgemm_split_factor), and
+ * split the last wave of a larger grid (see sgemm_tail_split).  Shapes a
+ * lean kernel does not take go to a guarded kernel.  beta == 0 selects an
+ * epilogue that never reads C.  Returns SGEMM_STATUS_*.
  */
 int sgemm(int M, int N, int K, float alpha,
           const float *A, int lda,
@@ -279,9 +281,13 @@ const char *sgemm_lowp_variant_name(int variant);
  * (1 = no split) that sgemm_ex() with this variant would use for an
  * M x N x K problem whose operands the variant's split-K kernel takes (see
  * "Workspace" above; environment variable SGEMM_SPLITK = S forces S for
- * sweeps).  Always 1 for variants without split-K.  No HIP call.  Returns
- * the factor, SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM
- * (negative sizes).
+ * sweeps).  Only grids of fewer than 512 tiles split; the factor (at most
+ * 16, at least four K tiles per split) is the one of least modelled time:
+ * the busiest compute unit's share of blocks, bounded below by the grid's
+ * operand traffic, plus writing and reading back the partial tiles; taken
+ * when that is at most 95% of the unsplit time.  Always 1 for variants
+ * without split-K.  No HIP call.  Returns the factor,
+ * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM (negative sizes).
  */
 int sgemm_split_factor(int variant, int M, int N, int K);
 

@@ -155,26 +155,34 @@ def test_variant_selection_by_shape(shape, expected):
 
 
 def test_split_factors():
-    """K is split only below 160 tiles of the variant's own tile, by at most
-    16, into splits of at least four K tiles, within 512 workgroups."""
+    """K is split only for grids under one full wave of resident blocks (512
+    tiles of the variant's own tile), by the factor of least modelled cost
+    (busiest CU, operand-traffic floor, partials), at most 16, into splits of
+    at least four K tiles, and only when that saves at least 5%."""
     names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
     v128, v64 = names["lean_128x128x32_w2x2_splitk"], names["lean_64x64x64_w4x1_splitk"]
     f = capi.sgemm_split_factor
-    assert f(v128, 1024, 1024, 1024) == 8          # 64 tiles, 32 K tiles
-    assert f(v128, 512, 512, 512) == 4             # 16 tiles, 16 K tiles
+    assert f(v128, 1024, 1024, 1024) == 4          # 64 tiles, 32 K tiles: one block per CU
+    assert f(v128, 512, 512, 512) == 4             # 16 tiles, 16 K tiles: four K tiles per split
     assert f(v128, 64, 64, 4096) == 16
     assert f(v128, 1536, 1536, 1536) == 3          # 144 tiles
     assert f(v128, 1920, 1536, 1024) == 1          # 180 tiles
     assert f(v128, 1024, 1024, 128) == 1           # 4 K tiles
-    assert f(v64, 1024, 1024, 1024) == 1           # 256 tiles of 64x64
-    assert f(v64, 512, 512, 2048) == 8             # 64 tiles, 32 K tiles of 64
-    assert f(v64, 256, 256, 8192) == 16
+    assert f(v64, 1024, 1024, 1024) == 1           # 256 tiles of 64x64: every CU busy
+    assert f(v64, 512, 512, 2048) == 4             # 64 tiles, 32 K tiles of 64
+    assert f(v64, 768, 768, 4096) == 3             # 144 tiles: 432 blocks
+    assert f(v64, 640, 640, 4096) == 5             # 100 tiles: 500 blocks
+    assert f(v64, 1152, 1152, 2048) == 2           # 324 tiles
+    assert f(v64, 1280, 1280, 2048) == 1           # 400 tiles: too little to gain
+    assert f(v64, 1024, 1024, 8192) == 1           # 256 tiles
+    assert f(v64, 256, 256, 8192) == 15
+    assert f(v64, 2048, 2048, 64) == 1             # whole waves: left to the last-wave split
     for v in (v128, v64):
-        for (M, N, K) in [(100, 100, 10000), (300, 200, 500), (1, 1, 100000)]:
+        for (M, N, K) in [(100, 100, 10000), (300, 200, 500), (1, 1, 100000), (900, 700, 3000)]:
             s = f(v, M, N, K)
             st, bm, bn, bk, _ = capi.sgemm_variant_info(v)
             tiles = -(-M // bm) * -(-N // bn)
-            assert 1 <= s <= 16 and s * tiles <= 512 and (s == 1 or -(-K // bk) >= 4 * s), (v, M, N, K, s)
+            assert 1 <= s <= 16 and (s == 1 or (tiles < 512 and -(-K // bk) >= 4 * s)), (v, M, N, K, s)
     # variants without split-K, bad ids, bad sizes
     assert f(names["lean_128x128x32_w2x2"], 64, 64, 4096) == 1
     assert f(capi.sgemm_num_variants(), 64, 64, 64) == capi.SGEMM_STATUS_INVALID_VARIANT
@@ -354,7 +362,7 @@ def test_lowp_split_factors():
 
 def test_tail_split_plan():
     """A grid of whole waves (512 workgroup slots) plus a last wave at most a
-    third full runs as two launches, the last wave's tiles with K split (at
+    quarter full runs as two launches, the last wave's tiles with K split (at
     least three K tiles per split); the any-alignment 64x64 kernel too."""
     names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
     v64, v128 = names["lean_64x64x64_w4x1_splitk"], names["lean_128x128x32_w2x2_splitk"]
@@ -365,7 +373,8 @@ def test_tail_split_plan():
     assert t(v128, 2944, 2944, 256) == (2, 17)      # 529 tiles, 8 K tiles
     assert t(v64, 2048, 2048, 2048) == (1, 0)       # whole waves
     assert t(v128, 4096, 4096, 4096) == (1, 0)
-    assert t(v64, 1664, 1664, 1664) == (3, 164)     # 676 tiles: last wave under a third full
+    assert t(v64, 1664, 1664, 1664) == (1, 0)       # 676 tiles: last wave a third full
+    assert t(v64, 1600, 1600, 1600) == (4, 113)     # 625 tiles: 113 left, 25 K tiles
     assert t(v64, 1792, 1792, 1792) == (1, 0)       # 784 tiles: last wave over half full
     assert t(v64, 2944, 2944, 128) == (1, 0)        # 2116 tiles, 2 K tiles
     assert t(v64, 512, 512, 4096) == (1, 0)         # a small grid splits K as a whole instead
@@ -373,7 +382,7 @@ def test_tail_split_plan():
     assert t(names["lean_64x64x64_w4x1"], 1536, 1536, 1536) == (1, 0)   # no split-K form
     vdw = names["lean_dw_64x64x64_w4x1_splitk"]
     assert t(vdw, 1535, 1537, 1535) == (5, 88)      # 600 tiles = 1 wave + 88
-    assert t(vdw, 3001, 4999, 2047) == (3, 129)     # 3713 tiles = 7 waves + 129
+    assert t(vdw, 3001, 4999, 2047) == (1, 0)       # 3713 tiles = 7 waves + 129: over a quarter
     assert t(vdw, 1536, 1536, 1535) == (8, 64)      # K not a multiple of 4: the 4-byte kernel takes it
     assert t(len(names), 8, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_VARIANT
     assert t(v64, -1, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_DIM
