@@ -196,6 +196,40 @@ def test_split_k(shape, ab):
         assert torch.equal(o, outs[0]), "split-K result changed between identical calls"
 
 
+AUTO_SPLIT_CASES = [
+    # (M, N, K, split factor the automatic choice takes)
+    (256, 256, 16384, 15),        # 128 K tiles over 15 splits: uneven shares
+    (640, 640, 4096, 5),
+    (1152, 1152, 2048, 2),
+    (767, 767, 4095, 3),          # any alignment: 4-byte loads, K remainder
+    (509, 515, 8191, 3),
+]
+
+
+@pytest.mark.parametrize("M,N,K,S", AUTO_SPLIT_CASES, ids=[f"{m}x{n}x{k}" for m, n, k, _ in AUTO_SPLIT_CASES])
+def test_auto_split_factors(M, N, K, S):
+    """The automatic choice on grids where the split-K cost model splits K:
+    the factor is the expected one, the result matches the oracle element by
+    element for beta = 0 (NaN in C) and beta != 0, and repeats bit for bit."""
+    torch = torch_cuda()
+    A, B, Cin = make_problem(M, N, K, seed=M + 2 * N + K, dist="normal", with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    probe = torch.empty((M, N), device="cuda")
+    v = capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, probe.data_ptr(), N)
+    assert capi.sgemm_split_factor(v, M, N, K) == S, (capi.sgemm_variant_name(v), S)
+    print(f"[auto split] {M}x{N}x{K} {capi.sgemm_variant_name(v)} S={S}", flush=True)
+    for alpha, beta in ((1.0, 0.0), (0.5, -1.5)):
+        ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+        outs = []
+        for _ in range(2):
+            dC = to_dev(Cin, torch) if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+            sgemm(dA, dB, dC, alpha=alpha, beta=beta)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().numpy())
+        check_close(outs[0], ref, f"auto split {M}x{N}x{K} beta={beta}")
+        assert np.array_equal(outs[0], outs[1])
+
+
 def test_split_k_on_two_streams():
     """Two split-K calls in flight on two streams use separate workspaces."""
     torch = torch_cuda()
