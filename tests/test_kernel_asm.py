@@ -1,13 +1,17 @@
-"""Checks on the gfx950 assembly of the split-K kernels (CPU only: hipcc
+"""Checks on the gfx950 assembly of the lean kernels (CPU only: hipcc
 cross-compiles).
 
 The lean kernels stream their K tiles with direct-to-LDS buffer loads and
-wait for them once per K tile.  If the compiler cannot tell those LDS writes
-apart from the kernel's LDS reads (it could not while the split-K ticket was
-a second __shared__ variable), it puts a wait for every outstanding load after
-each direct load, which serialises the loads of the K loop.  This test builds
-the split-K translation unit to assembly and counts, per kernel, the direct
-loads followed within a few instructions by a full `vmcnt(0)` wait.
+wait for them once per K tile.
+- If the compiler cannot tell those LDS writes apart from the kernel's LDS
+  reads (it could not while the split-K ticket was a second __shared__
+  variable), it puts a wait for every outstanding load after each direct
+  load, which serialises the loads of the K loop.
+- If a buffer descriptor ends up in vector registers (a wave-uniform value
+  merged through divergent control flow), every load using it runs inside a
+  waterfall loop (read the first lane, compare, mask, repeat).
+Both cost a large share of the kernel's speed and neither shows in results,
+so the tests build the translation units to assembly and look for them.
 """
 import os
 import re
@@ -20,17 +24,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc")
 
 
-def _device_asm(unit, tmp_path):
+def _device_asm(units, tmp_path):
+    """Device assembly of each unit, built in parallel: {unit: text}."""
     from fp32_sgemm_tuning_amd import build as b
     hipcc = b.HIPCC if os.path.exists(b.HIPCC) else shutil.which("hipcc")
     if not hipcc:
         pytest.skip("hipcc not available")
-    extra = dict(b.UNITS)[unit]
-    out = os.path.join(str(tmp_path), unit + ".s")
-    cmd = [hipcc, *b.HIP_FLAGS, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, unit), "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return open(out).read()
+    procs = {}
+    for unit in units:
+        out = os.path.join(str(tmp_path), unit + ".s")
+        cmd = [hipcc, *b.HIP_FLAGS, *dict(b.UNITS)[unit], "--cuda-device-only", "-S", os.path.join(CSRC, unit),
+               "-o", out]
+        procs[unit] = (out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    texts = {}
+    for unit, (out, proc) in procs.items():
+        _, err = proc.communicate()
+        assert proc.returncode == 0, err[-2000:]
+        texts[unit] = open(out).read()
+    return texts
+
+
+@pytest.fixture(scope="module")
+def lean_asm(tmp_path_factory):
+    return _device_asm(["sgemm_lean.hip", "sgemm_lean_split.hip"], tmp_path_factory.mktemp("asm"))
 
 
 def _waits_after_direct_loads(asm):
@@ -56,9 +72,48 @@ def _waits_after_direct_loads(asm):
     return out
 
 
-def test_split_k_loop_keeps_loads_in_flight(tmp_path):
-    asm = _device_asm("sgemm_lean_split.hip", tmp_path)
-    kernels = _waits_after_direct_loads(asm)
+def _kernels(asm):
+    for m in re.finditer(r"^(_Z\S+):", asm, re.M):
+        end = asm.find(".Lfunc_end", m.end())
+        yield m.group(1), asm[m.end():end].splitlines()
+
+
+def _waterfall_loops(lines):
+    """Loops (a label and a branch back to it) of under 40 lines holding a
+    buffer access and a v_readfirstlane: the shape of a waterfall loop."""
+    n = 0
+    for h, line in enumerate(lines):
+        if "Loop Header" not in line:
+            continue
+        label = line.split(":")[0]
+        back = [i for i, x in enumerate(lines) if "s_cbranch" in x and x.strip().endswith(label)]
+        if not back:
+            continue
+        body = lines[h:back[-1] + 1]
+        if len(body) < 40 and any("v_readfirstlane" in x for x in body) and any("buffer_" in x for x in body):
+            n += 1
+    return n
+
+
+def test_no_waterfall_loops(lean_asm):
+    """Every buffer descriptor of the lean kernels (plain and split-K, every
+    edge and alignment form) stays in scalar registers."""
+    bad = {}
+    count = 0
+    for unit, asm in lean_asm.items():
+        for name, lines in _kernels(asm):
+            if "sgemm_lean_kernel" not in name:
+                continue
+            count += 1
+            w = _waterfall_loops(lines)
+            if w:
+                bad[name] = w
+    assert count >= 60
+    assert not bad, bad
+
+
+def test_split_k_loop_keeps_loads_in_flight(lean_asm):
+    kernels = _waits_after_direct_loads(lean_asm["sgemm_lean_split.hip"])
     split = {k: v for k, v in kernels.items() if "sgemm_lean_kernel" in k}
     assert len(split) >= 20, sorted(kernels)
     # the K-remainder prologue and the edge paths may wait once or twice; a
