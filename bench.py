@@ -123,6 +123,7 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
         "single_thread_gflops": one_rate,
         "single_thread_sample": f"rows 0..{one_rows - 1}, {one_spent:.2f} s",
         "cpu_model": cpu_model(),
+        "cpu_simd": cpu_simd(),
         "nproc": os.cpu_count(),
         "parity_on_sample_max_err_over_tol": max_ratio,
         "parity_on_sample_ok": bool(max_ratio <= 1.0),
@@ -135,6 +136,20 @@ def cpu_model():
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
                 return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_simd():
+    """The host CPU's vector extensions that bear on an fp64 loop (from the
+    flags line of /proc/cpuinfo; None where absent)."""
+    wanted = ("sse4_2", "avx", "avx2", "fma", "avx512f", "avx512dq", "avx512vl")
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("flags"):
+                have = set(line.split(":", 1)[1].split())
+                return [f for f in wanted if f in have]
     except OSError:
         pass
     return None
