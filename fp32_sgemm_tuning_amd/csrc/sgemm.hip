@@ -534,8 +534,9 @@ bool prefer_64(int M, int N, long batch = 1) {
 }
 
 // Automatic choice: the lean kernel with 16-byte loads when the operands
-// allow them (the 64x64x64 form splits K below 160 of its tiles), else the
-// lean kernel with 4-byte loads; the tile by prefer_64().  No HIP call.
+// allow them, else the lean kernel with 4-byte loads; the tile by
+// prefer_64(); the 64x64x64 forms split K where choose_splits() or
+// choose_tail_splits() says so.  No HIP call.
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
     const bool small = prefer_64(M, N);

@@ -126,13 +126,13 @@ def _name(v):
 
 
 @pytest.mark.parametrize("shape,expected", [
-    # 128x128 grid below 160 tiles: the 64x64x64 tile (split-capable)
+    # 128x128 grid of at most 256 tiles: the 64x64x64 tile (split-capable)
     ((4, 4, 4), "lean_64x64x64_w4x1_splitk"),
     ((64, 64, 64), "lean_64x64x64_w4x1_splitk"),
     ((1024, 1024, 64), "lean_64x64x64_w4x1_splitk"),
     ((1024, 1024, 1024), "lean_64x64x64_w4x1_splitk"),
     ((1536, 1536, 1536), "lean_64x64x64_w4x1_splitk"),
-    # 128x128 grid of at most 256 tiles: half the two-per-CU slots
+    # (half the two-per-CU slots or fewer)
     ((2048, 2048, 2048), "lean_64x64x64_w4x1_splitk"),
     ((2000, 2000, 500), "lean_64x64x64_w4x1_splitk"),
     # last wave of 128x128 tiles fuller than that of 64x64 tiles less 3%
