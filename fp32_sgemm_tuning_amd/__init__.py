@@ -5,6 +5,8 @@ include/sgemm.h, raw binding in :mod:`.capi`).  This module marshals torch
 tensors into that call: device pointers, leading dimensions and the current
 HIP stream.  PyTorch only supplies device memory and streams.
 """
+import contextlib
+
 from . import capi
 
 __all__ = ["sgemm", "sgemm_op", "sgemm_lowp", "SgemmError", "capi", "variant_names"]
@@ -58,10 +60,9 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(M, N)}")
     lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
     _same_device(A, B, C)
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
-            float(beta), C.data_ptr(), ldc, s.cuda_stream)
-    with torch.cuda.device(A.device):
+    with _device_ctx(A.device):
+        args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                float(beta), C.data_ptr(), ldc, _stream_handle(A.device, stream))
         if variant is None:
             st = capi.sgemm(*args)
         else:
@@ -71,10 +72,30 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None):
     return C
 
 
-def _same_device(*tensors):
-    devs = {t.device for t in tensors}
-    if len(devs) != 1:
-        raise ValueError(f"A, B and C must be on one device, got {sorted(str(d) for d in devs)}")
+def _same_device(A, B, C):
+    if not (A.device == B.device == C.device):
+        raise ValueError(f"A, B and C must be on one device, got {A.device}, {B.device}, {C.device}")
+
+
+def _device_ctx(device):
+    """A context with `device` current; nothing to do when it already is."""
+    import torch
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
+def _stream_handle(device, stream):
+    """The HIP stream handle of `stream` (a torch stream), else of the
+    device's current stream."""
+    if stream is not None:
+        return stream.cuda_stream
+    import torch
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
 
 
 def variant_names():
@@ -128,17 +149,16 @@ def sgemm_op(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False, st
     _same_device(A, B, C)
     if (rc, cc) != (M, N) or (C.dim() == 3 and C.shape[0] != batch):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(batch, M, N) if batched else (M, N)}")
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
     op_a = capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N
     op_b = capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N
-    with torch.cuda.device(A.device):
+    with _device_ctx(A.device):
+        h = _stream_handle(A.device, stream)
         if batched:
             st = capi.sgemm_strided_batched(op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda, sa,
-                                            B.data_ptr(), ldb, sb, float(beta), C.data_ptr(), ldc, sc, batch,
-                                            s.cuda_stream)
+                                            B.data_ptr(), ldb, sb, float(beta), C.data_ptr(), ldc, sc, batch, h)
         else:
             st = capi.sgemm_op(op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
-                               float(beta), C.data_ptr(), ldc, s.cuda_stream)
+                               float(beta), C.data_ptr(), ldc, h)
     if st != capi.SGEMM_STATUS_OK:
         raise SgemmError(st)
     return C
@@ -175,21 +195,21 @@ def sgemm_lowp(A, B, C=None, alpha=1.0, beta=0.0, variant=None, stream=None, tra
     if (rc, cc) != (M, N) or (C.dim() == 3 and C.shape[0] != batch):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(batch, M, N) if batched else (M, N)}")
     _same_device(A, B, C)
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
     op_a = capi.SGEMM_OP_T if trans_a else capi.SGEMM_OP_N
     op_b = capi.SGEMM_OP_T if trans_b else capi.SGEMM_OP_N
-    with torch.cuda.device(A.device):
+    with _device_ctx(A.device):
+        h = _stream_handle(A.device, stream)
         if batched:
             st = capi.sgemm_lowp_strided_batched(codes[A.dtype], op_a, op_b, M, N, K, float(alpha), A.data_ptr(),
                                                  lda, sa, B.data_ptr(), ldb, sb, float(beta), C.data_ptr(), ldc, sc,
-                                                 batch, s.cuda_stream)
+                                                 batch, h)
         elif trans_a or trans_b:
             st = capi.sgemm_lowp_op(codes[A.dtype], op_a, op_b, M, N, K, float(alpha), A.data_ptr(), lda,
-                                    B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, s.cuda_stream,
+                                    B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, h,
                                     capi.SGEMM_VARIANT_AUTO if variant is None else int(variant))
         else:
             args = (codes[A.dtype], M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
-                    float(beta), C.data_ptr(), ldc, s.cuda_stream)
+                    float(beta), C.data_ptr(), ldc, h)
             st = capi.sgemm_lowp(*args) if variant is None else capi.sgemm_lowp_ex(*args, int(variant))
     if st != capi.SGEMM_STATUS_OK:
         raise SgemmError(st)

@@ -327,3 +327,25 @@ def test_last_wave_split(M, N, K, name):
             outs.append(dC.cpu().numpy())
         check_close(outs[0], ref, f"{M}x{N}x{K} {name} beta={beta}")
         assert np.array_equal(outs[0], outs[1])
+
+
+def test_binding_uses_the_current_stream():
+    """The binding passes the current stream's handle, also inside a
+    torch.cuda.stream() block, and a given stream's handle otherwise."""
+    torch = torch_cuda()
+    import fp32_sgemm_tuning_amd as pkg
+    dev = torch.device("cuda", torch.cuda.current_device())
+    assert pkg._stream_handle(dev, None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert pkg._stream_handle(dev, None) == side.cuda_stream
+    assert pkg._stream_handle(dev, side) == side.cuda_stream
+    # a product enqueued on the side stream is ordered on it
+    A, B, _ = make_problem(300, 200, 100, 5)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    dC = torch.full((300, 200), float("nan"), device="cuda")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sgemm(dA, dB, dC)
+    side.synchronize()
+    check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B), "side stream")
