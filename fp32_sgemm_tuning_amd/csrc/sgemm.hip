@@ -63,7 +63,8 @@ int record_hip_error(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Process-wide tuning knobs read once from the environment (tile raster
-// group height and the XCD remap), for sweeps; defaults otherwise.
+// group height, the XCD remap, a forced split-K factor), for sweeps;
+// defaults otherwise.
 struct Knobs {
     int group_m = 8;
     int xcd_remap = 1;
@@ -184,9 +185,9 @@ typedef void (*Launcher)(const Args &, hipStream_t);
 // Split-K (lean kernels).  A tile grid with fewer blocks than about two per
 // compute unit leaves CUs idle while each busy CU walks all of K; splitting
 // K over S blocks per tile multiplies the parallelism by S at the price of
-// writing and re-reading S partial tiles.  Every split-capable lean tile has
-// four waves and 64 KiB of LDS (two blocks per CU), so the model below
-// counts blocks alike for all of them.
+// writing and re-reading S partial tiles.  The model below counts two
+// resident blocks per CU, as for the 64x64x64 and 128x128x32 tiles (four
+// waves, 64 KiB of LDS); the automatic choice splits only the 64x64x64 ones.
 constexpr long kNumCUs = 256;                            // MI355X
 constexpr long kTailSlots = 2 * kNumCUs;                 // resident lean blocks: two per CU
 constexpr long kSplitMaxTiles = 4096;                    // tiles with counters
