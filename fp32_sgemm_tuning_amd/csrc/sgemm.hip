@@ -63,13 +63,18 @@ int record_hip_error(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Process-wide tuning knobs read once from the environment (tile raster
-// group height, the XCD remap, a forced split-K factor), for sweeps;
-// defaults otherwise.
+// group height, the XCD remap, a forced split-K factor, the copy of
+// unaligned transposed operands), for sweeps; defaults otherwise.
 struct Knobs {
     int group_m = 8;
     int xcd_remap = 1;
     int splitk = 0;         // 0: automatic split-K factor; >= 1: forced
+    int pack = 0;           // unaligned transposed operands: 0 automatic, 1 always copy, -1 never
     Knobs() {
+        if (const char *s = getenv("SGEMM_PACK")) {
+            int v = atoi(s);
+            if (v >= -1 && v <= 1) pack = v;
+        }
         if (const char *s = getenv("SGEMM_GROUP_M")) {
             int v = atoi(s);
             if (v >= 1 && v <= 1024) group_m = v;
@@ -541,7 +546,9 @@ bool prefer_64(int M, int N, long batch = 1) {
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
     const bool small = prefer_64(M, N);
-    if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc)) return small ? kAny64 : kAny;
+    // (the 16-byte kernels also need K and N multiples of 4: whole chunks
+    // at the edges; aligned operands with other K or N take the 4-byte ones)
+    if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc) || K % 4 || N % 4) return small ? kAny64 : kAny;
     return small ? kVec64 : kVec;
 }
 
@@ -614,6 +621,121 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 // for untransposed aligned operands, else 4-byte loads) on the tile
 // prefer_64() picks for batch x tiles, without split-K; shapes it does not
 // take go to the plain kernel.
+// ---------------------------------------------------------------------------
+// Unaligned transposed operands.  A transposed operand without 16-byte rows
+// takes the lean kernel's 4-byte gather, whose load instructions each touch
+// up to 32 rows of the stored matrix: 45-71 TFLOP/s on 3001x4999x2048
+// against about 125 untransposed.  (With 16-byte loads for the whole
+// product, transposed operands run at the untransposed rate and stay as
+// they are.)  For large enough single problems the
+// operand is instead transposed into a row-major copy (leading dimension
+// rounded up to a multiple of 4, in a buffer of the library's) and the
+// untransposed path runs on it.
+
+// dst[c][r] = src[r][c] for r < rows, c < cols: 32x32 tiles through LDS (a
+// padded row keeps the column reads conflict-free), both sides coalesced.
+__global__ void __launch_bounds__(256) transpose_kernel(const float *__restrict__ src, long ld_src, int rows,
+                                                        int cols, float *__restrict__ dst, long ld_dst) {
+    __shared__ float t[32][33];
+    const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) t[i][tx] = src[(long)r * ld_src + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) dst[(long)c * ld_dst + r] = t[tx][i];
+    }
+}
+
+// One copy buffer per (device, stream), grown on demand (the old one freed
+// once the stream has drained) and kept until the process ends.
+int get_copy_buffer(hipStream_t stream, size_t bytes, float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto &slot = cache[std::make_pair(dev, stream)];
+    if (slot.first != nullptr && slot.second >= bytes) {
+        *out = static_cast<float *>(slot.first);
+        return SGEMM_STATUS_OK;
+    }
+    if (slot.first != nullptr) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return record_hip_error(e, "hipStreamSynchronize (copy buffer)");
+        (void)hipFree(slot.first);
+        slot = std::make_pair(nullptr, (size_t)0);
+    }
+    void *mem = nullptr;
+    e = hipMalloc(&mem, bytes);
+    if (e != hipSuccess) return record_hip_error(e, "hipMalloc (copy buffer)");
+    slot = std::make_pair(mem, bytes);
+    *out = static_cast<float *>(mem);
+    return SGEMM_STATUS_OK;
+}
+
+// Whether a single transposed problem copies its unaligned transposed
+// operands: not under graph capture (no allocation there), grid dimensions
+// within the launch limits, and the copies' traffic (read and written once,
+// at about 3 TB/s) taking less time than the product would at 120 TFLOP/s.
+// Measured: the gather runs at 10-110 TFLOP/s (512^3 to 4095^3, 47-69 with
+// both operands transposed), the copies and the untransposed kernel at
+// 17-143, ahead at every size where this rule copies.
+// SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
+bool copy_plan(int M, int N, int K, bool copy_a, bool copy_b, void *stream) {
+    if (knobs().pack < 0 || (!copy_a && !copy_b)) return false;
+    if (ceil_div(K, 32) > 65535 || ceil_div(copy_a ? M : N, 32) > 65535 || ceil_div(N, 32) > 65535) return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+        cap != hipStreamCaptureStatusNone)
+        return false;
+    if (knobs().pack > 0) return true;
+    const double bytes = 8.0 * ((copy_a ? (double)M * K : 0.0) + (copy_b ? (double)K * N : 0.0));
+    return bytes / 3e12 < 2.0 * M * (double)N * K / 120e12;
+}
+
+int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
+                const float *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch,
+                void *stream);
+
+// The product with the marked transposed operands replaced by row-major
+// copies (A as M x K, B as K x N); an operand not copied keeps its form.
+int run_copied(int op_a, int op_b, bool copy_a, bool copy_b, int M, int N, int K, float alpha, const float *A,
+               int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const long lda2 = (K + 3) & ~3L, ldb2 = (N + 3) & ~3L;
+    const size_t a_floats = copy_a ? (((size_t)M * lda2 + 63) & ~(size_t)63) : 0;
+    const size_t b_floats = copy_b ? (size_t)K * ldb2 : 0;
+    float *buf = nullptr;
+    const int st = get_copy_buffer(s, (a_floats + b_floats) * sizeof(float), &buf);
+    if (st != SGEMM_STATUS_OK) return st;
+    (void)hipGetLastError();
+    if (copy_a) {   // stored K x M (leading dimension lda) -> M x K
+        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(M, 32), (unsigned)ceil_div(K, 32)), dim3(256),
+                           0, s, A, (long)lda, K, M, buf, lda2);
+        A = buf;
+        lda = (int)lda2;
+    }
+    if (copy_b) {   // stored N x K (leading dimension ldb) -> K x N
+        float *Bc = buf + a_floats;
+        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 32), (unsigned)ceil_div(N, 32)), dim3(256),
+                           0, s, B, (long)ldb, N, K, Bc, ldb2);
+        B = Bc;
+        ldb = (int)ldb2;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip_error(e, "kernel launch (transpose)");
+    // (the copies are row-major and aligned, so this call copies nothing)
+    return run_general(copy_a ? SGEMM_OP_N : op_a, copy_b ? SGEMM_OP_N : op_b, M, N, K, alpha, A, lda, 0, B, ldb, 0,
+                       beta, C, ldc, 0, 1, stream);
+}
+
 int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
                 const float *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch,
                 void *stream) {
@@ -630,6 +752,15 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
     if (!ta && !tb && batch == 1)
         return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
+    if (batch == 1 && K > 0) {
+        // without 16-byte loads for the whole product (an operand or C
+        // unaligned, or an edge not in whole chunks) every transposed operand
+        // would be gathered
+        const bool vec1 = vec_ok(K, A, lda, B, ldb, beta, C, ldc) && (ta ? M : K) % 4 == 0 && (tb ? K : N) % 4 == 0;
+        const bool copy_a = ta && !vec1, copy_b = tb && !vec1;
+        if (copy_plan(M, N, K, copy_a, copy_b, stream))
+            return run_copied(op_a, op_b, copy_a, copy_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    }
 
     Args a;
     a.A = A;

@@ -39,7 +39,9 @@
  * partial tiles of a tile are added in a fixed order, so split-K results are
  * deterministic too.  On a stream under graph capture K is never split (no
  * allocation happens during capture).  An allocation failure returns
- * SGEMM_STATUS_HIP_ERROR before anything is enqueued.
+ * SGEMM_STATUS_HIP_ERROR before anything is enqueued.  sgemm_op() and
+ * sgemm_cm() keep one more per-stream buffer, for copies of unaligned
+ * transposed operands (see sgemm_op).
  *
  * Errors.  Arguments are checked before anything is enqueued, so a call that
  * returns an error has written nothing.  M == 0 or N == 0 returns
@@ -148,9 +150,19 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
  * dot-product definition as sgemm() with the operands read through the
  * transpose ("Matmul I: tiling and shared memory", section 1); the pages
  * stop at packed untransposed operands and name the column-major BLAS
- * convention only in passing.  sgemm_op(N, N, ...) is sgemm().  Transposed
- * operands are read with 4-byte loads (any alignment).  Returns
- * SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for another op code.
+ * convention only in passing.  sgemm_op(N, N, ...) is sgemm().  A
+ * transposed operand with 16-byte aligned rows (base, leading dimension and
+ * its contiguous extent multiples of 4 floats) is read in its stored
+ * orientation with 16-byte loads.  One without is, for a problem large
+ * enough that the copy takes less time than the product, first transposed
+ * into a row-major copy in a buffer the library allocates with hipMalloc per
+ * (device, stream) on first need, grows (after draining the stream) and
+ * keeps until the process ends, and the product then runs as sgemm() on
+ * the copy; otherwise, and always under graph capture, it is gathered with
+ * 4-byte loads.  Environment variable SGEMM_PACK = 1 / -1 forces the copy
+ * on / off, for sweeps.  Returns SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for
+ * another op code; SGEMM_STATUS_HIP_ERROR if the buffer cannot be allocated
+ * (nothing enqueued).
  */
 int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha,
              const float *A, int lda,

@@ -202,6 +202,11 @@ def test_variant_selection_by_alignment():
     assert _name(sel(3072, 3072, 3071, AL, 3071, AL, 3072, 0.0, AL, 3072)) == "lean_dw_64x64x64_w4x1_splitk"
     # the ragged workload's leading dimensions (2047, 4999) are not multiples of 4
     assert not _needs_vec(sel(3001, 4999, 2047, AL, 2047, AL, 4999, -0.5, AL, 4999))
+    # aligned, padded operands whose K or N is not a multiple of 4: the
+    # 16-byte kernels would need whole chunks at the edge
+    assert _name(sel(1024, 1024, 1023, AL, 1024, AL, 1024, 0.0, AL, 1024)) == "lean_dw_64x64x64_w4x1_splitk"
+    assert _name(sel(4096, 4094, 4096, AL, 4096, AL, 4096, 0.0, AL, 4096)) == "lean_dw_128x128x32_w2x2"
+    assert _name(sel(1024, 1024, 1024, AL, 1024, AL, 1024, 0.0, AL, 1024)) == "lean_64x64x64_w4x1_splitk"
     assert sel(-1, 4, 4, AL, 4, AL, 4, 0.0, AL, 4) == capi.SGEMM_STATUS_INVALID_DIM
 
 

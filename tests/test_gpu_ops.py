@@ -194,3 +194,32 @@ def test_transposed_aligned_small(ops, shape):
     assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
     torch.cuda.synchronize()
     check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.0, beta=0.25), f"aligned op {ops} {shape}")
+
+
+@pytest.mark.parametrize("ops", OPS[1:], ids=OP_IDS[1:])
+@pytest.mark.parametrize("shape,pads", [((777, 333, 1501), (0, 0, 1)), ((1030, 1022, 515), (4, 4, 3)),
+                                        ((640, 700, 900), (1, 3, 0))],
+                         ids=["C-unaligned", "C-unaligned-padded", "operands-unaligned"])
+def test_transposed_operands_copied(ops, shape, pads):
+    """Problems without 16-byte loads for the whole product that are large
+    enough to copy their transposed operands into row-major buffers first:
+    parity with the oracle for beta = 0 (NaN C) and beta != 0, twice in a row
+    (the second call reuses the copy buffer)."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K = shape
+    pa, pb, pc = pads
+    A, B, Cin = make_problem(M, N, K, seed=M + N + K + op_a + 2 * op_b, dist="normal", with_c=True)
+    dA, lda = _stored(A, op_a == T_, pa, torch)
+    dB, ldb = _stored(B, op_b == T_, pb, torch)
+    for beta in (0.0, 0.75):
+        for _ in range(2):
+            dC, ldc = _stored(Cin, False, pc, torch, offset=1)
+            if beta == 0.0:
+                dC.fill_(float("nan"))
+            st = capi.sgemm_op(op_a, op_b, M, N, K, 1.5, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                               dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+            assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+            torch.cuda.synchronize()
+            check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.5, beta=beta),
+                        f"copied op {ops} {shape} beta={beta}")

@@ -349,3 +349,20 @@ def test_binding_uses_the_current_stream():
         sgemm(dA, dB, dC)
     side.synchronize()
     check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B), "side stream")
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [(1024, 1024, 1023, 1024, 1024, 1024), (2048, 2046, 2048, 2048, 2048, 2048),
+                                              (517, 301, 1001, 1004, 304, 308)])
+def test_aligned_rows_ragged_k_or_n(M, N, K, lda, ldb, ldc):
+    """Aligned, padded operands whose K or N is not a multiple of 4 (the
+    4-byte kernels take them): parity with the oracle, NaN in the padding."""
+    torch = torch_cuda()
+    A, B, Cin = make_problem(M, N, K, seed=M + N + K, dist="normal", with_c=True)
+    v = capi.sgemm_select_variant(M, N, K, 256, lda, 512, ldb, 0.0, 1024, ldc)
+    assert capi.sgemm_variant_info(v)[4] == 0, capi.sgemm_variant_name(v)
+    dA, _ = padded_device(A, lda, torch)
+    dB, _ = padded_device(B, ldb, torch)
+    dC, _ = padded_device(Cin, ldc, torch)
+    sgemm(dA, dB, dC, alpha=1.25, beta=-0.5)
+    torch.cuda.synchronize()
+    check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=-0.5), f"{M}x{N}x{K} ld {lda},{ldb},{ldc}")
