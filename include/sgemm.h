@@ -159,8 +159,10 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
  * (device, stream) on first need, grows (after draining the stream) and
  * keeps until the process ends, and the product then runs as sgemm() on
  * the copy; otherwise, and always under graph capture, it is gathered with
- * 4-byte loads.  Environment variable SGEMM_PACK = 1 / -1 forces the copy
- * on / off, for sweeps.  Returns SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for
+ * 4-byte loads.  The copy and the product are separate launches sharing
+ * the stream's buffer, so calls on one stream must come from one host thread
+ * at a time (calls on different streams are independent).  Environment
+ * variable SGEMM_PACK = 1 / -1 forces the copy on / off, for sweeps.  Returns SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for
  * another op code; SGEMM_STATUS_HIP_ERROR if the buffer cannot be allocated
  * (nothing enqueued).
  */
