@@ -912,9 +912,92 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
     return best;
 }
 
+// 16-bit operands the direct-to-LDS kernels cannot take (rows not 16-byte
+// aligned, or K or N not a multiple of 8) otherwise run on the plain kernel
+// at 58-65 TFLOP/s against 1000-1300 for the fast kernels (3000x5000x2047,
+// 4096^3 with odd leading dimensions).  A single untransposed problem instead
+// copies A into an M x K8 and B into a K8 x N8 buffer (K8, N8: K and N
+// rounded up to multiples of 8; padding zero, so the sums are unchanged; B's
+// padding columns only reach accumulators that are never stored) and runs
+// the fast kernels on the copies with K8 and the true N.
+
+// dst (rows_out x cols_out 16-bit values, leading dimension cols_out, a
+// multiple of 8) = src (rows x cols, leading dimension ld_src) padded with
+// zeros; one 16-byte chunk of dst per thread per step of a grid-stride loop.
+__global__ void __launch_bounds__(256) pack16_kernel(const unsigned short *__restrict__ src, long ld_src, int rows,
+                                                     int cols, unsigned short *__restrict__ dst, int rows_out,
+                                                     int cols_out) {
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    const long q8 = cols_out / 8;
+    const long n = (long)rows_out * q8;
+    for (long q = blockIdx.x * 256L + threadIdx.x; q < n; q += (long)gridDim.x * 256) {
+        const long r = q / q8;
+        const int c = (int)(q - r * q8) * 8;
+        u16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (r < rows && c + e < cols) ? src[r * ld_src + c + e] : (unsigned short)0;
+        *reinterpret_cast<u16x8 *>(dst + r * (long)cols_out + c) = v;
+    }
+}
+
+void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, int rows_out, int cols_out,
+                   hipStream_t s) {
+    const long n = (long)rows_out * (cols_out / 8);
+    const long blocks = std::min(ceil_div(n, 256), 4096L);
+    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const unsigned short *>(src), ld_src, rows, cols,
+                       static_cast<unsigned short *>(dst), rows_out, cols_out);
+}
+
+// Whether an untransposed single 16-bit problem that no fast kernel takes
+// is copied: K of at least one K tile, not under graph capture, and the
+// copies' traffic (at about 3 TB/s) plus about 6 us for the two extra
+// launches taking less time than the plain kernel's product (at 60
+// TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
+bool lowp_copy_plan(int M, int N, int K, void *stream) {
+    if (knobs().pack < 0 || K < 64) return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+        cap != hipStreamCaptureStatusNone)
+        return false;
+    const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
+    // (the copies' rows fit the smallest fast tile's 31-bit buffer ranges)
+    if (!lowp_fast_ok(kLowpVariants[1], M, (int)N8, (int)K8, nullptr, (int)K8, nullptr, (int)N8)) return false;
+    if (knobs().pack > 0) return true;
+    const double bytes = 4.0 * ((double)M * K8 + (double)K8 * N8);
+    return bytes / 3e12 + 6e-6 < 2.0 * M * (double)N * K / 60e12;
+}
+
 int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
              const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant,
-             long long sA = 0, long long sB = 0, long long sC = 0, int batch = 1) {
+             long long sA, long long sB, long long sC, int batch, bool padded_b);
+
+// The untransposed 16-bit product on zero-padded copies of A and B.
+int run_lowp_copied(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+                    float beta, float *C, int ldc, void *stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int K8 = (K + 7) & ~7, N8 = (N + 7) & ~7;
+    const size_t a_elems = ((size_t)M * K8 + 127) & ~(size_t)127, b_elems = (size_t)K8 * N8;
+    float *buf = nullptr;
+    const int st = get_copy_buffer(s, (a_elems + b_elems) * 2, &buf);
+    if (st != SGEMM_STATUS_OK) return st;
+    unsigned short *Ap = reinterpret_cast<unsigned short *>(buf), *Bp = Ap + a_elems;
+    (void)hipGetLastError();
+    launch_pack16(A, lda, M, K, Ap, M, K8, s);
+    launch_pack16(B, ldb, K, N, Bp, K8, N8, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return record_hip_error(e, "kernel launch (copy)");
+    // the fast kernels on the copies: chosen for the padded width, run on the
+    // true one (their loads of B's last chunk read the zero padding)
+    const int v = lowp_auto(M, N8, K8, Ap, K8, Bp, N8);
+    if (v == 0) return SGEMM_STATUS_UNSUPPORTED;
+    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v, 0, 0, 0,
+                    1, true);
+}
+
+int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
+             const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant,
+             long long sA = 0, long long sB = 0, long long sC = 0, int batch = 1, bool padded_b = false) {
     if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_STATUS_INVALID_DTYPE;
     if ((op_a != SGEMM_OP_N && op_a != SGEMM_OP_T) || (op_b != SGEMM_OP_N && op_b != SGEMM_OP_T))
         return SGEMM_STATUS_INVALID_OP;
@@ -926,15 +1009,22 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (batch < 0 || batch > kMaxBatch) return SGEMM_STATUS_INVALID_DIM;
     if (batch > 1 && (sA < 0 || sB < 0 || (M > 0 && N > 0 && sC < (long long)(M - 1) * ldc + N)))
         return SGEMM_STATUS_INVALID_DIM;
+    // (padded_b: A and B are the library's zero-padded copies, whose
+    // untransposed B may have N not a multiple of 8 but whole chunks)
     if (variant < SGEMM_VARIANT_AUTO || variant >= kNumLowpVariants) return SGEMM_STATUS_INVALID_VARIANT;
     if (M == 0 || N == 0 || batch == 0) return SGEMM_STATUS_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
     const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
     if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
-    if (variant == SGEMM_VARIANT_AUTO) variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch);
+    if (variant == SGEMM_VARIANT_AUTO) {
+        variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch);
+        if (variant == 0 && !ta && !tb && batch == 1 && lowp_copy_plan(M, N, K, stream))
+            return run_lowp_copied(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    }
     const LowpVariant &v = kLowpVariants[variant];
     if (variant > 0 && ((ta || tb) && !lowp_takes_ops(variant))) return SGEMM_STATUS_UNSUPPORTED;
-    if (variant > 0 && !lowp_fast_ok(v, M, N, K, A, lda, B, ldb, ta, tb)) return SGEMM_STATUS_UNSUPPORTED;
+    if (variant > 0 && !lowp_fast_ok(v, M, padded_b ? (N + 7) & ~7 : N, K, A, lda, B, ldb, ta, tb))
+        return SGEMM_STATUS_UNSUPPORTED;
     Args a;
     a.A = Af;
     a.B = Bf;

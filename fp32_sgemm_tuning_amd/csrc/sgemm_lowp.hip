@@ -205,7 +205,9 @@ sgemm_lowp_kernel(Args p) {
     const bool remainder_first = tail && t_first == 0;
     // Per-tile descriptors: the block's part of one K tile of each stored
     // operand (rows up to M or N, BK deep), based at that tile.
-    const long rowsA = min(BM, p.M - m0), colsB = min(BN, p.N - n0);
+    // (untransposed B is read in whole 8-element chunks: its range covers N
+    // rounded up to a chunk, which the library's padded copies hold)
+    const long rowsA = min(BM, p.M - m0), colsB = TB ? min(BN, p.N - n0) : min(BN, (p.N - n0 + 7) & ~7);
     const int rangeA = (int)(TA ? 2L * ((long)(BK - 1) * p.lda + rowsA) : 2L * ((rowsA - 1) * p.lda + BK));
     const int rangeB = (int)(TB ? 2L * ((colsB - 1) * p.ldb + BK) : 2L * ((long)(BK - 1) * p.ldb + colsB));
     const char *cornerA = TA ? Ab + 2L * m0 : Ab + 2L * m0 * p.lda;

@@ -218,8 +218,14 @@ int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alph
  * Fast path: A and B 16-byte aligned, lda, ldb, N and K multiples of 8 and
  * K >= 32.  It runs the matrix instructions v_mfma_f32_16x16x32_bf16 / _f16
  * on 128x128, 256x128 or 256x256 block tiles, picked from the shape, with
- * 16-byte C access when C is 16-byte aligned and ldc a multiple of 4.  Any
- * other shape runs a plain kernel that widens each element on load.  Small
+ * 16-byte C access when C is 16-byte aligned and ldc a multiple of 4.  Other
+ * operands (unaligned rows, K or N not multiples of 8) of a problem with
+ * K >= 64, large enough that copying them takes less time than the plain
+ * kernel would, are first copied into zero-padded aligned buffers (K and N
+ * rounded up to multiples of 8; the library's per-stream copy buffer, as
+ * for sgemm_op) and run on the fast path; the rest runs a plain kernel that
+ * widens each element on load.  Calls on one stream must then come from one
+ * host thread at a time.  SGEMM_PACK = 1 / -1 forces the copy on / off.  Small
  * tile grids split K and use the workspace described above (same rules:
  * allocated on first use per (device, stream), no split under graph
  * capture, deterministic).  Argument checks, layout rules and status codes
@@ -277,7 +283,9 @@ int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int 
                                int batch, void *stream);
 
 /* The variant sgemm_lowp() would run for these arguments (no launch; the
- * pointers are only inspected for alignment), or SGEMM_STATUS_INVALID_DIM. */
+ * pointers are only inspected for alignment), or SGEMM_STATUS_INVALID_DIM.
+ * 0 (the plain kernel) also where sgemm_lowp() copies the operands and runs
+ * a fast kernel on the copies. */
 int sgemm_lowp_select_variant(int M, int N, int K,
                               const void *A, int lda,
                               const void *B, int ldb);

@@ -327,3 +327,28 @@ def test_lowp_strided_batched(dtype, trans_a, trans_b, shared_b):
         C = dC.cpu().numpy()
         for z, (a, b, c) in enumerate(probs):
             check_close(C[z], oracle.sgemm_ref(a, b, c, alpha=0.5, beta=2.0), f"problem {z}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,lds,off", [((1001, 999, 1003), (1003, 999), 0), ((640, 1030, 700), (703, 1037), 1),
+                                           ((520, 264, 2048), (2049, 264), 0)],
+                         ids=["K-and-N-odd", "misaligned", "lda-odd"])
+def test_lowp_copied_operands(dtype, shape, lds, off):
+    """Operands the fast kernels cannot take, in problems large enough to be
+    copied into zero-padded aligned buffers first: parity with the oracle
+    for beta = 0 (NaN C) and beta != 0, NaN in the callers' padding, twice
+    in a row (the second call reuses the copy buffer)."""
+    torch = torch_cuda()
+    M, N, K = shape
+    lda, ldb = lds
+    A, B, Cin = make_problem_16bit(M, N, K, seed=M + N + K, dtype=dtype, with_c=True)
+    dA, _ = _dev16(A, dtype, torch, ld=lda, offset=off)
+    dB, _ = _dev16(B, dtype, torch, ld=ldb, offset=off)
+    print(f"[lowp copy] {dtype} {M}x{N}x{K} lda={lda} ldb={ldb} offset={off}", flush=True)
+    for beta in (0.0, -0.5):
+        ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=1.25, beta=beta)
+        for _ in range(2):
+            dC = torch.from_numpy(Cin).to("cuda") if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+            sgemm_lowp(dA, dB, dC, alpha=1.25, beta=beta)
+            torch.cuda.synchronize()
+            check_close(dC.cpu().numpy(), ref, f"{dtype} {shape} beta={beta}")
