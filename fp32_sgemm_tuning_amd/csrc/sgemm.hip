@@ -940,6 +940,28 @@ __global__ void __launch_bounds__(256) pack16_kernel(const unsigned short *__res
     }
 }
 
+// dst[r][c] (rows_out x cols_out 16-bit values, leading dimension cols_out)
+// = src[c][r] (src: cols x rows, leading dimension ld_src) for r < rows and
+// c < cols, else zero: 32x32 tiles through LDS, both sides coalesced.
+__global__ void __launch_bounds__(256) transpose16_kernel(const unsigned short *__restrict__ src, long ld_src,
+                                                          int rows, int cols, unsigned short *__restrict__ dst,
+                                                          int rows_out, int cols_out) {
+    __shared__ unsigned short t[32][33];
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int c = c0 + i, r = r0 + tx;           // source row c, column r
+        t[i][tx] = (c < cols && r < rows) ? src[(long)c * ld_src + r] : (unsigned short)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = ty; i < 32; i += 8) {
+        const int r = r0 + i, c = c0 + tx;
+        if (r < rows_out && c < cols_out) dst[(long)r * cols_out + c] = t[tx][i];
+    }
+}
+
 void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, int rows_out, int cols_out,
                    hipStream_t s) {
     const long n = (long)rows_out * (cols_out / 8);
@@ -961,6 +983,7 @@ bool lowp_copy_plan(int M, int N, int K, void *stream) {
         cap != hipStreamCaptureStatusNone)
         return false;
     const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
+    if (ceil_div(M, 32) > 65535 || ceil_div(K8, 32) > 65535) return false;   // transpose grids
     // (the copies' rows fit the smallest fast tile's 31-bit buffer ranges)
     if (!lowp_fast_ok(kLowpVariants[1], M, (int)N8, (int)K8, nullptr, (int)K8, nullptr, (int)N8)) return false;
     if (knobs().pack > 0) return true;
@@ -972,9 +995,10 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
              const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant,
              long long sA, long long sB, long long sC, int batch, bool padded_b);
 
-// The untransposed 16-bit product on zero-padded copies of A and B.
-int run_lowp_copied(int dtype, int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
-                    float beta, float *C, int ldc, void *stream) {
+// The 16-bit product on zero-padded row-major copies of op(A) and op(B)
+// (transposed operands transposed on the way).
+int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
+                    const void *B, int ldb, float beta, float *C, int ldc, void *stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int K8 = (K + 7) & ~7, N8 = (N + 7) & ~7;
     const size_t a_elems = ((size_t)M * K8 + 127) & ~(size_t)127, b_elems = (size_t)K8 * N8;
@@ -983,8 +1007,16 @@ int run_lowp_copied(int dtype, int M, int N, int K, float alpha, const void *A, 
     if (st != SGEMM_STATUS_OK) return st;
     unsigned short *Ap = reinterpret_cast<unsigned short *>(buf), *Bp = Ap + a_elems;
     (void)hipGetLastError();
-    launch_pack16(A, lda, M, K, Ap, M, K8, s);
-    launch_pack16(B, ldb, K, N, Bp, K8, N8, s);
+    if (ta)     // stored K x M
+        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32)), dim3(256),
+                           0, s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8);
+    else
+        launch_pack16(A, lda, M, K, Ap, M, K8, s);
+    if (tb)     // stored N x K
+        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32)), dim3(256),
+                           0, s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8);
+    else
+        launch_pack16(B, ldb, K, N, Bp, K8, N8, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch (copy)");
     // the fast kernels on the copies: chosen for the padded width, run on the
@@ -1018,8 +1050,8 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
     if (variant == SGEMM_VARIANT_AUTO) {
         variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch);
-        if (variant == 0 && !ta && !tb && batch == 1 && lowp_copy_plan(M, N, K, stream))
-            return run_lowp_copied(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        if (variant == 0 && batch == 1 && lowp_copy_plan(M, N, K, stream))
+            return run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
     const LowpVariant &v = kLowpVariants[variant];
     if (variant > 0 && ((ta || tb) && !lowp_takes_ops(variant))) return SGEMM_STATUS_UNSUPPORTED;

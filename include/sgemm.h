@@ -259,7 +259,11 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
  * automatic choice); transposed operands run on the alternating-schedule
  * variants or the plain kernel, with each operand kept in LDS in its stored
  * orientation (16-byte chunks along its contiguous extent, which must be a
- * multiple of 8 elements for the fast path).  No split-K.  Returns
+ * multiple of 8 elements for the fast path).  No split-K on stored
+ * transposed operands.  With SGEMM_VARIANT_AUTO, operands the fast path
+ * cannot take are copied as in sgemm_lowp(), transposed on the way into
+ * zero-padded row-major buffers, and the product runs untransposed on the
+ * copies (where it may split K, deterministically).  Returns
  * SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for another op code.
  */
 int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,

@@ -352,3 +352,26 @@ def test_lowp_copied_operands(dtype, shape, lds, off):
             sgemm_lowp(dA, dB, dC, alpha=1.25, beta=beta)
             torch.cuda.synchronize()
             check_close(dC.cpu().numpy(), ref, f"{dtype} {shape} beta={beta}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ops", [(True, False), (False, True), (True, True)], ids=["TN", "NT", "TT"])
+def test_lowp_copied_transposed_operands(dtype, ops):
+    """Transposed 16-bit operands the fast kernels cannot take (odd leading
+    dimensions, K and N not multiples of 8), copied into zero-padded
+    row-major buffers: parity with the oracle, NaN in the callers' padding."""
+    torch = torch_cuda()
+    ta, tb = ops
+    M, N, K = 901, 1003, 777
+    A, B, Cin = make_problem_16bit(M, N, K, seed=M + N + K + 2 * ta + tb, dtype=dtype, with_c=True)
+    sA = np.ascontiguousarray(A.T) if ta else A
+    sB = np.ascontiguousarray(B.T) if tb else B
+    dA, _ = _dev16(sA, dtype, torch, ld=sA.shape[1] + 3)
+    dB, _ = _dev16(sB, dtype, torch, ld=sB.shape[1] + 5)
+    print(f"[lowp copy op] {dtype} TA={ta} TB={tb}", flush=True)
+    for beta in (0.0, 1.5):
+        dC = torch.from_numpy(Cin).to("cuda") if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+        sgemm_lowp(dA, dB, dC, alpha=0.5, beta=beta, trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=0.5, beta=beta),
+                    f"{dtype} op TA={ta} TB={tb} beta={beta}")
