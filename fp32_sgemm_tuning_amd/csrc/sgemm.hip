@@ -971,11 +971,11 @@ void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, 
                        static_cast<unsigned short *>(dst), rows_out, cols_out);
 }
 
-// Whether an untransposed single 16-bit problem that no fast kernel takes
-// is copied: K of at least one K tile, not under graph capture, and the
-// copies' traffic (at about 3 TB/s) plus about 6 us for the two extra
-// launches taking less time than the plain kernel's product (at 60
-// TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
+// Whether a single 16-bit problem that no fast kernel takes (operands
+// transposed or not) is copied: K of at least one K tile, not under graph
+// capture, and the copies' traffic (at about 3 TB/s) plus about 6 us for
+// the two extra launches taking less time than the plain kernel's product
+// (at 60 TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
 bool lowp_copy_plan(int M, int N, int K, void *stream) {
     if (knobs().pack < 0 || K < 64) return false;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
