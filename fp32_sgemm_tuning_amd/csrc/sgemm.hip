@@ -915,11 +915,12 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
 // 16-bit operands the direct-to-LDS kernels cannot take (rows not 16-byte
 // aligned, or K or N not a multiple of 8) otherwise run on the plain kernel
 // at 58-65 TFLOP/s against 1000-1300 for the fast kernels (3000x5000x2047,
-// 4096^3 with odd leading dimensions).  A single untransposed problem instead
-// copies A into an M x K8 and B into a K8 x N8 buffer (K8, N8: K and N
-// rounded up to multiples of 8; padding zero, so the sums are unchanged; B's
-// padding columns only reach accumulators that are never stored) and runs
-// the fast kernels on the copies with K8 and the true N.
+// 4096^3 with odd leading dimensions).  A single problem instead copies
+// op(A) into an M x K8 and op(B) into a K8 x N8 row-major buffer (stored
+// transposed operands are transposed on the way; K8, N8: K and N rounded up
+// to multiples of 8; padding zero, so the sums are unchanged; B's padding
+// columns only reach accumulators that are never stored) and runs the fast
+// kernels on the copies with K8 and the true N.
 
 // dst (rows_out x cols_out 16-bit values, leading dimension cols_out, a
 // multiple of 8) = src (rows x cols, leading dimension ld_src) padded with
