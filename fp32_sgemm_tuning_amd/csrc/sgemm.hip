@@ -627,18 +627,22 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 // up to 32 rows of the stored matrix: 45-71 TFLOP/s on 3001x4999x2048
 // against about 125 untransposed.  (With 16-byte loads for the whole
 // product, transposed operands run at the untransposed rate and stay as
-// they are.)  For large enough single problems the
-// operand is instead transposed into a row-major copy (leading dimension
-// rounded up to a multiple of 4, in a buffer of the library's) and the
-// untransposed path runs on it.
+// they are.)  For large enough problems, single or batched, the operand is
+// instead transposed into a row-major copy (leading dimension rounded up to
+// a multiple of 4, in a buffer of the library's) and the untransposed path
+// runs on it.
 
 // dst[c][r] = src[r][c] for r < rows, c < cols: 32x32 tiles through LDS (a
-// padded row keeps the column reads conflict-free), both sides coalesced.
+// padded row keeps the column reads conflict-free), both sides coalesced;
+// problem z of a batch at src + z*src_stride and dst + z*dst_stride.
 __global__ void __launch_bounds__(256) transpose_kernel(const float *__restrict__ src, long ld_src, int rows,
-                                                        int cols, float *__restrict__ dst, long ld_dst) {
+                                                        int cols, float *__restrict__ dst, long ld_dst,
+                                                        long src_stride, long dst_stride) {
     __shared__ float t[32][33];
     const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    src += blockIdx.z * src_stride;
+    dst += blockIdx.z * dst_stride;
 #pragma unroll
     for (int i = ty; i < 32; i += 8) {
         const int r = r0 + i, c = c0 + tx;
@@ -680,24 +684,32 @@ int get_copy_buffer(hipStream_t stream, size_t bytes, float **out) {
     return SGEMM_STATUS_OK;
 }
 
-// Whether a single transposed problem copies its unaligned transposed
-// operands: not under graph capture (no allocation there), grid dimensions
-// within the launch limits, and the copies' traffic (read and written once,
-// at about 3 TB/s) taking less time than the product would at 120 TFLOP/s.
+// Whether a transposed problem (or batch of `batch` problems, of which
+// copies_a / copies_b distinct operands are copied) copies its unaligned
+// transposed operands: not under graph capture (no allocation there), grid
+// dimensions within the launch limits, copies within kCopyMaxBytes, and the
+// copies' traffic (read and written once, at about 3 TB/s) taking less time
+// than the product would at 120 TFLOP/s.
 // Measured: the gather runs at 10-110 TFLOP/s (512^3 to 4095^3, 47-69 with
 // both operands transposed), the copies and the untransposed kernel at
 // 17-143, ahead at every size where this rule copies.
 // SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
-bool copy_plan(int M, int N, int K, bool copy_a, bool copy_b, void *stream) {
+constexpr double kCopyMaxBytes = 4.0 * (1 << 30);
+
+bool copy_plan(int M, int N, int K, bool copy_a, bool copy_b, void *stream, int batch = 1, int copies_a = 1,
+               int copies_b = 1) {
     if (knobs().pack < 0 || (!copy_a && !copy_b)) return false;
     if (ceil_div(K, 32) > 65535 || ceil_div(copy_a ? M : N, 32) > 65535 || ceil_div(N, 32) > 65535) return false;
+    const double copied = 4.0 * ((copy_a ? (double)copies_a * M * ((K + 3) & ~3L) : 0.0) +
+                                 (copy_b ? (double)copies_b * K * ((N + 3) & ~3L) : 0.0));
+    if (copied > kCopyMaxBytes) return false;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
         cap != hipStreamCaptureStatusNone)
         return false;
     if (knobs().pack > 0) return true;
-    const double bytes = 8.0 * ((copy_a ? (double)M * K : 0.0) + (copy_b ? (double)K * N : 0.0));
-    return bytes / 3e12 < 2.0 * M * (double)N * K / 120e12;
+    const double bytes = 8.0 * ((copy_a ? (double)copies_a * M * K : 0.0) + (copy_b ? (double)copies_b * K * N : 0.0));
+    return bytes / 3e12 < 2.0 * batch * M * (double)N * K / 120e12;
 }
 
 int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
@@ -705,35 +717,41 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
                 void *stream);
 
 // The product with the marked transposed operands replaced by row-major
-// copies (A as M x K, B as K x N); an operand not copied keeps its form.
+// copies (A as M x K, B as K x N); an operand not copied keeps its form.  In
+// a batch, an operand with stride 0 (one matrix for every problem) is copied
+// once, and each other one per problem, 64-float aligned.
 int run_copied(int op_a, int op_b, bool copy_a, bool copy_b, int M, int N, int K, float alpha, const float *A,
-               int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+               int lda, long long sA, const float *B, int ldb, long long sB, float beta, float *C, int ldc,
+               long long sC, int batch, void *stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const long lda2 = (K + 3) & ~3L, ldb2 = (N + 3) & ~3L;
-    const size_t a_floats = copy_a ? (((size_t)M * lda2 + 63) & ~(size_t)63) : 0;
-    const size_t b_floats = copy_b ? (size_t)K * ldb2 : 0;
+    const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
+    const size_t a_one = ((size_t)M * lda2 + 63) & ~(size_t)63, b_one = ((size_t)K * ldb2 + 63) & ~(size_t)63;
+    const size_t a_floats = copy_a ? a_one * na : 0, b_floats = copy_b ? b_one * nb : 0;
     float *buf = nullptr;
     const int st = get_copy_buffer(s, (a_floats + b_floats) * sizeof(float), &buf);
     if (st != SGEMM_STATUS_OK) return st;
     (void)hipGetLastError();
     if (copy_a) {   // stored K x M (leading dimension lda) -> M x K
-        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(M, 32), (unsigned)ceil_div(K, 32)), dim3(256),
-                           0, s, A, (long)lda, K, M, buf, lda2);
+        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(M, 32), (unsigned)ceil_div(K, 32), (unsigned)na),
+                           dim3(256), 0, s, A, (long)lda, K, M, buf, lda2, na > 1 ? (long)sA : 0L, (long)a_one);
         A = buf;
         lda = (int)lda2;
+        sA = na > 1 ? (long long)a_one : 0;
     }
     if (copy_b) {   // stored N x K (leading dimension ldb) -> K x N
         float *Bc = buf + a_floats;
-        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 32), (unsigned)ceil_div(N, 32)), dim3(256),
-                           0, s, B, (long)ldb, N, K, Bc, ldb2);
+        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 32), (unsigned)ceil_div(N, 32), (unsigned)nb),
+                           dim3(256), 0, s, B, (long)ldb, N, K, Bc, ldb2, nb > 1 ? (long)sB : 0L, (long)b_one);
         B = Bc;
         ldb = (int)ldb2;
+        sB = nb > 1 ? (long long)b_one : 0;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch (transpose)");
     // (the copies are row-major and aligned, so this call copies nothing)
-    return run_general(copy_a ? SGEMM_OP_N : op_a, copy_b ? SGEMM_OP_N : op_b, M, N, K, alpha, A, lda, 0, B, ldb, 0,
-                       beta, C, ldc, 0, 1, stream);
+    return run_general(copy_a ? SGEMM_OP_N : op_a, copy_b ? SGEMM_OP_N : op_b, M, N, K, alpha, A, lda, sA, B, ldb, sB,
+                       beta, C, ldc, sC, batch, stream);
 }
 
 int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
@@ -752,14 +770,18 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
     if (!ta && !tb && batch == 1)
         return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
-    if (batch == 1 && K > 0) {
+    if ((ta || tb) && K > 0) {
         // without 16-byte loads for the whole product (an operand or C
-        // unaligned, or an edge not in whole chunks) every transposed operand
-        // would be gathered
-        const bool vec1 = vec_ok(K, A, lda, B, ldb, beta, C, ldc) && (ta ? M : K) % 4 == 0 && (tb ? K : N) % 4 == 0;
+        // unaligned, an edge not in whole chunks, or a batch stride not a
+        // multiple of 4) every transposed operand would be gathered
+        const bool strides4 = batch == 1 || (sA % 4 == 0 && sB % 4 == 0 && sC % 4 == 0);
+        const bool vec1 = strides4 && vec_ok(K, A, lda, B, ldb, beta, C, ldc) && (ta ? M : K) % 4 == 0 &&
+                          (tb ? K : N) % 4 == 0;
         const bool copy_a = ta && !vec1, copy_b = tb && !vec1;
-        if (copy_plan(M, N, K, copy_a, copy_b, stream))
-            return run_copied(op_a, op_b, copy_a, copy_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
+        if (copy_plan(M, N, K, copy_a, copy_b, stream, batch, na, nb))
+            return run_copied(op_a, op_b, copy_a, copy_b, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
+                              batch, stream);
     }
 
     Args a;

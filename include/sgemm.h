@@ -178,7 +178,11 @@ int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha,
  * elements).  0 <= batch <= 65535.  stride_a and stride_b may be 0 (one
  * operand shared by all problems); the C problems must not overlap:
  * stride_c >= (M-1)*ldc + N when batch > 1.  One kernel launch for the whole
- * batch (no split-K).  batch == 0 is a no-op.  Returns SGEMM_STATUS_*.
+ * batch (no split-K).  Unaligned transposed operands are copied as in
+ * sgemm_op(), for the whole batch in one launch per operand (an operand of
+ * stride 0 once), when the copies' traffic takes less time than the product
+ * and the copies fit in 4 GiB; the same buffer and one-host-thread-per-stream
+ * rule apply.  batch == 0 is a no-op.  Returns SGEMM_STATUS_*.
  */
 int sgemm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha,
                           const float *A, int lda, long long stride_a,

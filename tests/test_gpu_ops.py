@@ -223,3 +223,46 @@ def test_transposed_operands_copied(ops, shape, pads):
             torch.cuda.synchronize()
             check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin, alpha=1.5, beta=beta),
                         f"copied op {ops} {shape} beta={beta}")
+
+
+@pytest.mark.parametrize("ops", [(T_, N_), (N_, T_), (T_, T_)], ids=["TN", "NT", "TT"])
+@pytest.mark.parametrize("shared", ["none", "A", "B"])
+def test_batched_transposed_operands_copied(ops, shared):
+    """Strided batches whose transposed operands lack 16-byte rows (odd
+    strides and leading dimensions), large enough that they are copied into
+    row-major buffers (per problem, or once for an operand of stride 0):
+    every problem equals the oracle, NaN between the stored problems is
+    never read and C between problems is never written."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    M, N, K, batch = 700, 515, 611, 3
+    probs = [make_problem(M, N, K, seed=700 + z, dist="normal", with_c=True) for z in range(batch)]
+    if shared == "A":
+        probs = [(probs[0][0], B, C) for (_, B, C) in probs]
+    if shared == "B":
+        probs = [(A, probs[0][1], C) for (A, _, C) in probs]
+    ra, ca = (K, M) if op_a == T_ else (M, K)
+    rb, cb = (N, K) if op_b == T_ else (K, N)
+    lda, ldb = ca + 1, cb + 3
+    sa = 0 if shared == "A" else ra * lda + 17
+    sb = 0 if shared == "B" else rb * ldb + 9
+    sc = M * N + 5
+    bufA = torch.full((max(1, batch if sa else 1) * (ra * lda + 17),), float("nan"), device="cuda")
+    bufB = torch.full((max(1, batch if sb else 1) * (rb * ldb + 9),), float("nan"), device="cuda")
+    bufC = torch.full((batch * sc,), float("nan"), device="cuda")
+    for z, (A, B, Cin) in enumerate(probs):
+        sA_ = np.ascontiguousarray(A.T if op_a == T_ else A)
+        sB_ = np.ascontiguousarray(B.T if op_b == T_ else B)
+        bufA[z * sa:z * sa + ra * lda].view(ra, lda)[:, :ca].copy_(torch.from_numpy(sA_))
+        bufB[z * sb:z * sb + rb * ldb].view(rb, ldb)[:, :cb].copy_(torch.from_numpy(sB_))
+        bufC[z * sc:z * sc + M * N].copy_(torch.from_numpy(Cin).flatten())
+    print(f"[batched copy] {ops} shared={shared}", flush=True)
+    st = capi.sgemm_strided_batched(op_a, op_b, M, N, K, 1.25, bufA.data_ptr(), lda, sa, bufB.data_ptr(), ldb, sb,
+                                    -0.5, bufC.data_ptr(), N, sc, batch, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    host = bufC.cpu().numpy()
+    for z, (A, B, Cin) in enumerate(probs):
+        check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=-0.5),
+                    f"batched copy {ops} shared={shared} problem {z}")
+        assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
