@@ -1071,13 +1071,16 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) return SGEMM_STATUS_NULL_POINTER;
     const float *Af = static_cast<const float *>(A), *Bf = static_cast<const float *>(B);
     if (ceil_div(M, 64) * ceil_div(N, 64) > 0x7fffffffL) return SGEMM_STATUS_INVALID_DIM;
+    // the fast kernels' 16-byte loads need every problem of a batch aligned
+    // like the first: strides of A and B that are multiples of 8 elements
+    const bool strides8 = batch <= 1 || (sA % 8 == 0 && sB % 8 == 0);
     if (variant == SGEMM_VARIANT_AUTO) {
-        variant = lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch);
+        variant = strides8 ? lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch) : 0;
         if (variant == 0 && batch == 1 && lowp_copy_plan(M, N, K, stream))
             return run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
     const LowpVariant &v = kLowpVariants[variant];
-    if (variant > 0 && ((ta || tb) && !lowp_takes_ops(variant))) return SGEMM_STATUS_UNSUPPORTED;
+    if (variant > 0 && (((ta || tb) && !lowp_takes_ops(variant)) || !strides8)) return SGEMM_STATUS_UNSUPPORTED;
     if (variant > 0 && !lowp_fast_ok(v, M, padded_b ? (N + 7) & ~7 : N, K, A, lda, B, ldb, ta, tb))
         return SGEMM_STATUS_UNSUPPORTED;
     Args a;

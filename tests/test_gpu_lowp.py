@@ -330,6 +330,36 @@ def test_lowp_strided_batched(dtype, trans_a, trans_b, shared_b):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans_a,trans_b", [(False, False), (True, False), (False, True)], ids=["NN", "TN", "NT"])
+def test_lowp_strided_batched_unaligned_strides(dtype, trans_a, trans_b):
+    """Batch strides that are not multiples of 8 elements (problem 0 aligned,
+    later problems not) on a shape the fast kernels take for one problem:
+    every problem against the oracle, NaN in the gaps between problems."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    batch, (M, N, K) = 3, (256, 264, 136)
+    print(f"[lowp] batched odd strides {dtype} ta={trans_a} tb={trans_b}", flush=True)
+    probs = [make_problem_16bit(M, N, K, seed=200 + z, dtype=dtype, dist="normal", with_c=True) for z in range(batch)]
+    sa = [np.ascontiguousarray(a.T) if trans_a else a for a, _, _ in probs]
+    sb = [np.ascontiguousarray(b.T) if trans_b else b for _, b, _ in probs]
+
+    def stack(xs, gap):
+        r, c = xs[0].shape
+        buf = torch.full((len(xs) * (r * c + gap),), float("nan"), dtype=t, device="cuda")
+        view = buf.as_strided((len(xs), r, c), (r * c + gap, c, 1))
+        for z, x in enumerate(xs):
+            view[z].copy_(torch.from_numpy(x).to(t))
+        return view
+    dA, dB = stack(sa, 3), stack(sb, 5)
+    dC = torch.from_numpy(np.stack([c for _, _, c in probs])).cuda()
+    sgemm_lowp(dA, dB, dC, alpha=0.5, beta=2.0, trans_a=trans_a, trans_b=trans_b)
+    torch.cuda.synchronize()
+    C = dC.cpu().numpy()
+    for z, (a, b, c) in enumerate(probs):
+        check_close(C[z], oracle.sgemm_ref(a, b, c, alpha=0.5, beta=2.0), f"odd strides, problem {z}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape,lds,off", [((1001, 999, 1003), (1003, 999), 0), ((640, 1030, 700), (703, 1037), 1),
                                            ((520, 264, 2048), (2049, 264), 0)],
                          ids=["K-and-N-odd", "misaligned", "lda-odd"])
