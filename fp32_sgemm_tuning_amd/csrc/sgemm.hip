@@ -937,7 +937,8 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
 // 16-bit operands the direct-to-LDS kernels cannot take (rows not 16-byte
 // aligned, or K or N not a multiple of 8) otherwise run on the plain kernel
 // at 58-65 TFLOP/s against 1000-1300 for the fast kernels (3000x5000x2047,
-// 4096^3 with odd leading dimensions).  A single problem instead copies
+// 4096^3 with odd leading dimensions).  A large enough problem (or each
+// problem of a strided batch) instead copies
 // op(A) into an M x K8 and op(B) into a K8 x N8 row-major buffer (stored
 // transposed operands are transposed on the way; K8, N8: K and N rounded up
 // to multiples of 8; padding zero, so the sums are unchanged; B's padding
@@ -949,8 +950,10 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
 // zeros; one 16-byte chunk of dst per thread per step of a grid-stride loop.
 __global__ void __launch_bounds__(256) pack16_kernel(const unsigned short *__restrict__ src, long ld_src, int rows,
                                                      int cols, unsigned short *__restrict__ dst, int rows_out,
-                                                     int cols_out) {
+                                                     int cols_out, long src_stride, long dst_stride) {
     typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    src += blockIdx.y * src_stride;      // problem blockIdx.y of a batch
+    dst += blockIdx.y * dst_stride;
     const long q8 = cols_out / 8;
     const long n = (long)rows_out * q8;
     for (long q = blockIdx.x * 256L + threadIdx.x; q < n; q += (long)gridDim.x * 256) {
@@ -968,10 +971,13 @@ __global__ void __launch_bounds__(256) pack16_kernel(const unsigned short *__res
 // c < cols, else zero: 32x32 tiles through LDS, both sides coalesced.
 __global__ void __launch_bounds__(256) transpose16_kernel(const unsigned short *__restrict__ src, long ld_src,
                                                           int rows, int cols, unsigned short *__restrict__ dst,
-                                                          int rows_out, int cols_out) {
+                                                          int rows_out, int cols_out, long src_stride,
+                                                          long dst_stride) {
     __shared__ unsigned short t[32][33];
     const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    src += blockIdx.z * src_stride;      // problem blockIdx.z of a batch
+    dst += blockIdx.z * dst_stride;
 #pragma unroll
     for (int i = ty; i < 32; i += 8) {
         const int c = c0 + i, r = r0 + tx;           // source row c, column r
@@ -986,20 +992,21 @@ __global__ void __launch_bounds__(256) transpose16_kernel(const unsigned short *
 }
 
 void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, int rows_out, int cols_out,
-                   hipStream_t s) {
+                   hipStream_t s, int batch = 1, long src_stride = 0, long dst_stride = 0) {
     const long n = (long)rows_out * (cols_out / 8);
-    const long blocks = std::min(ceil_div(n, 256), 4096L);
-    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+    const long blocks = std::min(ceil_div(n, 256), std::max(4096L / batch, 16L));
+    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)blocks, (unsigned)batch), dim3(256), 0, s,
                        static_cast<const unsigned short *>(src), ld_src, rows, cols,
-                       static_cast<unsigned short *>(dst), rows_out, cols_out);
+                       static_cast<unsigned short *>(dst), rows_out, cols_out, src_stride, dst_stride);
 }
 
-// Whether a single 16-bit problem that no fast kernel takes (operands
-// transposed or not) is copied: K of at least one K tile, not under graph
-// capture, and the copies' traffic (at about 3 TB/s) plus about 6 us for
-// the two extra launches taking less time than the plain kernel's product
-// (at 60 TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
-bool lowp_copy_plan(int M, int N, int K, void *stream) {
+// Whether a 16-bit problem or strided batch that no fast kernel takes
+// (operands transposed or not; copies_a / copies_b distinct operands copied)
+// is copied: K of at least one K tile, not under graph capture, copies
+// within 4 GiB, and the copies' traffic (at about 3 TB/s) plus about 6 us
+// for the two extra launches taking less time than the plain kernel's
+// product (at 60 TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
+bool lowp_copy_plan(int M, int N, int K, void *stream, int batch = 1, int copies_a = 1, int copies_b = 1) {
     if (knobs().pack < 0 || K < 64) return false;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
@@ -1007,11 +1014,12 @@ bool lowp_copy_plan(int M, int N, int K, void *stream) {
         return false;
     const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
     if (ceil_div(M, 32) > 65535 || ceil_div(K8, 32) > 65535) return false;   // transpose grids
+    const double copied = 2.0 * ((double)copies_a * M * K8 + (double)copies_b * K8 * N8);
+    if (copied > 4.0 * (1 << 30)) return false;
     // (the copies' rows fit the smallest fast tile's 31-bit buffer ranges)
     if (!lowp_fast_ok(kLowpVariants[1], M, (int)N8, (int)K8, nullptr, (int)K8, nullptr, (int)N8)) return false;
     if (knobs().pack > 0) return true;
-    const double bytes = 4.0 * ((double)M * K8 + (double)K8 * N8);
-    return bytes / 3e12 + 6e-6 < 2.0 * M * (double)N * K / 60e12;
+    return 2.0 * copied / 3e12 + 6e-6 < 2.0 * batch * M * (double)N * K / 60e12;
 }
 
 int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
@@ -1019,35 +1027,42 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
              long long sA, long long sB, long long sC, int batch, bool padded_b);
 
 // The 16-bit product on zero-padded row-major copies of op(A) and op(B)
-// (transposed operands transposed on the way).
+// (transposed operands transposed on the way).  In a batch, an operand of
+// stride 0 is copied once and each other one per problem (strides of the
+// copies: multiples of 128 elements).
 int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
-                    const void *B, int ldb, float beta, float *C, int ldc, void *stream) {
+                    long long sA, const void *B, int ldb, long long sB, float beta, float *C, int ldc,
+                    long long sC, int batch, void *stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int K8 = (K + 7) & ~7, N8 = (N + 7) & ~7;
-    const size_t a_elems = ((size_t)M * K8 + 127) & ~(size_t)127, b_elems = (size_t)K8 * N8;
+    const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
+    const size_t a_one = ((size_t)M * K8 + 127) & ~(size_t)127, b_one = ((size_t)K8 * N8 + 127) & ~(size_t)127;
     float *buf = nullptr;
-    const int st = get_copy_buffer(s, (a_elems + b_elems) * 2, &buf);
+    const int st = get_copy_buffer(s, (a_one * na + b_one * nb) * 2, &buf);
     if (st != SGEMM_STATUS_OK) return st;
-    unsigned short *Ap = reinterpret_cast<unsigned short *>(buf), *Bp = Ap + a_elems;
+    unsigned short *Ap = reinterpret_cast<unsigned short *>(buf), *Bp = Ap + a_one * na;
+    const long src_a = na > 1 ? (long)sA : 0, src_b = nb > 1 ? (long)sB : 0;
     (void)hipGetLastError();
     if (ta)     // stored K x M
-        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32)), dim3(256),
-                           0, s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8);
+        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32), (unsigned)na),
+                           dim3(256), 0, s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8, src_a,
+                           (long)a_one);
     else
-        launch_pack16(A, lda, M, K, Ap, M, K8, s);
+        launch_pack16(A, lda, M, K, Ap, M, K8, s, na, src_a, (long)a_one);
     if (tb)     // stored N x K
-        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32)), dim3(256),
-                           0, s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8);
+        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32), (unsigned)nb),
+                           dim3(256), 0, s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8, src_b,
+                           (long)b_one);
     else
-        launch_pack16(B, ldb, K, N, Bp, K8, N8, s);
+        launch_pack16(B, ldb, K, N, Bp, K8, N8, s, nb, src_b, (long)b_one);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_hip_error(e, "kernel launch (copy)");
     // the fast kernels on the copies: chosen for the padded width, run on the
     // true one (their loads of B's last chunk read the zero padding)
-    const int v = lowp_auto(M, N8, K8, Ap, K8, Bp, N8);
+    const int v = lowp_auto(M, N8, K8, Ap, K8, Bp, N8, false, false, batch);
     if (v == 0) return SGEMM_STATUS_UNSUPPORTED;
-    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v, 0, 0, 0,
-                    1, true);
+    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v,
+                    na > 1 ? (long long)a_one : 0, nb > 1 ? (long long)b_one : 0, sC, batch, true);
 }
 
 int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
@@ -1076,8 +1091,10 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     const bool strides8 = batch <= 1 || (sA % 8 == 0 && sB % 8 == 0);
     if (variant == SGEMM_VARIANT_AUTO) {
         variant = strides8 ? lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch) : 0;
-        if (variant == 0 && batch == 1 && lowp_copy_plan(M, N, K, stream))
-            return run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
+        if (variant == 0 && lowp_copy_plan(M, N, K, stream, batch, na, nb))
+            return run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch,
+                                   stream);
     }
     const LowpVariant &v = kLowpVariants[variant];
     if (variant > 0 && (((ta || tb) && !lowp_takes_ops(variant)) || !strides8)) return SGEMM_STATUS_UNSUPPORTED;

@@ -282,9 +282,13 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * elements) and C + z*stride_c (in floats); the rules of
  * sgemm_strided_batched() (0 <= batch <= 65535, strides of A and B may be 0,
  * C problems must not overlap, one launch, no split-K) and the automatic
- * variant choice over batch x tiles; batches whose stride_a or stride_b is
- * not a multiple of 8 elements (problems after the first not 16-byte
- * aligned) run on the plain kernel.  Returns SGEMM_STATUS_*.
+ * variant choice over batch x tiles.  Batches the fast kernels cannot take
+ * (unaligned rows, K or N not multiples of 8, or stride_a or stride_b not a
+ * multiple of 8 elements, which leaves problems after the first unaligned)
+ * are copied into zero-padded buffers as in sgemm_lowp(), one launch per
+ * operand for the whole batch (an operand of stride 0 once), when that
+ * takes less time than the plain kernel and the copies fit in 4 GiB; the
+ * rest run on the plain kernel.  Returns SGEMM_STATUS_*.
  */
 int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
                                const void *A, int lda, long long stride_a,

@@ -405,3 +405,50 @@ def test_lowp_copied_transposed_operands(dtype, ops):
         torch.cuda.synchronize()
         check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=0.5, beta=beta),
                     f"{dtype} op TA={ta} TB={tb} beta={beta}")
+
+
+@pytest.mark.parametrize("dtype,ops,shared", [(d, o, "none") for d in DTYPES for o in ("NN", "TN", "NT", "TT")] +
+                         [("bf16", "NN", "A"), ("bf16", "TT", "B"), ("f16", "TN", "B"), ("f16", "NT", "A")])
+def test_lowp_batched_copied_operands(dtype, ops, shared):
+    """Strided batches of 16-bit problems the fast kernels cannot take (odd
+    leading dimensions and strides, K and N not multiples of 8), large
+    enough to be copied into zero-padded buffers (per problem, or once for
+    an operand of stride 0): every problem against the oracle, NaN in the
+    gaps between stored problems never read, C between problems never
+    written."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    batch, (M, N, K) = 3, (640, 517, 701)
+    probs = [make_problem_16bit(M, N, K, seed=400 + z, dtype=dtype, dist="normal", with_c=True) for z in range(batch)]
+    if shared == "A":
+        probs = [(probs[0][0], b, c) for _, b, c in probs]
+    if shared == "B":
+        probs = [(a, probs[0][1], c) for a, _, c in probs]
+    sa = [np.ascontiguousarray(a.T) if ta else a for a, _, _ in probs]
+    sb = [np.ascontiguousarray(b.T) if tb else b for _, b, _ in probs]
+
+    def stack(xs, pad, gap, one):
+        r, c = xs[0].shape
+        ld = c + pad
+        n = 1 if one else len(xs)
+        buf = torch.full((n * (r * ld + gap),), float("nan"), dtype=t, device="cuda")
+        view = buf.as_strided((len(xs), r, c), (0 if one else r * ld + gap, ld, 1))
+        for z in range(n):
+            view[z].copy_(torch.from_numpy(xs[z]).to(t))
+        return view
+    dA = stack(sa, 1, 3, shared == "A")
+    dB = stack(sb, 3, 5, shared == "B")
+    sc = M * N + 7
+    bufC = torch.full((batch * sc,), float("nan"), device="cuda")
+    dC = bufC.as_strided((batch, M, N), (sc, N, 1))
+    for z, (_, _, c) in enumerate(probs):
+        dC[z].copy_(torch.from_numpy(c))
+    print(f"[lowp] batched copy {dtype} {ops} shared={shared}", flush=True)
+    sgemm_lowp(dA, dB, dC, alpha=0.5, beta=-1.0, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    host = bufC.cpu().numpy()
+    for z, (a, b, c) in enumerate(probs):
+        check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(a, b, c, alpha=0.5, beta=-1.0),
+                    f"batched copy {dtype} {ops} shared={shared} problem {z}")
+        assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
