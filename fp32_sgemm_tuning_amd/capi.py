@@ -18,6 +18,11 @@ SGEMM_STATUS_UNSUPPORTED = -5
 SGEMM_STATUS_INVALID_OP = -6
 SGEMM_STATUS_INVALID_DTYPE = -7
 
+SGEMM_WORKSPACE_BYTES = 64 * 1024 * 1024 + 16 * 1024
+SGEMM_MAX_STREAM_WORKSPACES = 8
+SGEMM_MAX_COPY_BUFFERS = 2
+SGEMM_MAX_COPY_BUFFER_BYTES = 4 << 30
+
 SGEMM_DTYPE_BF16 = 1
 SGEMM_DTYPE_F16 = 2
 
@@ -35,7 +40,7 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
            "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
            "sgemm_lowp_variant_name", "sgemm_lowp_split_factor", "sgemm_tail_split", "sgemm_lowp_op",
-           "sgemm_lowp_strided_batched")
+           "sgemm_lowp_strided_batched", "sgemm_workspace_bytes", "sgemm_release_workspaces")
 
 _lib = None
 
@@ -108,6 +113,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_last_hip_error.restype = cp
     lib.sgemm_version.argtypes = []
     lib.sgemm_version.restype = i
+    lib.sgemm_workspace_bytes.argtypes = []
+    lib.sgemm_workspace_bytes.restype = ll
+    lib.sgemm_release_workspaces.argtypes = []
+    lib.sgemm_release_workspaces.restype = i
     _lib = lib
     return lib
 
@@ -224,3 +233,11 @@ def sgemm_last_hip_error():
 
 def sgemm_version():
     return load().sgemm_version()
+
+
+def sgemm_workspace_bytes():
+    return load().sgemm_workspace_bytes()
+
+
+def sgemm_release_workspaces():
+    return load().sgemm_release_workspaces()

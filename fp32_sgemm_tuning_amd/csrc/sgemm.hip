@@ -15,9 +15,11 @@
 #include <string.h>
 
 #include <algorithm>
-#include <map>
+#include <list>
 #include <mutex>
+#include <thread>
 #include <utility>
+#include <vector>
 
 #include "sgemm.h"
 #include "sgemm_kernels.hpp"
@@ -26,26 +28,26 @@
 
 namespace sgemm_mi355x {
 // Lean direct-to-LDS kernels (sgemm_lean.hip, built with MFMA results in
-// VGPRs): whole tiles only, offsets within the 31-bit buffer range.
-void launch_lean_128x128x64_w2x2(const Args &a, hipStream_t stream);
-void launch_lean_128x128x32_w2x2(const Args &a, hipStream_t stream);
-void launch_lean_256x128x32_w4x2(const Args &a, hipStream_t stream);
-void launch_lean_128x256x32_w2x4(const Args &a, hipStream_t stream);
-void launch_lean_256x256x32_w4x2(const Args &a, hipStream_t stream);
-void launch_lean_64x64x32_w4x1(const Args &a, hipStream_t stream);
-void launch_lean_64x64x64_w4x1(const Args &a, hipStream_t stream);
-void launch_lean_64x128x32_w2x2(const Args &a, hipStream_t stream);
-void launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
-void launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
-void launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
-void launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
-void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t stream);
-void launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
-void launch_lean_splitk_dw_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
-void launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
-void launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
-void launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
-void launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
+// VGPRs): whole tiles only, offsets within the 31-bit buffer range.  Every
+// launcher returns its launch's status.
+hipError_t launch_lean_128x128x64_w2x2(const Args &a, hipStream_t stream);
+hipError_t launch_lean_128x128x32_w2x2(const Args &a, hipStream_t stream);
+hipError_t launch_lean_256x128x32_w4x2(const Args &a, hipStream_t stream);
+hipError_t launch_lean_128x256x32_w2x4(const Args &a, hipStream_t stream);
+hipError_t launch_lean_64x64x32_w4x1(const Args &a, hipStream_t stream);
+hipError_t launch_lean_64x64x64_w4x1(const Args &a, hipStream_t stream);
+hipError_t launch_lean_64x128x32_w2x2(const Args &a, hipStream_t stream);
+hipError_t launch_lean_128x64x32_w4x1(const Args &a, hipStream_t stream);
+hipError_t launch_lean_dw_128x128x32_w2x2(const Args &a, hipStream_t stream);
+hipError_t launch_lean_dw_64x64x64_w4x1(const Args &a, hipStream_t stream);
+hipError_t launch_lean_general(const Args &a, bool tile64, bool dw, bool ta, bool tb, int batch, hipStream_t stream);
+hipError_t launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t stream);
+hipError_t launch_lean_splitk_128x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_dw_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
 }  // namespace sgemm_mi355x
 
 using namespace sgemm_mi355x;
@@ -114,77 +116,55 @@ bool vec_ok(int K, const float *A, int lda, const float *B, int ldb, float beta,
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
-void launch_db(const Args &a0, hipStream_t stream) {
+hipError_t launch_db(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
-#define SGEMM_LAUNCH(G, Z) \
-    hipLaunchKernelGGL((sgemm_db_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
-    if (guard) {
-        if (beta0) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(true, false);
-    } else {
-        if (beta0) SGEMM_LAUNCH(false, true);
-        else SGEMM_LAUNCH(false, false);
-    }
+#define SGEMM_LAUNCH(G, Z) launch_k(sgemm_db_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>, grid, block, stream, a)
+    if (guard) return beta0 ? SGEMM_LAUNCH(true, true) : SGEMM_LAUNCH(true, false);
+    return beta0 ? SGEMM_LAUNCH(false, true) : SGEMM_LAUNCH(false, false);
 #undef SGEMM_LAUNCH
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
-void launch_pipe(const Args &a0, hipStream_t stream) {
+hipError_t launch_pipe(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % 16);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
-#define SGEMM_LAUNCH(G, Z) \
-    hipLaunchKernelGGL((sgemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
-    if (guard) {
-        if (beta0) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(true, false);
-    } else {
-        if (beta0) SGEMM_LAUNCH(false, true);
-        else SGEMM_LAUNCH(false, false);
-    }
+#define SGEMM_LAUNCH(G, Z) launch_k(sgemm_pipe_kernel<BM, BN, WAVES_M, WAVES_N, VEC, G, Z>, grid, block, stream, a)
+    if (guard) return beta0 ? SGEMM_LAUNCH(true, true) : SGEMM_LAUNCH(true, false);
+    return beta0 ? SGEMM_LAUNCH(false, true) : SGEMM_LAUNCH(false, false);
 #undef SGEMM_LAUNCH
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VEC>
-void launch_sec(const Args &a0, hipStream_t stream) {
+hipError_t launch_sec(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const bool guard = (a.M % BM) || (a.N % BN) || (a.K % BK);
     const bool beta0 = a.beta == 0.0f;
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
-#define SGEMM_LAUNCH(G, Z) \
-    hipLaunchKernelGGL((sgemm_sec_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>), grid, block, 0, stream, a)
-    if (guard) {
-        if (beta0) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(true, false);
-    } else {
-        if (beta0) SGEMM_LAUNCH(false, true);
-        else SGEMM_LAUNCH(false, false);
-    }
+#define SGEMM_LAUNCH(G, Z) launch_k(sgemm_sec_kernel<BM, BN, BK, WAVES_M, WAVES_N, VEC, G, Z>, grid, block, stream, a)
+    if (guard) return beta0 ? SGEMM_LAUNCH(true, true) : SGEMM_LAUNCH(true, false);
+    return beta0 ? SGEMM_LAUNCH(false, true) : SGEMM_LAUNCH(false, false);
 #undef SGEMM_LAUNCH
 }
 
 // Direct-to-LDS kernel for whole tiles; shapes that are not whole tiles
 // fall back to the section-pipelined kernel of the same tile (guarded loads).
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES>
-void launch_dtl(const Args &a0, hipStream_t stream) {
+hipError_t launch_dtl(const Args &a0, hipStream_t stream) {
     const Args a = tiled(a0, BM, BN);
     const bool whole = !(a.M % BM) && !(a.N % BN) && !(a.K % BK);
-    if (!whole) {
-        launch_sec<BM, BN, BK, WAVES_M, WAVES_N, true>(a, stream);
-        return;
-    }
+    if (!whole) return launch_sec<BM, BN, BK, WAVES_M, WAVES_N, true>(a, stream);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(64 * WAVES_M * WAVES_N);
     if (a.beta == 0.0f)
-        hipLaunchKernelGGL((sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, false>), grid, block, 0, stream, a);
+        return launch_k(sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, true>, grid, block, stream, a);
+    return launch_k(sgemm_dtl_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, false>, grid, block, stream, a);
 }
 
-typedef void (*Launcher)(const Args &, hipStream_t);
+typedef hipError_t (*Launcher)(const Args &, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Split-K (lean kernels).  A tile grid with fewer blocks than about two per
@@ -198,6 +178,7 @@ constexpr long kTailSlots = 2 * kNumCUs;                 // resident lean blocks
 constexpr long kSplitMaxTiles = 4096;                    // tiles with counters
 constexpr size_t kSplitPartialBytes = 64u << 20;         // 1024 partial tiles of 128x128, 256 of 256x256
 constexpr size_t kSplitWorkspaceBytes = kSplitPartialBytes + kSplitMaxTiles * sizeof(unsigned);
+static_assert(kSplitWorkspaceBytes == (size_t)SGEMM_WORKSPACE_BYTES, "workspace size in sgemm.h");
 
 // Split factor for an M x N x K problem on bm x bn x bk tiles (1 = no
 // split), for grids of fewer than one full wave of resident blocks (larger
@@ -250,61 +231,194 @@ int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
     return best_cost <= 0.95 * base ? (int)best : 1;
 }
 
-// One split-K workspace per (device, stream), allocated on first use and
-// kept until the process ends: calls on one stream run in order, so they
-// can share it; calls on different streams get different ones.  The
-// counters are zeroed once, on the stream, before the first kernel that uses
-// them; every split-K kernel leaves them zero.
-struct Workspace {
-    float *partials = nullptr;
-    unsigned *counters = nullptr;
+// ---------------------------------------------------------------------------
+// Device memory kept between calls.  Two kinds: split-K workspaces (partial
+// tiles and tile counters, kSplitWorkspaceBytes each) and copy buffers (for
+// operands copied before the product, grown on demand).  A device keeps at
+// most SGEMM_MAX_STREAM_WORKSPACES workspaces and SGEMM_MAX_COPY_BUFFERS
+// copy buffers, each bound to one stream (the per-thread default stream
+// counts once per host thread).
+//
+// A call leases its stream's slot from before its first launch to after its
+// last; the end of the lease records an event on the stream, which marks
+// the slot's last use.  A stream without a slot gets a new one while the
+// device has fewer than the maximum, else the least recently used slot that
+// no call holds, once that slot's event has completed: however many streams
+// a process creates and destroys, the memory stays bounded, and a buffer is
+// never handed to another stream while kernels that use it are queued.  All
+// waits (on that event, or before a copy buffer grows) happen outside the
+// lock, so a call never blocks calls on other streams.
+//
+// When no slot can be had without waiting for another call (every slot of
+// the device held), the call takes a path that needs none: K is not split,
+// or the operand is not copied.  Nothing is allocated, cleared or waited
+// for under graph capture; such calls take those paths too.
+//
+// Workspaces may be shared by calls on one stream, which run in stream
+// order; a copy buffer is held by one call at a time (its copies and the
+// product that reads them are separate launches).
+enum SlotKind { kWorkspaceSlot = 0, kCopySlot = 1 };
+constexpr int kUnavailable = 1;          // acquire(): no slot without waiting
+
+struct Slot {
+    int kind = 0;
+    int dev = -1;
+    hipStream_t stream = nullptr;
+    std::thread::id thread;              // the host thread, for hipStreamPerThread
+    void *mem = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;           // recorded at the end of every lease
+    int users = 0;                       // calls holding a lease
+    bool moving = false;                 // being set up, grown or handed over (unlocked)
+    bool pinned = false;                 // an event record failed: never handed over
+    unsigned long long stamp = 0;        // last use, for least-recently-used choice
 };
 
-int get_workspace(hipStream_t stream, Workspace &out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, Workspace> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair(dev, stream);
-    auto it = cache.find(key);
-    if (it != cache.end()) {
-        out = it->second;
-        return SGEMM_STATUS_OK;
-    }
+struct Lease {
+    Slot *slot = nullptr;
     void *mem = nullptr;
-    e = hipMalloc(&mem, kSplitWorkspaceBytes);
-    if (e != hipSuccess) return record_hip_error(e, "hipMalloc (split-K workspace)");
-    Workspace w;
-    w.partials = static_cast<float *>(mem);
-    w.counters = reinterpret_cast<unsigned *>(static_cast<char *>(mem) + kSplitPartialBytes);
-    e = hipMemsetAsync(w.counters, 0, kSplitMaxTiles * sizeof(unsigned), stream);
-    if (e != hipSuccess) {
-        (void)hipFree(mem);
-        return record_hip_error(e, "hipMemsetAsync (split-K counters)");
+};
+
+std::mutex g_slot_mu;
+std::list<Slot> g_slots;                 // node addresses stay valid
+unsigned long long g_slot_clock = 0;
+
+int max_slots(int kind) { return kind == kWorkspaceSlot ? SGEMM_MAX_STREAM_WORKSPACES : SGEMM_MAX_COPY_BUFFERS; }
+
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
+}
+
+// (Unlocked; the slot is marked moving.)  Make `s` hold at least `bytes`
+// for `stream`: wait for its last use, replace memory that is too small, and
+// clear a workspace's tile counters on the stream.
+int prepare_slot(Slot &s, size_t bytes, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    if (s.done == nullptr) {
+        e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            s.done = nullptr;
+            return record_hip_error(e, "hipEventCreateWithFlags");
+        }
+    } else {
+        e = hipEventSynchronize(s.done);
+        if (e != hipSuccess) return record_hip_error(e, "hipEventSynchronize (buffer hand-over)");
     }
-    cache[key] = w;
-    out = w;
+    if (s.mem == nullptr || s.bytes < bytes) {
+        if (s.mem != nullptr) {
+            e = hipFree(s.mem);
+            s.mem = nullptr;
+            s.bytes = 0;
+            if (e != hipSuccess) return record_hip_error(e, "hipFree (buffer)");
+        }
+        e = hipMalloc(&s.mem, bytes);
+        if (e != hipSuccess) {
+            s.mem = nullptr;
+            return record_hip_error(e, s.kind == kWorkspaceSlot ? "hipMalloc (split-K workspace)"
+                                                               : "hipMalloc (copy buffer)");
+        }
+        s.bytes = bytes;
+    }
+    if (s.kind == kWorkspaceSlot) {
+        e = hipMemsetAsync(static_cast<char *>(s.mem) + kSplitPartialBytes, 0, kSplitMaxTiles * sizeof(unsigned),
+                           stream);
+        if (e != hipSuccess) return record_hip_error(e, "hipMemsetAsync (split-K counters)");
+    }
+    return SGEMM_STATUS_OK;
+}
+
+// Lease the slot of `kind` for `stream` with at least `bytes`: returns
+// SGEMM_STATUS_OK (out.mem set), kUnavailable (take a path without the
+// buffer) or an error status.
+int acquire_slot(int kind, hipStream_t stream, size_t bytes, Lease &out) {
+    out = Lease{};
+    if (capturing(stream)) return kUnavailable;
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    const std::thread::id thread = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+    std::unique_lock<std::mutex> lock(g_slot_mu);
+    Slot *s = nullptr, *lru = nullptr;
+    int held = 0;
+    for (Slot &x : g_slots) {
+        if (x.kind != kind || x.dev != dev) continue;
+        ++held;
+        if (x.stream == stream && x.thread == thread) s = &x;
+        if (x.users == 0 && !x.moving && !x.pinned && (lru == nullptr || x.stamp < lru->stamp)) lru = &x;
+    }
+    if (s != nullptr) {
+        if (s->moving || (kind == kCopySlot && s->users > 0) || s->pinned) return kUnavailable;
+        if (s->bytes >= bytes) {
+            ++s->users;
+            s->stamp = ++g_slot_clock;
+            out = Lease{s, s->mem};
+            return SGEMM_STATUS_OK;
+        }
+        if (s->users > 0) return kUnavailable;         // grow only while no call holds it
+    } else if (held < max_slots(kind)) {
+        g_slots.emplace_back();
+        s = &g_slots.back();
+        s->kind = kind;
+        s->dev = dev;
+    } else if (lru != nullptr) {
+        s = lru;
+    } else {
+        return kUnavailable;
+    }
+    s->stream = stream;
+    s->thread = thread;
+    s->moving = true;
+    lock.unlock();
+    const int st = prepare_slot(*s, bytes, stream);
+    lock.lock();
+    s->moving = false;
+    s->stamp = ++g_slot_clock;
+    if (st != SGEMM_STATUS_OK) return st;
+    ++s->users;
+    out = Lease{s, s->mem};
+    return SGEMM_STATUS_OK;
+}
+
+// End a lease: the slot's event marks this call's last use on `stream`.
+// Returns SGEMM_STATUS_OK or, if the event cannot be recorded, the HIP error
+// (the slot is then never handed over or released).
+int release_slot(Lease &l, hipStream_t stream) {
+    if (l.slot == nullptr) return SGEMM_STATUS_OK;
+    Slot *s = l.slot;
+    l = Lease{};
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    const hipError_t e = hipEventRecord(s->done, stream);
+    --s->users;
+    s->stamp = ++g_slot_clock;
+    if (e != hipSuccess) {
+        s->pinned = true;
+        return record_hip_error(e, "hipEventRecord (buffer release)");
+    }
     return SGEMM_STATUS_OK;
 }
 
 // Split K `splits` ways (when above one) with the stream's workspace: sets
-// a.splits, a.ws and a.counters.  A stream under graph capture cannot
-// allocate or clear memory, so K is split only outside capture.
-int attach_workspace(Args &a, int splits, void *stream) {
+// a.splits, a.ws and a.counters and the lease; leaves a.splits at 1 when
+// no workspace is available (graph capture, every workspace held).
+int attach_workspace(Args &a, int splits, hipStream_t stream, Lease &lease) {
     if (splits <= 1) return SGEMM_STATUS_OK;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    const bool capturing = hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
-                           cap != hipStreamCaptureStatusNone;
-    if (capturing) return SGEMM_STATUS_OK;
-    Workspace w;
-    const int ws = get_workspace(reinterpret_cast<hipStream_t>(stream), w);
-    if (ws != SGEMM_STATUS_OK) return ws;
+    if (lease.slot == nullptr) {
+        const int st = acquire_slot(kWorkspaceSlot, stream, kSplitWorkspaceBytes, lease);
+        if (st == kUnavailable) return SGEMM_STATUS_OK;
+        if (st != SGEMM_STATUS_OK) return st;
+    }
     a.splits = splits;
-    a.ws = w.partials;
-    a.counters = w.counters;
+    a.ws = static_cast<float *>(lease.mem);
+    a.counters = reinterpret_cast<unsigned *>(static_cast<char *>(lease.mem) + kSplitPartialBytes);
     return SGEMM_STATUS_OK;
+}
+
+// The first error of a call's launches and its lease's release.
+int finish(hipError_t launch, Lease &lease, hipStream_t stream) {
+    const int rel = release_slot(lease, stream);
+    if (launch != hipSuccess) return record_hip_error(launch, "kernel launch");
+    return rel;
 }
 
 // Wave quantization: a grid of whole waves plus a last wave at most a
@@ -318,13 +432,10 @@ int choose_tail_splits(const VariantDesc &d, const Args &a);
 
 // A split-capable variant: split-K when a.splits > 1, else the plain lean
 // kernel of the same tile.
-typedef void (*SplitLauncher)(const Args &, int, hipStream_t);
+typedef hipError_t (*SplitLauncher)(const Args &, int, hipStream_t);
 template <SplitLauncher SPLIT, Launcher PLAIN>
-void launch_split_or_plain(const Args &a, hipStream_t stream) {
-    if (a.splits > 1)
-        SPLIT(a, a.splits, stream);
-    else
-        PLAIN(a, stream);
+hipError_t launch_split_or_plain(const Args &a, hipStream_t stream) {
+    return a.splits > 1 ? SPLIT(a, a.splits, stream) : PLAIN(a, stream);
 }
 
 // Whether the byte offsets within one K tile of the lean kernel's part of A
@@ -351,60 +462,48 @@ bool lean_dw_takes(int bm, int bn, int bk, const Args &a) {
 // be whole tiles) and offsets within a tile that fit the descriptors' range;
 // other shapes go to FALLBACK, a guarded kernel.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
-void launch_lean_or(const Args &a, hipStream_t stream) {
+hipError_t launch_lean_or(const Args &a, hipStream_t stream) {
     // (a launch over part of the grid, a.tile_count > 0, is made only for
     // operands the lean kernel takes; the fallback always covers the whole
     // grid)
-    if (lean_takes(BM, BN, BK, a)) {
-        LEAN(a, stream);
-    } else {
-        Args whole = a;
-        whole.tile_base = whole.tile_count = 0;
-        FALLBACK(whole, stream);
-    }
+    if (lean_takes(BM, BN, BK, a)) return LEAN(a, stream);
+    Args whole = a;
+    whole.tile_base = whole.tile_count = 0;
+    return FALLBACK(whole, stream);
 }
 
 // The lean kernel with 4-byte loads takes any alignment and any K >= BK, with
 // offsets within a tile that fit as above; other shapes go to FALLBACK.
 template <int BM, int BN, int BK, Launcher LEAN, Launcher FALLBACK>
-void launch_lean_dw_or(const Args &a, hipStream_t stream) {
-    if (lean_dw_takes(BM, BN, BK, a)) {
-        LEAN(a, stream);
-    } else {
-        Args whole = a;                      // the fallback covers the whole grid
-        whole.tile_base = whole.tile_count = 0;
-        FALLBACK(whole, stream);
-    }
+hipError_t launch_lean_dw_or(const Args &a, hipStream_t stream) {
+    if (lean_dw_takes(BM, BN, BK, a)) return LEAN(a, stream);
+    Args whole = a;                      // the fallback covers the whole grid
+    whole.tile_base = whole.tile_count = 0;
+    return FALLBACK(whole, stream);
 }
 
-void launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStream_t stream) {
+hipError_t launch_simple_general(const Args &a0, bool ta, bool tb, int batch, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch);
-    if (ta && tb)
-        hipLaunchKernelGGL((sgemm_simple_kernel<true, true>), grid, dim3(256), 0, stream, a);
-    else if (ta)
-        hipLaunchKernelGGL((sgemm_simple_kernel<true, false>), grid, dim3(256), 0, stream, a);
-    else if (tb)
-        hipLaunchKernelGGL((sgemm_simple_kernel<false, true>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_simple_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch), block(256);
+    if (ta && tb) return launch_k(sgemm_simple_kernel<true, true>, grid, block, stream, a);
+    if (ta) return launch_k(sgemm_simple_kernel<true, false>, grid, block, stream, a);
+    if (tb) return launch_k(sgemm_simple_kernel<false, true>, grid, block, stream, a);
+    return launch_k(sgemm_simple_kernel<false, false>, grid, block, stream, a);
 }
 
-void launch_simple(const Args &a, hipStream_t stream) { launch_simple_general(a, false, false, 1, stream); }
+hipError_t launch_simple(const Args &a, hipStream_t stream) { return launch_simple_general(a, false, false, 1, stream); }
 
 // The plain kernel on 16-bit inputs (each element widened to FP32 on load).
-void launch_simple_lowp(const Args &a0, bool f16, bool ta, bool tb, int batch, hipStream_t stream) {
+hipError_t launch_simple_lowp(const Args &a0, bool f16, bool ta, bool tb, int batch, hipStream_t stream) {
     const Args a = tiled(a0, 64, 64);
-    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch);
-#define SGEMM_S(A, B)                                                                                         \
-    do {                                                                                                      \
-        if (f16) hipLaunchKernelGGL((sgemm_simple_kernel<A, B, kF16>), grid, dim3(256), 0, stream, a);        \
-        else hipLaunchKernelGGL((sgemm_simple_kernel<A, B, kBF16>), grid, dim3(256), 0, stream, a);           \
-    } while (0)
-    if (ta && tb) SGEMM_S(true, true);
-    else if (ta) SGEMM_S(true, false);
-    else if (tb) SGEMM_S(false, true);
-    else SGEMM_S(false, false);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)batch), block(256);
+#define SGEMM_S(A, B)                                                             \
+    (f16 ? launch_k(sgemm_simple_kernel<A, B, kF16>, grid, block, stream, a)      \
+         : launch_k(sgemm_simple_kernel<A, B, kBF16>, grid, block, stream, a))
+    if (ta && tb) return SGEMM_S(true, true);
+    if (ta) return SGEMM_S(true, false);
+    if (tb) return SGEMM_S(false, true);
+    return SGEMM_S(false, false);
 #undef SGEMM_S
 }
 
@@ -419,7 +518,7 @@ struct VariantDesc {
 
 // Ids 0..2 are the stable ones named in sgemm.h; the rest are tile shapes
 // kept for sweeps (128-bit access only).
-const VariantDesc kVariants[] = {
+constexpr VariantDesc kVariants[] = {
     {"simple_64x64x16", 64, 64, 16, false, launch_simple},
     {"db_128x128x32_w2x2_vec", 128, 128, 32, true, launch_db<128, 128, 32, 2, 2, true>},
     {"db_128x128x32_w2x2_scalar", 128, 128, 32, false, launch_db<128, 128, 32, 2, 2, false>},
@@ -451,8 +550,6 @@ const VariantDesc kVariants[] = {
      launch_lean_or<256, 128, 32, launch_lean_256x128x32_w4x2, launch_db<256, 128, 32, 4, 2, true>>},
     {"lean_128x256x32_w2x4", 128, 256, 32, true,
      launch_lean_or<128, 256, 32, launch_lean_128x256x32_w2x4, launch_db<128, 256, 32, 2, 4, true>>},
-    {"lean_256x256x32_w4x2", 256, 256, 32, true,
-     launch_lean_or<256, 256, 32, launch_lean_256x256x32_w4x2, launch_db<256, 256, 32, 4, 2, true>>},
     {"lean_128x128x32_w2x2_splitk", 128, 128, 32, true,
      launch_lean_or<128, 128, 32,
                     launch_split_or_plain<launch_lean_splitk_128x128x32_w2x2, launch_lean_128x128x32_w2x2>,
@@ -510,12 +607,25 @@ int choose_tail_splits(const VariantDesc &d, const Args &a) {
     return s < 2 ? 1 : (int)s;
 }
 
-// Variants the automatic choice uses for 128-bit operands (indices into
-// kVariants).
-constexpr int kVec = 24;       // lean_128x128x32_w2x2
-constexpr int kVec64 = 32;     // lean_64x64x64_w4x1_splitk (splits K only below 160 tiles)
-constexpr int kAny = 37;       // lean_dw_128x128x32_w2x2: 4-byte loads, any alignment
-constexpr int kAny64 = 39;     // lean_dw_64x64x64_w4x1_splitk
+// Variants the automatic choice uses (indices into kVariants, looked up by
+// name at compile time).
+constexpr bool same_name(const char *x, const char *y) {
+    while (*x != 0 && *x == *y) {
+        ++x;
+        ++y;
+    }
+    return *x == *y;
+}
+constexpr int variant_id(const char *name) {
+    for (int i = 0; i < kNumVariants; ++i)
+        if (same_name(kVariants[i].name, name)) return i;
+    return -1;
+}
+constexpr int kVec = variant_id("lean_128x128x32_w2x2");
+constexpr int kVec64 = variant_id("lean_64x64x64_w4x1_splitk");
+constexpr int kAny = variant_id("lean_dw_128x128x32_w2x2");          // 4-byte loads, any alignment
+constexpr int kAny64 = variant_id("lean_dw_64x64x64_w4x1_splitk");
+static_assert(kVec >= 0 && kVec64 >= 0 && kAny >= 0 && kAny64 >= 0, "variant table");
 constexpr int kMaxBatch = 65535;  // problems per strided batch (launch grid z extent)
 
 // Fill of the last wave of blocks: with t tiles spread over the CUs, the
@@ -586,13 +696,12 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.ws = nullptr;
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Lease lease;
     if (d.split_k) {
-        const int ws = attach_workspace(a, choose_splits(M, N, K, d.bm, d.bn, d.bk), stream);
+        const int ws = attach_workspace(a, choose_splits(M, N, K, d.bm, d.bn, d.bk), s, lease);
         if (ws != SGEMM_STATUS_OK) return ws;
     }
-
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
     const int tail_splits = d.split_k && a.splits == 1 ? choose_tail_splits(d, a) : 1;
     if (tail_splits > 1) {
         // Whole waves of tiles first, then the last, partly filled wave with
@@ -602,16 +711,15 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
         head.tile_count = (int)(tiles - rem);
         tail.tile_base = (int)(tiles - rem);
         tail.tile_count = (int)rem;
-        const int ws = attach_workspace(tail, tail_splits, stream);
+        const int ws = attach_workspace(tail, tail_splits, s, lease);
         if (ws != SGEMM_STATUS_OK) return ws;
-        d.launch(head, s);
-        d.launch(tail, s);
-    } else {
-        d.launch(a, s);
+        if (tail.splits > 1) {
+            hipError_t e = d.launch(head, s);
+            if (e == hipSuccess) e = d.launch(tail, s);
+            return finish(e, lease, s);
+        }
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return record_hip_error(e, "kernel launch");
-    return SGEMM_STATUS_OK;
+    return finish(d.launch(a, s), lease, s);
 }
 
 // Transposed operands and strided batches (row-major).  op_a / op_b are
@@ -656,45 +764,18 @@ __global__ void __launch_bounds__(256) transpose_kernel(const float *__restrict_
     }
 }
 
-// One copy buffer per (device, stream), grown on demand (the old one freed
-// once the stream has drained) and kept until the process ends.
-int get_copy_buffer(hipStream_t stream, size_t bytes, float **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    auto &slot = cache[std::make_pair(dev, stream)];
-    if (slot.first != nullptr && slot.second >= bytes) {
-        *out = static_cast<float *>(slot.first);
-        return SGEMM_STATUS_OK;
-    }
-    if (slot.first != nullptr) {
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return record_hip_error(e, "hipStreamSynchronize (copy buffer)");
-        (void)hipFree(slot.first);
-        slot = std::make_pair(nullptr, (size_t)0);
-    }
-    void *mem = nullptr;
-    e = hipMalloc(&mem, bytes);
-    if (e != hipSuccess) return record_hip_error(e, "hipMalloc (copy buffer)");
-    slot = std::make_pair(mem, bytes);
-    *out = static_cast<float *>(mem);
-    return SGEMM_STATUS_OK;
-}
-
 // Whether a transposed problem (or batch of `batch` problems, of which
 // copies_a / copies_b distinct operands are copied) copies its unaligned
 // transposed operands: not under graph capture (no allocation there), grid
-// dimensions within the launch limits, copies within kCopyMaxBytes, and the
+// dimensions within the launch limits, copies within kCopyMaxBytes (the
+// largest copy buffer, SGEMM_MAX_COPY_BUFFER_BYTES), and the
 // copies' traffic (read and written once, at about 3 TB/s) taking less time
 // than the product would at 120 TFLOP/s.
 // Measured: the gather runs at 10-110 TFLOP/s (512^3 to 4095^3, 47-69 with
 // both operands transposed), the copies and the untransposed kernel at
 // 17-143, ahead at every size where this rule copies.
 // SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
-constexpr double kCopyMaxBytes = 4.0 * (1 << 30);
+constexpr double kCopyMaxBytes = (double)SGEMM_MAX_COPY_BUFFER_BYTES;
 
 bool copy_plan(int M, int N, int K, bool copy_a, bool copy_b, void *stream, int batch = 1, int copies_a = 1,
                int copies_b = 1) {
@@ -703,10 +784,7 @@ bool copy_plan(int M, int N, int K, bool copy_a, bool copy_b, void *stream, int 
     const double copied = 4.0 * ((copy_a ? (double)copies_a * M * ((K + 3) & ~3L) : 0.0) +
                                  (copy_b ? (double)copies_b * K * ((N + 3) & ~3L) : 0.0));
     if (copied > kCopyMaxBytes) return false;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
-        cap != hipStreamCaptureStatusNone)
-        return false;
+    if (capturing(reinterpret_cast<hipStream_t>(stream))) return false;
     if (knobs().pack > 0) return true;
     const double bytes = 8.0 * ((copy_a ? (double)copies_a * M * K : 0.0) + (copy_b ? (double)copies_b * K * N : 0.0));
     return bytes / 3e12 < 2.0 * batch * M * (double)N * K / 120e12;
@@ -719,7 +797,9 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
 // The product with the marked transposed operands replaced by row-major
 // copies (A as M x K, B as K x N); an operand not copied keeps its form.  In
 // a batch, an operand with stride 0 (one matrix for every problem) is copied
-// once, and each other one per problem, 64-float aligned.
+// once, and each other one per problem, 64-float aligned.  Returns
+// kUnavailable, with nothing enqueued, when the stream's copy buffer is held
+// by another call (the caller then gathers the operands instead).
 int run_copied(int op_a, int op_b, bool copy_a, bool copy_b, int M, int N, int K, float alpha, const float *A,
                int lda, long long sA, const float *B, int ldb, long long sB, float beta, float *C, int ldc,
                long long sC, int batch, void *stream) {
@@ -728,30 +808,32 @@ int run_copied(int op_a, int op_b, bool copy_a, bool copy_b, int M, int N, int K
     const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
     const size_t a_one = ((size_t)M * lda2 + 63) & ~(size_t)63, b_one = ((size_t)K * ldb2 + 63) & ~(size_t)63;
     const size_t a_floats = copy_a ? a_one * na : 0, b_floats = copy_b ? b_one * nb : 0;
-    float *buf = nullptr;
-    const int st = get_copy_buffer(s, (a_floats + b_floats) * sizeof(float), &buf);
+    Lease lease;
+    const int st = acquire_slot(kCopySlot, s, (a_floats + b_floats) * sizeof(float), lease);
     if (st != SGEMM_STATUS_OK) return st;
-    (void)hipGetLastError();
+    float *buf = static_cast<float *>(lease.mem);
+    hipError_t e = hipSuccess;
     if (copy_a) {   // stored K x M (leading dimension lda) -> M x K
-        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(M, 32), (unsigned)ceil_div(K, 32), (unsigned)na),
-                           dim3(256), 0, s, A, (long)lda, K, M, buf, lda2, na > 1 ? (long)sA : 0L, (long)a_one);
+        e = launch_k(transpose_kernel, dim3((unsigned)ceil_div(M, 32), (unsigned)ceil_div(K, 32), (unsigned)na),
+                     dim3(256), s, A, (long)lda, K, M, buf, lda2, na > 1 ? (long)sA : 0L, (long)a_one);
         A = buf;
         lda = (int)lda2;
         sA = na > 1 ? (long long)a_one : 0;
     }
-    if (copy_b) {   // stored N x K (leading dimension ldb) -> K x N
+    if (copy_b && e == hipSuccess) {   // stored N x K (leading dimension ldb) -> K x N
         float *Bc = buf + a_floats;
-        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 32), (unsigned)ceil_div(N, 32), (unsigned)nb),
-                           dim3(256), 0, s, B, (long)ldb, N, K, Bc, ldb2, nb > 1 ? (long)sB : 0L, (long)b_one);
+        e = launch_k(transpose_kernel, dim3((unsigned)ceil_div(K, 32), (unsigned)ceil_div(N, 32), (unsigned)nb),
+                     dim3(256), s, B, (long)ldb, N, K, Bc, ldb2, nb > 1 ? (long)sB : 0L, (long)b_one);
         B = Bc;
         ldb = (int)ldb2;
         sB = nb > 1 ? (long long)b_one : 0;
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return record_hip_error(e, "kernel launch (transpose)");
+    if (e != hipSuccess) return finish(e, lease, s);
     // (the copies are row-major and aligned, so this call copies nothing)
-    return run_general(copy_a ? SGEMM_OP_N : op_a, copy_b ? SGEMM_OP_N : op_b, M, N, K, alpha, A, lda, sA, B, ldb, sB,
-                       beta, C, ldc, sC, batch, stream);
+    const int prod = run_general(copy_a ? SGEMM_OP_N : op_a, copy_b ? SGEMM_OP_N : op_b, M, N, K, alpha, A, lda, sA,
+                                 B, ldb, sB, beta, C, ldc, sC, batch, stream);
+    const int rel = release_slot(lease, s);
+    return prod != SGEMM_STATUS_OK ? prod : rel;
 }
 
 int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const float *A, int lda, long long sA,
@@ -779,9 +861,11 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
                           (tb ? K : N) % 4 == 0;
         const bool copy_a = ta && !vec1, copy_b = tb && !vec1;
         const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
-        if (copy_plan(M, N, K, copy_a, copy_b, stream, batch, na, nb))
-            return run_copied(op_a, op_b, copy_a, copy_b, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
-                              batch, stream);
+        if (copy_plan(M, N, K, copy_a, copy_b, stream, batch, na, nb)) {
+            const int st = run_copied(op_a, op_b, copy_a, copy_b, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C,
+                                      ldc, sC, batch, stream);
+            if (st != kUnavailable) return st;
+        }
     }
 
     Args a;
@@ -818,12 +902,8 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     const bool lean = K >= bk && lean_fits(bm, bn, bk, lda, ldb, ta, tb);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (lean)
-        launch_lean_general(a, tile64, !vec, ta, tb, batch, s);
-    else
-        launch_simple_general(a, ta, tb, batch, s);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        lean ? launch_lean_general(a, tile64, !vec, ta, tb, batch, s) : launch_simple_general(a, ta, tb, batch, s);
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");
     return SGEMM_STATUS_OK;
 }
@@ -991,13 +1071,13 @@ __global__ void __launch_bounds__(256) transpose16_kernel(const unsigned short *
     }
 }
 
-void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, int rows_out, int cols_out,
-                   hipStream_t s, int batch = 1, long src_stride = 0, long dst_stride = 0) {
+hipError_t launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, int rows_out, int cols_out,
+                         hipStream_t s, int batch = 1, long src_stride = 0, long dst_stride = 0) {
     const long n = (long)rows_out * (cols_out / 8);
     const long blocks = std::min(ceil_div(n, 256), std::max(4096L / batch, 16L));
-    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)blocks, (unsigned)batch), dim3(256), 0, s,
-                       static_cast<const unsigned short *>(src), ld_src, rows, cols,
-                       static_cast<unsigned short *>(dst), rows_out, cols_out, src_stride, dst_stride);
+    return launch_k(pack16_kernel, dim3((unsigned)blocks, (unsigned)batch), dim3(256), s,
+                    static_cast<const unsigned short *>(src), ld_src, rows, cols, static_cast<unsigned short *>(dst),
+                    rows_out, cols_out, src_stride, dst_stride);
 }
 
 // Whether a 16-bit problem or strided batch that no fast kernel takes
@@ -1008,14 +1088,11 @@ void launch_pack16(const void *src, long ld_src, int rows, int cols, void *dst, 
 // product (at 60 TFLOP/s).  SGEMM_PACK = 1 / -1 forces it on / off (where it can run).
 bool lowp_copy_plan(int M, int N, int K, void *stream, int batch = 1, int copies_a = 1, int copies_b = 1) {
     if (knobs().pack < 0 || K < 64) return false;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
-        cap != hipStreamCaptureStatusNone)
-        return false;
+    if (capturing(reinterpret_cast<hipStream_t>(stream))) return false;
     const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
     if (ceil_div(M, 32) > 65535 || ceil_div(K8, 32) > 65535) return false;   // transpose grids
     const double copied = 2.0 * ((double)copies_a * M * K8 + (double)copies_b * K8 * N8);
-    if (copied > 4.0 * (1 << 30)) return false;
+    if (copied > kCopyMaxBytes) return false;
     // (the copies' rows fit the smallest fast tile's 31-bit buffer ranges)
     if (!lowp_fast_ok(kLowpVariants[1], M, (int)N8, (int)K8, nullptr, (int)K8, nullptr, (int)N8)) return false;
     if (knobs().pack > 0) return true;
@@ -1029,7 +1106,8 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
 // The 16-bit product on zero-padded row-major copies of op(A) and op(B)
 // (transposed operands transposed on the way).  In a batch, an operand of
 // stride 0 is copied once and each other one per problem (strides of the
-// copies: multiples of 128 elements).
+// copies: multiples of 128 elements).  Returns kUnavailable, with nothing
+// enqueued, when the stream's copy buffer is held by another call.
 int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
                     long long sA, const void *B, int ldb, long long sB, float beta, float *C, int ldc,
                     long long sC, int batch, void *stream) {
@@ -1037,32 +1115,33 @@ int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alph
     const int K8 = (K + 7) & ~7, N8 = (N + 7) & ~7;
     const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
     const size_t a_one = ((size_t)M * K8 + 127) & ~(size_t)127, b_one = ((size_t)K8 * N8 + 127) & ~(size_t)127;
-    float *buf = nullptr;
-    const int st = get_copy_buffer(s, (a_one * na + b_one * nb) * 2, &buf);
-    if (st != SGEMM_STATUS_OK) return st;
-    unsigned short *Ap = reinterpret_cast<unsigned short *>(buf), *Bp = Ap + a_one * na;
-    const long src_a = na > 1 ? (long)sA : 0, src_b = nb > 1 ? (long)sB : 0;
-    (void)hipGetLastError();
-    if (ta)     // stored K x M
-        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32), (unsigned)na),
-                           dim3(256), 0, s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8, src_a,
-                           (long)a_one);
-    else
-        launch_pack16(A, lda, M, K, Ap, M, K8, s, na, src_a, (long)a_one);
-    if (tb)     // stored N x K
-        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32), (unsigned)nb),
-                           dim3(256), 0, s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8, src_b,
-                           (long)b_one);
-    else
-        launch_pack16(B, ldb, K, N, Bp, K8, N8, s, nb, src_b, (long)b_one);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return record_hip_error(e, "kernel launch (copy)");
     // the fast kernels on the copies: chosen for the padded width, run on the
-    // true one (their loads of B's last chunk read the zero padding)
-    const int v = lowp_auto(M, N8, K8, Ap, K8, Bp, N8, false, false, batch);
+    // true one (their loads of B's last chunk read the zero padding); the
+    // copies are 16-byte aligned, so only the pointer alignment matters here
+    const int v = lowp_auto(M, N8, K8, nullptr, K8, nullptr, N8, false, false, batch);
     if (v == 0) return SGEMM_STATUS_UNSUPPORTED;
-    return run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v,
-                    na > 1 ? (long long)a_one : 0, nb > 1 ? (long long)b_one : 0, sC, batch, true);
+    Lease lease;
+    const int st = acquire_slot(kCopySlot, s, (a_one * na + b_one * nb) * 2, lease);
+    if (st != SGEMM_STATUS_OK) return st;
+    unsigned short *Ap = static_cast<unsigned short *>(lease.mem), *Bp = Ap + a_one * na;
+    const long src_a = na > 1 ? (long)sA : 0, src_b = nb > 1 ? (long)sB : 0;
+    hipError_t e = ta   // stored K x M
+                       ? launch_k(transpose16_kernel,
+                                  dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32), (unsigned)na), dim3(256),
+                                  s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8, src_a,
+                                  (long)a_one)
+                       : launch_pack16(A, lda, M, K, Ap, M, K8, s, na, src_a, (long)a_one);
+    if (e == hipSuccess)
+        e = tb   // stored N x K
+                ? launch_k(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32), (unsigned)nb),
+                           dim3(256), s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8, src_b,
+                           (long)b_one)
+                : launch_pack16(B, ldb, K, N, Bp, K8, N8, s, nb, src_b, (long)b_one);
+    if (e != hipSuccess) return finish(e, lease, s);
+    const int prod = run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v,
+                              na > 1 ? (long long)a_one : 0, nb > 1 ? (long long)b_one : 0, sC, batch, true);
+    const int rel = release_slot(lease, s);
+    return prod != SGEMM_STATUS_OK ? prod : rel;
 }
 
 int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, const void *A, int lda,
@@ -1092,9 +1171,11 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (variant == SGEMM_VARIANT_AUTO) {
         variant = strides8 ? lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch) : 0;
         const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
-        if (variant == 0 && lowp_copy_plan(M, N, K, stream, batch, na, nb))
-            return run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, batch,
-                                   stream);
+        if (variant == 0 && lowp_copy_plan(M, N, K, stream, batch, na, nb)) {
+            const int st = run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
+                                           batch, stream);
+            if (st != kUnavailable) return st;
+        }
     }
     const LowpVariant &v = kLowpVariants[variant];
     if (variant > 0 && (((ta || tb) && !lowp_takes_ops(variant)) || !strides8)) return SGEMM_STATUS_UNSUPPORTED;
@@ -1122,18 +1203,14 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     a.strideA = batch > 1 ? (long)sA : 0;
     a.strideB = batch > 1 ? (long)sB : 0;
     a.strideC = batch > 1 ? (long)sC : 0;
-    const int ws = attach_workspace(a, ta || tb || batch > 1 ? 1 : lowp_splits(variant, M, N, K), stream);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Lease lease;
+    const int ws = attach_workspace(a, ta || tb || batch > 1 ? 1 : lowp_splits(variant, M, N, K), s, lease);
     if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (variant > 0)
-        launch_lowp_tile(a, f16, variant - 1, ta, tb, batch, s);
-    else
-        launch_simple_lowp(a, f16, ta, tb, batch, s);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return record_hip_error(e, "kernel launch");
-    return SGEMM_STATUS_OK;
+    return finish(variant > 0 ? launch_lowp_tile(a, f16, variant - 1, ta, tb, batch, s)
+                              : launch_simple_lowp(a, f16, ta, tb, batch, s),
+                  lease, s);
 }
 
 }  // namespace
@@ -1284,5 +1361,50 @@ const char *sgemm_strerror(int status) {
 const char *sgemm_last_hip_error(void) { return g_last_hip_error; }
 
 int sgemm_version(void) { return SGEMM_LIB_VERSION; }
+
+long long sgemm_workspace_bytes(void) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    long long total = 0;
+    for (const Slot &x : g_slots)
+        if (x.dev == dev) total += (long long)x.bytes;
+    return total;
+}
+
+int sgemm_release_workspaces(void) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    std::vector<std::list<Slot>::iterator> victims;
+    {
+        std::lock_guard<std::mutex> lock(g_slot_mu);
+        for (auto it = g_slots.begin(); it != g_slots.end(); ++it) {
+            if (it->dev != dev || it->users > 0 || it->moving || it->pinned) continue;
+            it->moving = true;
+            victims.push_back(it);
+        }
+    }
+    int st = SGEMM_STATUS_OK;
+    std::vector<std::list<Slot>::iterator> freed;
+    for (auto it : victims) {
+        // the slot's last use must be over before its memory goes
+        e = it->done != nullptr ? hipEventSynchronize(it->done) : hipSuccess;
+        if (e == hipSuccess && it->mem != nullptr) e = hipFree(it->mem);
+        if (e != hipSuccess) {
+            if (st == SGEMM_STATUS_OK) st = record_hip_error(e, "releasing a buffer");
+            std::lock_guard<std::mutex> lock(g_slot_mu);
+            it->moving = false;
+            it->pinned = true;      // state unknown: never reused
+            continue;
+        }
+        if (it->done != nullptr) (void)hipEventDestroy(it->done);
+        freed.push_back(it);
+    }
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    for (auto it : freed) g_slots.erase(it);
+    return st;
+}
 
 }  // extern "C"

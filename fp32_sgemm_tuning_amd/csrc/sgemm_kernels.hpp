@@ -75,6 +75,21 @@ inline Args tiled(const Args &a, int bm, int bn) {
     return t;
 }
 
+// Launch `kernel` on `stream` and return that launch's own status.
+// hipLaunchKernel reports an error of this launch directly, so the library
+// never reads the thread's last-error state: a HIP error the caller left
+// pending is neither consumed nor taken for the library's own.
+template <class T>
+struct SameType {
+    using type = T;
+};
+template <class... P>
+inline hipError_t launch_k(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                           typename SameType<P>::type... args) {
+    void *argv[] = {static_cast<void *>(&args)..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

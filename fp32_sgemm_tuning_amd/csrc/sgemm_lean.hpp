@@ -374,7 +374,7 @@ sgemm_lean_kernel(Args p) {
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool SPLIT, bool DW = false, bool TA = false,
           bool TB = false>
-void launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) {
+hipError_t launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) {
     const Args a = tiled(a0, BM, BN);
     // a.tile_count > 0: this launch covers tiles a.tile_base .. + tile_count - 1
     const int tiles = a0.tile_count > 0 ? a0.tile_count : a.tiles_m * a.tiles_n;
@@ -382,15 +382,13 @@ void launch_lean(const Args &a0, int splits, hipStream_t stream, int batch = 1) 
     const dim3 block(64 * WAVES_M * WAVES_N);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
 #define SGEMM_LAUNCH(Z, E) \
-    hipLaunchKernelGGL((sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW, TA, TB>), grid, block, 0, \
-                       stream, a)
+    launch_k(sgemm_lean_kernel<BM, BN, BK, WAVES_M, WAVES_N, Z, E, SPLIT, DW, TA, TB>, grid, block, stream, a)
     if (edge) {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(false, true);
-    } else {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, false);
-        else SGEMM_LAUNCH(false, false);
+        if (a.beta == 0.0f) return SGEMM_LAUNCH(true, true);
+        return SGEMM_LAUNCH(false, true);
     }
+    if (a.beta == 0.0f) return SGEMM_LAUNCH(true, false);
+    return SGEMM_LAUNCH(false, false);
 #undef SGEMM_LAUNCH
 }
 

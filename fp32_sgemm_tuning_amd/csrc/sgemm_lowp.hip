@@ -485,7 +485,10 @@ sgemm_lowp_kernel(Args p) {
 
     // C = alpha * acc (+ beta * C): block (mi, nb) holds row l%16 and
     // columns 4*(l/16) .. +3 of its 16x16 output block; 16-byte accesses
-    // when C's rows are 16-byte aligned
+    // when C's rows are 16-byte aligned and the four columns lie below N.
+    // (N need not be a multiple of 4: the product on the library's padded
+    // copies runs with the true N, so the last vector of a row may straddle
+    // N; its columns are then stored one by one.)
     const float alpha = p.alpha, beta = p.beta;
     const bool vecc = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc & 3) == 0;
 #pragma unroll
@@ -496,9 +499,7 @@ sgemm_lowp_kernel(Args p) {
             const int col = n0 + wn * WN + nb * 16 + 4 * lg;
             if (EDGE && row >= p.M) continue;
             float *dst = p.C + (long)row * p.ldc + col;
-            if (vecc) {
-                // N is a multiple of 8 here, so a vector starting below N ends below N
-                if (EDGE && col >= p.N) continue;
+            if (vecc && (!EDGE || col + 3 < p.N)) {
                 f32x4 o = acc[mi][nb] * alpha;
                 if (!BETA0) o += *reinterpret_cast<const f32x4 *>(dst) * beta;
                 *reinterpret_cast<f32x4 *>(dst) = o;
@@ -516,39 +517,36 @@ sgemm_lowp_kernel(Args p) {
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT, bool TA = false,
           bool TB = false>
-void launch_lowp(const Args &a0, hipStream_t stream, int batch = 1) {
+hipError_t launch_lowp(const Args &a0, hipStream_t stream, int batch = 1) {
     const Args a = tiled(a0, BM, BN);
     const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(SPLIT ? a.splits : 1), (unsigned)batch);
     const dim3 block(64 * WM * WN);
     const bool edge = (a.M % BM) || (a.N % BN) || (a.K % BK);
-#define SGEMM_LAUNCH(Z, E)                                                                                        \
-    hipLaunchKernelGGL((sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT, TA, TB>), grid, block, \
-                       0, stream, a)
+#define SGEMM_LAUNCH(Z, E) \
+    launch_k(sgemm_lowp_kernel<BM, BN, BK, WM, WN, NSTAGE, PP, Z, E, F16, SPLIT, TA, TB>, grid, block, stream, a)
     if (edge) {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, true);
-        else SGEMM_LAUNCH(false, true);
-    } else {
-        if (a.beta == 0.0f) SGEMM_LAUNCH(true, false);
-        else SGEMM_LAUNCH(false, false);
+        if (a.beta == 0.0f) return SGEMM_LAUNCH(true, true);
+        return SGEMM_LAUNCH(false, true);
     }
+    if (a.beta == 0.0f) return SGEMM_LAUNCH(true, false);
+    return SGEMM_LAUNCH(false, false);
 #undef SGEMM_LAUNCH
 }
 
 // One alternating kernel with each of the four operand orientations.
 template <int BM, int BN, int BK, int NS>
-void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int batch, hipStream_t s) {
+hipError_t launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int batch, hipStream_t s) {
 #define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, false, A, B>(a, s, batch)
     if (f16) {
-        if (ta && tb) SGEMM_O(true, true, true);
-        else if (ta) SGEMM_O(true, true, false);
-        else if (tb) SGEMM_O(true, false, true);
-        else SGEMM_O(true, false, false);
-    } else {
-        if (ta && tb) SGEMM_O(false, true, true);
-        else if (ta) SGEMM_O(false, true, false);
-        else if (tb) SGEMM_O(false, false, true);
-        else SGEMM_O(false, false, false);
+        if (ta && tb) return SGEMM_O(true, true, true);
+        if (ta) return SGEMM_O(true, true, false);
+        if (tb) return SGEMM_O(true, false, true);
+        return SGEMM_O(true, false, false);
     }
+    if (ta && tb) return SGEMM_O(false, true, true);
+    if (ta) return SGEMM_O(false, true, false);
+    if (tb) return SGEMM_O(false, false, true);
+    return SGEMM_O(false, false, false);
 #undef SGEMM_O
 }
 
@@ -557,23 +555,20 @@ void launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int batch, hi
 // ABI's translation unit lists them in this order).  a.splits > 1 runs the
 // split-K form (built for the 128x128 two-stage kernel); ta / tb (transposed
 // operands) are built for the two alternating kernels; batch problems on
-// gridDim.z.
-void launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t s) {
-#define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                  \
-    do {                                                                         \
-        if (f16) launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s, batch); \
-        else launch_lowp<BM, BN, BK, WM, WN, NS, false, PP, SP>(a, s, batch);    \
-    } while (0)
+// gridDim.z.  Returns the launch's status.
+hipError_t launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t s) {
+#define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                          \
+    (f16 ? launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s, batch)                \
+         : launch_lowp<BM, BN, BK, WM, WN, NS, false, PP, SP>(a, s, batch))
     const bool split = a.splits > 1;
     switch (tile) {
-        case 1: SGEMM_T(256, 128, 64, 2, 4, 3, false, false); break;
-        case 2: SGEMM_T(256, 256, 32, 2, 4, 4, false, false); break;
-        case 3: launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, batch, s); break;
-        case 4: launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, batch, s); break;
+        case 1: return SGEMM_T(256, 128, 64, 2, 4, 3, false, false);
+        case 2: return SGEMM_T(256, 256, 32, 2, 4, 4, false, false);
+        case 3: return launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, batch, s);
+        case 4: return launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, batch, s);
         default:
-            if (split) SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
-            else SGEMM_T(128, 128, 64, 2, 2, 2, false, false);
-            break;
+            if (split) return SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
+            return SGEMM_T(128, 128, 64, 2, 2, 2, false, false);
     }
 #undef SGEMM_T
 }

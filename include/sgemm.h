@@ -27,21 +27,37 @@
  * its arguments, enqueues one kernel on `stream` (a hipStream_t; NULL is the
  * null stream; two kernels when the last wave of tiles is split, see
  * sgemm_tail_split) and returns without synchronising.  Calls are thread-safe
- * and deterministic: the same inputs give the same bits.
+ * and deterministic: the same inputs and the same split of K (see
+ * "Workspace") give the same bits.
  *
  * Workspace.  Small tile grids split K over several workgroups per output
- * tile (split-K).  Those calls use a workspace that the library allocates
- * with hipMalloc on the first such call for each (device, stream) pair and
- * keeps until the process ends: 64 MiB of partial tiles and 4096 tile
- * counters, the counters cleared once on the stream before first use and
- * left cleared by every call.  Calls on one stream share the workspace in
- * stream order; calls on different streams use different workspaces.  The
- * partial tiles of a tile are added in a fixed order, so split-K results are
- * deterministic too.  On a stream under graph capture K is never split (no
- * allocation happens during capture).  An allocation failure returns
- * SGEMM_STATUS_HIP_ERROR before anything is enqueued.  sgemm_op() and
- * sgemm_cm() keep one more per-stream buffer, for copies of unaligned
- * transposed operands (see sgemm_op).
+ * tile (split-K).  Those calls use a workspace of SGEMM_WORKSPACE_BYTES
+ * (64 MiB of partial tiles and 4096 tile counters) that the library
+ * allocates with hipMalloc for a stream on its first such call.  A device
+ * keeps at most SGEMM_MAX_STREAM_WORKSPACES of them, each bound to one stream
+ * (the per-thread default stream counts once per host thread); when more
+ * streams ask, the least recently used workspace that no call in progress
+ * holds is handed to the new stream once the kernels queued on it have
+ * finished (an event recorded at the end of each call marks that), so
+ * device memory stays bounded however many streams a process creates and
+ * destroys.  The counters are cleared on the stream before a workspace's
+ * first use and left cleared by every call.  Calls on one stream share its
+ * workspace in stream order.  The partial tiles of a tile are added in a
+ * fixed order, so split-K results are deterministic too.  A call that finds
+ * no workspace free without waiting for another call (every one held at
+ * that moment), and every call on a stream under graph capture, runs with K
+ * unsplit: the same result within rounding, nothing allocated or waited
+ * for.  No call waits while holding the library's lock, so calls on
+ * different streams never block each other.  An allocation failure returns
+ * SGEMM_STATUS_HIP_ERROR before anything is enqueued.  sgemm_op(), sgemm_cm()
+ * and sgemm_lowp() keep copy buffers the same way (see sgemm_op).
+ * sgemm_workspace_bytes() reports the device memory held and
+ * sgemm_release_workspaces() frees it.
+ *
+ * HIP errors.  Every launch's status is taken from the launch call itself:
+ * the library never calls hipGetLastError or hipPeekAtLastError, so it
+ * neither consumes a HIP error the caller left pending nor reports such an
+ * error as its own.
  *
  * Errors.  Arguments are checked before anything is enqueued, so a call that
  * returns an error has written nothing.  M == 0 or N == 0 returns
@@ -64,6 +80,12 @@ extern "C" {
 #define SGEMM_STATUS_INVALID_OP (-6)        /* an operation code other than SGEMM_OP_N / SGEMM_OP_T */
 
 #define SGEMM_STATUS_INVALID_DTYPE (-7)     /* sgemm_lowp: an input type other than SGEMM_DTYPE_BF16 / _F16 */
+
+/* Device memory the library keeps between calls (see "Workspace" above). */
+#define SGEMM_WORKSPACE_BYTES (64ll * 1024 * 1024 + 16 * 1024)  /* one split-K workspace */
+#define SGEMM_MAX_STREAM_WORKSPACES 8       /* split-K workspaces kept per device */
+#define SGEMM_MAX_COPY_BUFFERS 2            /* copy buffers kept per device */
+#define SGEMM_MAX_COPY_BUFFER_BYTES (4ll << 30)  /* largest copy buffer; larger copies are not made */
 
 /* Input element types of sgemm_lowp. */
 #define SGEMM_DTYPE_BF16 1                  /* bfloat16: 1 sign, 8 exponent, 7 fraction bits */
@@ -155,14 +177,14 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
  * its contiguous extent multiples of 4 floats) is read in its stored
  * orientation with 16-byte loads.  One without is, for a problem large
  * enough that the copy takes less time than the product, first transposed
- * into a row-major copy in a buffer the library allocates with hipMalloc per
- * (device, stream) on first need, grows (after draining the stream) and
- * keeps until the process ends, and the product then runs as sgemm() on
- * the copy; otherwise, and always under graph capture, it is gathered with
- * 4-byte loads.  The copy and the product are separate launches sharing
- * the stream's buffer, so calls on one stream must come from one host thread
- * at a time (calls on different streams are independent).  Environment
- * variable SGEMM_PACK = 1 / -1 forces the copy on / off, for sweeps.  Returns SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for
+ * into a row-major copy in the stream's copy buffer (allocated with
+ * hipMalloc on first need, grown once the kernels queued with it have
+ * finished, at most SGEMM_MAX_COPY_BUFFERS per device, handed between
+ * streams like the split-K workspaces), and the product then runs as sgemm()
+ * on the copy; otherwise, always under graph capture, and when the stream's
+ * buffer is held by a call in progress on another host thread, it is
+ * gathered with 4-byte loads.  Environment variable SGEMM_PACK = 1 / -1
+ * forces the copy on / off, for sweeps.  Returns SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for
  * another op code; SGEMM_STATUS_HIP_ERROR if the buffer cannot be allocated
  * (nothing enqueued).
  */
@@ -181,8 +203,8 @@ int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha,
  * batch (no split-K).  Unaligned transposed operands are copied as in
  * sgemm_op(), for the whole batch in one launch per operand (an operand of
  * stride 0 once), when the copies' traffic takes less time than the product
- * and the copies fit in 4 GiB; the same buffer and one-host-thread-per-stream
- * rule apply.  batch == 0 is a no-op.  Returns SGEMM_STATUS_*.
+ * and the copies fit in SGEMM_MAX_COPY_BUFFER_BYTES; the same buffer rules
+ * apply.  batch == 0 is a no-op.  Returns SGEMM_STATUS_*.
  */
 int sgemm_strided_batched(int op_a, int op_b, int M, int N, int K, float alpha,
                           const float *A, int lda, long long stride_a,
@@ -226,10 +248,10 @@ int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alph
  * operands (unaligned rows, K or N not multiples of 8) of a problem with
  * K >= 64, large enough that copying them takes less time than the plain
  * kernel would, are first copied into zero-padded aligned buffers (K and N
- * rounded up to multiples of 8; the library's per-stream copy buffer, as
- * for sgemm_op) and run on the fast path; the rest runs a plain kernel that
- * widens each element on load.  Calls on one stream must then come from one
- * host thread at a time.  SGEMM_PACK = 1 / -1 forces the copy on / off.  Small
+ * rounded up to multiples of 8; the stream's copy buffer, as for
+ * sgemm_op) and run on the fast path; the rest (and a call whose stream's
+ * buffer is held by another call at that moment) runs a plain kernel that
+ * widens each element on load.  SGEMM_PACK = 1 / -1 forces the copy on / off.  Small
  * tile grids split K and use the workspace described above (same rules:
  * allocated on first use per (device, stream), no split under graph
  * capture, deterministic).  Argument checks, layout rules and status codes
@@ -287,8 +309,9 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * multiple of 8 elements, which leaves problems after the first unaligned)
  * are copied into zero-padded buffers as in sgemm_lowp(), one launch per
  * operand for the whole batch (an operand of stride 0 once), when that
- * takes less time than the plain kernel and the copies fit in 4 GiB; the
- * rest run on the plain kernel.  Returns SGEMM_STATUS_*.
+ * takes less time than the plain kernel and the copies fit in
+ * SGEMM_MAX_COPY_BUFFER_BYTES; the rest run on the plain kernel.  Returns
+ * SGEMM_STATUS_*.
  */
 int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
                                const void *A, int lda, long long stride_a,
@@ -339,6 +362,25 @@ int sgemm_split_factor(int variant, int M, int N, int K);
  * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM on bad arguments.
  */
 int sgemm_tail_split(int variant, int M, int N, int K, int *tail_tiles);
+
+/*
+ * sgemm_workspace_bytes: device memory (bytes) the library holds on the
+ * current device for split-K workspaces and copy buffers; at most
+ * SGEMM_MAX_STREAM_WORKSPACES * SGEMM_WORKSPACE_BYTES + SGEMM_MAX_COPY_BUFFERS
+ * * SGEMM_MAX_COPY_BUFFER_BYTES.  SGEMM_STATUS_HIP_ERROR if the current
+ * device cannot be read.
+ */
+long long sgemm_workspace_bytes(void);
+
+/*
+ * sgemm_release_workspaces: free the workspaces and copy buffers the library
+ * holds on the current device, each after the kernels queued with it have
+ * finished (this call waits for them).  Buffers held by calls in progress on
+ * other host threads at that moment are left alone.  Later calls allocate
+ * again as needed.  Returns SGEMM_STATUS_OK or SGEMM_STATUS_HIP_ERROR (a
+ * buffer whose wait or free failed is kept and never reused).
+ */
+int sgemm_release_workspaces(void);
 
 /* Static text for a status code. */
 const char *sgemm_strerror(int status);
