@@ -415,3 +415,15 @@ def test_lowp_op_argument_checks():
             capi.SGEMM_STATUS_UNSUPPORTED
     assert f(bf, T, N_, 256, 256, 256, 1.0, AL, 256, AL, 256, 0.0, AL, 256, None, len(names)) == \
         capi.SGEMM_STATUS_INVALID_VARIANT
+
+
+def test_header_constants_match_binding():
+    """The limits the header states for the library's kept device memory are
+    the binding's (the C side asserts its own at compile time)."""
+    text = open(HEADER).read()
+    for name in ("SGEMM_WORKSPACE_BYTES", "SGEMM_MAX_STREAM_WORKSPACES", "SGEMM_MAX_COPY_BUFFERS",
+                 "SGEMM_MAX_COPY_BUFFER_BYTES"):
+        m = re.search(r"#define\s+%s\s+(.+?)(?:/\*|$)" % name, text, flags=re.M)
+        assert m, name
+        value = eval(m.group(1).replace("ll", ""), {})
+        assert value == getattr(capi, name), (name, value)

@@ -1,13 +1,13 @@
 """GPU cases with a unique exact answer, compared bit for bit against the
 oracle's exact value (identity, permutation, all-ones, small integers whose
 partial sums are exact in FP32 in any order, half-integer epilogue, beta == 0
-with NaN in C, K == 0)."""
+with NaN in C, alpha == 0, K == 0)."""
 import numpy as np
 import pytest
 
 import oracle
 from fp32_sgemm_tuning_amd import capi, sgemm
-from fp32_sgemm_tuning_amd.inputs import small_int_matrix
+from fp32_sgemm_tuning_amd.inputs import make_problem, small_int_matrix
 from gpu_util import padded_device, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
@@ -126,3 +126,32 @@ def test_k_zero(variant):
     sgemm(dA, dB, dC, alpha=3.0, beta=0.0, variant=variant)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(dC.cpu().numpy(), np.zeros((12, 20), np.float32))
+
+
+ALPHA0_VARIANTS = ["auto", "lean_dw_64x64x64_w4x1_splitk", "lean_dw_128x128x32_w2x2"]
+
+
+@pytest.mark.parametrize("name", ALPHA0_VARIANTS)
+@pytest.mark.parametrize("shape", [(300, 260, 517), (1024, 1024, 1024), (130, 67, 77)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_alpha_zero(name, shape):
+    """alpha == 0 with finite A and B follows the formula: C = beta*C_in +
+    0*(A B).  The product term is a signed zero, so the result is beta*C_in
+    rounded once to FP32 (with or without a fused multiply-add), which is the
+    oracle's fp64 value rounded to FP32: a unique answer, compared bit for
+    bit.  The default choice (16-byte kernels, split K at 1024^3) and the
+    any-alignment kernels, also on operands with odd leading dimensions 4
+    bytes off alignment (which the default choice sends to the 4-byte
+    kernels)."""
+    torch = torch_cuda()
+    M, N, K = shape
+    A, B, Cin = make_problem(M, N, K, seed=M + N + K, dist="normal", with_c=True)
+    expect = oracle.sgemm_ref(A, B, Cin, alpha=0.0, beta=-1.5).astype(np.float32)
+    variant = None if name == "auto" else {capi.sgemm_variant_name(v): v for v in VARIANTS}[name]
+    for lds, off in (((_up4(K), _up4(N), _up4(N)), 0), ((K + 1, N + 3, N + 1), 1)):
+        dA, _ = padded_device(A, lds[0], torch, offset=off)
+        dB, _ = padded_device(B, lds[1], torch, offset=off)
+        dC, _ = padded_device(Cin, lds[2], torch, offset=off)
+        sgemm(dA, dB, dC, alpha=0.0, beta=-1.5, variant=variant)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(dC.cpu().numpy(), expect, err_msg=f"{name} {shape} ld {lds} offset {off}")

@@ -3,10 +3,10 @@ element by element, |C - C_ref| <= 1e-3 + 1e-4 |C_ref|.
 
 Workloads: the five SGEMM configurations (256^3, 1024^3, 4096^3 with
 beta = 0 and with alpha = 0.5, beta = 2, the ragged 3001 x 4999 x 2047 with
-alpha = 1.5, beta = -0.5, and 512^3 / 2048^3 / 8192^3).  Sizes the oracle
-finishes in seconds are compared in full; 4096^3 and 8192^3 are compared on
-a seeded 4096-entry sample plus the four corners, and 4096^3 also on two
-full 128-row slabs (the first and the last tile row).
+alpha = 1.5, beta = -0.5, and 512^3 / 2048^3 / 8192^3).  Every configuration
+but 8192^3 is compared on every element (the compiled fp64 oracle takes
+about a second and a half for 4096^3 on 16 host threads); 8192^3 is compared
+on a seeded 4096-entry sample plus the four corners.
 """
 import numpy as np
 import pytest
@@ -18,8 +18,8 @@ from gpu_util import check_close, padded_device, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["sq256", "sq512", "sq1024", "sq2048", "ragged"]
-SAMPLED = ["sq4096", "sq4096_beta", "sq8192"]
+FULL = ["sq256", "sq512", "sq1024", "sq2048", "ragged", "sq4096", "sq4096_beta"]
+SAMPLED = ["sq8192"]
 
 
 def _run(w, torch):
@@ -50,11 +50,6 @@ def test_workload_sampled(name):
     I, J = sample_indices(w.M, w.N, w.seed)
     ref = oracle.sgemm_ref_sampled(A, B, I, J, Cin, alpha=w.alpha, beta=w.beta)
     check_close(C[I, J], ref, name + " sample")
-    if w.M == 4096:
-        for r0 in (0, w.M - 128):
-            sl = slice(r0, r0 + 128)
-            ref = oracle.sgemm_ref(A[sl], B, None if Cin is None else Cin[sl], alpha=w.alpha, beta=w.beta)
-            check_close(C[sl], ref, f"{name} rows {r0}..{r0 + 127}")
 
 
 try:
