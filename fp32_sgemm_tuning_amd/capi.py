@@ -17,11 +17,13 @@ SGEMM_STATUS_INVALID_VARIANT = -4
 SGEMM_STATUS_UNSUPPORTED = -5
 SGEMM_STATUS_INVALID_OP = -6
 SGEMM_STATUS_INVALID_DTYPE = -7
+SGEMM_STATUS_SCRATCH_TOO_SMALL = -8
 
 SGEMM_WORKSPACE_BYTES = 64 * 1024 * 1024 + 16 * 1024
 SGEMM_MAX_STREAM_WORKSPACES = 8
 SGEMM_MAX_COPY_BUFFERS = 2
 SGEMM_MAX_COPY_BUFFER_BYTES = 4 << 30
+SGEMM_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024 + 16 * 1024
 
 SGEMM_DTYPE_BF16 = 1
 SGEMM_DTYPE_F16 = 2
@@ -40,7 +42,8 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_select_variant", "sgemm_num_variants",
            "sgemm_last_hip_error", "sgemm_version", "sgemm_op", "sgemm_strided_batched", "sgemm_cm",
            "sgemm_cm_strided_batched", "sgemm_lowp", "sgemm_lowp_ex", "sgemm_lowp_select_variant",
            "sgemm_lowp_variant_name", "sgemm_lowp_split_factor", "sgemm_tail_split", "sgemm_lowp_op",
-           "sgemm_lowp_strided_batched", "sgemm_workspace_bytes", "sgemm_release_workspaces")
+           "sgemm_lowp_strided_batched", "sgemm_workspace_bytes", "sgemm_release_workspaces",
+           "sgemm_noalloc")
 
 _lib = None
 
@@ -71,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     gemm_args = [i, i, i, f, vp, i, vp, i, f, vp, i, vp]
     lib.sgemm.argtypes = gemm_args
     lib.sgemm.restype = i
+    lib.sgemm_noalloc.argtypes = gemm_args
+    lib.sgemm_noalloc.restype = i
     lib.sgemm_ex.argtypes = gemm_args + [i]
     lib.sgemm_ex.restype = i
     lib.sgemm_select_variant.argtypes = [i, i, i, vp, i, vp, i, f, vp, i]
@@ -124,6 +129,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
     """Raw C call; pointers and stream are integers (device addresses / hipStream_t)."""
     return load().sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    """sgemm with split-K partials in the library's static scratch: no allocation."""
+    return load().sgemm_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant):

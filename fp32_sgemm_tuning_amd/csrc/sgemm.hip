@@ -421,6 +421,62 @@ int finish(hipError_t launch, Lease &lease, hipStream_t stream) {
     return rel;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of sgemm_noalloc(), for callers that cannot allocate: the split-K
+// partial tiles and tile counters of a call live in this file-scope device
+// array, which exists from the moment the library's code is loaded on a
+// device until the process ends (one copy per device).  Its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept; host code uses only that address, never the array's
+// name, which on the host is a stand-in without device meaning.  The
+// counters a call uses are cleared by a small kernel on the call's stream
+// before the product (no hipMemsetAsync, so the calls can be captured into
+// a graph).  Every call on a device shares the array: calls that overlap
+// in time on one device race.
+constexpr size_t kScratchPartialBytes = 32u << 20;     // largest automatic plan: about 24.4 MiB
+constexpr size_t kScratchBytes = kScratchPartialBytes + kSplitMaxTiles * sizeof(unsigned);
+static_assert(kScratchBytes == (size_t)SGEMM_NOALLOC_SCRATCH_BYTES, "scratch size in sgemm.h");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void *>> g_scratch_ptr;   // (device, address of `scratch` there)
+
+// The device address of this device's `scratch`.
+int scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const auto &x : g_scratch_ptr)
+        if (x.first == dev) {
+            *out = x.second;
+            return SGEMM_STATUS_OK;
+        }
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+        return record_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress (scratch)");
+    g_scratch_ptr.emplace_back(dev, ptr);
+    *out = ptr;
+    return SGEMM_STATUS_OK;
+}
+
+__global__ void __launch_bounds__(256) clear_counters_kernel(unsigned *counters, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) counters[i] = 0u;
+}
+
+// Split K `splits` ways over the launch's `tiles` tiles in the scratch at
+// `ptr`: clears the counters on the stream and sets a.splits, a.ws and
+// a.counters.  The caller has checked that the partials fit.
+hipError_t attach_scratch(Args &a, int splits, long tiles, void *ptr, hipStream_t stream) {
+    a.splits = splits;
+    a.ws = static_cast<float *>(ptr);
+    a.counters = reinterpret_cast<unsigned *>(static_cast<char *>(ptr) + kScratchPartialBytes);
+    return launch_k(clear_counters_kernel, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), stream, a.counters,
+                    (int)tiles);
+}
+
 // Wave quantization: a grid of whole waves plus a last wave at most a
 // quarter full runs as two launches, the whole waves as they are and the
 // last wave with K split S ways, so that the last wave's few tiles spread
@@ -662,8 +718,46 @@ int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, i
     return small ? kVec64 : kVec;
 }
 
+// noalloc: split-K partials and counters in `scratch` (sgemm_noalloc), the
+// same plan as with the library's workspaces; a plan whose partials do not
+// fit is refused with SGEMM_STATUS_SCRATCH_TOO_SMALL before any launch.
+// The plan of run() with the split-K partials and counters in `scratch`:
+// K split over the whole grid (choose_splits), or the last wave split
+// (choose_tail_splits), or neither; nothing allocated.
+int run_noalloc(const VariantDesc &d, Args a, hipStream_t s) {
+    const long tiles = (long)a.tiles_m * a.tiles_n, rem = tiles % kTailSlots;
+    const size_t tile_bytes = (size_t)d.bm * d.bn * sizeof(float);
+    const int splits = d.split_k ? choose_splits(a.M, a.N, a.K, d.bm, d.bn, d.bk) : 1;
+    const int tail_splits = d.split_k && splits == 1 ? choose_tail_splits(d, a) : 1;
+    const size_t need = splits > 1 ? (size_t)splits * tiles * tile_bytes
+                                   : (tail_splits > 1 ? (size_t)tail_splits * rem * tile_bytes : 0);
+    if (need > kScratchPartialBytes) return SGEMM_STATUS_SCRATCH_TOO_SMALL;
+    if (need == 0) {
+        const hipError_t e = d.launch(a, s);
+        return e == hipSuccess ? SGEMM_STATUS_OK : record_hip_error(e, "kernel launch");
+    }
+    void *ptr = nullptr;
+    const int st = scratch_address(&ptr);
+    if (st != SGEMM_STATUS_OK) return st;
+    hipError_t e = hipSuccess;
+    if (splits > 1) {
+        e = attach_scratch(a, splits, tiles, ptr, s);
+        if (e == hipSuccess) e = d.launch(a, s);
+    } else {
+        // whole waves first, then the last wave with K split, as in run()
+        Args head = a, tail = a;
+        head.tile_count = (int)(tiles - rem);
+        tail.tile_base = (int)(tiles - rem);
+        tail.tile_count = (int)rem;
+        e = attach_scratch(tail, tail_splits, rem, ptr, s);
+        if (e == hipSuccess) e = d.launch(head, s);
+        if (e == hipSuccess) e = d.launch(tail, s);
+    }
+    return e == hipSuccess ? SGEMM_STATUS_OK : record_hip_error(e, "kernel launch");
+}
+
 int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-        float beta, float *C, int ldc, void *stream, int variant) {
+        float beta, float *C, int ldc, void *stream, int variant, bool noalloc = false) {
     int st = check_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != SGEMM_STATUS_OK) return st;
     if (variant < SGEMM_VARIANT_AUTO || variant >= kNumVariants) return SGEMM_STATUS_INVALID_VARIANT;
@@ -697,6 +791,7 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
     a.counters = nullptr;
     a.strideA = a.strideB = a.strideC = 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (noalloc) return run_noalloc(d, a, s);
     Lease lease;
     if (d.split_k) {
         const int ws = attach_workspace(a, choose_splits(M, N, K, d.bm, d.bn, d.bk), s, lease);
@@ -1261,6 +1356,11 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float
     return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO);
 }
 
+int sgemm_noalloc(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                  float beta, float *C, int ldc, void *stream) {
+    return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_VARIANT_AUTO, true);
+}
+
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream, int variant) {
     return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
@@ -1354,6 +1454,8 @@ const char *sgemm_strerror(int status) {
         case SGEMM_STATUS_UNSUPPORTED: return "variant needs 16-byte aligned pointers and leading dimensions";
         case SGEMM_STATUS_INVALID_OP: return "operation code is neither SGEMM_OP_N nor SGEMM_OP_T";
         case SGEMM_STATUS_INVALID_DTYPE: return "input type is neither SGEMM_DTYPE_BF16 nor SGEMM_DTYPE_F16";
+        case SGEMM_STATUS_SCRATCH_TOO_SMALL:
+            return "sgemm_noalloc: the split of K needs more scratch than SGEMM_NOALLOC_SCRATCH_BYTES";
         default: return "unknown status";
     }
 }

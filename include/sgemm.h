@@ -80,12 +80,14 @@ extern "C" {
 #define SGEMM_STATUS_INVALID_OP (-6)        /* an operation code other than SGEMM_OP_N / SGEMM_OP_T */
 
 #define SGEMM_STATUS_INVALID_DTYPE (-7)     /* sgemm_lowp: an input type other than SGEMM_DTYPE_BF16 / _F16 */
+#define SGEMM_STATUS_SCRATCH_TOO_SMALL (-8) /* sgemm_noalloc: the split of K needs more than its scratch */
 
 /* Device memory the library keeps between calls (see "Workspace" above). */
 #define SGEMM_WORKSPACE_BYTES (64ll * 1024 * 1024 + 16 * 1024)  /* one split-K workspace */
 #define SGEMM_MAX_STREAM_WORKSPACES 8       /* split-K workspaces kept per device */
 #define SGEMM_MAX_COPY_BUFFERS 2            /* copy buffers kept per device */
 #define SGEMM_MAX_COPY_BUFFER_BYTES (4ll << 30)  /* largest copy buffer; larger copies are not made */
+#define SGEMM_NOALLOC_SCRATCH_BYTES (32ll * 1024 * 1024 + 16 * 1024)  /* sgemm_noalloc's static scratch, per device */
 
 /* Input element types of sgemm_lowp. */
 #define SGEMM_DTYPE_BF16 1                  /* bfloat16: 1 sign, 8 exponent, 7 fraction bits */
@@ -138,6 +140,33 @@ int sgemm_ex(int M, int N, int K, float alpha,
              const float *B, int ldb,
              float beta, float *C, int ldc,
              void *stream, int variant);
+
+/*
+ * sgemm_noalloc: sgemm() for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, operation, variant choice and split of K as
+ * sgemm(), so the same bits; it never calls hipMalloc or hipFree, on the
+ * first call or later.  Its split-K partial tiles and tile counters live in
+ * a static device array of SGEMM_NOALLOC_SCRATCH_BYTES that the library's
+ * code holds on every device it is loaded on, until the process ends; the
+ * first call on a device looks up that array's address there.  Each call
+ * that splits K first clears the counters it uses with a small kernel on
+ * `stream` (no memset, so the call can be captured into a graph; under
+ * capture K is split as outside it).  Every call on a device shares that
+ * device's array and the array keeps the last call's contents: calls that
+ * overlap in time on one device (on different streams, or from different
+ * host threads) race and must be ordered by the caller; calls in order on
+ * one stream are safe.  A problem whose split of K needs more partial-tile
+ * storage than the array holds (32 MiB; the automatic choice needs at most
+ * about 24.4 MiB, unless SGEMM_SPLITK forces larger splits) returns
+ * SGEMM_STATUS_SCRATCH_TOO_SMALL with nothing enqueued.  Other statuses as
+ * for sgemm().
+ */
+int sgemm_noalloc(int M, int N, int K, float alpha,
+                  const float *A, int lda,
+                  const float *B, int ldb,
+                  float beta, float *C, int ldc,
+                  void *stream);
 
 /*
  * sgemm_select_variant: the variant id sgemm() would run for these arguments

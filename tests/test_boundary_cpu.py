@@ -61,7 +61,7 @@ def test_version_and_variants(lib):
     assert capi.sgemm_last_hip_error() == ""
 
 
-@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5, -6, -7])
+@pytest.mark.parametrize("status", [0, -1, -2, -3, -4, -5, -6, -7, -8])
 def test_strerror_known(status):
     s = capi.sgemm_strerror(status)
     assert s and s != "unknown status"
@@ -422,7 +422,7 @@ def test_header_constants_match_binding():
     the binding's (the C side asserts its own at compile time)."""
     text = open(HEADER).read()
     for name in ("SGEMM_WORKSPACE_BYTES", "SGEMM_MAX_STREAM_WORKSPACES", "SGEMM_MAX_COPY_BUFFERS",
-                 "SGEMM_MAX_COPY_BUFFER_BYTES"):
+                 "SGEMM_MAX_COPY_BUFFER_BYTES", "SGEMM_NOALLOC_SCRATCH_BYTES"):
         m = re.search(r"#define\s+%s\s+(.+?)(?:/\*|$)" % name, text, flags=re.M)
         assert m, name
         value = eval(m.group(1).replace("ll", ""), {})
