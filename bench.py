@@ -7,10 +7,17 @@
     python bench.py --sweep VARIANTS --sweep-sizes SIZES [--rounds R]
 
 A step is one SGEMM call (the whole path: one kernel launch over the
-device-resident A, B and C).  W untimed warm-up steps, then exactly K timed
+device-resident A, B and C).  The GPU idles at a low shader clock and takes
+tens of milliseconds of load to reach its steady clock; the clock cannot be
+locked on this machine (the pages lock theirs at 2002 MHz for the same
+reason, "gpu_matmul", Results).  So before the W warm-up steps the bench
+runs untimed steps for --settle-seconds of wall time (the count and time
+are in the JSON line).  Then W untimed warm-up steps, then exactly K timed
 steps between two device synchronisations.  Per-launch kernel time comes
-from HIP events recorded on the stream the kernel is launched on.  Prints
-one JSON line.
+from HIP events recorded on the stream the kernel is launched on.  The
+shader clock the power firmware reports (per XCD; its table refreshes about
+once a second) is read at idle, just before and just after the timed
+steps.  Prints one JSON line.
 
 --sweep times the given variant ids (comma separated; -1 = the automatic
 choice, "mm" = torch.mm in FP32 for context, "op:TN" and the like = sgemm_op
@@ -77,7 +84,7 @@ def measured_traffic(variant_name):
         return None
 
 
-def cpu_baseline(A, B, C_gpu, w, target_seconds):
+def cpu_baseline(A, B, Cin, C_gpu, w, target_seconds):
     """Time the oracle on leading row slabs of the problem until about
     target_seconds of CPU work; check the GPU rows of that slab."""
     import numpy as np
@@ -90,7 +97,7 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
     while spent < target_seconds and rows < w.M:
         r1 = min(rows + step, w.M)
         t0 = time.perf_counter()
-        ref = oracle.sgemm_ref(A[rows:r1], B, alpha=w.alpha, beta=w.beta)
+        ref = oracle.sgemm_ref(A[rows:r1], B, None if Cin is None else Cin[rows:r1], alpha=w.alpha, beta=w.beta)
         dt = time.perf_counter() - t0
         spent += dt
         flop += 2 * (r1 - rows) * w.N * w.K
@@ -101,13 +108,14 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
         if dt < target_seconds / 8:
             step *= 2
     # the same oracle on one thread, over a small leading slab (about a tenth
-    # of the time budget), for the per-core rate
+    # of the time budget): its rate, extrapolated to the whole problem
     oracle.set_threads(1)
     one_spent, one_rows = 0.0, 0
     while one_spent < target_seconds / 10 and one_rows < w.M:
         r_end = min(one_rows + 8, w.M)
         t0 = time.perf_counter()
-        oracle.sgemm_ref(A[one_rows:r_end], B, alpha=w.alpha, beta=w.beta)
+        oracle.sgemm_ref(A[one_rows:r_end], B, None if Cin is None else Cin[one_rows:r_end], alpha=w.alpha,
+                         beta=w.beta)
         one_spent += time.perf_counter() - t0
         one_rows = r_end
     oracle.set_threads(threads)
@@ -121,13 +129,52 @@ def cpu_baseline(A, B, C_gpu, w, target_seconds):
                   f"problem, fp64 oracle, {spent:.1f} s",
         "seconds": spent,
         "single_thread_gflops": one_rate,
-        "single_thread_sample": f"rows 0..{one_rows - 1}, {one_spent:.2f} s",
+        "single_thread_sample": f"rows 0..{one_rows - 1} of {w.M} ({100.0 * one_rows / w.M:.1f}% of C), "
+                                f"{one_spent:.2f} s on one thread; the rate is that slab's, not a full run",
+        "single_thread_full_problem_s_extrapolated": (2.0 * w.M * w.N * w.K / (one_rate * 1e9)) if one_rate else None,
         "cpu_model": cpu_model(),
         "cpu_simd": cpu_simd(),
         "nproc": os.cpu_count(),
         "parity_on_sample_max_err_over_tol": max_ratio,
         "parity_on_sample_ok": bool(max_ratio <= 1.0),
     }
+
+
+class GpuClock:
+    """The shader clock (MHz, mean over the XCDs) and socket power (W) that
+    the power firmware reports, through amdsmi; None where unavailable.
+    The firmware refreshes this table about once a second, so a reading
+    describes the last second or so, not an instant."""
+
+    def __init__(self, pci_bus_id=None):
+        self.handle = None
+        self.max_mhz = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if pci_bus_id is not None and len(handles) > 1:
+                handles = [h for h in handles
+                           if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == pci_bus_id] or handles
+            self.amdsmi = amdsmi
+            self.handle = handles[0]
+            self.max_mhz = amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX).get("max_clk")
+        except Exception:        # no amdsmi, or no permission: the line says null
+            self.handle = None
+
+    def read(self):
+        if self.handle is None:
+            return None
+        try:
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+            power = m.get("current_socket_power")
+            return {"sclk_mhz": round(sum(clks) / len(clks), 1) if clks else m.get("current_gfxclk"),
+                    "sclk_mhz_per_xcd": clks or None,
+                    "socket_power_w": power if isinstance(power, (int, float)) else None,
+                    "hotspot_c": m.get("temperature_hotspot")}
+        except Exception:
+            return None
 
 
 def cpu_model():
@@ -268,6 +315,7 @@ def main():
     ap.add_argument("--workload", default="sq4096")
     ap.add_argument("--variant", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-seconds", type=float, default=1.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--sweep", default=None)
@@ -309,16 +357,31 @@ def main():
     variant_name = capi.sgemm_variant_name(chosen)
     stream = torch.cuda.current_stream(dev)
 
+    props = torch.cuda.get_device_properties(dev)
+    clock = GpuClock(getattr(props, "pci_bus_id", None))
+    clock_idle = clock.read()
+
     # Correctness run on pristine C (beta != 0 reads it), kept for the CPU check.
     sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
     torch.cuda.synchronize()
     C_first = dC.cpu().numpy()
+
+    # Clock settle: untimed steps until the shader clock has left idle and
+    # held under load for a while (--settle-seconds of wall time).
+    settle_steps, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(8):
+            sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
+        settle_steps += 8
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
 
     for _ in range(args.warmup):
         sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clock_before = clock.read()
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -326,6 +389,7 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock_after = clock.read()
     kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     if args.copy_calibration_mib > 0:
@@ -364,7 +428,10 @@ def main():
             "parallelism": "single GPU",
         },
         "kernel_ms": {"mean": round(float(kernel_ms.mean()), 5), "median": round(float(np.median(kernel_ms)), 5),
-                      "min": round(float(kernel_ms.min()), 5), "max": round(float(kernel_ms.max()), 5)},
+                      "min": round(float(kernel_ms.min()), 5), "max": round(float(kernel_ms.max()), 5),
+                      "first_quarter_mean": round(float(kernel_ms[:max(1, len(kernel_ms) // 4)].mean()), 5),
+                      "last_quarter_mean": round(float(kernel_ms[-max(1, len(kernel_ms) // 4):].mean()), 5),
+                      "source": "HIP events around each call on the launching stream"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
@@ -372,12 +439,30 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(variant_name),
+            "traffic_source": "rocprofv3 FETCH_SIZE and WRITE_SIZE per launch, scaled by a device copy of "
+                              "known size, from " + os.path.relpath(TRAFFIC_FILE, ROOT) +
+                              " (null unless taken on these kernel sources and this variant)",
         },
-        "device": torch.cuda.get_device_name(dev),
+        "clock_settle": {"steps": settle_steps, "seconds": round(settle_s, 3),
+                         "why": "the shader clock idles near 100 MHz and ramps up over tens of ms of load; it "
+                                "cannot be locked here"},
+        "gpu_clock": {"idle": clock_idle, "before_timed": clock_before, "after_timed": clock_after,
+                      "max_sclk_mhz": clock.max_mhz,
+                      "source": "amdsmi gpu_metrics (power firmware, refreshed about once a second)"},
+        "device": {
+            "name": torch.cuda.get_device_name(dev),
+            "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "memory_bytes": props.total_memory,
+            # peak check: CUs x 256 FP32 MFMA FLOP per clock per CU x the
+            # highest shader clock the firmware allows
+            "peak_from_cus_and_max_sclk_tflops": (round(props.multi_processor_count * 256 * clock.max_mhz * 1e6
+                                                        / 1e12, 2) if clock.max_mhz else None),
+        },
         "kernel_source_sha256": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, C_first, w, args.cpu_seconds) if w.beta == 0.0 else None
+        out["cpu_baseline"] = cpu_baseline(A, B, Cin, C_first, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
