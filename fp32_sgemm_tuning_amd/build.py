@@ -1,6 +1,13 @@
-"""Build libsgemm.so (HIP, gfx950) in-tree with hipcc.
+"""Build libsgemm.so (HIP, gfx950) in-tree with hipcc, and its race-check
+twin libsgemm_poison.so.
 
     python -m fp32_sgemm_tuning_amd.build [--isa]
+
+libsgemm_poison.so is the same library with the lean FP32 and the 16-bit
+kernel units compiled with SGEMM_LDS_POISON=1: every LDS stage is filled
+with NaN bits as soon as its last reader has passed its barrier, so a
+missing barrier gives a wrong result (tests only; the C-ABI object is the
+normal build's).
 
 Flags: -O3 for gfx950 only, packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass warns
@@ -19,6 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgemm.so")
+POISON_LIB = os.path.join(PKG, "libsgemm_poison.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 # (source, extra flags): each translation unit is compiled on its own (in
 # parallel), then linked into one shared library.  The sgemm_lean*.hip units
@@ -33,6 +41,9 @@ UNITS = [
     ("sgemm_lowp.hip", VGPR_FORM),
 ]
 SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS]
+# units rebuilt with the LDS poison for the race-check library (the rest of
+# that library is the normal build's sgemm.o)
+POISON_UNITS = [(u, extra + ["-DSGEMM_LDS_POISON=1"]) for u, extra in UNITS if u != "sgemm.hip"]
 DEPS = SOURCES + [os.path.join(CSRC, h) for h in ("sgemm_kernels.hpp", "sgemm_lean.hpp")] + \
     [os.path.join(INCLUDE, "sgemm.h")]
 
@@ -48,27 +59,39 @@ HIP_FLAGS = [
 
 
 def needs_build() -> bool:
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(POISON_LIB)):
         return True
-    t = os.path.getmtime(LIB)
+    t = min(os.path.getmtime(LIB), os.path.getmtime(POISON_LIB))
     return any(os.path.getmtime(p) > t for p in DEPS)
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True, cwd=BUILD_DIR)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError(f"hipcc link failed ({r.returncode})")
+    os.replace(tmp, out)
 
 
 def build(verbose: bool = False, isa: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    procs, objs = [], []
-    for unit, extra in UNITS:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(unit)[0] + ".o")
+    procs, objs, poison_objs = [], [], []
+    jobs = [(u, extra, "") for u, extra in UNITS] + [(u, extra, "_poison") for u, extra in POISON_UNITS]
+    for unit, extra, suffix in jobs:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(unit)[0] + suffix + ".o")
         cmd = [HIPCC, *HIP_FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c",
                os.path.join(CSRC, unit), "-o", obj]
-        if isa:
+        if isa and not suffix:
             cmd += ["-save-temps"]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((unit, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
-                                             cwd=BUILD_DIR)))
-        objs.append(obj)
+        procs.append((unit + suffix, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                      text=True, cwd=BUILD_DIR)))
+        (poison_objs if suffix else objs).append(obj)
     report, failed = [], []
     for unit, p in procs:
         out, err = p.communicate()
@@ -81,14 +104,9 @@ def build(verbose: bool = False, isa: bool = False) -> str:
         sys.stderr.write(err)
     if failed:
         raise RuntimeError("hipcc failed on " + ", ".join(u for u, _ in failed))
-    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    r = subprocess.run(link, capture_output=True, text=True, cwd=BUILD_DIR)
-    if r.returncode != 0:
-        sys.stderr.write(r.stderr)
-        raise RuntimeError(f"hipcc link failed ({r.returncode})")
-    os.replace(tmp, LIB)
+    _link(objs, LIB, verbose)
+    # the race-check library: the normal C-ABI object and the poisoned kernels
+    _link([objs[0]] + poison_objs, POISON_LIB, verbose)
     return LIB
 
 

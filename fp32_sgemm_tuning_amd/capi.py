@@ -8,6 +8,9 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsgemm.so")
+# The race-check build (LDS stages poisoned with NaN between their last read
+# and their refill); for tests.
+POISON_LIB_PATH = os.path.join(PKG, "libsgemm_poison.so")
 
 SGEMM_STATUS_OK = 0
 SGEMM_STATUS_INVALID_DIM = -1
@@ -57,6 +60,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A separate handle on a build of the library at `path` (the race-check
+    build, for tests), with the signatures declared; not the module's own."""
     # libsgemm.so needs libamdhip64.so.7.  PyTorch-ROCm ships its own copy of
     # that runtime under the same soname; whichever copy is loaded first is
     # the one the whole process uses.  Import torch first so this library
@@ -122,7 +132,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_workspace_bytes.restype = ll
     lib.sgemm_release_workspaces.argtypes = []
     lib.sgemm_release_workspaces.restype = i
-    _lib = lib
     return lib
 
 

@@ -22,6 +22,27 @@ namespace sgemm_mi355x {
 // A buffer offset past every descriptor's range (ranges are below 2^31).
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// Race-check build.  With SGEMM_LDS_POISON set to 1 (a separate build of
+// these kernels, libsgemm_poison.so), every LDS stage is filled with NaN
+// bits (0xFFFFFFFF: NaN as FP32, BF16 and FP16) as soon as its last reader
+// has passed the barrier that frees it, and before the direct loads that
+// refill it are issued; the split-K ticket word holds the same bits between
+// its two barriers.  A barrier missing or misplaced then lets a wave read
+// NaN, or an invalid ticket, and the result goes wrong whatever the timing,
+// where the plain build would read stale or half-written values that happen
+// to be right most of the time.  The counterpart of running each thread as
+// far as it can go before switching, which makes a missing barrier give a
+// wrong answer every time ("Matmul I: tiling and shared memory", section 6,
+// note 3).
+#ifndef SGEMM_LDS_POISON
+#define SGEMM_LDS_POISON 0
+#endif
+constexpr unsigned kPoisonBits = 0xFFFFFFFFu;
+
+// s_waitcnt with lgkmcnt 0 and the other counters at their maximum: the
+// wave's LDS writes have landed (gfx9 encoding, as wait_vmcnt0 below).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // One direct load per lane into LDS: 16 or 4 bytes from the buffer at
 // voffset + soffset to the LDS address of `dst` plus 16 or 4 bytes per lane.
 // (The size must be a literal at the call, hence one function per size.)
@@ -76,7 +97,10 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
         __builtin_amdgcn_raw_buffer_store_b128(acc(c), slab, (c * NT + tid) * 16, y * TILE * 4, kDeviceScope);
     wait_vmcnt0();
     __syncthreads();
-    if (tid == 0) *ticket = atomicAdd(p.counters + tile_id, 1u);
+    if (tid == 0) {
+        if constexpr (SGEMM_LDS_POISON) *reinterpret_cast<volatile unsigned *>(ticket) = kPoisonBits;
+        *ticket = atomicAdd(p.counters + tile_id, 1u);
+    }
     __syncthreads();
     if (*ticket != (unsigned)(S - 1)) return false;
     // every partial, this block's own included, is read back in split
@@ -316,6 +340,24 @@ sgemm_lean_kernel(Args p) {
 
     typename T::Frags F[2];
 
+    // Race-check build: NaN bits into the LDS units this lane's direct loads
+    // of `stage` fill, landed before those loads are issued.
+    auto poison = [&](float *stage) {
+        if constexpr (SGEMM_LDS_POISON) {
+            const float nan = __uint_as_float(kPoisonBits);
+#pragma unroll
+            for (int i = 0; i < NA + NB; ++i) {
+                float *u = i < NA ? stage + (i * NWAVES + wave) * LSTEP
+                                  : stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP;
+                if constexpr (DW)
+                    u[lane] = nan;
+                else
+                    *reinterpret_cast<f32x4 *>(u + 4 * lane) = f32x4{nan, nan, nan, nan};
+            }
+            wait_lgkmcnt0();
+        }
+    };
+
     // one K tile held in stage SC (compile time); loads of tile t+1 go to
     // the other stage
     auto tile = [&](int t, auto sc) {
@@ -324,6 +366,7 @@ sgemm_lean_kernel(Args p) {
         const float *cs = lds + SC * T::STAGE;
         float *ns = lds + SN * T::STAGE;
         const int t_next = min(t + 1, t_end - 1);
+        poison(ns);     // its last reads were before the barrier that ended the previous tile
         auto section = [&](auto hc) {
             constexpr int h = decltype(hc)::value;
             constexpr int g_lo = h * PER < NA + NB ? h * PER : NA + NB;
@@ -349,6 +392,8 @@ sgemm_lean_kernel(Args p) {
     };
 
     if (t_end > t_begin) {
+        poison(lds);
+        poison(lds + T::STAGE);
         if (tail && t_begin == 0) {
             issue_remainder(lds);
         } else {

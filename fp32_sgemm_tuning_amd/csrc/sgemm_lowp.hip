@@ -351,6 +351,17 @@ sgemm_lowp_kernel(Args p) {
         wait_vm_lgkm0<(NSTAGE - 2) * L>();
         __builtin_amdgcn_s_barrier();
     };
+    // Race-check build (SGEMM_LDS_POISON, see sgemm_lean.hpp): NaN bits into
+    // the LDS units this lane's loads of stage `st` fill, landed before those
+    // loads are issued.
+    auto poison = [&](int st) {
+        if constexpr (SGEMM_LDS_POISON) {
+#pragma unroll
+            for (int g = 0; g < L; ++g)
+                *reinterpret_cast<i32x4 *>(lds + (dst(st, g) - lds0) + 16 * lane) = i32x4{-1, -1, -1, -1};
+            wait_lgkmcnt0();
+        }
+    };
     // BK = 64: one K tile in stage SC.  Step 0 reads step 1 of the same
     // stage.  Step 1 runs its first MFMAs, syncs, then reads step 0 of tile
     // t+1 and loads tile t+NSTAGE into SC.  BK = 32: the one step of tile t
@@ -365,11 +376,17 @@ sgemm_lowp_kernel(Args p) {
         auto none = [&](int) {};
         if constexpr (BK == 64) {
             step(IntC<0>{}, cs, 1, IntC<0>{}, IntC<0>{}, [&]() {}, none);
-            step(IntC<1>{}, ns, 0, IntC<QSYNC>{}, IntC<L>{}, sync_tile, [&](int g) { issue_one(t + NSTAGE, SC, g); });
+            step(IntC<1>{}, ns, 0, IntC<QSYNC>{}, IntC<L>{},
+                 [&]() {
+                     sync_tile();
+                     poison(SC);     // every wave's reads of SC are done
+                 },
+                 [&](int g) { issue_one(t + NSTAGE, SC, g); });
         } else {
             step(pc, ns, 0, IntC<QSYNC>{}, IntC<0>{},
                  [&]() {
                      sync_tile();
+                     poison(SC);
 #pragma unroll
                      for (int g = 0; g < L; ++g) issue_one(t + NSTAGE, SC, g);
                  },
@@ -387,6 +404,7 @@ sgemm_lowp_kernel(Args p) {
             // SIMD one wave multiplies while the other reads.  Every phase
             // ends with a barrier of all eight waves.
             const int group = wave >> 2;
+            static_for<0, NSTAGE>([&](auto sc) { poison(decltype(sc)::value); });
             if (remainder_first) {
                 issue_remainder();
             } else {
@@ -416,6 +434,7 @@ sgemm_lowp_kernel(Args p) {
 #pragma unroll
                     for (int r = 0; r < NRB; ++r) read_b(r, cs, ks, pb[ks]);
                 }
+                poison((SC + NSTAGE - 1) % NSTAGE);
 #pragma unroll
                 for (int g = 0; g < L; ++g) issue_one(t + NSTAGE - 1, (SC + NSTAGE - 1) % NSTAGE, g);
                 __builtin_amdgcn_sched_barrier(0);
@@ -445,6 +464,7 @@ sgemm_lowp_kernel(Args p) {
             wait_vmcnt0();
         }
     } else if (ntiles > 0) {
+        static_for<0, NSTAGE>([&](auto sc) { poison(decltype(sc)::value); });
         if (remainder_first) {
             issue_remainder();
         } else {

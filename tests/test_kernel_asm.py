@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc")
 
 
-def _device_asm(units, tmp_path):
+def _device_asm(units, tmp_path, extra=()):
     """Device assembly of each unit, built in parallel: {unit: text}."""
     from fp32_sgemm_tuning_amd import build as b
     hipcc = b.HIPCC if os.path.exists(b.HIPCC) else shutil.which("hipcc")
@@ -33,8 +33,8 @@ def _device_asm(units, tmp_path):
     procs = {}
     for unit in units:
         out = os.path.join(str(tmp_path), unit + ".s")
-        cmd = [hipcc, *b.HIP_FLAGS, *dict(b.UNITS)[unit], "--cuda-device-only", "-S", os.path.join(CSRC, unit),
-               "-o", out]
+        cmd = [hipcc, *b.HIP_FLAGS, *dict(b.UNITS)[unit], *extra, "--cuda-device-only", "-S",
+               os.path.join(CSRC, unit), "-o", out]
         procs[unit] = (out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
     texts = {}
     for unit, (out, proc) in procs.items():
@@ -121,3 +121,18 @@ def test_split_k_loop_keeps_loads_in_flight(lean_asm):
     # kernel before the ticket moved into the kernel's LDS buffer)
     bad = {k: v for k, v in split.items() if v[1] > 4}
     assert not bad, bad
+
+
+def test_race_check_build_poisons_the_stages(lean_asm, tmp_path):
+    """The lean kernels fill LDS only through direct loads, so the normal
+    build has no LDS write instruction in them at all; the race-check build
+    (SGEMM_LDS_POISON=1, as libsgemm_poison.so is built) writes the NaN
+    bits with ds_write before every stage's refill."""
+    def ds_writes(asm):
+        return {name: sum("ds_write" in x for x in lines) for name, lines in _kernels(asm)
+                if "sgemm_lean_kernel" in name}
+    plain = ds_writes(lean_asm["sgemm_lean.hip"])
+    poisoned = ds_writes(_device_asm(["sgemm_lean.hip"], tmp_path, ["-DSGEMM_LDS_POISON=1"])["sgemm_lean.hip"])
+    assert plain and set(plain) == set(poisoned)
+    assert all(n == 0 for n in plain.values()), plain
+    assert all(n > 0 for n in poisoned.values()), poisoned
