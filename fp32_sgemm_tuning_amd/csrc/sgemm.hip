@@ -72,7 +72,12 @@ struct Knobs {
     int xcd_remap = 1;
     int splitk = 0;         // 0: automatic split-K factor; >= 1: forced
     int pack = 0;           // unaligned transposed operands: 0 automatic, 1 always copy, -1 never
+    int tail_fill = 25;     // last-wave split: largest fill of the last wave split, percent of its slots
     Knobs() {
+        if (const char *s = getenv("SGEMM_TAIL_FILL")) {
+            int v = atoi(s);
+            if (v >= 0 && v <= 100) tail_fill = v;
+        }
         if (const char *s = getenv("SGEMM_PACK")) {
             int v = atoi(s);
             if (v >= -1 && v <= 1) pack = v;
@@ -655,7 +660,8 @@ int choose_tail_splits(const VariantDesc &d, const Args &a) {
     if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
     const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
     const long rem = tiles % kTailSlots;
-    if (tiles < kTailSlots || rem == 0 || rem * 4 > kTailSlots || rem > kSplitMaxTiles) return 1;
+    if (tiles < kTailSlots || rem == 0 || rem * 100 > kTailSlots * knobs().tail_fill || rem > kSplitMaxTiles)
+        return 1;
     long s = kTailSlots / rem;
     s = std::min(s, ceil_div(a.K, d.bk) / 3);
     s = std::min(s, 16L);

@@ -169,9 +169,11 @@ __device__ __forceinline__ bool split_reduce(const Args &p, int tile_id, int tid
 //     inside its operand;
 //   - elements of rows past M or columns past N get an offset beyond every
 //     range (set once, before the K loop);
-//   - a K remainder kr = K % BK is taken as the first tile, k in [0, kr), whose
-//     elements at k >= kr get that offset too, and the full tiles follow from
-//     k = kr.
+//   - a K remainder kr = K % BK is the last kr columns of A and rows of B,
+//     k in [K - kr, K), taken as the first tile, whose elements past K get
+//     that offset too; the full tiles follow, from k = 0, so they keep the
+//     operands' own alignment (from k = kr every row segment of A would
+//     start kr floats off a 16-byte boundary).
 // Out-of-range loads access no memory and deposit zeros, which is what the
 // K remainder needs (A's padding past column K may hold anything).  Rows past
 // M and columns past N only reach accumulators that the guarded epilogue
@@ -267,10 +269,11 @@ sgemm_lean_kernel(Args p) {
         const int e = TB ? col * (int)p.ldb + r : r * (int)p.ldb + col;
         offB[i] = (EDGE && n0 + col >= p.N) ? kOutOfRange : 4u * (unsigned)e;
     }
-    // K remainder taken first (EDGE only): tile 0 covers k in [0, kr), full
-    // tiles follow from k = kr.
+    // K remainder taken first (EDGE only): tile 0 covers k in [K - kr, K),
+    // full tiles t >= 1 cover k from (t - 1) * BK.
     const int kr = EDGE ? p.K % BK : 0;
     const int tail = kr != 0;
+    const long kfull = (long)p.K - kr;
     const int ntiles = p.K / BK + tail;
     // K tiles of this block: all of them, or this split's share
     int t_begin = 0, t_end = ntiles;
@@ -298,11 +301,11 @@ sgemm_lean_kernel(Args p) {
         return __builtin_amdgcn_make_buffer_rsrc((void *)(corner + kfirst * kstride), (short)0, range, 0x00020000);
     };
 
-    // Loads of tile t >= tail (a full tile, k from kr + (t - tail) * BK).
+    // Loads of tile t >= tail (a full tile, k from (t - tail) * BK).
     // (The explicit int conversions matter: with the array element passed as
     // is, the host pass drops the kernel and its launch stub.)
     auto issue_one = [&](int t, float *stage, int i) {
-        const long kfirst = kr + (long)max(t - tail, 0) * BK;
+        const long kfirst = (long)max(t - tail, 0) * BK;
         if (i < NA)
             dma<DW>(tile_rsrc(cornerA, kstrideA, kfirst, rangeA), (lds_ptr)(stage + (i * NWAVES + wave) * LSTEP),
                     (int)offA[i], 0);
@@ -310,10 +313,11 @@ sgemm_lean_kernel(Args p) {
             dma<DW>(tile_rsrc(cornerB, kstrideB, kfirst, rangeB),
                     (lds_ptr)(stage + BM * BK + ((i - NA) * NWAVES + wave) * LSTEP), (int)offB[i - NA], 0);
     };
-    // Loads of the K remainder tile, on descriptors based at k = 0.
+    // Loads of the K remainder tile, on descriptors based at k = K - kr
+    // (the ranges reach past K, where every offset is out of range).
     auto issue_remainder = [&](float *stage) {
-        const __amdgpu_buffer_rsrc_t rA0 = tile_rsrc(cornerA, kstrideA, 0, rangeA);
-        const __amdgpu_buffer_rsrc_t rB0 = tile_rsrc(cornerB, kstrideB, 0, rangeB);
+        const __amdgpu_buffer_rsrc_t rA0 = tile_rsrc(cornerA, kstrideA, kfull, rangeA);
+        const __amdgpu_buffer_rsrc_t rB0 = tile_rsrc(cornerB, kstrideB, kfull, rangeB);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             int m, k;

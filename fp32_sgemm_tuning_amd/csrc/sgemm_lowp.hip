@@ -192,8 +192,11 @@ sgemm_lowp_kernel(Args p) {
         offB[i] = out ? kOutOfRange : 2u * (unsigned)(TB ? x * (int)p.ldb + 8 * c : k * (int)p.ldb + 8 * c);
     }
 
-    const int kr = EDGE ? p.K % BK : 0;                     // K remainder, taken first
+    // K remainder: k in [K - kr, K), taken first; full tiles from k = 0, on
+    // the operands' own alignment (as in the lean FP32 kernel)
+    const int kr = EDGE ? p.K % BK : 0;
     const int tail = kr != 0;
+    const long kfull = (long)p.K - kr;
     // K tiles of this block: all of them, or this split's share; ntiles
     // counts this block's tiles, t_first is the first one's index
     int t_first = 0, ntiles = p.K / BK + tail;
@@ -225,7 +228,7 @@ sgemm_lowp_kernel(Args p) {
     // issues the same number of loads and the vmcnt waits stay constant.
     auto issue_one = [&](int t, int st, int g) {
         const bool live = t < ntiles;
-        const long kfirst = kr + (long)max(t_first + t - tail, 0) * BK;
+        const long kfirst = (long)max(t_first + t - tail, 0) * BK;
         if (g < NA)
             dma16_lowp(cornerA + 2 * kfirst * kstrideA, live ? rangeA : 0, dst(st, g), (int)offA[g]);
         else
@@ -236,13 +239,13 @@ sgemm_lowp_kernel(Args p) {
         for (int i = 0; i < NA; ++i) {
             int x, c, k;
             coords(!TA, ACH, i, x, c, k);
-            dma16_lowp(cornerA, rangeA, dst(0, i), (int)(k < kr ? offA[i] : kOutOfRange));
+            dma16_lowp(cornerA + 2 * kfull * kstrideA, rangeA, dst(0, i), (int)(k < kr ? offA[i] : kOutOfRange));
         }
 #pragma unroll
         for (int i = 0; i < NBL; ++i) {
             int x, c, k;
             coords(TB, BCH, i, x, c, k);
-            dma16_lowp(cornerB, rangeB, dst(0, NA + i), (int)(k < kr ? offB[i] : kOutOfRange));
+            dma16_lowp(cornerB + 2 * kfull * kstrideB, rangeB, dst(0, NA + i), (int)(k < kr ? offB[i] : kOutOfRange));
         }
     };
 
