@@ -27,8 +27,9 @@ sgemm_lowp_ex variant V, "lowp:bf16:op:TN" and the like run sgemm_lowp_op
 with the operands stored transposed as named), "mm:bf16" / "mm:f16" =
 torch.mm in that type, 16-bit output, for context) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
-every variant alike, and prints one JSON line per (size, variant) with the
-median kernel time.  It is the evidence behind the automatic tile choice.
+every variant alike (after half a second of untimed calls per size, for
+the clock), and prints one JSON line per (size, variant) with the median
+kernel time.  It is the evidence behind the automatic tile choice.
 
 The CPU baseline times the fp64 oracle on a bounded slab of rows of the
 same problem (host cores, OpenMP over rows) and checks the GPU result on
@@ -212,7 +213,7 @@ def parse_shape(text):
     return tuple(parts)
 
 
-def sweep(variants, sizes, rounds):
+def sweep(variants, sizes, rounds, settle_s=0.5):
     import statistics
 
     import torch
@@ -289,6 +290,12 @@ def sweep(variants, sizes, rounds):
                 print(json.dumps({"sweep": label(v), "variant": v, "shape": f"{M}x{N}x{K}",
                                   "skipped": str(e)}), flush=True)
         torch.cuda.synchronize()
+        # clock settle: the usable variants in turn for settle_s of wall time
+        t_settle = time.perf_counter()
+        while usable and time.perf_counter() - t_settle < settle_s:
+            for v in usable:
+                run(v)
+            torch.cuda.synchronize()
         times = {v: [] for v in usable}
         for _ in range(rounds):
             for v in usable:
@@ -330,8 +337,20 @@ def main():
         sys.exit(2)
 
     if args.sweep is not None:
-        variants = [v if v == "mm" or ":" in v else int(v) for v in args.sweep.split(",")]
-        sweep(variants, [parse_shape(x) for x in args.sweep_sizes.split(",")], args.rounds)
+        def variant_arg(v):
+            if v == "mm" or ":" in v:
+                return v
+            try:
+                return int(v)
+            except ValueError:        # a variant name
+                from fp32_sgemm_tuning_amd import capi
+                names = {capi.sgemm_variant_name(i): i for i in capi.all_variants()}
+                if v not in names:
+                    raise SystemExit(f"unknown variant {v!r}")
+                return names[v]
+        variants = [variant_arg(v) for v in args.sweep.split(",")]
+        sweep(variants, [parse_shape(x) for x in args.sweep_sizes.split(",")], args.rounds,
+              settle_s=min(args.settle_seconds, 0.5))
         return
 
     import numpy as np

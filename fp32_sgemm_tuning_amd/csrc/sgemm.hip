@@ -72,7 +72,7 @@ struct Knobs {
     int xcd_remap = 1;
     int splitk = 0;         // 0: automatic split-K factor; >= 1: forced
     int pack = 0;           // unaligned transposed operands: 0 automatic, 1 always copy, -1 never
-    int tail_fill = 25;     // last-wave split: largest fill of the last wave split, percent of its slots
+    int tail_fill = 100;    // last-wave split: largest fill of the last wave split, percent of its slots
     Knobs() {
         if (const char *s = getenv("SGEMM_TAIL_FILL")) {
             int v = atoi(s);
@@ -192,22 +192,31 @@ static_assert(kSplitWorkspaceBytes == (size_t)SGEMM_WORKSPACE_BYTES, "workspace 
 // 157.3 TFLOP/s peak):
 //   - the busiest CU: a CU runs its blocks at about the same aggregate rate
 //     whether it holds one or two, so ceil(tiles * S / 256) blocks of
-//     ceil(kt / S) steps and about half a step of pipeline fill each;
+//     ceil(kt / S) steps and kBlockFixed steps of their own (first loads,
+//     pipeline fill, epilogue) each;
 //   - a floor set by the operand traffic of the whole grid, which every S
 //     moves alike: 0.15 * tiles * kt * (bm + bn) / (bm * bn) steps;
 //   - the partials, written and read back once each (8 * S * bm * bn bytes
-//     per tile at about 5 TB/s): 0.49 * S * tiles / bk steps.
-// The cost is the larger of the first two plus the third.  S is the factor
-// of least cost, with at least four K tiles per split, at most 16, within
-// the workspace, taken when it costs at most 95% of no split.  The floor's
-// and the fill's constants are fitted to measured sweeps (19 shapes from
-// 16 to 484 tiles of 64x64, S = 1 to 16): the factor chosen is the fastest
-// measured one, or within 6% of it, on every shape.  SGEMM_SPLITK forces a
-// factor (clamped to the K tiles and the workspace) for sweeps.
+//     per tile at about 5 TB/s): 0.49 * S * tiles / bk steps;
+//   - a fixed cost of splitting at all (the device-scope hand-off, the
+//     ticket and the serial read-back before the epilogue): kSplitFixed.
+// The cost is the larger of the first two plus the others.  S is the
+// factor of least cost, with at least four K tiles per split, at most 16,
+// within the workspace, taken when it costs at most 95% of no split.  The
+// floor's constant is fitted to measured sweeps (19 shapes from 16 to 484
+// tiles of 64x64, S = 1 to 16); the two fixed costs to the split and
+// unsplit 64x64x64 kernel timed side by side on 12 small grids, where
+// they make every split decision the measured one (512^3, where S = 2
+// measured no faster than no split, 1216^2 x 2048 and 1152^2 x 2048, where
+// S = 2 measured 10% faster, up to 256^2 x 16384).
+// SGEMM_SPLITK forces a factor (clamped to the K tiles and the workspace)
+// for sweeps.
+constexpr double kBlockFixed = 3.0;
+constexpr double kSplitFixed = 3.0;
 double split_cost(long tiles, long kt, long s, int bm, int bn, int bk) {
-    const double busiest = (double)ceil_div(tiles * s, kNumCUs) * ((double)ceil_div(kt, s) + 0.5);
+    const double busiest = (double)ceil_div(tiles * s, kNumCUs) * ((double)ceil_div(kt, s) + kBlockFixed);
     const double floor = 0.15 * (double)(tiles * kt) * (double)(bm + bn) / ((double)bm * bn);
-    const double partials = s > 1 ? 0.49 * (double)(s * tiles) / bk : 0.0;
+    const double partials = s > 1 ? 0.49 * (double)(s * tiles) / bk + kSplitFixed : 0.0;
     return (busiest > floor ? busiest : floor) + partials;
 }
 
@@ -482,12 +491,23 @@ hipError_t attach_scratch(Args &a, int splits, long tiles, void *ptr, hipStream_
                     (int)tiles);
 }
 
-// Wave quantization: a grid of whole waves plus a last wave at most a
-// quarter full runs as two launches, the whole waves as they are and the
-// last wave with K split S ways, so that the last wave's few tiles spread
-// over the whole chip.  Workgroup slots: two per compute unit (kTailSlots).
-// S: up to the slots over the tiles left, at least three K tiles per split,
-// at most 16, within the workspace; 1 = one launch.
+// Wave quantization: a grid of whole waves plus a partly filled last wave
+// can run as two launches, the whole waves as they are and the last wave
+// with K split S ways, so that the last wave's few tiles spread over the
+// whole chip.  Workgroup slots: two per compute unit (kTailSlots).  Cost of
+// the last wave in the K-tile steps of split_cost: unsplit, its `rem` tiles
+// run one per CU, kt + kBlockFixed steps; split S ways, ceil(rem * S / 256)
+// blocks of ceil(kt / S) + kBlockFixed steps on the busiest CU, plus the
+// partials (as in split_cost) and a fixed kTailFixed for the second launch
+// and the hand-off.  S (at most 16, at least three K tiles per split, within
+// the workspace) is the factor of least cost, taken when it costs at most
+// 95% of the unsplit last wave; 1 = one launch.  kTailFixed is fitted to the
+// split and unsplit 64x64x64 kernel timed side by side with the earlier rule
+// of splitting every last wave up to a quarter full (1536^3 +4%,
+// 2560x2624x2560 +2%, 1600^3 level, 1552x1572x1000 -7%, and 2944^2 x 256 on
+// 64x64x32 tiles -16%): 4.5 to 13 steps, 8 taken, which splits the first
+// two and neither of the last two.  SGEMM_TAIL_FILL (percent) caps the fill
+// of a last wave that may be split, for sweeps.
 struct VariantDesc;
 int choose_tail_splits(const VariantDesc &d, const Args &a);
 
@@ -656,17 +676,27 @@ constexpr VariantDesc kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
+constexpr double kTailFixed = 8.0;
 int choose_tail_splits(const VariantDesc &d, const Args &a) {
     if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
     const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
     const long rem = tiles % kTailSlots;
     if (tiles < kTailSlots || rem == 0 || rem * 100 > kTailSlots * knobs().tail_fill || rem > kSplitMaxTiles)
         return 1;
-    long s = kTailSlots / rem;
-    s = std::min(s, ceil_div(a.K, d.bk) / 3);
-    s = std::min(s, 16L);
-    s = std::min(s, (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem)));
-    return s < 2 ? 1 : (int)s;
+    const long kt = ceil_div(a.K, d.bk);
+    const long fit = (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem));
+    const double base = (double)ceil_div(rem, kNumCUs) * ((double)kt + kBlockFixed);
+    long best = 1;
+    double best_cost = base;
+    for (long s = 2; s <= 16 && s <= kt / 3 && s <= fit; ++s) {
+        const double cost = (double)ceil_div(rem * s, kNumCUs) * ((double)ceil_div(kt, s) + kBlockFixed) +
+                            0.49 * (double)(s * rem) / d.bk + kTailFixed;
+        if (cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return best_cost <= 0.95 * base ? (int)best : 1;
 }
 
 // Variants the automatic choice uses (indices into kVariants, looked up by

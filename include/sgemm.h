@@ -371,9 +371,10 @@ const char *sgemm_lowp_variant_name(int variant);
  * "Workspace" above; environment variable SGEMM_SPLITK = S forces S for
  * sweeps).  Only grids of fewer than 512 tiles split; the factor (at most
  * 16, at least four K tiles per split) is the one of least modelled time:
- * the busiest compute unit's share of blocks, bounded below by the grid's
- * operand traffic, plus writing and reading back the partial tiles; taken
- * when that is at most 95% of the unsplit time.  Always 1 for variants
+ * the busiest compute unit's share of blocks (each with a fixed cost of its
+ * own), bounded below by the grid's operand traffic, plus writing and
+ * reading back the partial tiles and a fixed cost of splitting; taken when
+ * that is at most 95% of the unsplit time.  Always 1 for variants
  * without split-K.  No HIP call.  Returns the factor,
  * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM (negative sizes).
  */
@@ -383,10 +384,12 @@ int sgemm_split_factor(int variant, int M, int N, int K);
  * sgemm_tail_split: the split of the last wave that sgemm_ex() with this
  * variant would make for an M x N x K problem with packed leading dimensions
  * outside graph capture (no HIP call).  A split-capable variant whose grid
- * is whole waves of tiles (two workgroups per compute unit) plus a last wave
- * at most a quarter full, and that does not split K already, runs as two
- * launches on the stream: the whole waves, then the last wave's tiles with K
- * split S ways.  Returns S (1: a single launch) and, if tail_tiles is not
+ * is whole waves of tiles (two workgroups per compute unit) plus a partly
+ * filled last wave, and that does not split K already, runs as two launches
+ * on the stream when the same cost model as sgemm_split_factor (plus a fixed
+ * cost for the second launch) says that saves at least 5%: the whole waves,
+ * then the last wave's tiles with K split S ways.  Returns S (1: a single
+ * launch) and, if tail_tiles is not
  * NULL, stores the number of tiles in the second launch (0 when S is 1);
  * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM on bad arguments.
  */

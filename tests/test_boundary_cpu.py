@@ -175,7 +175,9 @@ def test_split_factors():
     assert f(v64, 1152, 1152, 2048) == 2           # 324 tiles
     assert f(v64, 1280, 1280, 2048) == 1           # 400 tiles: too little to gain
     assert f(v64, 1024, 1024, 8192) == 1           # 256 tiles
-    assert f(v64, 256, 256, 8192) == 15
+    assert f(v64, 256, 256, 8192) == 16            # 128 K tiles: eight per split
+    assert f(v64, 512, 512, 512) == 1              # measured no faster split: fixed costs dominate
+    assert f(v64, 1216, 1216, 2048) == 2           # measured 10% faster split
     assert f(v64, 2048, 2048, 64) == 1             # whole waves: left to the last-wave split
     for v in (v128, v64):
         for (M, N, K) in [(100, 100, 10000), (300, 200, 500), (1, 1, 100000), (900, 700, 3000)]:
@@ -366,29 +368,34 @@ def test_lowp_split_factors():
 
 
 def test_tail_split_plan():
-    """A grid of whole waves (512 workgroup slots) plus a last wave at most a
-    quarter full runs as two launches, the last wave's tiles with K split (at
-    least three K tiles per split); the any-alignment 64x64 kernel too."""
+    """A grid of whole waves (512 workgroup slots) plus a partly filled last
+    wave runs as two launches, the last wave's tiles with K split (at least
+    three K tiles per split), where the cost model says that saves 5%: the
+    plans measured faster split (1536^3, 2560x2624x2560) split, those
+    measured slower (1550x1572x1000, 2944^2 x 256) do not; the
+    any-alignment 64x64 kernel too."""
     names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
     v64, v128 = names["lean_64x64x64_w4x1_splitk"], names["lean_128x128x32_w2x2_splitk"]
     t = capi.sgemm_tail_split
-    assert t(v64, 1536, 1536, 1536) == (8, 64)      # 576 tiles = 512 + 64
-    assert t(v64, 1550, 1572, 1000) == (4, 113)     # 625 tiles, 16 K tiles
+    assert t(v64, 1536, 1536, 1536) == (4, 64)      # 576 tiles = 512 + 64
+    assert t(v64, 2560, 2624, 2560) == (2, 104)     # 1640 tiles = 3 waves + 104
+    assert t(v64, 1550, 1572, 1000) == (1, 0)       # 625 tiles, 16 K tiles: too short to gain
     assert t(v64, 1550, 1570, 1000) == (1, 0)       # N not a multiple of 4: no lean kernel
-    assert t(v128, 2944, 2944, 256) == (2, 17)      # 529 tiles, 8 K tiles
+    assert t(v128, 2944, 2944, 256) == (1, 0)       # 529 tiles, 8 K tiles: too short
+    assert t(v128, 3072, 3072, 3072) == (4, 64)     # 576 tiles of 128x128, 96 K tiles
     assert t(v64, 2048, 2048, 2048) == (1, 0)       # whole waves
     assert t(v128, 4096, 4096, 4096) == (1, 0)
     assert t(v64, 1664, 1664, 1664) == (1, 0)       # 676 tiles: last wave a third full
-    assert t(v64, 1600, 1600, 1600) == (4, 113)     # 625 tiles: 113 left, 25 K tiles
+    assert t(v64, 1600, 1600, 1600) == (2, 113)     # 625 tiles: 113 left, 25 K tiles
     assert t(v64, 1792, 1792, 1792) == (1, 0)       # 784 tiles: last wave over half full
     assert t(v64, 2944, 2944, 128) == (1, 0)        # 2116 tiles, 2 K tiles
     assert t(v64, 512, 512, 4096) == (1, 0)         # a small grid splits K as a whole instead
     assert t(v64, 1536, 1536, 64) == (1, 0)         # one K tile
     assert t(names["lean_64x64x64_w4x1"], 1536, 1536, 1536) == (1, 0)   # no split-K form
     vdw = names["lean_dw_64x64x64_w4x1_splitk"]
-    assert t(vdw, 1535, 1537, 1535) == (5, 88)      # 600 tiles = 1 wave + 88
-    assert t(vdw, 3001, 4999, 2047) == (1, 0)       # 3713 tiles = 7 waves + 129: over a quarter
-    assert t(vdw, 1536, 1536, 1535) == (8, 64)      # K not a multiple of 4: the 4-byte kernel takes it
+    assert t(vdw, 1535, 1537, 1535) == (2, 88)      # 600 tiles = 1 wave + 88
+    assert t(vdw, 3001, 4999, 2047) == (1, 0)       # 3713 tiles = 7 waves + 129: two per CU would remain
+    assert t(vdw, 1536, 1536, 1535) == (4, 64)      # K not a multiple of 4: the 4-byte kernel takes it
     assert t(len(names), 8, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_VARIANT
     assert t(v64, -1, 8, 8)[0] == capi.SGEMM_STATUS_INVALID_DIM
     # the automatic choice at 1536^3 is the split-capable 64x64 kernel

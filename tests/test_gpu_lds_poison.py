@@ -23,7 +23,7 @@ SHAPES = [
     (17, 260, 320), (520, 772, 192), (256, 256, 100), (130, 200, 36), (300, 260, 1028), (256, 128, 68),
 ]
 # the automatic choice where it splits K or the last wave of tiles
-SPLIT_SHAPES = [(256, 256, 16384), (640, 640, 4096), (767, 767, 4095), (509, 515, 8191), (1550, 1572, 1000),
+SPLIT_SHAPES = [(256, 256, 16384), (640, 640, 4096), (767, 767, 4095), (509, 515, 8191), (1536, 1532, 1000),
                 (1535, 1537, 1535)]
 
 

@@ -193,7 +193,7 @@ def test_split_k(shape, ab):
 
 AUTO_SPLIT_CASES = [
     # (M, N, K, split factor the automatic choice takes)
-    (256, 256, 16384, 15),        # 128 K tiles over 15 splits: uneven shares
+    (256, 256, 16384, 16),        # 256 K tiles over 16 splits
     (640, 640, 4096, 5),
     (1152, 1152, 2048, 2),
     (767, 767, 4095, 3),          # any alignment: 4-byte loads, K remainder
@@ -291,8 +291,8 @@ TAIL_CASES = [
     # (M, N, K, variant name): the grid is whole waves plus a last wave at
     # most a quarter full, which runs as a second launch with K split
     (1536, 1536, 1536, None),
-    (1550, 1572, 1000, "lean_64x64x64_w4x1_splitk"),
-    (2944, 2944, 256, "lean_128x128x32_w2x2_splitk"),
+    (2560, 2624, 2560, "lean_64x64x64_w4x1_splitk"),
+    (3072, 3072, 3072, "lean_128x128x32_w2x2_splitk"),
     (1600, 1600, 1600, "lean_64x64x64_w4x1_splitk"),
     # the any-alignment kernel: K and N not multiples of 4
     (1535, 1537, 1535, "lean_dw_64x64x64_w4x1_splitk"),

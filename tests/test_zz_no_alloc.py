@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # last pair splits the last wave of tiles into a second launch).
 PAIRS = [
     ((640, 640, 4096), (512, 512, 2048)),          # S = 5, then S = 4
-    ((1550, 1572, 1000), (256, 256, 8192)),        # last-wave split, then S = 15
+    ((1536, 1532, 1000), (256, 256, 8192)),        # last-wave split, then S = 16
     ((767, 767, 4095), (509, 515, 1021)),          # 4-byte loads (K, N not multiples of 4)
 ]
 
