@@ -92,14 +92,17 @@ def build(verbose: bool = False, isa: bool = False) -> str:
         procs.append((unit + suffix, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
                                                       text=True, cwd=BUILD_DIR)))
         (poison_objs if suffix else objs).append(obj)
-    report, failed = [], []
+    report, poison_report, failed = [], [], []
     for unit, p in procs:
         out, err = p.communicate()
-        report.append(f"==== {unit}\n{err}")
+        (poison_report if unit.endswith("_poison") else report).append(f"==== {unit}\n{err}")
         if p.returncode != 0:
             failed.append((unit, err))
+    # the product library's kernels, and the race-check build's apart (same names)
     with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
         f.write("\n".join(report))
+    with open(os.path.join(BUILD_DIR, "resource_usage_poison.txt"), "w") as f:
+        f.write("\n".join(poison_report))
     for unit, err in failed:
         sys.stderr.write(err)
     if failed:
