@@ -81,3 +81,13 @@ def test_printed_time_throughput_pairs(ms, thr, scale):
     # the printed time and the printed rate are each rounded to their last digit
     tol = _half_ulp(thr) + got * _half_ulp(ms) / G[ms]
     assert abs(got - G[thr]) <= tol
+
+
+def test_bench_quotes_the_pages_figures():
+    """The context figures on the bench line are the ones the pages print."""
+    import bench
+    c = bench.PAGES_CONTEXT
+    assert c["rtx3060_vendor_library_tflops"] == G["rtx3060_cublas_tflops"]
+    assert c["rtx3060_pipelined_kernel_tflops"] == G["rtx3060_staged_tflops"]
+    assert c["rtx3060_locked_clock_mhz"] == G["rtx3060_locked_clock_mhz"]
+    assert c["t4_shared_memory_tile32_tflops"] == pytest.approx(G["t4_tile32_4096_gflops"] / 1000.0)
