@@ -24,29 +24,40 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "fp32_sgemm_tuning_amd", "csrc")
 
 
-def _device_asm(units, tmp_path, extra=()):
-    """Device assembly of each unit, built in parallel: {unit: text}."""
+def _device_asm(builds, tmp_path):
+    """Device assembly of each build {key: (unit, extra flags)}, compiled in
+    parallel: {key: text}."""
     from fp32_sgemm_tuning_amd import build as b
     hipcc = b.HIPCC if os.path.exists(b.HIPCC) else shutil.which("hipcc")
     if not hipcc:
         pytest.skip("hipcc not available")
     procs = {}
-    for unit in units:
-        out = os.path.join(str(tmp_path), unit + ".s")
+    for key, (unit, extra) in builds.items():
+        out = os.path.join(str(tmp_path), key + ".s")
         cmd = [hipcc, *b.HIP_FLAGS, *dict(b.UNITS)[unit], *extra, "--cuda-device-only", "-S",
                os.path.join(CSRC, unit), "-o", out]
-        procs[unit] = (out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+        procs[key] = (out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
     texts = {}
-    for unit, (out, proc) in procs.items():
+    for key, (out, proc) in procs.items():
         _, err = proc.communicate()
         assert proc.returncode == 0, err[-2000:]
-        texts[unit] = open(out).read()
+        texts[key] = open(out).read()
     return texts
 
 
 @pytest.fixture(scope="module")
-def lean_asm(tmp_path_factory):
-    return _device_asm(["sgemm_lean.hip", "sgemm_lean_split.hip"], tmp_path_factory.mktemp("asm"))
+def asm_builds(tmp_path_factory):
+    """The lean units as the library builds them, and the plain lean unit
+    as the race-check library builds it."""
+    return _device_asm({"sgemm_lean.hip": ("sgemm_lean.hip", []),
+                        "sgemm_lean_split.hip": ("sgemm_lean_split.hip", []),
+                        "poison:sgemm_lean.hip": ("sgemm_lean.hip", ["-DSGEMM_LDS_POISON=1"])},
+                       tmp_path_factory.mktemp("asm"))
+
+
+@pytest.fixture(scope="module")
+def lean_asm(asm_builds):
+    return {k: v for k, v in asm_builds.items() if not k.startswith("poison:")}
 
 
 def _waits_after_direct_loads(asm):
@@ -123,7 +134,7 @@ def test_split_k_loop_keeps_loads_in_flight(lean_asm):
     assert not bad, bad
 
 
-def test_race_check_build_poisons_the_stages(lean_asm, tmp_path):
+def test_race_check_build_poisons_the_stages(lean_asm, asm_builds):
     """The lean kernels fill LDS only through direct loads, so the normal
     build has no LDS write instruction in them at all; the race-check build
     (SGEMM_LDS_POISON=1, as libsgemm_poison.so is built) writes the NaN
@@ -132,7 +143,7 @@ def test_race_check_build_poisons_the_stages(lean_asm, tmp_path):
         return {name: sum("ds_write" in x for x in lines) for name, lines in _kernels(asm)
                 if "sgemm_lean_kernel" in name}
     plain = ds_writes(lean_asm["sgemm_lean.hip"])
-    poisoned = ds_writes(_device_asm(["sgemm_lean.hip"], tmp_path, ["-DSGEMM_LDS_POISON=1"])["sgemm_lean.hip"])
+    poisoned = ds_writes(asm_builds["poison:sgemm_lean.hip"])
     assert plain and set(plain) == set(poisoned)
     assert all(n == 0 for n in plain.values()), plain
     assert all(n > 0 for n in poisoned.values()), poisoned
