@@ -1,0 +1,75 @@
+"""Seeded random problems through the C ABI against the fp64 oracle, every
+element compared at |C - C_ref| <= 1e-3 + 1e-4 |C_ref|.
+
+Case i draws from default_rng(9000 + i): M and N each either log-uniform in
+1..1500 or uniform in 256..1500 (even odds), K either log-uniform in
+1..3000 or uniform in 512..3000; each leading dimension padded by 0 to 7 elements,
+with NaN in the padding; in a third of the cases one operand's base pointer
+4 bytes off the 16-byte grid; alpha from {1, -0.5, 2.25} and beta from
+{0, 1, -1.5}, C filled with NaN when beta is 0.  Every case runs the
+automatic choice (which may split K, split the last wave or take the
+4-byte kernels) and, on every other case, one variant drawn from all of
+them, forced (a variant that needs 16-byte alignment the case lacks
+refuses with its status, which is accepted).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from fp32_sgemm_tuning_amd import capi
+from fp32_sgemm_tuning_amd.inputs import make_problem
+from gpu_util import check_close, padded_device, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+CASES = 48
+
+
+def _draw_case(i):
+    rng = np.random.default_rng(9000 + i)
+
+    def size(lo, hi):
+        if rng.random() < 0.5:
+            return max(1, int(round(math.exp(rng.uniform(0.0, math.log(hi))))))
+        return int(rng.integers(lo, hi + 1))
+
+    M, N, K = size(256, 1500), size(256, 1500), size(512, 3000)
+    pads = [int(x) for x in rng.integers(0, 8, size=3)]
+    shift = int(rng.integers(0, 9))          # 0..2: A, B or C one float off; else none
+    alpha = float(rng.choice([1.0, -0.5, 2.25]))
+    beta = float(rng.choice([0.0, 1.0, -1.5]))
+    forced = None
+    if i % 2 == 1:
+        try:
+            forced = int(rng.choice(capi.all_variants()))
+        except capi.LibraryMissing:
+            forced = None
+    return M, N, K, pads, shift, alpha, beta, forced
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_problem(i):
+    torch = torch_cuda()
+    M, N, K, pads, shift, alpha, beta, forced = _draw_case(i)
+    lda, ldb, ldc = K + pads[0], N + pads[1], N + pads[2]
+    print(f"[random {i}] {M}x{N}x{K} ld {lda},{ldb},{ldc} shift {shift} alpha {alpha} beta {beta} "
+          f"forced {forced}", flush=True)
+    A, B, Cin = make_problem(M, N, K, seed=9000 + i, dist="normal", with_c=True)
+    dA, _ = padded_device(A, lda, torch, offset=1 if shift == 0 else 0)
+    dB, _ = padded_device(B, ldb, torch, offset=1 if shift == 1 else 0)
+    ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+    h = torch.cuda.current_stream().cuda_stream
+    for variant in ([None] if forced is None else [None, forced]):
+        dC, _ = padded_device(Cin, ldc, torch, offset=1 if shift == 2 else 0)
+        if beta == 0.0:
+            dC.fill_(float("nan"))
+        args = (M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta, dC.data_ptr(), ldc, h)
+        st = capi.sgemm(*args) if variant is None else capi.sgemm_ex(*args, variant)
+        if variant is not None and st == capi.SGEMM_STATUS_UNSUPPORTED:
+            continue
+        assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+        torch.cuda.synchronize()
+        name = "auto" if variant is None else capi.sgemm_variant_name(variant)
+        check_close(dC.cpu().numpy(), ref, f"random {i} {name} {M}x{N}x{K}")
