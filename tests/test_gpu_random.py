@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 from fp32_sgemm_tuning_amd import capi
-from fp32_sgemm_tuning_amd.inputs import make_problem
+from fp32_sgemm_tuning_amd.inputs import make_problem, make_problem_16bit
 from gpu_util import check_close, padded_device, torch_cuda
 
 pytestmark = pytest.mark.gpu
@@ -73,3 +73,88 @@ def test_random_problem(i):
         torch.cuda.synchronize()
         name = "auto" if variant is None else capi.sgemm_variant_name(variant)
         check_close(dC.cpu().numpy(), ref, f"random {i} {name} {M}x{N}x{K}")
+
+
+def _stored(x, transposed, pad, offset, dtype, torch):
+    """Device buffer holding x (or x^T) row-major with `pad` extra NaN
+    elements per row, starting `offset` elements in; (view, ld)."""
+    s = np.ascontiguousarray(x.T if transposed else x)
+    rows, cols = s.shape
+    ld = cols + pad
+    buf = torch.full((offset + rows * ld + 16,), float("nan"), dtype=dtype, device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(torch.from_numpy(s).to("cuda").to(dtype))
+    return view, max(ld, 1)
+
+
+OP_CASES = 32
+
+
+def _draw_op_case(i, base):
+    rng = np.random.default_rng(base + i)
+
+    def size(lo, hi):
+        if rng.random() < 0.5:
+            return max(1, int(round(math.exp(rng.uniform(0.0, math.log(hi))))))
+        return int(rng.integers(lo, hi + 1))
+
+    M, N, K = size(256, 1500), size(256, 1500), size(512, 3000)
+    ta, tb = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    pads = [int(x) for x in rng.integers(0, 9, size=3)]
+    offs = [int(x) for x in rng.integers(0, 3, size=2)]
+    alpha = float(rng.choice([1.0, -0.5, 2.25]))
+    beta = float(rng.choice([0.0, 1.0, -1.5]))
+    f16 = bool(rng.integers(0, 2))
+    return M, N, K, ta, tb, pads, offs, alpha, beta, f16
+
+
+def _run_op(i, lowp):
+    torch = torch_cuda()
+    M, N, K, ta, tb, pads, offs, alpha, beta, f16 = _draw_op_case(i, 9200 if lowp else 9100)
+    tag = f"{'lowp ' + ('f16' if f16 else 'bf16') if lowp else 'op'} {i}: {M}x{N}x{K} " \
+          f"{'T' if ta else 'N'}{'T' if tb else 'N'} pads {pads} offsets {offs} alpha {alpha} beta {beta}"
+    print(f"[random {tag}]", flush=True)
+    if lowp:
+        A, B, Cin = make_problem_16bit(M, N, K, seed=9200 + i, dtype="f16" if f16 else "bf16", dist="normal",
+                                       with_c=True)
+        t = torch.float16 if f16 else torch.bfloat16
+    else:
+        A, B, Cin = make_problem(M, N, K, seed=9100 + i, dist="normal", with_c=True)
+        t = torch.float32
+    dA, lda = _stored(A, ta, pads[0], offs[0], t, torch)
+    dB, ldb = _stored(B, tb, pads[1], offs[1], t, torch)
+    dC, ldc = _stored(Cin, False, pads[2], 0, torch.float32, torch)
+    if beta == 0.0:
+        dC.fill_(float("nan"))
+    h = torch.cuda.current_stream().cuda_stream
+    op_a = capi.SGEMM_OP_T if ta else capi.SGEMM_OP_N
+    op_b = capi.SGEMM_OP_T if tb else capi.SGEMM_OP_N
+    if lowp:
+        code = capi.SGEMM_DTYPE_F16 if f16 else capi.SGEMM_DTYPE_BF16
+        st = capi.sgemm_lowp_op(code, op_a, op_b, M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                                dC.data_ptr(), ldc, h, -1)
+    else:
+        st = capi.sgemm_op(op_a, op_b, M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                           dC.data_ptr(), ldc, h)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+    check_close(dC.cpu().numpy(), ref, tag)
+
+
+@pytest.mark.parametrize("i", range(OP_CASES))
+def test_random_transposed(i):
+    """sgemm_op on seeded random problems: op(A), op(B) drawn, operands
+    stored transposed as drawn with padded rows (NaN) and base offsets of 0
+    to 2 floats, so both the transposed lean kernels and the copy to
+    row-major (unaligned transposed operands) are exercised."""
+    _run_op(i, lowp=False)
+
+
+@pytest.mark.parametrize("i", range(OP_CASES))
+def test_random_16bit(i):
+    """sgemm_lowp_op (automatic choice) on seeded random problems: BF16 or
+    FP16 drawn, op(A), op(B), padding and base offsets of 0 to 2 elements
+    drawn, so the fast kernels, the copies into padded buffers and the plain
+    kernel are all exercised; inputs are exact 16-bit values."""
+    _run_op(i, lowp=True)
