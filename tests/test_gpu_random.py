@@ -158,3 +158,62 @@ def test_random_16bit(i):
     drawn, so the fast kernels, the copies into padded buffers and the plain
     kernel are all exercised; inputs are exact 16-bit values."""
     _run_op(i, lowp=True)
+
+
+BATCH_CASES = 16
+
+
+@pytest.mark.parametrize("i", range(BATCH_CASES))
+def test_random_strided_batch(i):
+    """sgemm_strided_batched on seeded random batches: 1 to 6 problems of
+    up to 700 x 700 x 1200, op(A), op(B) drawn, padded rows and gaps
+    between problems (NaN), A or B shared across the batch (stride 0) in a
+    quarter of the cases each; every problem against the oracle and every
+    gap of C untouched."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(9300 + i)
+    M, N, K = (int(rng.integers(1, 701)), int(rng.integers(1, 701)), int(rng.integers(1, 1201)))
+    batch = int(rng.integers(1, 7))
+    ta, tb = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    share = int(rng.integers(0, 4))          # 0: A shared, 1: B shared, else neither
+    pa, pb, pc = (int(x) for x in rng.integers(0, 6, size=3))
+    alpha, beta = float(rng.choice([1.0, -0.5, 2.25])), float(rng.choice([0.0, 1.0, -1.5]))
+    print(f"[random batch {i}] {batch} x {M}x{N}x{K} {'T' if ta else 'N'}{'T' if tb else 'N'} share {share} "
+          f"pads {pa},{pb},{pc} alpha {alpha} beta {beta}", flush=True)
+    probs = [make_problem(M, N, K, seed=9300 + 16 * i + z, dist="normal", with_c=True) for z in range(batch)]
+    if share == 0:
+        probs = [(probs[0][0], B, C) for _, B, C in probs]
+    elif share == 1:
+        probs = [(A, probs[0][1], C) for A, _, C in probs]
+    ra, ca = (K, M) if ta else (M, K)
+    rb, cb = (N, K) if tb else (K, N)
+    lda, ldb, ldc = ca + pa, cb + pb, N + pc
+    sa = 0 if share == 0 else ra * lda + 3
+    sb = 0 if share == 1 else rb * ldb + 5
+    sc = M * ldc + 7
+    bufA = torch.full((max(batch * sa, ra * lda) + 8,), float("nan"), device="cuda")
+    bufB = torch.full((max(batch * sb, rb * ldb) + 8,), float("nan"), device="cuda")
+    bufC = torch.full((batch * sc + 8,), float("nan"), device="cuda")
+
+    def put(buf, off, x, ld):
+        rows, cols = x.shape
+        buf[off:off + rows * ld].view(rows, ld)[:, :cols].copy_(torch.from_numpy(np.ascontiguousarray(x)))
+
+    for z, (A, B, Cin) in enumerate(probs):
+        put(bufA, z * sa, A.T if ta else A, lda)
+        put(bufB, z * sb, B.T if tb else B, ldb)
+        if beta != 0.0:
+            put(bufC, z * sc, Cin, ldc)
+    st = capi.sgemm_strided_batched(capi.SGEMM_OP_T if ta else capi.SGEMM_OP_N,
+                                    capi.SGEMM_OP_T if tb else capi.SGEMM_OP_N, M, N, K, alpha,
+                                    bufA.data_ptr(), lda, sa, bufB.data_ptr(), ldb, sb, beta,
+                                    bufC.data_ptr(), ldc, sc, batch, torch.cuda.current_stream().cuda_stream)
+    assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+    torch.cuda.synchronize()
+    host = bufC.cpu().numpy()
+    for z, (A, B, Cin) in enumerate(probs):
+        got = host[z * sc:z * sc + M * ldc].reshape(M, ldc)
+        check_close(got[:, :N], oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta),
+                    f"random batch {i} problem {z}")
+        assert np.isnan(got[:, N:]).all(), "write into C's row padding"
+        assert np.isnan(host[z * sc + M * ldc:(z + 1) * sc]).all(), "write between C problems"
