@@ -190,33 +190,35 @@ static_assert(kSplitWorkspaceBytes == (size_t)SGEMM_WORKSPACE_BYTES, "workspace 
 // grids are left to the last-wave split).  Cost model, in K-tile steps of
 // one block on a CU of its own (2 * bm * bn * bk flops at 1/256 of the
 // 157.3 TFLOP/s peak):
-//   - the busiest CU: a CU runs its blocks at about the same aggregate rate
-//     whether it holds one or two, so ceil(tiles * S / 256) blocks of
-//     ceil(kt / S) steps and kBlockFixed steps of their own (first loads,
-//     pipeline fill, epilogue) each;
+//   - the busiest CU: ceil(tiles * S / 256) = r blocks of ceil(kt / S)
+//     steps (a CU runs its blocks at about the same aggregate rate whether
+//     it holds one or two), plus kBlockFixed steps (first loads, pipeline
+//     fill, epilogue) for every pair of blocks it holds: two resident
+//     blocks overlap their fixed parts;
 //   - a floor set by the operand traffic of the whole grid, which every S
 //     moves alike: 0.15 * tiles * kt * (bm + bn) / (bm * bn) steps;
-//   - the partials, written and read back once each (8 * S * bm * bn bytes
-//     per tile at about 5 TB/s): 0.49 * S * tiles / bk steps;
-//   - a fixed cost of splitting at all (the device-scope hand-off, the
-//     ticket and the serial read-back before the epilogue): kSplitFixed.
-// The cost is the larger of the first two plus the others.  S is the
-// factor of least cost, with at least four K tiles per split, at most 16,
-// within the workspace, taken when it costs at most 95% of no split.  The
-// floor's constant is fitted to measured sweeps (19 shapes from 16 to 484
-// tiles of 64x64, S = 1 to 16); the two fixed costs to the split and
-// unsplit 64x64x64 kernel timed side by side on 12 small grids, where
-// they make every split decision the measured one (512^3, where S = 2
-// measured no faster than no split, 1216^2 x 2048 and 1152^2 x 2048, where
-// S = 2 measured 10% faster, up to 256^2 x 16384).
-// SGEMM_SPLITK forces a factor (clamped to the K tiles and the workspace)
-// for sweeps.
-constexpr double kBlockFixed = 3.0;
-constexpr double kSplitFixed = 3.0;
-double split_cost(long tiles, long kt, long s, int bm, int bn, int bk) {
-    const double busiest = (double)ceil_div(tiles * s, kNumCUs) * ((double)ceil_div(kt, s) + kBlockFixed);
+//   - splitting at all: kSplitFixed steps (the device-scope hand-off and
+//     the ticket) and kSplitPerPartial per split (the last block of a tile
+//     reads the S partial tiles back one after the other).  The partials'
+//     own traffic (at most 64 MiB, held in the caches) fitted to nothing
+//     measurable and is left out.
+// The cost is the larger of the first two plus the third.  S is the factor
+// of least cost, with at least two K tiles per split (the pipeline's depth),
+// at most 16, within the workspace, taken when it costs at most 95% of no
+// split.  The constants are fitted to kernel-trace durations of the
+// 64x64x64 tile on 30 grids of 16 to 361 tiles (K from 256 to 8192), each
+// at S = 1, 2, 3, 4, 5, 6, 8, 12 and 16 (log residuals 6% rms); over those
+// grids the chosen factor runs within 0.8% of the fastest measured one on
+// average (17% at worst, 320^3).  SGEMM_SPLITK forces a factor (clamped to
+// the K tiles and the workspace) for sweeps.
+constexpr double kBlockFixed = 2.8;
+constexpr double kSplitFixed = 1.7;
+constexpr double kSplitPerPartial = 0.45;
+double split_cost(long tiles, long kt, long s, int bm, int bn) {
+    const long r = ceil_div(tiles * s, kNumCUs);
+    const double busiest = (double)(r * ceil_div(kt, s)) + (double)ceil_div(r, 2) * kBlockFixed;
     const double floor = 0.15 * (double)(tiles * kt) * (double)(bm + bn) / ((double)bm * bn);
-    const double partials = s > 1 ? 0.49 * (double)(s * tiles) / bk + kSplitFixed : 0.0;
+    const double partials = s > 1 ? kSplitFixed + kSplitPerPartial * (double)s : 0.0;
     return (busiest > floor ? busiest : floor) + partials;
 }
 
@@ -232,11 +234,11 @@ int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
         return s < 1 ? 1 : (int)s;
     }
     if (tiles >= kTailSlots) return 1;
-    const double base = split_cost(tiles, kt, 1, bm, bn, bk);
+    const double base = split_cost(tiles, kt, 1, bm, bn);
     long best = 1;
     double best_cost = base;
-    for (long s = 2; s <= 16 && s <= kt / 4 && s * tiles <= fit; ++s) {
-        const double cost = split_cost(tiles, kt, s, bm, bn, bk);
+    for (long s = 2; s <= 16 && s <= kt / 2 && s * tiles <= fit; ++s) {
+        const double cost = split_cost(tiles, kt, s, bm, bn);
         if (cost < best_cost) {
             best = s;
             best_cost = cost;
@@ -254,14 +256,22 @@ int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
 // counts once per host thread).
 //
 // A call leases its stream's slot from before its first launch to after its
-// last; the end of the lease records an event on the stream, which marks
-// the slot's last use.  A stream without a slot gets a new one while the
-// device has fewer than the maximum, else the least recently used slot that
-// no call holds, once that slot's event has completed: however many streams
-// a process creates and destroys, the memory stays bounded, and a buffer is
-// never handed to another stream while kernels that use it are queued.  All
-// waits (on that event, or before a copy buffer grows) happen outside the
-// lock, so a call never blocks calls on other streams.
+// last.  A stream without a slot gets a new one while the device has fewer
+// than the maximum, else the least recently used slot that no call holds,
+// once the kernels queued on it have finished: however many streams a
+// process creates and destroys, the memory stays bounded, and a buffer is
+// never handed to another stream while kernels that use it are queued.
+//
+// What marks a slot's last use: the end of a lease records an event on the
+// stream.  A workspace skips that record while no stream of its device has
+// ever found every workspace taken (the event's marker costs the queue
+// about 3 us, as much as a small split saves): then no workspace is handed
+// over, so none needs it.  The first stream to find them all taken sets the
+// device "contended" for good, from which point every lease end records;
+// idle workspaces whose last use went unrecorded are handed over only after
+// one hipDeviceSynchronize, once.  Copy buffers record at every lease end.
+// All waits (on an event, the one drain, or before a copy buffer grows)
+// happen outside the lock, so a call never blocks calls on other streams.
 //
 // When no slot can be had without waiting for another call (every slot of
 // the device held), the call takes a path that needs none: K is not split,
@@ -274,6 +284,13 @@ int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
 enum SlotKind { kWorkspaceSlot = 0, kCopySlot = 1 };
 constexpr int kUnavailable = 1;          // acquire(): no slot without waiting
 
+// How a slot's last use is known to be over.
+enum LastUse {
+    kNoUse = 0,                          // new or drained: nothing queued uses it
+    kEventMarks = 1,                     // `done` was recorded after the last lease
+    kUnmarked = 2,                       // a lease ended without a record: only its own stream may use it
+};
+
 struct Slot {
     int kind = 0;
     int dev = -1;
@@ -281,7 +298,8 @@ struct Slot {
     std::thread::id thread;              // the host thread, for hipStreamPerThread
     void *mem = nullptr;
     size_t bytes = 0;
-    hipEvent_t done = nullptr;           // recorded at the end of every lease
+    hipEvent_t done = nullptr;           // recorded at the end of a lease (see LastUse)
+    int last_use = kNoUse;
     int users = 0;                       // calls holding a lease
     bool moving = false;                 // being set up, grown or handed over (unlocked)
     bool pinned = false;                 // an event record failed: never handed over
@@ -296,12 +314,17 @@ struct Lease {
 std::mutex g_slot_mu;
 std::list<Slot> g_slots;                 // node addresses stay valid
 unsigned long long g_slot_clock = 0;
+std::vector<int> g_contended;            // devices where a stream found every workspace taken (never cleared)
 
 int max_slots(int kind) { return kind == kWorkspaceSlot ? SGEMM_MAX_STREAM_WORKSPACES : SGEMM_MAX_COPY_BUFFERS; }
 
 bool capturing(hipStream_t stream) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     return hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
+}
+
+bool contended(int dev) {
+    return std::find(g_contended.begin(), g_contended.end(), dev) != g_contended.end();
 }
 
 // (Unlocked; the slot is marked moving.)  Make `s` hold at least `bytes`
@@ -315,9 +338,18 @@ int prepare_slot(Slot &s, size_t bytes, hipStream_t stream) {
             s.done = nullptr;
             return record_hip_error(e, "hipEventCreateWithFlags");
         }
-    } else {
+    }
+    if (s.last_use == kUnmarked) {
+        // only the slot's own stream gets here (acquire_slot hands over no
+        // unmarked slot): the kernels queued on it include the last use
+        e = hipEventRecord(s.done, stream);
+        if (e != hipSuccess) return record_hip_error(e, "hipEventRecord (buffer growth)");
+        s.last_use = kEventMarks;
+    }
+    if (s.last_use == kEventMarks) {
         e = hipEventSynchronize(s.done);
         if (e != hipSuccess) return record_hip_error(e, "hipEventSynchronize (buffer hand-over)");
+        s.last_use = kNoUse;
     }
     if (s.mem == nullptr || s.bytes < bytes) {
         if (s.mem != nullptr) {
@@ -353,32 +385,61 @@ int acquire_slot(int kind, hipStream_t stream, size_t bytes, Lease &out) {
     if (e != hipSuccess) return record_hip_error(e, "hipGetDevice");
     const std::thread::id thread = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
     std::unique_lock<std::mutex> lock(g_slot_mu);
-    Slot *s = nullptr, *lru = nullptr;
-    int held = 0;
-    for (Slot &x : g_slots) {
-        if (x.kind != kind || x.dev != dev) continue;
-        ++held;
-        if (x.stream == stream && x.thread == thread) s = &x;
-        if (x.users == 0 && !x.moving && !x.pinned && (lru == nullptr || x.stamp < lru->stamp)) lru = &x;
-    }
-    if (s != nullptr) {
-        if (s->moving || (kind == kCopySlot && s->users > 0) || s->pinned) return kUnavailable;
-        if (s->bytes >= bytes) {
-            ++s->users;
-            s->stamp = ++g_slot_clock;
-            out = Lease{s, s->mem};
-            return SGEMM_STATUS_OK;
+    Slot *s = nullptr;
+    for (bool drained = false;;) {
+        Slot *lru = nullptr;
+        std::vector<Slot *> unmarked;
+        int held = 0;
+        s = nullptr;
+        for (Slot &x : g_slots) {
+            if (x.kind != kind || x.dev != dev) continue;
+            ++held;
+            if (x.stream == stream && x.thread == thread) s = &x;
+            if (x.users != 0 || x.moving || x.pinned) continue;
+            if (x.last_use == kUnmarked) {
+                unmarked.push_back(&x);
+            } else if (lru == nullptr || x.stamp < lru->stamp) {
+                lru = &x;
+            }
         }
-        if (s->users > 0) return kUnavailable;         // grow only while no call holds it
-    } else if (held < max_slots(kind)) {
-        g_slots.emplace_back();
-        s = &g_slots.back();
-        s->kind = kind;
-        s->dev = dev;
-    } else if (lru != nullptr) {
-        s = lru;
-    } else {
-        return kUnavailable;
+        if (s != nullptr) {
+            if (s->moving || (kind == kCopySlot && s->users > 0) || s->pinned) return kUnavailable;
+            if (s->bytes >= bytes) {
+                ++s->users;
+                s->stamp = ++g_slot_clock;
+                out = Lease{s, s->mem};
+                return SGEMM_STATUS_OK;
+            }
+            if (s->users > 0) return kUnavailable;         // grow only while no call holds it
+            break;
+        }
+        if (held < max_slots(kind)) {
+            g_slots.emplace_back();
+            s = &g_slots.back();
+            s->kind = kind;
+            s->dev = dev;
+            break;
+        }
+        if (kind == kWorkspaceSlot && !contended(dev)) g_contended.push_back(dev);   // lease ends record from now on
+        if (lru != nullptr) {
+            s = lru;
+            break;
+        }
+        if (unmarked.empty() || drained) return kUnavailable;
+        // Idle workspaces whose last use went unrecorded: wait once for the
+        // device to drain (outside the lock), after which they hold nothing
+        // queued.  A failed wait leaves them as they were and this call
+        // unsplit.
+        for (Slot *x : unmarked) x->moving = true;
+        lock.unlock();
+        const hipError_t se = hipDeviceSynchronize();
+        lock.lock();
+        for (Slot *x : unmarked) {
+            x->moving = false;
+            if (se == hipSuccess && x->last_use == kUnmarked) x->last_use = kNoUse;
+        }
+        if (se != hipSuccess) return kUnavailable;
+        drained = true;
     }
     s->stream = stream;
     s->thread = thread;
@@ -394,7 +455,8 @@ int acquire_slot(int kind, hipStream_t stream, size_t bytes, Lease &out) {
     return SGEMM_STATUS_OK;
 }
 
-// End a lease: the slot's event marks this call's last use on `stream`.
+// End a lease: the slot's event marks this call's last use on `stream`
+// (a workspace of a device never contended: left unmarked, see LastUse).
 // Returns SGEMM_STATUS_OK or, if the event cannot be recorded, the HIP error
 // (the slot is then never handed over or released).
 int release_slot(Lease &l, hipStream_t stream) {
@@ -402,13 +464,18 @@ int release_slot(Lease &l, hipStream_t stream) {
     Slot *s = l.slot;
     l = Lease{};
     std::lock_guard<std::mutex> lock(g_slot_mu);
-    const hipError_t e = hipEventRecord(s->done, stream);
     --s->users;
     s->stamp = ++g_slot_clock;
+    if (s->kind == kWorkspaceSlot && !contended(s->dev)) {
+        s->last_use = kUnmarked;
+        return SGEMM_STATUS_OK;
+    }
+    const hipError_t e = hipEventRecord(s->done, stream);
     if (e != hipSuccess) {
         s->pinned = true;
         return record_hip_error(e, "hipEventRecord (buffer release)");
     }
+    s->last_use = kEventMarks;
     return SGEMM_STATUS_OK;
 }
 
@@ -496,9 +563,11 @@ hipError_t attach_scratch(Args &a, int splits, long tiles, void *ptr, hipStream_
 // with K split S ways, so that the last wave's few tiles spread over the
 // whole chip.  Workgroup slots: two per compute unit (kTailSlots).  Cost of
 // the last wave in the K-tile steps of split_cost: unsplit, its `rem` tiles
-// run one per CU, kt + kBlockFixed steps; split S ways, ceil(rem * S / 256)
-// blocks of ceil(kt / S) + kBlockFixed steps on the busiest CU, plus the
-// partials (as in split_cost) and a fixed kTailFixed for the second launch
+// run one per CU, kt + kTailBlockFixed steps; split S ways,
+// ceil(rem * S / 256) blocks of ceil(kt / S) + kTailBlockFixed steps on the
+// busiest CU, plus the partials' traffic (0.49 * S * rem / bk steps: 8 * S
+// * bm * bn bytes per tile at about 5 TB/s) and a fixed kTailFixed for the
+// second launch
 // and the hand-off.  S (at most 16, at least three K tiles per split, within
 // the workspace) is the factor of least cost, taken when it costs at most
 // 95% of the unsplit last wave; 1 = one launch.  kTailFixed is fitted to the
@@ -677,6 +746,7 @@ constexpr VariantDesc kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr double kTailFixed = 8.0;
+constexpr double kTailBlockFixed = 3.0;
 int choose_tail_splits(const VariantDesc &d, const Args &a) {
     if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
     const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
@@ -685,11 +755,11 @@ int choose_tail_splits(const VariantDesc &d, const Args &a) {
         return 1;
     const long kt = ceil_div(a.K, d.bk);
     const long fit = (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem));
-    const double base = (double)ceil_div(rem, kNumCUs) * ((double)kt + kBlockFixed);
+    const double base = (double)ceil_div(rem, kNumCUs) * ((double)kt + kTailBlockFixed);
     long best = 1;
     double best_cost = base;
     for (long s = 2; s <= 16 && s <= kt / 3 && s <= fit; ++s) {
-        const double cost = (double)ceil_div(rem * s, kNumCUs) * ((double)ceil_div(kt, s) + kBlockFixed) +
+        const double cost = (double)ceil_div(rem * s, kNumCUs) * ((double)ceil_div(kt, s) + kTailBlockFixed) +
                             0.49 * (double)(s * rem) / d.bk + kTailFixed;
         if (cost < best_cost) {
             best = s;
@@ -1526,9 +1596,21 @@ int sgemm_release_workspaces(void) {
     }
     int st = SGEMM_STATUS_OK;
     std::vector<std::list<Slot>::iterator> freed;
+    // a last use that no event marks: wait for the whole device, once
+    hipError_t drain = hipSuccess;
+    for (auto it : victims) {
+        if (it->last_use == kUnmarked) {
+            drain = hipDeviceSynchronize();
+            break;
+        }
+    }
     for (auto it : victims) {
         // the slot's last use must be over before its memory goes
-        e = it->done != nullptr ? hipEventSynchronize(it->done) : hipSuccess;
+        if (it->last_use == kUnmarked) {
+            e = drain;
+        } else {
+            e = it->last_use == kEventMarks ? hipEventSynchronize(it->done) : hipSuccess;
+        }
         if (e == hipSuccess && it->mem != nullptr) e = hipFree(it->mem);
         if (e != hipSuccess) {
             if (st == SGEMM_STATUS_OK) st = record_hip_error(e, "releasing a buffer");

@@ -38,9 +38,13 @@
  * (the per-thread default stream counts once per host thread); when more
  * streams ask, the least recently used workspace that no call in progress
  * holds is handed to the new stream once the kernels queued on it have
- * finished (an event recorded at the end of each call marks that), so
- * device memory stays bounded however many streams a process creates and
- * destroys.  The counters are cleared on the stream before a workspace's
+ * finished, so device memory stays bounded however many streams a process
+ * creates and destroys.  Until a stream first finds every workspace of its
+ * device taken, calls record nothing at their end (each stream keeps its
+ * workspace); that call waits once for the device to drain
+ * (hipDeviceSynchronize) before it takes over an idle workspace, and from
+ * then on every split call records an event at its end that marks the
+ * workspace's last use.  The counters are cleared on the stream before a workspace's
  * first use and left cleared by every call.  Calls on one stream share its
  * workspace in stream order.  The partial tiles of a tile are added in a
  * fixed order, so split-K results are deterministic too.  A call that finds
@@ -370,11 +374,13 @@ const char *sgemm_lowp_variant_name(int variant);
  * M x N x K problem whose operands the variant's split-K kernel takes (see
  * "Workspace" above; environment variable SGEMM_SPLITK = S forces S for
  * sweeps).  Only grids of fewer than 512 tiles split; the factor (at most
- * 16, at least four K tiles per split) is the one of least modelled time:
- * the busiest compute unit's share of blocks (each with a fixed cost of its
- * own), bounded below by the grid's operand traffic, plus writing and
- * reading back the partial tiles and a fixed cost of splitting; taken when
- * that is at most 95% of the unsplit time.  Always 1 for variants
+ * 16, at least two K tiles per split) is the one of least modelled kernel
+ * time: the busiest compute unit's share of K tiles plus a fixed cost per
+ * pair of resident blocks, bounded below by the grid's operand traffic,
+ * plus a fixed cost of splitting and one per split (the partials read
+ * back); taken when that is at most 95% of the unsplit time.  The model's
+ * constants are fitted to kernel-trace durations of 46 small grids at up
+ * to 12 factors each.  Always 1 for variants
  * without split-K.  No HIP call.  Returns the factor,
  * SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM (negative sizes).
  */
@@ -407,7 +413,8 @@ long long sgemm_workspace_bytes(void);
 /*
  * sgemm_release_workspaces: free the workspaces and copy buffers the library
  * holds on the current device, each after the kernels queued with it have
- * finished (this call waits for them).  Buffers held by calls in progress on
+ * finished (this call waits for them: on an event where one marks the last
+ * use, else once for the whole device, hipDeviceSynchronize).  Buffers held by calls in progress on
  * other host threads at that moment are left alone.  Later calls allocate
  * again as needed.  Returns SGEMM_STATUS_OK or SGEMM_STATUS_HIP_ERROR (a
  * buffer whose wait or free failed is kept and never reused).

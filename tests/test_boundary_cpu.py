@@ -157,34 +157,37 @@ def test_variant_selection_by_shape(shape, expected):
 def test_split_factors():
     """K is split only for grids under one full wave of resident blocks (512
     tiles of the variant's own tile), by the factor of least modelled cost
-    (busiest CU, operand-traffic floor, partials), at most 16, into splits of
-    at least four K tiles, and only when that saves at least 5%."""
+    (busiest CU, operand-traffic floor, a fixed and a per-split cost of the
+    hand-off), at most 16, into splits of at least two K tiles, and only
+    when that saves at least 5%."""
     names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
     v128, v64 = names["lean_128x128x32_w2x2_splitk"], names["lean_64x64x64_w4x1_splitk"]
     f = capi.sgemm_split_factor
     assert f(v128, 1024, 1024, 1024) == 4          # 64 tiles, 32 K tiles: one block per CU
-    assert f(v128, 512, 512, 512) == 4             # 16 tiles, 16 K tiles: four K tiles per split
+    assert f(v128, 512, 512, 512) == 8             # 16 tiles, 16 K tiles: two K tiles per split
     assert f(v128, 64, 64, 4096) == 16
     assert f(v128, 1536, 1536, 1536) == 3          # 144 tiles
     assert f(v128, 1920, 1536, 1024) == 1          # 180 tiles
-    assert f(v128, 1024, 1024, 128) == 1           # 4 K tiles
+    assert f(v128, 1024, 1024, 128) == 1           # 4 K tiles: too few to gain
     assert f(v64, 1024, 1024, 1024) == 1           # 256 tiles of 64x64: every CU busy
     assert f(v64, 512, 512, 2048) == 4             # 64 tiles, 32 K tiles of 64
-    assert f(v64, 768, 768, 4096) == 3             # 144 tiles: 432 blocks
+    assert f(v64, 768, 768, 4096) == 5             # 144 tiles: 720 blocks, three per CU at most
     assert f(v64, 640, 640, 4096) == 5             # 100 tiles: 500 blocks
-    assert f(v64, 1152, 1152, 2048) == 2           # 324 tiles
+    assert f(v64, 1152, 1152, 2048) == 3           # 324 tiles
     assert f(v64, 1280, 1280, 2048) == 1           # 400 tiles: too little to gain
-    assert f(v64, 1024, 1024, 8192) == 1           # 256 tiles
+    assert f(v64, 1024, 1024, 8192) == 1           # 256 tiles: the operand traffic bounds every S
     assert f(v64, 256, 256, 8192) == 16            # 128 K tiles: eight per split
-    assert f(v64, 512, 512, 512) == 1              # measured no faster split: fixed costs dominate
-    assert f(v64, 1216, 1216, 2048) == 2           # measured 10% faster split
+    assert f(v64, 512, 512, 512) == 4              # 64 tiles, 8 K tiles: two per split
+    assert f(v64, 384, 384, 384) == 3              # 36 tiles, 6 K tiles
+    assert f(v64, 256, 256, 256) == 1              # 16 tiles, 4 K tiles: the fixed costs eat the gain
+    assert f(v64, 1216, 1216, 2048) == 2
     assert f(v64, 2048, 2048, 64) == 1             # whole waves: left to the last-wave split
     for v in (v128, v64):
         for (M, N, K) in [(100, 100, 10000), (300, 200, 500), (1, 1, 100000), (900, 700, 3000)]:
             s = f(v, M, N, K)
             st, bm, bn, bk, _ = capi.sgemm_variant_info(v)
             tiles = -(-M // bm) * -(-N // bn)
-            assert 1 <= s <= 16 and (s == 1 or (tiles < 512 and -(-K // bk) >= 4 * s)), (v, M, N, K, s)
+            assert 1 <= s <= 16 and (s == 1 or (tiles < 512 and -(-K // bk) >= 2 * s)), (v, M, N, K, s)
     # variants without split-K, bad ids, bad sizes
     assert f(names["lean_128x128x32_w2x2"], 64, 64, 4096) == 1
     assert f(capi.sgemm_num_variants(), 64, 64, 64) == capi.SGEMM_STATUS_INVALID_VARIANT

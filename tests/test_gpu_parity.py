@@ -195,9 +195,11 @@ AUTO_SPLIT_CASES = [
     # (M, N, K, split factor the automatic choice takes)
     (256, 256, 16384, 16),        # 256 K tiles over 16 splits
     (640, 640, 4096, 5),
-    (1152, 1152, 2048, 2),
-    (767, 767, 4095, 3),          # any alignment: 4-byte loads, K remainder
-    (509, 515, 8191, 3),
+    (1152, 1152, 2048, 3),
+    (512, 512, 512, 4),           # two K tiles per split
+    (384, 384, 384, 3),
+    (767, 767, 4095, 5),          # any alignment: 4-byte loads, K remainder
+    (509, 515, 8191, 7),
 ]
 
 
