@@ -13,8 +13,12 @@ locked on this machine (the pages lock theirs at 2002 MHz for the same
 reason, "gpu_matmul", Results).  So before the W warm-up steps the bench
 runs untimed steps for --settle-seconds of wall time (the count and time
 are in the JSON line).  Then W untimed warm-up steps, then exactly K timed
-steps between two device synchronisations.  Per-launch kernel time comes
-from HIP events recorded on the stream the kernel is launched on.  The
+steps, back to back, between two device synchronisations; a pair of HIP
+events on the stream the kernel is launched on brackets them, and the
+per-launch kernel time of the roofline is their elapsed time over K (an
+event around every call would put its own marker in the queue).  A second,
+untimed pass of K calls with events around each reports the spread of
+single calls (kernel_ms).  The
 shader clock the power firmware reports (per XCD; its table refreshes about
 once a second) is read at idle, just before and just after the timed
 steps.  Prints one JSON line.
@@ -28,8 +32,10 @@ with the operands stored transposed as named), "mm:bf16" / "mm:f16" =
 torch.mm in that type, 16-bit output, for context) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike (after half a second of untimed calls per size, for
-the clock), and prints one JSON line per (size, variant) with the median
-kernel time.  It is the evidence behind the automatic tile choice.
+the clock): each round times a batch of back-to-back calls of every
+variant under one HIP event pair, and one JSON line per (size, variant)
+gives the median over the rounds of the time per call.  It is the
+evidence behind the automatic tile choice.
 
 The CPU baseline times the fp64 oracle on a bounded slab of rows of the
 same problem (host cores, OpenMP over rows) and checks the GPU result on
@@ -315,18 +321,18 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
             for v in usable:
                 run(v)
             torch.cuda.synchronize()
+        # each round times a batch of `reps` back-to-back calls of every
+        # variant under one event pair (no marker between the calls)
         times = {v: [] for v in usable}
         for _ in range(rounds):
             for v in usable:
-                evs = []
+                st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                st.record()
                 for _ in range(reps):
-                    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    st.record()
                     run(v)
-                    en.record()
-                    evs.append((st, en))
+                en.record()
                 torch.cuda.synchronize()
-                times[v] += [a.elapsed_time(b) for a, b in evs]
+                times[v].append(st.elapsed_time(en) / reps)
         for v in usable:
             ms = statistics.median(times[v])
             print(json.dumps({"sweep": label(v), "variant": v, "shape": f"{M}x{N}x{K}", "median_ms": round(ms, 5),
@@ -416,18 +422,32 @@ def main():
 
     for _ in range(args.warmup):
         sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The timed steps run back to back, as a caller's stream of products
+    # would; one pair of HIP events on the launching stream brackets them
+    # (an event around every call would add its own marker to the queue:
+    # about 0.8% of a 4096^3 step, half of a 512^3 one).
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     clock_before = clock.read()
     t0 = time.perf_counter()
+    region[0].record(stream)
+    for _ in range(args.steps):
+        sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    clock_after = clock.read()
+    region_ms = region[0].elapsed_time(region[1])
+
+    # Spread of single calls: a second pass of the same steps with an event
+    # pair around each call (not the timed region).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
         starts[i].record(stream)
         sgemm(dA, dB, dC, alpha=w.alpha, beta=w.beta, variant=variant)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    clock_after = clock.read()
     kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     if args.copy_calibration_mib > 0:
@@ -441,7 +461,7 @@ def main():
     flop = w.flops
     ms_per_step = wall / args.steps * 1e3
     value = flop / (wall / args.steps) / 1e12
-    avg_kernel_s = float(kernel_ms.mean()) / 1e3
+    avg_kernel_s = region_ms / args.steps / 1e3        # per launch, back to back in the timed region
     achieved = flop / avg_kernel_s / 1e12
     peak = model.MI355X_FP32_MATRIX_TFLOPS
     out = {
@@ -465,11 +485,13 @@ def main():
             "variant": variant_name,
             "parallelism": "single GPU",
         },
+        "timed_region_ms_per_launch": round(region_ms / args.steps, 5),
         "kernel_ms": {"mean": round(float(kernel_ms.mean()), 5), "median": round(float(np.median(kernel_ms)), 5),
                       "min": round(float(kernel_ms.min()), 5), "max": round(float(kernel_ms.max()), 5),
                       "first_quarter_mean": round(float(kernel_ms[:max(1, len(kernel_ms) // 4)].mean()), 5),
                       "last_quarter_mean": round(float(kernel_ms[-max(1, len(kernel_ms) // 4):].mean()), 5),
-                      "source": "HIP events around each call on the launching stream"},
+                      "source": "HIP events around each call on the launching stream, in a second pass of "
+                                "the same steps after the timed region"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),

@@ -7,9 +7,10 @@ checked against.
         --command "the sweep command" --out profiles/tuning_fp32.json
 
 The table holds, per problem shape (packed row-major FP32, alpha = 1,
-beta = 0), the median kernel time of every lean variant and of the
-automatic choice from an interleaved sweep (bench.py --sweep, one process,
-clock settled), the resources of every kernel instantiation from the
+beta = 0), the time per call of every lean variant and of the automatic
+choice from an interleaved sweep (bench.py --sweep, one process, clock
+settled; the median over rounds of batches of back-to-back calls), the
+resources of every kernel instantiation from the
 build's resource report, whether each variant passes cfg_valid(), hardware
 counters per variant at 4096^3, and the MFMA-busy share of the automatic
 choice on every workload.  The autotuner of the "gpu_matmul" blog (1D
@@ -32,6 +33,7 @@ SIMDS = 4 * CUS
 PEAK_TFLOPS = 157.3
 # Measurement spread the table's comparisons allow.  The same plan (same
 # variant, split and shape) timed in interleaved sweeps on different boxes
+# (each call between its own event pair, as the sweep timed them then)
 # measured up to 7.9% apart for kernels of 50-400 us (1088^2 x 2048 on the
 # 64x64x64 split kernel: 53.1 and 57.3 us; 3072^3 and 1600^3 6.5-6.6%), the
 # median over 41 such pairs 1.5%; kernels under 50 us, which launch and
@@ -204,8 +206,9 @@ def build_table(sweep_lines, resources, counters_4096, workload_counters, comman
             busy = _mfma_busy(c[key])
             wl[name] = {"kernel_template_args": list(key), "mfma_busy": None if busy is None else round(busy, 4)}
     return {
-        "about": "Tile-choice evidence for the FP32 SGEMM on MI355X (gfx950): per shape, median kernel "
-                 "time of every lean variant and of the automatic choice; per variant, resources and the "
+        "about": "Tile-choice evidence for the FP32 SGEMM on MI355X (gfx950): per shape, the time per call "
+                 "(median over rounds of back-to-back batches) of every lean variant and of the automatic "
+                 "choice; per variant, resources and the "
                  "cfg_valid filter (LDS <= 160 KiB, no scratch); counters at 4096^3.",
         "sweep_command": command,
         "spread": SPREAD,

@@ -1,5 +1,5 @@
 """The automatic tile choice checked against the tuning table
-(profiles/tuning_fp32.json: per shape, the measured median kernel time of
+(profiles/tuning_fp32.json: per shape, the measured time per call of
 every lean variant and of the automatic choice, taken on MI355X; per
 variant, resources and the cfg_valid filter).  CPU only: the table holds
 the measurements, the library's variant choice makes no HIP call.
@@ -47,9 +47,14 @@ def test_auto_choice_within_spread_of_the_best(table):
         if e["auto_plan_us"] > e["best_us"] * (1.0 + spread):
             worse[shape] = (e["auto_variant"], e["auto_plan_us"], e["best_variant"], e["best_us"])
     assert not worse, worse
-    # and the plan is the fastest measured, or within 2%, on most shapes
-    close = [s for s, e in table["shapes"].items() if e["auto_plan_us"] <= e["best_us"] * 1.02]
-    assert len(close) >= 0.7 * len(table["shapes"]), sorted(set(table["shapes"]) - set(close))
+    # and the plan is the fastest measured, or within 2%, on most shapes of
+    # at least 50 us (below that the sweep's event times hold the host's
+    # launch latency, which the choice of kernel does not set; the split
+    # of small grids is checked on kernel-trace times in test_splitk_fit)
+    long = {s: e for s, e in table["shapes"].items() if e["best_us"] >= table["short_us"]}
+    close = [s for s, e in long.items() if e["auto_plan_us"] <= e["best_us"] * 1.02]
+    assert len(long) >= 10
+    assert len(close) >= 0.7 * len(long), sorted(set(long) - set(close))
 
 
 def test_dispatch_uses_only_valid_configurations(table):
