@@ -38,6 +38,7 @@ UNITS = [
     ("sgemm_lean.hip", VGPR_FORM),
     ("sgemm_lean_split.hip", VGPR_FORM),
     ("sgemm_lean_ops.hip", VGPR_FORM),
+    ("sgemm_lean_split_t.hip", VGPR_FORM),
     ("sgemm_lowp.hip", VGPR_FORM),
 ]
 SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS]

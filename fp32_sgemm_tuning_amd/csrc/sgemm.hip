@@ -48,6 +48,7 @@ hipError_t launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream
 hipError_t launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
 hipError_t launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 hipError_t launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
+hipError_t launch_lean_splitk_t_64x64x64_w4x1(const Args &a, int splits, bool ta, bool tb, hipStream_t stream);
 }  // namespace sgemm_mi355x
 
 using namespace sgemm_mi355x;
@@ -747,26 +748,31 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr double kTailFixed = 8.0;
 constexpr double kTailBlockFixed = 3.0;
-int choose_tail_splits(const VariantDesc &d, const Args &a) {
-    if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
-    const long tiles = ceil_div(a.M, d.bm) * ceil_div(a.N, d.bn);
+// The last-wave split factor of an M x N x K grid of bm x bn x bk tiles.
+int tail_split_factor(int M, int N, int K, int bm, int bn, int bk) {
+    const long tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const long rem = tiles % kTailSlots;
     if (tiles < kTailSlots || rem == 0 || rem * 100 > kTailSlots * knobs().tail_fill || rem > kSplitMaxTiles)
         return 1;
-    const long kt = ceil_div(a.K, d.bk);
-    const long fit = (long)(kSplitPartialBytes / ((size_t)d.bm * d.bn * sizeof(float) * rem));
+    const long kt = ceil_div(K, bk);
+    const long fit = (long)(kSplitPartialBytes / ((size_t)bm * bn * sizeof(float) * rem));
     const double base = (double)ceil_div(rem, kNumCUs) * ((double)kt + kTailBlockFixed);
     long best = 1;
     double best_cost = base;
     for (long s = 2; s <= 16 && s <= kt / 3 && s <= fit; ++s) {
         const double cost = (double)ceil_div(rem * s, kNumCUs) * ((double)ceil_div(kt, s) + kTailBlockFixed) +
-                            0.49 * (double)(s * rem) / d.bk + kTailFixed;
+                            0.49 * (double)(s * rem) / bk + kTailFixed;
         if (cost < best_cost) {
             best = s;
             best_cost = cost;
         }
     }
     return best_cost <= 0.95 * base ? (int)best : 1;
+}
+
+int choose_tail_splits(const VariantDesc &d, const Args &a) {
+    if (!(d.dw ? lean_dw_takes(d.bm, d.bn, d.bk, a) : lean_takes(d.bm, d.bn, d.bk, a))) return 1;
+    return tail_split_factor(a.M, a.N, a.K, d.bm, d.bn, d.bk);
 }
 
 // Variants the automatic choice uses (indices into kVariants, looked up by
@@ -928,8 +934,10 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 // K x N (stored N x K when transposed).  An untransposed single problem takes
 // run() and its automatic choice.  Otherwise: the lean kernel (16-byte loads
 // for untransposed aligned operands, else 4-byte loads) on the tile
-// prefer_64() picks for batch x tiles, without split-K; shapes it does not
-// take go to the plain kernel.
+// prefer_64() picks for batch x tiles; a single problem on 64x64x64 tiles
+// with 16-byte loads splits K as run() does (over the grid or the last
+// wave), batches and the other forms do not; shapes the lean kernel does
+// not take go to the plain kernel.
 // ---------------------------------------------------------------------------
 // Unaligned transposed operands.  A transposed operand without 16-byte rows
 // takes the lean kernel's 4-byte gather, whose load instructions each touch
@@ -1103,6 +1111,31 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     const bool lean = K >= bk && lean_fits(bm, bn, bk, lda, ldb, ta, tb);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (lean && vec && tile64 && batch == 1) {
+        // One transposed problem on 64x64x64 tiles with 16-byte loads: K
+        // split over the whole grid or over the last wave, by the cost
+        // models and with the workspaces of run().
+        Lease lease;
+        int ws = attach_workspace(a, choose_splits(M, N, K, 64, 64, 64), s, lease);
+        if (ws != SGEMM_STATUS_OK) return ws;
+        if (a.splits > 1) return finish(launch_lean_splitk_t_64x64x64_w4x1(a, a.splits, ta, tb, s), lease, s);
+        const int tail_splits = tail_split_factor(M, N, K, 64, 64, 64);
+        if (tail_splits > 1) {
+            const long tiles = ceil_div(M, 64) * ceil_div(N, 64), rem = tiles % kTailSlots;
+            Args head = a, tail = a;
+            head.tile_count = (int)(tiles - rem);
+            tail.tile_base = (int)(tiles - rem);
+            tail.tile_count = (int)rem;
+            ws = attach_workspace(tail, tail_splits, s, lease);
+            if (ws != SGEMM_STATUS_OK) return ws;
+            if (tail.splits > 1) {
+                hipError_t e = launch_lean_general(head, true, false, ta, tb, 1, s);
+                if (e == hipSuccess) e = launch_lean_splitk_t_64x64x64_w4x1(tail, tail.splits, ta, tb, s);
+                return finish(e, lease, s);
+            }
+        }
+        return finish(launch_lean_general(a, true, false, ta, tb, 1, s), lease, s);
+    }
     const hipError_t e =
         lean ? launch_lean_general(a, tile64, !vec, ta, tb, batch, s) : launch_simple_general(a, ta, tb, batch, s);
     if (e != hipSuccess) return record_hip_error(e, "kernel launch");

@@ -208,7 +208,11 @@ int sgemm_variant_info(int variant, int *bm, int *bn, int *bk, int *needs_vec);
  * convention only in passing.  sgemm_op(N, N, ...) is sgemm().  A
  * transposed operand with 16-byte aligned rows (base, leading dimension and
  * its contiguous extent multiples of 4 floats) is read in its stored
- * orientation with 16-byte loads.  One without is, for a problem large
+ * orientation with 16-byte loads; such a product on 64x64 tiles splits K
+ * (over the whole grid or over its last wave of tiles) by the rule and with
+ * the workspaces of sgemm(), so the factor sgemm_split_factor() and
+ * sgemm_tail_split() give for the variant lean_64x64x64_w4x1_splitk
+ * applies.  One without is, for a problem large
  * enough that the copy takes less time than the product, first transposed
  * into a row-major copy in the stream's copy buffer (allocated with
  * hipMalloc on first need, grown once the kernels queued with it have

@@ -126,3 +126,31 @@ def test_lowp_poisoned(dtype, ops):
             what = f"poisoned lowp {dtype} {ops} {capi.sgemm_lowp_variant_name(v)} {M}x{N}x{K}"
             check_close(outs[0], ref, what)
             assert np.array_equal(outs[0], outs[1]), what + ": differs from the normal build"
+
+
+@pytest.mark.parametrize("ops", ["TN", "NT", "TT"])
+@pytest.mark.parametrize("shape", [(512, 512, 4096), (516, 772, 4100), (1536, 1536, 1536)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_transposed_split_poisoned(ops, shape):
+    """Transposed operands on grids that split K (the first two) or the last
+    wave (1536^3), through sgemm_op, beta != 0."""
+    torch = torch_cuda()
+    P = _lib()
+    M, N, K = shape
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    A, B, Cin = make_problem(M, N, K, seed=M + 5 * N + K, dist="normal", with_c=True)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T if ta else A)).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T if tb else B)).cuda()
+    lda, ldb = (M if ta else K), (K if tb else N)
+    h = torch.cuda.current_stream().cuda_stream
+    outs = []
+    for lib in (P, capi.load()):
+        dC = torch.from_numpy(Cin).cuda()
+        st = lib.sgemm_op(int(ta), int(tb), M, N, K, 0.75, dA.data_ptr(), lda, dB.data_ptr(), ldb, -0.5,
+                          dC.data_ptr(), N, h)
+        assert st == 0, capi.sgemm_strerror(st)
+        torch.cuda.synchronize()
+        outs.append(dC.cpu().numpy())
+    what = f"poisoned transposed split {ops} {M}x{N}x{K}"
+    check_close(outs[0], oracle.sgemm_ref(A, B, Cin, alpha=0.75, beta=-0.5), what)
+    assert np.array_equal(outs[0], outs[1]), what + ": differs from the normal build"

@@ -266,3 +266,60 @@ def test_batched_transposed_operands_copied(ops, shared):
         check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(A, B, Cin, alpha=1.25, beta=-0.5),
                     f"batched copy {ops} shared={shared} problem {z}")
         assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
+
+
+V64 = None
+
+
+def _v64():
+    global V64
+    if V64 is None:
+        V64 = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}["lean_64x64x64_w4x1_splitk"]
+    return V64
+
+
+# One transposed problem with 16-byte loads on 64x64x64 tiles splits K as
+# sgemm() does: over the whole grid (the split-K factor of the 64x64x64
+# variant above 1) or over the last wave (its last-wave split above 1).
+OP_SPLIT_CASES = [
+    # (M, N, K, plan)
+    (512, 512, 4096, "grid"),
+    (384, 384, 384, "grid"),
+    (516, 772, 4100, "grid"),       # edge tiles and a 4-deep K remainder
+    (1536, 1536, 1536, "tail"),
+    (1600, 1600, 1600, "tail"),
+]
+
+
+@pytest.mark.parametrize("ops", OPS[1:], ids=OP_IDS[1:])
+@pytest.mark.parametrize("M,N,K,plan", OP_SPLIT_CASES, ids=[f"{m}x{n}x{k}" for m, n, k, _ in OP_SPLIT_CASES])
+@pytest.mark.parametrize("ab", [(1.0, 0.0), (-0.75, 1.5)], ids=["b0", "b1"])
+def test_transposed_split(ops, M, N, K, plan, ab):
+    """Transposed operands on grids whose plan splits K: the result matches
+    the oracle element by element (NaN in C's padding and, with beta = 0, in
+    C itself) and repeats bit for bit."""
+    torch = torch_cuda()
+    op_a, op_b = ops
+    alpha, beta = ab
+    if plan == "grid":
+        assert capi.sgemm_split_factor(_v64(), M, N, K) > 1
+    else:
+        assert capi.sgemm_split_factor(_v64(), M, N, K) == 1 and capi.sgemm_tail_split(_v64(), M, N, K)[0] > 1
+    print(f"[op split] {OP_IDS[OPS.index(ops)]} {M}x{N}x{K} {plan} alpha {alpha} beta {beta}", flush=True)
+    A, B, Cin = make_problem(M, N, K, seed=M + 3 * N + K + op_a + 2 * op_b, dist="normal", with_c=True)
+    dA, lda = _stored(A, op_a == T_, 4, torch)
+    dB, ldb = _stored(B, op_b == T_, 8, torch)
+    ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta)
+    outs = []
+    for _ in range(2):
+        dC, ldc = _stored(Cin, False, 4, torch)
+        if beta == 0.0:
+            dC.fill_(float("nan"))
+        st = capi.sgemm_op(op_a, op_b, M, N, K, alpha, dA.data_ptr(), lda, dB.data_ptr(), ldb, beta,
+                           dC.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream)
+        assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+        torch.cuda.synchronize()
+        full = dC.cpu().numpy()
+        outs.append(full)
+    check_close(outs[0], ref, f"transposed split {ops} {M}x{N}x{K}")
+    assert np.array_equal(outs[0], outs[1]), "split result changed between identical calls"

@@ -51,6 +51,7 @@ def asm_builds(tmp_path_factory):
     as the race-check library builds it."""
     return _device_asm({"sgemm_lean.hip": ("sgemm_lean.hip", []),
                         "sgemm_lean_split.hip": ("sgemm_lean_split.hip", []),
+                        "sgemm_lean_split_t.hip": ("sgemm_lean_split_t.hip", []),
                         "poison:sgemm_lean.hip": ("sgemm_lean.hip", ["-DSGEMM_LDS_POISON=1"])},
                        tmp_path_factory.mktemp("asm"))
 
@@ -125,8 +126,9 @@ def test_no_waterfall_loops(lean_asm):
 
 def test_split_k_loop_keeps_loads_in_flight(lean_asm):
     kernels = _waits_after_direct_loads(lean_asm["sgemm_lean_split.hip"])
+    kernels.update(_waits_after_direct_loads(lean_asm["sgemm_lean_split_t.hip"]))
     split = {k: v for k, v in kernels.items() if "sgemm_lean_kernel" in k}
-    assert len(split) >= 20, sorted(kernels)
+    assert len(split) >= 32, sorted(kernels)
     # the K-remainder prologue and the edge paths may wait once or twice; a
     # serialised K loop waits after every load (17 of 32 in the 64x64x64
     # kernel before the ticket moved into the kernel's LDS buffer)
