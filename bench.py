@@ -29,7 +29,9 @@ with the operands stored transposed as named, "lowp:bf16" / "lowp:f16" =
 sgemm_lowp on the same values in that 16-bit type ("lowp:bf16:V" forces
 sgemm_lowp_ex variant V, "lowp:bf16:op:TN" and the like run sgemm_lowp_op
 with the operands stored transposed as named), "mm:bf16" / "mm:f16" =
-torch.mm in that type, 16-bit output, for context) on problems of the given sizes
+torch.mm in that type, 16-bit output, for context; "batch:B:TN" and the
+like = sgemm_strided_batched over B copies of the problem, stored as
+named, TFLOP/s over all B) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike (after half a second of untimed calls per size, for
 the clock): each round times a batch of back-to-back calls of every
@@ -254,11 +256,18 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
         flop = 2 * M * N * K
         reps = max(5, min(200, int(2e11 / max(flop, 1))))
 
-        stored, half = {}, {}
+        stored, half, batched = {}, {}, {}
         for v in variants:
             if isinstance(v, str) and v.startswith("op:"):
                 ta, tb = v[3] == "T", v[4] == "T"
                 stored[v] = (dA.t().contiguous() if ta else dA, dB.t().contiguous() if tb else dB, ta, tb)
+            if isinstance(v, str) and v.startswith("batch:"):
+                nb, ops = v.split(":")[1:3]
+                ta, tb = ops[0] == "T", ops[1] == "T"
+                a1 = dA.t().contiguous() if ta else dA
+                b1 = dB.t().contiguous() if tb else dB
+                batched[v] = (a1.unsqueeze(0).repeat(int(nb), 1, 1), b1.unsqueeze(0).repeat(int(nb), 1, 1),
+                              torch.empty((int(nb), M, N), device="cuda"), ta, tb)
             if isinstance(v, str) and v.split(":")[0] in ("lowp", "mm") and ":" in v:
                 parts = v.split(":")
                 t = {"bf16": torch.bfloat16, "f16": torch.float16}[parts[1]]
@@ -273,6 +282,8 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
                 return "torch.mm fp32"
             if v in stored:
                 return "sgemm_op " + v[3:5]
+            if v in batched:
+                return f"sgemm_strided_batched {v.split(':')[1]} x {v.split(':')[2]}"
             if v in half:
                 if v.startswith("lowp"):
                     parts = v.split(":")
@@ -303,6 +314,9 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
             elif v in stored:
                 sa, sb, ta, tb = stored[v]
                 sgemm_op(sa, sb, dC, trans_a=ta, trans_b=tb)
+            elif v in batched:
+                sa, sb, sc, ta, tb = batched[v]
+                sgemm_op(sa, sb, sc, trans_a=ta, trans_b=tb)
             else:
                 sgemm(dA, dB, dC, variant=None if v == -1 else v)
         usable = []
@@ -335,8 +349,9 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
                 times[v].append(st.elapsed_time(en) / reps)
         for v in usable:
             ms = statistics.median(times[v])
+            f = flop * (int(v.split(":")[1]) if v in batched else 1)
             print(json.dumps({"sweep": label(v), "variant": v, "shape": f"{M}x{N}x{K}", "median_ms": round(ms, 5),
-                              "tflops": round(flop / ms / 1e9, 2)}), flush=True)
+                              "tflops": round(f / ms / 1e9, 2)}), flush=True)
 
 
 def main():

@@ -48,7 +48,8 @@ hipError_t launch_lean_splitk_64x64x32_w4x1(const Args &a, int splits, hipStream
 hipError_t launch_lean_splitk_64x64x64_w4x1(const Args &a, int splits, hipStream_t stream);
 hipError_t launch_lean_splitk_64x128x32_w2x2(const Args &a, int splits, hipStream_t stream);
 hipError_t launch_lean_splitk_128x64x32_w4x1(const Args &a, int splits, hipStream_t stream);
-hipError_t launch_lean_splitk_t_64x64x64_w4x1(const Args &a, int splits, bool ta, bool tb, hipStream_t stream);
+hipError_t launch_lean_splitk_g_64x64x64_w4x1(const Args &a, int splits, bool ta, bool tb, int batch,
+                                              hipStream_t stream);
 }  // namespace sgemm_mi355x
 
 using namespace sgemm_mi355x;
@@ -223,8 +224,9 @@ double split_cost(long tiles, long kt, long s, int bm, int bn) {
     return (busiest > floor ? busiest : floor) + partials;
 }
 
-int choose_splits(int M, int N, int K, int bm, int bn, int bk) {
-    const long tiles = ceil_div(M, bm) * ceil_div(N, bn);
+// (`batch` problems of one strided batch count as batch times the tiles)
+int choose_splits(int M, int N, int K, int bm, int bn, int bk, long batch = 1) {
+    const long tiles = ceil_div(M, bm) * ceil_div(N, bn) * batch;
     const long kt = ceil_div(K, bk);
     const long fit = (long)(kSplitPartialBytes / ((size_t)bm * bn * sizeof(float)));
     if (tiles > kSplitMaxTiles || kt < 2) return 1;
@@ -934,10 +936,10 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
 // K x N (stored N x K when transposed).  An untransposed single problem takes
 // run() and its automatic choice.  Otherwise: the lean kernel (16-byte loads
 // for untransposed aligned operands, else 4-byte loads) on the tile
-// prefer_64() picks for batch x tiles; a single problem on 64x64x64 tiles
-// with 16-byte loads splits K as run() does (over the grid or the last
-// wave), batches and the other forms do not; shapes the lean kernel does
-// not take go to the plain kernel.
+// prefer_64() picks for batch x tiles; on 64x64x64 tiles with 16-byte
+// loads K splits as in run(): over the whole grid (a batch's tiles counted
+// together) or, for one problem, over the last wave; the other forms do not
+// split; shapes the lean kernel does not take go to the plain kernel.
 // ---------------------------------------------------------------------------
 // Unaligned transposed operands.  A transposed operand without 16-byte rows
 // takes the lean kernel's 4-byte gather, whose load instructions each touch
@@ -1111,15 +1113,16 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
     const bool lean = K >= bk && lean_fits(bm, bn, bk, lda, ldb, ta, tb);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (lean && vec && tile64 && batch == 1) {
-        // One transposed problem on 64x64x64 tiles with 16-byte loads: K
-        // split over the whole grid or over the last wave, by the cost
-        // models and with the workspaces of run().
+    if (lean && vec && tile64) {
+        // 64x64x64 tiles with 16-byte loads: K split over the whole grid
+        // (the tiles of every problem of a batch) or, for one problem, over
+        // the last wave, by the cost models and with the workspaces of run().
         Lease lease;
-        int ws = attach_workspace(a, choose_splits(M, N, K, 64, 64, 64), s, lease);
+        int ws = attach_workspace(a, choose_splits(M, N, K, 64, 64, 64, batch), s, lease);
         if (ws != SGEMM_STATUS_OK) return ws;
-        if (a.splits > 1) return finish(launch_lean_splitk_t_64x64x64_w4x1(a, a.splits, ta, tb, s), lease, s);
-        const int tail_splits = tail_split_factor(M, N, K, 64, 64, 64);
+        if (a.splits > 1)
+            return finish(launch_lean_splitk_g_64x64x64_w4x1(a, a.splits, ta, tb, batch, s), lease, s);
+        const int tail_splits = batch == 1 ? tail_split_factor(M, N, K, 64, 64, 64) : 1;
         if (tail_splits > 1) {
             const long tiles = ceil_div(M, 64) * ceil_div(N, 64), rem = tiles % kTailSlots;
             Args head = a, tail = a;
@@ -1130,11 +1133,11 @@ int run_general(int op_a, int op_b, int M, int N, int K, float alpha, const floa
             if (ws != SGEMM_STATUS_OK) return ws;
             if (tail.splits > 1) {
                 hipError_t e = launch_lean_general(head, true, false, ta, tb, 1, s);
-                if (e == hipSuccess) e = launch_lean_splitk_t_64x64x64_w4x1(tail, tail.splits, ta, tb, s);
+                if (e == hipSuccess) e = launch_lean_splitk_g_64x64x64_w4x1(tail, tail.splits, ta, tb, 1, s);
                 return finish(e, lease, s);
             }
         }
-        return finish(launch_lean_general(a, true, false, ta, tb, 1, s), lease, s);
+        return finish(launch_lean_general(a, true, false, ta, tb, batch, s), lease, s);
     }
     const hipError_t e =
         lean ? launch_lean_general(a, tile64, !vec, ta, tb, batch, s) : launch_simple_general(a, ta, tb, batch, s);

@@ -69,7 +69,9 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F7
 // accumulators (NACC 16-byte chunks per thread, acc(c) for chunk c) to
 // workspace slot blockIdx.y of the tile (chunk-major: chunk c of thread t at
 // c * NT + t, so each store and load instruction covers one contiguous run)
-// and takes a ticket from the tile's counter.  Returns false
+// and takes a ticket from the tile's counter.  The tiles of problem
+// blockIdx.z of a strided batch follow those of the problems before it, in
+// the partials and in the counters.  Returns false
 // for all blocks but the last; the last one reads all partials back, leaves
 // their sum in split order in acc and resets the counter for the next call.
 // The ticket is shared through word 0 of the kernel's own LDS buffer
@@ -90,8 +92,9 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
     constexpr int TILE = NT * NACC * 4;                 // floats per partial tile
     constexpr int kDeviceScope = 16;                    // cache policy bits: sc1
     const int S = gridDim.y, y = blockIdx.y;
+    const long tile = (long)blockIdx.z * gridDim.x + tile_id;
     const __amdgpu_buffer_rsrc_t slab = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.ws + (long)tile_id * S * TILE), (short)0, S * TILE * 4, 0x00020000);
+        (void *)(p.ws + tile * S * TILE), (short)0, S * TILE * 4, 0x00020000);
 #pragma unroll
     for (int c = 0; c < NACC; ++c)
         __builtin_amdgcn_raw_buffer_store_b128(acc(c), slab, (c * NT + tid) * 16, y * TILE * 4, kDeviceScope);
@@ -99,7 +102,7 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
     __syncthreads();
     if (tid == 0) {
         if constexpr (SGEMM_LDS_POISON) *reinterpret_cast<volatile unsigned *>(ticket) = kPoisonBits;
-        *ticket = atomicAdd(p.counters + tile_id, 1u);
+        *ticket = atomicAdd(p.counters + tile, 1u);
     }
     __syncthreads();
     if (*ticket != (unsigned)(S - 1)) return false;
@@ -113,7 +116,7 @@ __device__ __forceinline__ bool split_reduce_n(const Args &p, int tile_id, int t
             acc(c) = s == 0 ? x : acc(c) + x;
         }
     }
-    if (tid == 0) atomicExch(p.counters + tile_id, 0u);
+    if (tid == 0) atomicExch(p.counters + tile, 0u);
     return true;
 }
 

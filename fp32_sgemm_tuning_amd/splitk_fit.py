@@ -55,9 +55,10 @@ def _shape(s):
     return (p[0],) * 3 if len(p) == 1 else tuple(p)
 
 
-def model_cost(M, N, K, S, bm=64, bn=64, bk=64, block_fixed=2.8, split_fixed=1.7, per_partial=0.45):
-    """Modelled time of an M x N x K grid split S ways, in K-tile steps."""
-    tiles = _cd(M, bm) * _cd(N, bn)
+def model_cost(M, N, K, S, bm=64, bn=64, bk=64, block_fixed=2.8, split_fixed=1.7, per_partial=0.45, batch=1):
+    """Modelled time of an M x N x K grid (`batch` of them in one strided
+    batch) split S ways, in K-tile steps."""
+    tiles = _cd(M, bm) * _cd(N, bn) * batch
     kt = _cd(K, bk)
     r = _cd(tiles * S, CUS)
     busiest = r * _cd(kt, S) + _cd(r, 2) * block_fixed
@@ -66,10 +67,11 @@ def model_cost(M, N, K, S, bm=64, bn=64, bk=64, block_fixed=2.8, split_fixed=1.7
     return max(busiest, floor) + partials
 
 
-def choose(M, N, K, bm=64, bn=64, bk=64, **params):
-    """The factor the library's automatic choice takes (1 = no split)."""
-    params = {**LIB_PARAMS, **params}
-    tiles = _cd(M, bm) * _cd(N, bn)
+def choose(M, N, K, bm=64, bn=64, bk=64, batch=1, **params):
+    """The factor the library's automatic choice takes (1 = no split); a
+    strided batch counts its problems' tiles together."""
+    params = {**LIB_PARAMS, **params, "batch": batch}
+    tiles = _cd(M, bm) * _cd(N, bn) * batch
     kt = _cd(K, bk)
     fit = MAX_SPLIT_TILES * 64 * 64 // (bm * bn)
     if tiles > MAX_SPLIT_TILES or kt < 2 or tiles >= 2 * CUS:

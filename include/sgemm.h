@@ -237,7 +237,10 @@ int sgemm_op(int op_a, int op_b, int M, int N, int K, float alpha,
  * elements).  0 <= batch <= 65535.  stride_a and stride_b may be 0 (one
  * operand shared by all problems); the C problems must not overlap:
  * stride_c >= (M-1)*ldc + N when batch > 1.  One kernel launch for the whole
- * batch (no split-K).  Unaligned transposed operands are copied as in
+ * batch.  On 64x64 tiles with 16-byte loads K is split as in sgemm() with
+ * the tiles of all problems counted together (so a batch of small problems
+ * with long K spreads over the chip), using the stream's split-K workspace;
+ * other batches do not split.  Unaligned transposed operands are copied as in
  * sgemm_op(), for the whole batch in one launch per operand (an operand of
  * stride 0 once), when the copies' traffic takes less time than the product
  * and the copies fit in SGEMM_MAX_COPY_BUFFER_BYTES; the same buffer rules

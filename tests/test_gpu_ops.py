@@ -323,3 +323,74 @@ def test_transposed_split(ops, M, N, K, plan, ab):
         outs.append(full)
     check_close(outs[0], ref, f"transposed split {ops} {M}x{N}x{K}")
     assert np.array_equal(outs[0], outs[1]), "split result changed between identical calls"
+
+
+# Strided batches on 64x64x64 tiles with 16-byte loads split K over the
+# tiles of all their problems together (the factor of the restated rule,
+# splitk_fit.choose with the batch).
+BATCH_SPLIT_CASES = [
+    # (batch, M, N, K, shared): shared "A" / "B" = that operand's stride is 0
+    (4, 256, 256, 4096, None),
+    (3, 128, 192, 8192, "A"),
+    (2, 260, 516, 4100, None),      # edge tiles and a 4-deep K remainder
+    (6, 64, 64, 2048, "B"),
+    (5, 320, 320, 1024, None),
+]
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("case", BATCH_SPLIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}")
+def test_batched_split(ops, case):
+    """A strided batch whose grid splits K: every problem matches the oracle
+    element by element (beta != 0 and, in a second call, beta = 0 over NaN
+    C), the gaps between the C problems stay NaN, and a repeat is bit for
+    bit the same."""
+    from fp32_sgemm_tuning_amd import splitk_fit
+    torch = torch_cuda()
+    op_a, op_b = ops
+    batch, M, N, K, shared = case
+    assert splitk_fit.choose(M, N, K, batch=batch) > 1
+    print(f"[batch split] {OP_IDS[OPS.index(ops)]} {case}", flush=True)
+    probs = [make_problem(M, N, K, seed=100 * batch + M + N + K + z, dist="normal", with_c=True) for z in range(batch)]
+    if shared == "A":
+        probs = [(probs[0][0], B, C) for _, B, C in probs]
+    elif shared == "B":
+        probs = [(A, probs[0][1], C) for A, _, C in probs]
+    ta, tb = op_a == T_, op_b == T_
+    ra, ca = (K, M) if ta else (M, K)
+    rb, cb = (N, K) if tb else (K, N)
+    lda, ldb, ldc = ca + 4, cb + 8, N + 4
+    sa = 0 if shared == "A" else ra * lda + 8
+    sb = 0 if shared == "B" else rb * ldb + 4
+    sc = M * ldc + 12
+    bufA = torch.full((max(batch * sa, ra * lda) + 8,), float("nan"), device="cuda")
+    bufB = torch.full((max(batch * sb, rb * ldb) + 8,), float("nan"), device="cuda")
+
+    def put(buf, off, x, ld):
+        rows, cols = x.shape
+        buf[off:off + rows * ld].view(rows, ld)[:, :cols].copy_(torch.from_numpy(np.ascontiguousarray(x)))
+
+    for z, (A, B, _) in enumerate(probs):
+        put(bufA, z * sa, A.T if ta else A, lda)
+        put(bufB, z * sb, B.T if tb else B, ldb)
+    h = torch.cuda.current_stream().cuda_stream
+    for alpha, beta in ((-0.5, 1.25), (1.0, 0.0)):
+        results = []
+        for _ in range(2):
+            bufC = torch.full((batch * sc + 8,), float("nan"), device="cuda")
+            if beta != 0.0:
+                for z, (_, _, Cin) in enumerate(probs):
+                    put(bufC, z * sc, Cin, ldc)
+            st = capi.sgemm_strided_batched(op_a, op_b, M, N, K, alpha, bufA.data_ptr(), lda, sa, bufB.data_ptr(),
+                                            ldb, sb, beta, bufC.data_ptr(), ldc, sc, batch, h)
+            assert st == capi.SGEMM_STATUS_OK, capi.sgemm_strerror(st)
+            torch.cuda.synchronize()
+            results.append(bufC.cpu().numpy())
+        host = results[0]
+        for z, (A, B, Cin) in enumerate(probs):
+            got = host[z * sc:z * sc + M * ldc].reshape(M, ldc)
+            check_close(got[:, :N], oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta),
+                        f"batched split {ops} {case} problem {z} beta={beta}")
+            assert np.isnan(got[:, N:]).all(), "write into C's row padding"
+            assert np.isnan(host[z * sc + M * ldc:(z + 1) * sc]).all(), "write between C problems"
+        assert np.array_equal(results[0], results[1], equal_nan=True), "split result changed between calls"
