@@ -31,7 +31,8 @@ sgemm_lowp_ex variant V, "lowp:bf16:op:TN" and the like run sgemm_lowp_op
 with the operands stored transposed as named), "mm:bf16" / "mm:f16" =
 torch.mm in that type, 16-bit output, for context; "batch:B:TN" and the
 like = sgemm_strided_batched over B copies of the problem, stored as
-named, TFLOP/s over all B) on problems of the given sizes
+named, TFLOP/s over all B, "batch:B:NN:bf16" the same through
+sgemm_lowp on 16-bit copies) on problems of the given sizes
 ("N" for N^3 or "MxNxK"; packed row-major, so lda = K and ldb = ldc = N), interleaved round by round in one process so that clock drift hits
 every variant alike (after half a second of untimed calls per size, for
 the clock): each round times a batch of back-to-back calls of every
@@ -262,10 +263,14 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
                 ta, tb = v[3] == "T", v[4] == "T"
                 stored[v] = (dA.t().contiguous() if ta else dA, dB.t().contiguous() if tb else dB, ta, tb)
             if isinstance(v, str) and v.startswith("batch:"):
-                nb, ops = v.split(":")[1:3]
+                parts = v.split(":")
+                nb, ops = parts[1:3]
                 ta, tb = ops[0] == "T", ops[1] == "T"
                 a1 = dA.t().contiguous() if ta else dA
                 b1 = dB.t().contiguous() if tb else dB
+                if len(parts) > 3:           # 16-bit inputs
+                    t = {"bf16": torch.bfloat16, "f16": torch.float16}[parts[3]]
+                    a1, b1 = a1.to(t), b1.to(t)
                 batched[v] = (a1.unsqueeze(0).repeat(int(nb), 1, 1), b1.unsqueeze(0).repeat(int(nb), 1, 1),
                               torch.empty((int(nb), M, N), device="cuda"), ta, tb)
             if isinstance(v, str) and v.split(":")[0] in ("lowp", "mm") and ":" in v:
@@ -283,7 +288,10 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
             if v in stored:
                 return "sgemm_op " + v[3:5]
             if v in batched:
-                return f"sgemm_strided_batched {v.split(':')[1]} x {v.split(':')[2]}"
+                parts = v.split(":")
+                if len(parts) > 3:
+                    return f"sgemm_lowp_strided_batched {parts[3]} {parts[1]} x {parts[2]}"
+                return f"sgemm_strided_batched {parts[1]} x {parts[2]}"
             if v in half:
                 if v.startswith("lowp"):
                     parts = v.split(":")
@@ -316,7 +324,10 @@ def sweep(variants, sizes, rounds, settle_s=0.5):
                 sgemm_op(sa, sb, dC, trans_a=ta, trans_b=tb)
             elif v in batched:
                 sa, sb, sc, ta, tb = batched[v]
-                sgemm_op(sa, sb, sc, trans_a=ta, trans_b=tb)
+                if sa.dtype == torch.float32:
+                    sgemm_op(sa, sb, sc, trans_a=ta, trans_b=tb)
+                else:
+                    sgemm_lowp(sa, sb, sc, trans_a=ta, trans_b=tb)
             else:
                 sgemm(dA, dB, dC, variant=None if v == -1 else v)
         usable = []

@@ -1185,11 +1185,12 @@ bool lowp_fast_ok(const LowpVariant &v, int M, int N, int K, const void *A, int 
 // split-K) may use: the tile grid must fill less than 3/4 of its 512
 // workgroup slots (two per compute unit), each split keeps at least eight K
 // tiles, and the partial tiles fit the workspace.  1 for other variants.
-int lowp_max_splits(int variant, int M, int N, int K) {
+// (`batch` problems of one strided batch count as batch times the tiles)
+int lowp_max_splits(int variant, int M, int N, int K, long batch = 1) {
     if (variant != 1) return 1;
     const LowpVariant &v = kLowpVariants[variant];
     const long slots = 512;
-    const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
+    const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn) * batch;
     if (tiles * 4 >= slots * 3 || tiles > kSplitMaxTiles) return 1;
     long s = slots / tiles;
     s = std::min(s, ceil_div(K, v.bk) / 8);
@@ -1216,15 +1217,18 @@ double lowp_predict_us(int variant, int s, int M, int N, int K, long batch = 1) 
                                        : 5.0;
     const long waves = ceil_div(blocks, two_per_cu ? 512 : 256);
     double t = (double)waves * (2.0 * v.bm * v.bn * ((double)K / s) / (rate * 1e6) + 3.0);
-    if (s > 1) t += 2.0 * s * (double)M * N * 4 / 5e6 + 2.0;
+    if (s > 1) t += 2.0 * s * (double)M * N * batch * 4 / 5e6 + 2.0;
     return t;
 }
 
 // The split factor of a variant: the better of no split and the largest
 // allowed split by the prediction above.
-int lowp_splits(int variant, int M, int N, int K) {
-    const int s = lowp_max_splits(variant, M, N, K);
-    return s > 1 && lowp_predict_us(variant, s, M, N, K) < lowp_predict_us(variant, 1, M, N, K) ? s : 1;
+// SGEMM_SPLITK = S forces min(S, the largest allowed) for sweeps.
+int lowp_splits(int variant, int M, int N, int K, long batch = 1) {
+    const int s = lowp_max_splits(variant, M, N, K, batch);
+    if (knobs().splitk > 0) return std::min(s, knobs().splitk);
+    return s > 1 && lowp_predict_us(variant, s, M, N, K, batch) < lowp_predict_us(variant, 1, M, N, K, batch) ? s
+                                                                                                              : 1;
 }
 
 // Automatic choice among the 128x128 two-stage kernel (up to two workgroups
@@ -1241,7 +1245,7 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
     for (int id : {1, 2, 4, 5}) {
         if ((ta || tb) && !lowp_takes_ops(id)) continue;
         if (!lowp_fast_ok(kLowpVariants[id], M, N, K, A, lda, B, ldb, ta, tb)) continue;
-        const int s = ta || tb || batch > 1 ? 1 : lowp_splits(id, M, N, K);
+        const int s = ta || tb ? 1 : lowp_splits(id, M, N, K, batch);
         const double t = lowp_predict_us(id, s, M, N, K, batch);
         if (best == 0 || t < best_t) {
             best = id;
@@ -1442,7 +1446,7 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     a.strideC = batch > 1 ? (long)sC : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Lease lease;
-    const int ws = attach_workspace(a, ta || tb || batch > 1 ? 1 : lowp_splits(variant, M, N, K), s, lease);
+    const int ws = attach_workspace(a, ta || tb ? 1 : lowp_splits(variant, M, N, K, batch), s, lease);
     if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
     return finish(variant > 0 ? launch_lowp_tile(a, f16, variant - 1, ta, tb, batch, s)

@@ -368,8 +368,11 @@ int sgemm_lowp_select_variant(int M, int N, int K,
                               const void *B, int ldb);
 
 /* Split-K factor (1 = no split) that sgemm_lowp_ex() with this variant would
- * use for an M x N x K problem outside graph capture; no HIP call.  Returns
- * the factor, SGEMM_STATUS_INVALID_VARIANT or SGEMM_STATUS_INVALID_DIM. */
+ * use for an M x N x K problem outside graph capture; no HIP call.  (A strided
+ * batch of untransposed problems counts its problems' tiles together; the
+ * environment variable SGEMM_SPLITK = S caps the factor at S, for sweeps.)
+ * Returns the factor, SGEMM_STATUS_INVALID_VARIANT or
+ * SGEMM_STATUS_INVALID_DIM. */
 int sgemm_lowp_split_factor(int variant, int M, int N, int K);
 
 /* Static name of a sgemm_lowp_ex() variant, or NULL for an unknown id. */

@@ -452,3 +452,36 @@ def test_lowp_batched_copied_operands(dtype, ops, shared):
         check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(a, b, c, alpha=0.5, beta=-1.0),
                     f"batched copy {dtype} {ops} shared={shared} problem {z}")
         assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("batch,M,N,K,shared_b", [(4, 256, 256, 4096, False), (3, 128, 256, 8192, True),
+                                                  (8, 128, 128, 4096, False), (2, 200, 264, 2056, False)],
+                         ids=lambda x: str(x))
+def test_lowp_strided_batched_split(dtype, batch, M, N, K, shared_b):
+    """Strided batches of untransposed 16-bit problems whose tiles together
+    leave the chip mostly idle split K (the 128x128 two-stage kernel's
+    split-K, each problem's partials and counters after those of the
+    problems before it): every problem against the oracle, repeats bit for
+    bit, beta != 0 and beta = 0."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    print(f"[lowp] batched split {dtype} {batch} x {M}x{N}x{K} shared_b={shared_b}", flush=True)
+    probs = [make_problem_16bit(M, N, K, seed=300 + z, dtype=dtype, dist="normal", with_c=True) for z in range(batch)]
+    if shared_b:
+        probs = [(a, probs[0][1], c) for a, _, c in probs]
+    dA = torch.from_numpy(np.stack([a for a, _, _ in probs])).to(t).cuda()
+    dB = torch.from_numpy(probs[0][1][None] if shared_b else np.stack([b for _, b, _ in probs])).to(t).cuda()
+    for alpha, beta in ((0.75, -1.5), (1.0, 0.0)):
+        outs = []
+        for _ in range(2):
+            dC = torch.from_numpy(np.stack([c for _, _, c in probs])).cuda()
+            if beta == 0.0:
+                dC.fill_(float("nan"))
+            sgemm_lowp(dA, dB, dC, alpha=alpha, beta=beta)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().numpy())
+        for z, (a, b, c) in enumerate(probs):
+            check_close(outs[0][z], oracle.sgemm_ref(a, b, c if beta != 0.0 else None, alpha=alpha, beta=beta),
+                        f"batched split problem {z} beta={beta}")
+        assert np.array_equal(outs[0], outs[1]), "split result changed between calls"
