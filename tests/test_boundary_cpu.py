@@ -136,10 +136,12 @@ def _name(v):
     ((2048, 2048, 2048), "lean_64x64x64_w4x1_splitk"),
     ((2000, 2000, 500), "lean_64x64x64_w4x1_splitk"),
     # last wave of 128x128 tiles fuller than that of 64x64 tiles less 3%
-    ((4096, 4096, 4096), "lean_128x128x32_w2x2"),
-    ((8192, 8192, 8192), "lean_128x128x32_w2x2"),
-    ((4096, 4000, 100), "lean_128x128x32_w2x2"),
-    ((6000, 6000, 6000), "lean_128x128x32_w2x2"),
+    # (the split-capable form: whole waves launch the plain kernel, a partly
+    # filled last wave may split)
+    ((4096, 4096, 4096), "lean_128x128x32_w2x2_splitk"),
+    ((8192, 8192, 8192), "lean_128x128x32_w2x2_splitk"),
+    ((4096, 4000, 100), "lean_128x128x32_w2x2_splitk"),
+    ((6000, 6000, 6000), "lean_128x128x32_w2x2_splitk"),
     # a partly empty last wave of 128x128 tiles
     ((3072, 3072, 3072), "lean_64x64x64_w4x1_splitk"),
     ((2560, 2560, 2560), "lean_64x64x64_w4x1_splitk"),
@@ -388,6 +390,8 @@ def test_tail_split_plan():
     assert t(v128, 3072, 3072, 3072) == (4, 64)     # 576 tiles of 128x128, 96 K tiles
     assert t(v64, 2048, 2048, 2048) == (1, 0)       # whole waves
     assert t(v128, 4096, 4096, 4096) == (1, 0)
+    assert t(v128, 6016, 6016, 6016) == (3, 161)    # 2209 tiles of 128x128, 188 K tiles
+    assert t(v128, 7744, 7744, 7744) == (5, 137)
     assert t(v64, 1664, 1664, 1664) == (1, 0)       # 676 tiles: last wave a third full
     assert t(v64, 1600, 1600, 1600) == (2, 113)     # 625 tiles: 113 left, 25 K tiles
     assert t(v64, 1792, 1792, 1792) == (1, 0)       # 784 tiles: last wave over half full

@@ -326,6 +326,37 @@ def test_last_wave_split(M, N, K, name):
         assert np.array_equal(outs[0], outs[1])
 
 
+def test_last_wave_split_128_tiles():
+    """The automatic choice on 128x128 tiles splits a partly filled last wave
+    too (6016^3: 2209 tiles, 161 in the last wave, split 3 ways): the seeded
+    sample of 4096 entries plus the corners, and the full last 128 rows
+    (the last tile row, where the raster order puts the second launch's
+    tiles) and first 128 rows against the oracle, beta = 0 over NaN C and
+    beta != 0."""
+    torch = torch_cuda()
+    M = N = K = 6016
+    names = {capi.sgemm_variant_name(v): v for v in capi.all_variants()}
+    probe = torch.empty(1, device="cuda")
+    v = capi.sgemm_select_variant(M, N, K, probe.data_ptr(), K, probe.data_ptr(), N, 0.0, probe.data_ptr(), N)
+    assert capi.sgemm_variant_name(v) == "lean_128x128x32_w2x2_splitk"
+    assert capi.sgemm_tail_split(v, M, N, K) == (3, 161)
+    A, B, Cin = make_problem(M, N, K, 41, with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    I, J = sample_indices(M, N, 41)
+    for alpha, beta in ((1.0, 0.0), (0.5, 2.0)):
+        dC = to_dev(Cin, torch) if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+        sgemm(dA, dB, dC, alpha=alpha, beta=beta)
+        torch.cuda.synchronize()
+        got = dC.cpu().numpy()
+        cin = Cin if beta != 0.0 else None
+        check_close(got[I, J], oracle.sgemm_ref_sampled(A, B, I, J, cin, alpha=alpha, beta=beta),
+                    f"6016^3 sample beta={beta}")
+        for r0 in (0, M - 128):
+            slab_c = None if cin is None else np.ascontiguousarray(cin[r0:r0 + 128])
+            ref = oracle.sgemm_ref(np.ascontiguousarray(A[r0:r0 + 128]), B, slab_c, alpha=alpha, beta=beta)
+            check_close(got[r0:r0 + 128], ref, f"6016^3 rows {r0}.. beta={beta}")
+
+
 def test_binding_uses_the_current_stream():
     """The binding passes the current stream's handle, also inside a
     torch.cuda.stream() block, and a given stream's handle otherwise."""
