@@ -793,7 +793,7 @@ constexpr int variant_id(const char *name) {
 }
 // (the 128x128x32 form the automatic choice takes is the split-capable one:
 // on whole waves it launches the plain kernel, and a partly filled last wave
-// of tiles is split as for 64x64x64 tiles: 6000^3 to 7744^3 1.9-3.3% faster)
+// of tiles is split as for 64x64x64 tiles: 6000^3 to 7744^3 1.8-3.2% faster)
 constexpr int kVec = variant_id("lean_128x128x32_w2x2_splitk");
 constexpr int kVec64 = variant_id("lean_64x64x64_w4x1_splitk");
 constexpr int kAny = variant_id("lean_dw_128x128x32_w2x2");          // 4-byte loads, any alignment
