@@ -143,3 +143,67 @@ def test_pending_hip_error_left_alone():
         assert after == HIP_ERROR_INVALID_DEVICE, after
     torch.cuda.synchronize()
     check_close(C.cpu().numpy(), oracle.sgemm_ref(A, B), "with a pending error")
+
+
+def test_concurrent_streams_contend_for_workspaces():
+    """Twelve host threads, each on a stream of its own (more streams than
+    the library keeps workspaces), run split-K products concurrently: the
+    workspaces are handed between streams (the first such hand-over drains
+    the device once, later ones wait on the event recorded at the end of
+    each call), the memory held stays within the maximum, and every result
+    is bit for bit the single-stream split one, or, for a call that found
+    every workspace held at that moment and ran K unsplit, the unsplit
+    kernel's."""
+    import threading
+    torch = torch_cuda()
+    M, N, K = 512, 512, 2048                     # 64 tiles of 64x64: K split
+    A, B, _ = make_problem(M, N, K, 64)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    v = capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dA.data_ptr(), N)
+    assert capi.sgemm_split_factor(v, M, N, K) > 1
+    ref_c = torch.empty((M, N), device="cuda")
+    h0 = torch.cuda.current_stream().cuda_stream
+    assert capi.sgemm(M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, ref_c.data_ptr(), N, h0) == 0
+    names = {capi.sgemm_variant_name(x): x for x in capi.all_variants()}
+    plain_c = torch.empty((M, N), device="cuda")
+    assert capi.sgemm_ex(M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, plain_c.data_ptr(), N, h0,
+                         names["lean_64x64x64_w4x1"]) == 0
+    torch.cuda.synchronize()
+    expect, plain = ref_c.cpu().numpy(), plain_c.cpu().numpy()
+    check_close(expect, oracle.sgemm_ref(A, B), "single stream")
+    threads, calls = 12, 20
+    streams = [torch.cuda.Stream() for _ in range(threads)]
+    outs = [torch.full((calls, M, N), float("nan"), device="cuda") for _ in range(threads)]
+    errors = []
+    torch.cuda.synchronize()
+
+    def work(t):
+        try:
+            h = streams[t].cuda_stream
+            for i in range(calls):
+                st = capi.sgemm(M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, outs[t][i].data_ptr(), N, h)
+                if st != capi.SGEMM_STATUS_OK:
+                    errors.append((t, i, capi.sgemm_strerror(st)))
+                    return
+        except Exception as e:                   # reported below
+            errors.append((t, repr(e)))
+
+    pool = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+    for p in pool:
+        p.start()
+    for p in pool:
+        p.join(timeout=120)
+    assert not any(p.is_alive() for p in pool), "a thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    cap = capi.SGEMM_MAX_STREAM_WORKSPACES * capi.SGEMM_WORKSPACE_BYTES + capi.SGEMM_MAX_COPY_BUFFERS * (4 << 30)
+    assert capi.sgemm_workspace_bytes() <= cap
+    unsplit = 0
+    for t in range(threads):
+        got = outs[t].cpu().numpy()
+        for i in range(calls):
+            if np.array_equal(got[i], expect):
+                continue
+            assert np.array_equal(got[i], plain), f"thread {t} call {i} matches neither plan"
+            unsplit += 1
+    print(f"[boundary] {threads * calls} concurrent calls, {unsplit} ran unsplit", flush=True)
