@@ -179,7 +179,9 @@ typedef hipError_t (*Launcher)(const Args &, hipStream_t);
 // K over S blocks per tile multiplies the parallelism by S at the price of
 // writing and re-reading S partial tiles.  The model below counts two
 // resident blocks per CU, as for the 64x64x64 and 128x128x32 tiles (four
-// waves, 64 KiB of LDS); the automatic choice splits only the 64x64x64 ones.
+// waves, 64 KiB of LDS); in the automatic choice the grid splits on
+// 64x64x64 tiles (128x128x32 grids it picks hold at least 256 tiles and
+// never gain), and a partly filled last wave splits on either.
 constexpr long kNumCUs = 256;                            // MI355X
 constexpr long kTailSlots = 2 * kNumCUs;                 // resident lean blocks: two per CU
 constexpr long kSplitMaxTiles = 4096;                    // tiles with counters

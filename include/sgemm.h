@@ -343,8 +343,9 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * one shape, problem z on A + z*stride_a, B + z*stride_b (in 16-bit
  * elements) and C + z*stride_c (in floats); the rules of
  * sgemm_strided_batched() (0 <= batch <= 65535, strides of A and B may be 0,
- * C problems must not overlap, one launch, no split-K) and the automatic
- * variant choice over batch x tiles.  Batches the fast kernels cannot take
+ * C problems must not overlap, one launch) and the automatic variant choice
+ * over batch x tiles; an untransposed batch on the 128x128 two-stage kernel
+ * splits K over its problems' tiles together (sgemm_lowp_split_factor).  Batches the fast kernels cannot take
  * (unaligned rows, K or N not multiples of 8, or stride_a or stride_b not a
  * multiple of 8 elements, which leaves problems after the first unaligned)
  * are copied into zero-padded buffers as in sgemm_lowp(), one launch per
