@@ -161,22 +161,31 @@ def test_random_16bit(i):
 
 
 BATCH_CASES = 16
+LONG_K_BATCH_CASES = 16
 
 
-@pytest.mark.parametrize("i", range(BATCH_CASES))
+@pytest.mark.parametrize("i", range(BATCH_CASES + LONG_K_BATCH_CASES))
 def test_random_strided_batch(i):
     """sgemm_strided_batched on seeded random batches: 1 to 6 problems of
-    up to 700 x 700 x 1200, op(A), op(B) drawn, padded rows and gaps
-    between problems (NaN), A or B shared across the batch (stride 0) in a
-    quarter of the cases each; every problem against the oracle and every
-    gap of C untouched."""
+    up to 700 x 700 x 1200 (the first 16 cases) or of up to 300 x 300 with
+    K from 1024 to 8192 (the next 16: sizes, row padding and the gaps
+    between problems in whole 16-byte chunks, so these take the 16-byte
+    kernels, and their grids split K over the batch's tiles), op(A), op(B)
+    drawn, padded rows and gaps between problems (NaN), A or B shared across
+    the batch (stride 0) in a quarter of the cases each; every problem
+    against the oracle and every gap of C untouched."""
     torch = torch_cuda()
     rng = np.random.default_rng(9300 + i)
-    M, N, K = (int(rng.integers(1, 701)), int(rng.integers(1, 701)), int(rng.integers(1, 1201)))
+    if i < BATCH_CASES:
+        M, N, K = (int(rng.integers(1, 701)), int(rng.integers(1, 701)), int(rng.integers(1, 1201)))
+    else:
+        M, N, K = (4 * int(rng.integers(1, 76)), 4 * int(rng.integers(1, 76)), 4 * int(rng.integers(256, 2049)))
     batch = int(rng.integers(1, 7))
     ta, tb = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
     share = int(rng.integers(0, 4))          # 0: A shared, 1: B shared, else neither
     pa, pb, pc = (int(x) for x in rng.integers(0, 6, size=3))
+    if i >= BATCH_CASES:
+        pa, pb, pc = 4 * (pa % 2), 4 * (pb % 2), 4 * (pc % 2)
     alpha, beta = float(rng.choice([1.0, -0.5, 2.25])), float(rng.choice([0.0, 1.0, -1.5]))
     print(f"[random batch {i}] {batch} x {M}x{N}x{K} {'T' if ta else 'N'}{'T' if tb else 'N'} share {share} "
           f"pads {pa},{pb},{pc} alpha {alpha} beta {beta}", flush=True)
@@ -188,9 +197,10 @@ def test_random_strided_batch(i):
     ra, ca = (K, M) if ta else (M, K)
     rb, cb = (N, K) if tb else (K, N)
     lda, ldb, ldc = ca + pa, cb + pb, N + pc
-    sa = 0 if share == 0 else ra * lda + 3
-    sb = 0 if share == 1 else rb * ldb + 5
-    sc = M * ldc + 7
+    gap = (lambda g: 4 * g) if i >= BATCH_CASES else (lambda g: g)
+    sa = 0 if share == 0 else ra * lda + gap(3)
+    sb = 0 if share == 1 else rb * ldb + gap(5)
+    sc = M * ldc + gap(7)
     bufA = torch.full((max(batch * sa, ra * lda) + 8,), float("nan"), device="cuda")
     bufB = torch.full((max(batch * sb, rb * ldb) + 8,), float("nan"), device="cuda")
     bufC = torch.full((batch * sc + 8,), float("nan"), device="cuda")
