@@ -26,7 +26,7 @@ SGEMM_WORKSPACE_BYTES = 64 * 1024 * 1024 + 16 * 1024
 SGEMM_MAX_STREAM_WORKSPACES = 8
 SGEMM_MAX_COPY_BUFFERS = 2
 SGEMM_MAX_COPY_BUFFER_BYTES = 4 << 30
-SGEMM_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024 + 16 * 1024
+SGEMM_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024 + 16 * 1024
 
 SGEMM_DTYPE_BF16 = 1
 SGEMM_DTYPE_F16 = 2

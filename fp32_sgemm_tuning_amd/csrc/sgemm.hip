@@ -519,7 +519,10 @@ int finish(hipError_t launch, Lease &lease, hipStream_t stream) {
 // before the product (no hipMemsetAsync, so the calls can be captured into
 // a graph).  Every call on a device shares the array: calls that overlap
 // in time on one device race.
-constexpr size_t kScratchPartialBytes = 32u << 20;     // largest automatic plan: about 24.4 MiB
+// As large as a split-K workspace: the planner keeps every split, forced
+// factors included, within kSplitPartialBytes (128x128 last-wave splits of
+// the automatic choice reach 63 MiB), so each plan sgemm() makes fits.
+constexpr size_t kScratchPartialBytes = kSplitPartialBytes;
 constexpr size_t kScratchBytes = kScratchPartialBytes + kSplitMaxTiles * sizeof(unsigned);
 static_assert(kScratchBytes == (size_t)SGEMM_NOALLOC_SCRATCH_BYTES, "scratch size in sgemm.h");
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

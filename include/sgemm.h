@@ -91,7 +91,7 @@ extern "C" {
 #define SGEMM_MAX_STREAM_WORKSPACES 8       /* split-K workspaces kept per device */
 #define SGEMM_MAX_COPY_BUFFERS 2            /* copy buffers kept per device */
 #define SGEMM_MAX_COPY_BUFFER_BYTES (4ll << 30)  /* largest copy buffer; larger copies are not made */
-#define SGEMM_NOALLOC_SCRATCH_BYTES (32ll * 1024 * 1024 + 16 * 1024)  /* sgemm_noalloc's static scratch, per device */
+#define SGEMM_NOALLOC_SCRATCH_BYTES (64ll * 1024 * 1024 + 16 * 1024)  /* sgemm_noalloc's static scratch, per device */
 
 /* Input element types of sgemm_lowp. */
 #define SGEMM_DTYPE_BF16 1                  /* bfloat16: 1 sign, 8 exponent, 7 fraction bits */
@@ -160,11 +160,12 @@ int sgemm_ex(int M, int N, int K, float alpha,
  * device's array and the array keeps the last call's contents: calls that
  * overlap in time on one device (on different streams, or from different
  * host threads) race and must be ordered by the caller; calls in order on
- * one stream are safe.  A problem whose split of K needs more partial-tile
- * storage than the array holds (32 MiB; the automatic choice needs at most
- * about 24.4 MiB, unless SGEMM_SPLITK forces larger splits) returns
- * SGEMM_STATUS_SCRATCH_TOO_SMALL with nothing enqueued.  Other statuses as
- * for sgemm().
+ * one stream are safe.  The array holds 64 MiB of partial tiles, as much
+ * as a split-K workspace, and sgemm() keeps every split within that (the
+ * automatic choice reaches 63 MiB on large 128x128 grids whose last wave
+ * splits; SGEMM_SPLITK is clamped to it), so every plan fits;
+ * SGEMM_STATUS_SCRATCH_TOO_SMALL, with nothing enqueued, guards a plan that
+ * would not.  Other statuses as for sgemm().
  */
 int sgemm_noalloc(int M, int N, int K, float alpha,
                   const float *A, int lda,
