@@ -801,9 +801,10 @@ constexpr int variant_id(const char *name) {
 // of tiles is split as for 64x64x64 tiles: 6000^3 to 7744^3 1.8-3.2% faster)
 constexpr int kVec = variant_id("lean_128x128x32_w2x2_splitk");
 constexpr int kVec64 = variant_id("lean_64x64x64_w4x1_splitk");
+constexpr int kVec64ShortK = variant_id("lean_64x64x32_w4x1_splitk");
 constexpr int kAny = variant_id("lean_dw_128x128x32_w2x2");          // 4-byte loads, any alignment
 constexpr int kAny64 = variant_id("lean_dw_64x64x64_w4x1_splitk");
-static_assert(kVec >= 0 && kVec64 >= 0 && kAny >= 0 && kAny64 >= 0, "variant table");
+static_assert(kVec >= 0 && kVec64 >= 0 && kVec64ShortK >= 0 && kAny >= 0 && kAny64 >= 0, "variant table");
 constexpr int kMaxBatch = 65535;  // problems per strided batch (launch grid z extent)
 
 // Fill of the last wave of blocks: with t tiles spread over the CUs, the
@@ -829,14 +830,21 @@ bool prefer_64(int M, int N, long batch = 1) {
 
 // Automatic choice: the lean kernel with 16-byte loads when the operands
 // allow them, else the lean kernel with 4-byte loads; the tile by
-// prefer_64(); the 64x64x64 forms split K where choose_splits() or
-// choose_tail_splits() says so.  No HIP call.
+// prefer_64(); the split-capable forms split K where choose_splits() or
+// choose_tail_splits() says so.  Short K (at most 256) on a grid of at
+// least one full wave of 64x64 tiles takes the 32-deep K tile, whose
+// shorter first loads and pipeline fill weigh less over few K tiles:
+// 1536^2, 1600^2, 2048^2, 2560x2624 and 2944^2 at K = 128 and 256 2-9%
+// faster than the 64-deep one (at K = 384 and 512 the two trade places
+// with the shape, at K = 1024 the 64-deep one leads by 8%; with at most 8
+// K tiles of 32 no last-wave split pays).  No HIP call.
 int auto_variant(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float beta,
                  const float *C, int ldc) {
     const bool small = prefer_64(M, N);
     // (the 16-byte kernels also need K and N multiples of 4: whole chunks
     // at the edges; aligned operands with other K or N take the 4-byte ones)
     if (!vec_ok(K, A, lda, B, ldb, beta, C, ldc) || K % 4 || N % 4) return small ? kAny64 : kAny;
+    if (small && K <= 256 && ceil_div(M, 64) * ceil_div(N, 64) >= kTailSlots) return kVec64ShortK;
     return small ? kVec64 : kVec;
 }
 

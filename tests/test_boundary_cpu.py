@@ -142,6 +142,14 @@ def _name(v):
     ((8192, 8192, 8192), "lean_128x128x32_w2x2_splitk"),
     ((4096, 4000, 100), "lean_128x128x32_w2x2_splitk"),
     ((6000, 6000, 6000), "lean_128x128x32_w2x2_splitk"),
+    # short K (at most 256) on at least one full wave of 64x64 tiles: the
+    # 32-deep K tile; fewer tiles, or longer K, keep the 64-deep one
+    ((2944, 2944, 256), "lean_64x64x32_w4x1_splitk"),
+    ((2048, 2048, 128), "lean_64x64x32_w4x1_splitk"),
+    ((1536, 1536, 256), "lean_64x64x32_w4x1_splitk"),
+    ((1024, 1024, 256), "lean_64x64x64_w4x1_splitk"),
+    ((2944, 2944, 512), "lean_64x64x64_w4x1_splitk"),
+    ((4096, 4096, 256), "lean_128x128x32_w2x2_splitk"),
     # a partly empty last wave of 128x128 tiles
     ((3072, 3072, 3072), "lean_64x64x64_w4x1_splitk"),
     ((2560, 2560, 2560), "lean_64x64x64_w4x1_splitk"),

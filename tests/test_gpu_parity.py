@@ -326,6 +326,28 @@ def test_last_wave_split(M, N, K, name):
         assert np.array_equal(outs[0], outs[1])
 
 
+SHORT_K_CASES = [(2944, 2944, 256), (2048, 2056, 132), (1536, 1540, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", SHORT_K_CASES, ids=[f"{m}x{n}x{k}" for m, n, k in SHORT_K_CASES])
+def test_short_k_auto(M, N, K):
+    """Short K on a full wave of 64x64 tiles: the automatic choice takes the
+    32-deep K tile (a K remainder in the second case, one K tile in the
+    third); every element against the oracle, beta = 0 over NaN C and
+    beta != 0."""
+    torch = torch_cuda()
+    A, B, Cin = make_problem(M, N, K, seed=M + N + K, dist="normal", with_c=True)
+    dA, dB = to_dev(A, torch), to_dev(B, torch)
+    v = capi.sgemm_select_variant(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dA.data_ptr(), N)
+    assert capi.sgemm_variant_name(v) == "lean_64x64x32_w4x1_splitk"
+    for alpha, beta in ((1.0, 0.0), (-0.5, 1.5)):
+        dC = to_dev(Cin, torch) if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+        sgemm(dA, dB, dC, alpha=alpha, beta=beta)
+        torch.cuda.synchronize()
+        check_close(dC.cpu().numpy(), oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=alpha, beta=beta),
+                    f"short K {M}x{N}x{K} beta={beta}")
+
+
 def test_last_wave_split_128_tiles():
     """The automatic choice on 128x128 tiles splits a partly filled last wave
     too (6016^3: 2209 tiles, 161 in the last wave, split 3 ways): the seeded
