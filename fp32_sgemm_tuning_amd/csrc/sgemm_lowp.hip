@@ -514,28 +514,71 @@ sgemm_lowp_kernel(Args p) {
     // N; its columns are then stored one by one.)
     const float alpha = p.alpha, beta = p.beta;
     const bool vecc = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc & 3) == 0;
+    if constexpr (BETA0 || EDGE) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = m0 + wm * WM + mi * 16 + lrow;
+                const int col = n0 + wn * WN + nb * 16 + 4 * lg;
+                if (EDGE && row >= p.M) continue;
+                float *dst = p.C + (long)row * p.ldc + col;
+                if (vecc && (!EDGE || col + 3 < p.N)) {
+                    f32x4 o = acc[mi][nb] * alpha;
+                    if (!BETA0) o += *reinterpret_cast<const f32x4 *>(dst) * beta;
+                    *reinterpret_cast<f32x4 *>(dst) = o;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (EDGE && col + r >= p.N) continue;
+                        float o = alpha * acc[mi][nb][r];
+                        if (!BETA0) o += beta * dst[r];
+                        dst[r] = o;
+                    }
+                }
+            }
+        return;
+    }
+    // Whole tiles with beta != 0: the C values of a row group's NB blocks
+    // are loaded before the first of their stores.  Each is read and written
+    // by this lane alone and the rows of C are disjoint (ldc >= N), so the
+    // order is free, and the loads wait for memory once per row group
+    // instead of once per block (a compiler cannot move a load above a store
+    // it cannot prove disjoint).  The 16-byte test of C is taken once,
+    // outside the loops, so that no branch splits a row group's loads from
+    // its stores.  (4096^3 BF16, alpha = beta = 1: 117.7 -> 112.3 us.  Edge
+    // tiles keep the per-block order: their guarded loads, made branch-free,
+    // ran slower than the waits they saved.)
+    auto write = [&](auto vec_c) __attribute__((always_inline)) {
+        constexpr bool VC = decltype(vec_c)::value;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
             const int row = m0 + wm * WM + mi * 16 + lrow;
-            const int col = n0 + wn * WN + nb * 16 + 4 * lg;
-            if (EDGE && row >= p.M) continue;
-            float *dst = p.C + (long)row * p.ldc + col;
-            if (vecc && (!EDGE || col + 3 < p.N)) {
-                f32x4 o = acc[mi][nb] * alpha;
-                if (!BETA0) o += *reinterpret_cast<const f32x4 *>(dst) * beta;
-                *reinterpret_cast<f32x4 *>(dst) = o;
-            } else {
+            f32x4 cin[NB];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (EDGE && col + r >= p.N) continue;
-                    float o = alpha * acc[mi][nb][r];
-                    if (!BETA0) o += beta * dst[r];
-                    dst[r] = o;
+            for (int nb = 0; nb < NB; ++nb) {
+                const float *src = p.C + (long)row * p.ldc + n0 + wn * WN + nb * 16 + 4 * lg;
+                if constexpr (VC) {
+                    cin[nb] = *reinterpret_cast<const f32x4 *>(src);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) cin[nb][r] = src[r];
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float *dst = p.C + (long)row * p.ldc + n0 + wn * WN + nb * 16 + 4 * lg;
+                if constexpr (VC) {
+                    *reinterpret_cast<f32x4 *>(dst) = acc[mi][nb] * alpha + cin[nb] * beta;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[r] = alpha * acc[mi][nb][r] + beta * cin[nb][r];
                 }
             }
         }
+    };
+    if (vecc) write(std::true_type{});
+    else write(std::false_type{});
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool F16, bool PP, bool SPLIT, bool TA = false,
