@@ -1360,11 +1360,55 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
              const void *B, int ldb, float beta, float *C, int ldc, void *stream, int variant,
              long long sA, long long sB, long long sC, int batch, bool padded_b);
 
+// Whether the fast kernels on the copies can take an untransposed operand
+// as it is instead of a copy of it: 16-byte aligned rows whose length
+// (`cols`, K for A and N for B) and K are multiples of 8, so that the
+// padded K8 and N8 are K and N; in a batch, a stride of whole chunks.
+bool lowp_keeps(const void *X, int ldx, int cols, int K, long long stride, int batch) {
+    return aligned16(X) && ldx % 8 == 0 && cols % 8 == 0 && K % 8 == 0 && (batch <= 1 || stride % 8 == 0);
+}
+
+// Whether a problem (or strided batch) with transposed operands that an
+// alternating kernel takes runs faster as the product of row-major copies:
+// those kernels have no split form, so a grid of few tiles with long K keeps
+// a few compute units busy for a long time, while the product on the copies
+// splits K.  Compares the predicted times (lowp_predict_us, plus the copies'
+// traffic at about 3 TB/s and 6 us per copy launch, which a 0.5 MB copy
+// measured) with a margin for the model: the copies must save a quarter.
+// Only transposed operands and untransposed ones the fast kernels cannot
+// take as they are get copied.  Measured on MI355X (BF16, beta = 0, us,
+// direct -> copies): 512x512x8192 TN 69.4 -> 35.1, NT 51.0 -> 34.8, TT
+// 60.2 -> 41.3; 768x1024x16384 TN 136 -> 71, NT 98 -> 75, TT 116 -> 87;
+// 384x256x8192 TN 69.0 -> 32.3; 256x256x4096 NT 27.7 -> 22.2.  SGEMM_PACK
+// = -1 keeps the direct kernels.
+bool lowp_transpose_copy_pays(int variant, bool ta, bool tb, int M, int N, int K, const void *A, int lda,
+                              long long sA, const void *B, int ldb, long long sB, int batch, void *stream) {
+    if (!(ta || tb) || knobs().pack < 0 || K < 64) return false;
+    if (capturing(reinterpret_cast<hipStream_t>(stream))) return false;
+    const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
+    if (ceil_div(M, 32) > 65535 || ceil_div(K8, 32) > 65535) return false;   // transpose grids
+    const bool ca = ta || !lowp_keeps(A, lda, K, K, sA, batch);
+    const bool cb = tb || !lowp_keeps(B, ldb, N, K, sB, batch);
+    const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
+    const double copied = 2.0 * ((ca ? (double)na * M * K8 : 0.0) + (cb ? (double)nb * K8 * N8 : 0.0));
+    if (copied > kCopyMaxBytes) return false;
+    const int vc = lowp_auto(M, (int)N8, (int)K8, ca ? nullptr : A, ca ? (int)K8 : lda, cb ? nullptr : B,
+                             cb ? (int)N8 : ldb, false, false, batch);
+    if (vc == 0) return false;
+    if (knobs().pack > 0) return true;
+    const double t_copy = 2.0 * copied / 3e12 * 1e6 + 6.0 * (ca + cb) +
+                          lowp_predict_us(vc, lowp_splits(vc, M, (int)N8, (int)K8, batch), M, (int)N8, (int)K8, batch);
+    return t_copy < 0.75 * lowp_predict_us(variant, 1, M, N, K, batch);
+}
+
+
 // The 16-bit product on zero-padded row-major copies of op(A) and op(B)
-// (transposed operands transposed on the way).  In a batch, an operand of
-// stride 0 is copied once and each other one per problem (strides of the
-// copies: multiples of 128 elements).  Returns kUnavailable, with nothing
-// enqueued, when the stream's copy buffer is held by another call.
+// (transposed operands transposed on the way); an untransposed operand the
+// fast kernels take as it is (lowp_keeps) is used in place.  In a batch, an
+// operand of stride 0 is copied once and each other one per problem
+// (strides of the copies: multiples of 128 elements).  Returns kUnavailable,
+// with nothing enqueued, when the stream's copy buffer is held by another
+// call.
 int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alpha, const void *A, int lda,
                     long long sA, const void *B, int ldb, long long sB, float beta, float *C, int ldc,
                     long long sC, int batch, void *stream) {
@@ -1372,31 +1416,46 @@ int run_lowp_copied(int dtype, bool ta, bool tb, int M, int N, int K, float alph
     const int K8 = (K + 7) & ~7, N8 = (N + 7) & ~7;
     const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
     const size_t a_one = ((size_t)M * K8 + 127) & ~(size_t)127, b_one = ((size_t)K8 * N8 + 127) & ~(size_t)127;
+    bool ca = ta || !lowp_keeps(A, lda, K, K, sA, batch);
+    bool cb = tb || !lowp_keeps(B, ldb, N, K, sB, batch);
     // the fast kernels on the copies: chosen for the padded width, run on the
     // true one (their loads of B's last chunk read the zero padding); the
-    // copies are 16-byte aligned, so only the pointer alignment matters here
-    const int v = lowp_auto(M, N8, K8, nullptr, K8, nullptr, N8, false, false, batch);
+    // copies are 16-byte aligned (null stands for them here)
+    auto pick = [&] {
+        return lowp_auto(M, N8, K8, ca ? nullptr : A, ca ? K8 : lda, cb ? nullptr : B, cb ? N8 : ldb, false, false,
+                         batch);
+    };
+    int v = pick();
+    if (v == 0 && !(ca && cb)) {      // an operand in place is outside the kernels' ranges: copy both
+        ca = cb = true;
+        v = pick();
+    }
     if (v == 0) return SGEMM_STATUS_UNSUPPORTED;
+    const size_t a_elems = ca ? a_one * na : 0, b_elems = cb ? b_one * nb : 0;
     Lease lease;
-    const int st = acquire_slot(kCopySlot, s, (a_one * na + b_one * nb) * 2, lease);
+    const int st = acquire_slot(kCopySlot, s, (a_elems + b_elems) * 2, lease);
     if (st != SGEMM_STATUS_OK) return st;
-    unsigned short *Ap = static_cast<unsigned short *>(lease.mem), *Bp = Ap + a_one * na;
+    unsigned short *Ap = static_cast<unsigned short *>(lease.mem), *Bp = Ap + a_elems;
     const long src_a = na > 1 ? (long)sA : 0, src_b = nb > 1 ? (long)sB : 0;
-    hipError_t e = ta   // stored K x M
-                       ? launch_k(transpose16_kernel,
-                                  dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32), (unsigned)na), dim3(256),
-                                  s, static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8, src_a,
-                                  (long)a_one)
-                       : launch_pack16(A, lda, M, K, Ap, M, K8, s, na, src_a, (long)a_one);
-    if (e == hipSuccess)
+    hipError_t e = hipSuccess;
+    if (ca)
+        e = ta   // stored K x M
+                ? launch_k(transpose16_kernel,
+                           dim3((unsigned)ceil_div(K8, 32), (unsigned)ceil_div(M, 32), (unsigned)na), dim3(256), s,
+                           static_cast<const unsigned short *>(A), (long)lda, M, K, Ap, M, K8, src_a, (long)a_one)
+                : launch_pack16(A, lda, M, K, Ap, M, K8, s, na, src_a, (long)a_one);
+    if (e == hipSuccess && cb)
         e = tb   // stored N x K
                 ? launch_k(transpose16_kernel, dim3((unsigned)ceil_div(N8, 32), (unsigned)ceil_div(K8, 32), (unsigned)nb),
                            dim3(256), s, static_cast<const unsigned short *>(B), (long)ldb, K, N, Bp, K8, N8, src_b,
                            (long)b_one)
                 : launch_pack16(B, ldb, K, N, Bp, K8, N8, s, nb, src_b, (long)b_one);
     if (e != hipSuccess) return finish(e, lease, s);
-    const int prod = run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, Ap, K8, Bp, N8, beta, C, ldc, stream, v,
-                              na > 1 ? (long long)a_one : 0, nb > 1 ? (long long)b_one : 0, sC, batch, true);
+    const long long pa = ca ? (na > 1 ? (long long)a_one : 0) : (batch > 1 ? sA : 0);
+    const long long pb = cb ? (nb > 1 ? (long long)b_one : 0) : (batch > 1 ? sB : 0);
+    const int prod = run_lowp(dtype, SGEMM_OP_N, SGEMM_OP_N, M, N, K8, alpha, ca ? (const void *)Ap : A,
+                              ca ? K8 : lda, cb ? (const void *)Bp : B, cb ? N8 : ldb, beta, C, ldc, stream, v, pa, pb,
+                              sC, batch, true);
     const int rel = release_slot(lease, s);
     return prod != SGEMM_STATUS_OK ? prod : rel;
 }
@@ -1428,7 +1487,10 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (variant == SGEMM_VARIANT_AUTO) {
         variant = strides8 ? lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch) : 0;
         const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
-        if (variant == 0 && lowp_copy_plan(M, N, K, stream, batch, na, nb)) {
+        const bool copy = variant == 0 ? lowp_copy_plan(M, N, K, stream, batch, na, nb)
+                                       : lowp_transpose_copy_pays(variant, ta, tb, M, N, K, A, lda, sA, B, ldb, sB,
+                                                                  batch, stream);
+        if (copy) {
             const int st = run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
                                            batch, stream);
             if (st != kUnavailable) return st;

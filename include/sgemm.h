@@ -290,7 +290,8 @@ int sgemm_cm_strided_batched(int op_a, int op_b, int M, int N, int K, float alph
  * K >= 64, large enough that copying them takes less time than the plain
  * kernel would, are first copied into zero-padded aligned buffers (K and N
  * rounded up to multiples of 8; the stream's copy buffer, as for
- * sgemm_op) and run on the fast path; the rest (and a call whose stream's
+ * sgemm_op; an operand the fast path takes as it is, with K a multiple of
+ * 8, is used in place) and run on the fast path; the rest (and a call whose stream's
  * buffer is held by another call at that moment) runs a plain kernel that
  * widens each element on load.  SGEMM_PACK = 1 / -1 forces the copy on / off.  Small
  * tile grids split K and use the workspace described above (same rules:
@@ -326,12 +327,17 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
  * automatic choice); transposed operands run on the alternating-schedule
  * variants or the plain kernel, with each operand kept in LDS in its stored
  * orientation (16-byte chunks along its contiguous extent, which must be a
- * multiple of 8 elements for the fast path).  No split-K on stored
- * transposed operands.  With SGEMM_VARIANT_AUTO, operands the fast path
- * cannot take are copied as in sgemm_lowp(), transposed on the way into
- * zero-padded row-major buffers, and the product runs untransposed on the
- * copies (where it may split K, deterministically).  Returns
- * SGEMM_STATUS_*; SGEMM_STATUS_INVALID_OP for another op code.
+ * multiple of 8 elements for the fast path).  Those variants do not split
+ * K.  With SGEMM_VARIANT_AUTO, operands the fast path cannot take are
+ * copied as in sgemm_lowp(), transposed on the way into zero-padded
+ * row-major buffers, and the product runs untransposed on the copies (where
+ * it may split K, deterministically); so are transposed operands the fast
+ * path takes when the predicted time of copies plus split product is at
+ * most 3/4 of the alternating kernels' (a grid of few tiles with long K:
+ * 512x512x8192 BF16 TN 69 -> 35 us).  An untransposed operand the fast path
+ * takes as it is (K a multiple of 8) is used in place.  SGEMM_PACK = -1
+ * keeps every operand in place.  Returns SGEMM_STATUS_*;
+ * SGEMM_STATUS_INVALID_OP for another op code.
  */
 int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
                   const void *A, int lda,
@@ -352,8 +358,9 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * are copied into zero-padded buffers as in sgemm_lowp(), one launch per
  * operand for the whole batch (an operand of stride 0 once), when that
  * takes less time than the plain kernel and the copies fit in
- * SGEMM_MAX_COPY_BUFFER_BYTES; the rest run on the plain kernel.  Returns
- * SGEMM_STATUS_*.
+ * SGEMM_MAX_COPY_BUFFER_BYTES; the rest run on the plain kernel.
+ * Transposed batches of few tiles with long K are copied as for
+ * sgemm_lowp_op().  Returns SGEMM_STATUS_*.
  */
 int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
                                const void *A, int lda, long long stride_a,

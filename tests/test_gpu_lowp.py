@@ -485,3 +485,81 @@ def test_lowp_strided_batched_split(dtype, batch, M, N, K, shared_b):
             check_close(outs[0][z], oracle.sgemm_ref(a, b, c if beta != 0.0 else None, alpha=alpha, beta=beta),
                         f"batched split problem {z} beta={beta}")
         assert np.array_equal(outs[0], outs[1]), "split result changed between calls"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ops", [(True, False), (False, True), (True, True)], ids=["TN", "NT", "TT"])
+@pytest.mark.parametrize("shape", [(384, 256, 8192), (200, 264, 4104)], ids=lambda s: "x".join(map(str, s)))
+def test_lowp_transposed_long_k_copies(dtype, ops, shape):
+    """Transposed operands that the alternating kernels take, on a grid of
+    few tiles with long K: the automatic choice copies the transposed
+    operands into row-major buffers and runs the split untransposed product,
+    with an untransposed operand used in place.  Parity with the oracle,
+    NaN in the padding of the stored operands, beta = 0 (NaN C) and
+    beta != 0, twice in a row (the copy buffer reused), bit-identical
+    repeats."""
+    torch = torch_cuda()
+    ta, tb = ops
+    M, N, K = shape
+    A, B, Cin = make_problem_16bit(M, N, K, seed=M + N + K + 2 * ta + tb, dtype=dtype, dist="normal", with_c=True)
+    sA = np.ascontiguousarray(A.T) if ta else A
+    sB = np.ascontiguousarray(B.T) if tb else B
+    dA, _ = _dev16(sA, dtype, torch, ld=sA.shape[1] + 8)
+    dB, _ = _dev16(sB, dtype, torch, ld=sB.shape[1] + 16)
+    print(f"[lowp long-K op] {dtype} TA={ta} TB={tb} {M}x{N}x{K}", flush=True)
+    for beta in (0.0, -0.75):
+        ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=1.5, beta=beta)
+        outs = []
+        for _ in range(2):
+            dC = torch.from_numpy(Cin).to("cuda") if beta != 0.0 else torch.full((M, N), float("nan"), device="cuda")
+            sgemm_lowp(dA, dB, dC, alpha=1.5, beta=beta, trans_a=ta, trans_b=tb)
+            torch.cuda.synchronize()
+            outs.append(dC.cpu().numpy())
+            check_close(outs[-1], ref, f"{dtype} TA={ta} TB={tb} {shape} beta={beta}")
+        assert np.array_equal(outs[0], outs[1]), "result changed between calls"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ops,shared", [("TN", "B"), ("NT", "A"), ("TT", "none")])
+def test_lowp_batched_transposed_long_k_copies(dtype, ops, shared):
+    """A strided batch of transposed long-K problems on few tiles: copies of
+    the transposed operands (per problem, or once for stride 0), an
+    untransposed operand in place (stride 0 when shared), the split product
+    over the batch; every problem against the oracle, C between problems
+    never written."""
+    torch = torch_cuda()
+    t = _tdtype(torch, dtype)
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    batch, (M, N, K) = 3, (256, 128, 4096)
+    probs = [make_problem_16bit(M, N, K, seed=900 + z, dtype=dtype, dist="normal", with_c=True) for z in range(batch)]
+    if shared == "A":
+        probs = [(probs[0][0], b, c) for _, b, c in probs]
+    if shared == "B":
+        probs = [(a, probs[0][1], c) for a, _, c in probs]
+    sa = [np.ascontiguousarray(a.T) if ta else a for a, _, _ in probs]
+    sb = [np.ascontiguousarray(b.T) if tb else b for _, b, _ in probs]
+
+    def stack(xs, one):
+        r, c = xs[0].shape
+        ld, gap = c + 8, 64
+        n = 1 if one else len(xs)
+        buf = torch.full((n * (r * ld + gap),), float("nan"), dtype=t, device="cuda")
+        view = buf.as_strided((len(xs), r, c), (0 if one else r * ld + gap, ld, 1))
+        for z in range(n):
+            view[z].copy_(torch.from_numpy(xs[z]).to(t))
+        return view
+    dA = stack(sa, shared == "A")
+    dB = stack(sb, shared == "B")
+    sc = M * N + 8
+    bufC = torch.full((batch * sc,), float("nan"), device="cuda")
+    dC = bufC.as_strided((batch, M, N), (sc, N, 1))
+    for z, (_, _, c) in enumerate(probs):
+        dC[z].copy_(torch.from_numpy(c))
+    print(f"[lowp] batched long-K op {dtype} {ops} shared={shared}", flush=True)
+    sgemm_lowp(dA, dB, dC, alpha=0.5, beta=2.0, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    host = bufC.cpu().numpy()
+    for z, (a, b, c) in enumerate(probs):
+        check_close(host[z * sc:z * sc + M * N].reshape(M, N), oracle.sgemm_ref(a, b, c, alpha=0.5, beta=2.0),
+                    f"batched long-K {dtype} {ops} shared={shared} problem {z}")
+        assert np.isnan(host[z * sc + M * N:(z + 1) * sc]).all(), "write between C problems"
