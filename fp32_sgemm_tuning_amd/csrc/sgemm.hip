@@ -1197,15 +1197,19 @@ bool lowp_fast_ok(const LowpVariant &v, int M, int N, int K, const void *A, int 
            (tb ? K : N) % 8 == 0 && K >= v.bk && 2L * spanA < lim && 2L * spanB < lim;
 }
 
-// The largest split-K factor the 128x128 16-bit kernel (the one built with
-// split-K) may use: the tile grid must fill less than 3/4 of its 512
-// workgroup slots (two per compute unit), each split keeps at least eight K
-// tiles, and the partial tiles fit the workspace.  1 for other variants.
-// (`batch` problems of one strided batch count as batch times the tiles)
-int lowp_max_splits(int variant, int M, int N, int K, long batch = 1) {
-    if (variant != 1) return 1;
+// The largest split-K factor a 16-bit kernel built with split-K may use:
+// the 128x128 two-stage kernel, and with transposed operands (`ops`) the
+// 128x128 alternating kernel.  The tile grid must fill less than 3/4 of the
+// kernel's workgroup slots (two per compute unit for the two-stage kernel,
+// one for the alternating one), each split keeps at least eight K tiles,
+// and the partial tiles fit the workspace.  1 for other variants.
+// (`batch` problems of one strided batch count as batch times the tiles;
+// untransposed problems keep the two-stage kernel's split, which the
+// automatic choice was measured with)
+int lowp_max_splits(int variant, int M, int N, int K, long batch = 1, bool ops = false) {
+    if (variant != 1 && !(ops && variant == 5)) return 1;
     const LowpVariant &v = kLowpVariants[variant];
-    const long slots = 512;
+    const long slots = variant == 1 ? 512 : 256;
     const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn) * batch;
     if (tiles * 4 >= slots * 3 || tiles > kSplitMaxTiles) return 1;
     long s = slots / tiles;
@@ -1240,8 +1244,8 @@ double lowp_predict_us(int variant, int s, int M, int N, int K, long batch = 1) 
 // The split factor of a variant: the better of no split and the largest
 // allowed split by the prediction above.
 // SGEMM_SPLITK = S forces min(S, the largest allowed) for sweeps.
-int lowp_splits(int variant, int M, int N, int K, long batch = 1) {
-    const int s = lowp_max_splits(variant, M, N, K, batch);
+int lowp_splits(int variant, int M, int N, int K, long batch = 1, bool ops = false) {
+    const int s = lowp_max_splits(variant, M, N, K, batch, ops);
     if (knobs().splitk > 0) return std::min(s, knobs().splitk);
     return s > 1 && lowp_predict_us(variant, s, M, N, K, batch) < lowp_predict_us(variant, 1, M, N, K, batch) ? s
                                                                                                               : 1;
@@ -1261,7 +1265,7 @@ int lowp_auto(int M, int N, int K, const void *A, int lda, const void *B, int ld
     for (int id : {1, 2, 4, 5}) {
         if ((ta || tb) && !lowp_takes_ops(id)) continue;
         if (!lowp_fast_ok(kLowpVariants[id], M, N, K, A, lda, B, ldb, ta, tb)) continue;
-        const int s = ta || tb ? 1 : lowp_splits(id, M, N, K, batch);
+        const int s = lowp_splits(id, M, N, K, batch, ta || tb);
         const double t = lowp_predict_us(id, s, M, N, K, batch);
         if (best == 0 || t < best_t) {
             best = id;
@@ -1368,40 +1372,6 @@ bool lowp_keeps(const void *X, int ldx, int cols, int K, long long stride, int b
     return aligned16(X) && ldx % 8 == 0 && cols % 8 == 0 && K % 8 == 0 && (batch <= 1 || stride % 8 == 0);
 }
 
-// Whether a problem (or strided batch) with transposed operands that an
-// alternating kernel takes runs faster as the product of row-major copies:
-// those kernels have no split form, so a grid of few tiles with long K keeps
-// a few compute units busy for a long time, while the product on the copies
-// splits K.  Compares the predicted times (lowp_predict_us, plus the copies'
-// traffic at about 3 TB/s and 6 us per copy launch, which a 0.5 MB copy
-// measured) with a margin for the model: the copies must save a quarter.
-// Only transposed operands and untransposed ones the fast kernels cannot
-// take as they are get copied.  Measured on MI355X (BF16, beta = 0, us,
-// direct -> copies): 512x512x8192 TN 69.4 -> 35.1, NT 51.0 -> 34.8, TT
-// 60.2 -> 41.3; 768x1024x16384 TN 136 -> 71, NT 98 -> 75, TT 116 -> 87;
-// 384x256x8192 TN 69.0 -> 32.3; 256x256x4096 NT 27.7 -> 22.2.  SGEMM_PACK
-// = -1 keeps the direct kernels.
-bool lowp_transpose_copy_pays(int variant, bool ta, bool tb, int M, int N, int K, const void *A, int lda,
-                              long long sA, const void *B, int ldb, long long sB, int batch, void *stream) {
-    if (!(ta || tb) || knobs().pack < 0 || K < 64) return false;
-    if (capturing(reinterpret_cast<hipStream_t>(stream))) return false;
-    const long K8 = (K + 7) & ~7L, N8 = (N + 7) & ~7L;
-    if (ceil_div(M, 32) > 65535 || ceil_div(K8, 32) > 65535) return false;   // transpose grids
-    const bool ca = ta || !lowp_keeps(A, lda, K, K, sA, batch);
-    const bool cb = tb || !lowp_keeps(B, ldb, N, K, sB, batch);
-    const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
-    const double copied = 2.0 * ((ca ? (double)na * M * K8 : 0.0) + (cb ? (double)nb * K8 * N8 : 0.0));
-    if (copied > kCopyMaxBytes) return false;
-    const int vc = lowp_auto(M, (int)N8, (int)K8, ca ? nullptr : A, ca ? (int)K8 : lda, cb ? nullptr : B,
-                             cb ? (int)N8 : ldb, false, false, batch);
-    if (vc == 0) return false;
-    if (knobs().pack > 0) return true;
-    const double t_copy = 2.0 * copied / 3e12 * 1e6 + 6.0 * (ca + cb) +
-                          lowp_predict_us(vc, lowp_splits(vc, M, (int)N8, (int)K8, batch), M, (int)N8, (int)K8, batch);
-    return t_copy < 0.75 * lowp_predict_us(variant, 1, M, N, K, batch);
-}
-
-
 // The 16-bit product on zero-padded row-major copies of op(A) and op(B)
 // (transposed operands transposed on the way); an untransposed operand the
 // fast kernels take as it is (lowp_keeps) is used in place.  In a batch, an
@@ -1487,10 +1457,7 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     if (variant == SGEMM_VARIANT_AUTO) {
         variant = strides8 ? lowp_auto(M, N, K, A, lda, B, ldb, ta, tb, batch) : 0;
         const int na = batch > 1 && sA != 0 ? batch : 1, nb = batch > 1 && sB != 0 ? batch : 1;
-        const bool copy = variant == 0 ? lowp_copy_plan(M, N, K, stream, batch, na, nb)
-                                       : lowp_transpose_copy_pays(variant, ta, tb, M, N, K, A, lda, sA, B, ldb, sB,
-                                                                  batch, stream);
-        if (copy) {
+        if (variant == 0 && lowp_copy_plan(M, N, K, stream, batch, na, nb)) {
             const int st = run_lowp_copied(dtype, ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC,
                                            batch, stream);
             if (st != kUnavailable) return st;
@@ -1524,7 +1491,7 @@ int run_lowp(int dtype, int op_a, int op_b, int M, int N, int K, float alpha, co
     a.strideC = batch > 1 ? (long)sC : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Lease lease;
-    const int ws = attach_workspace(a, ta || tb ? 1 : lowp_splits(variant, M, N, K, batch), s, lease);
+    const int ws = attach_workspace(a, lowp_splits(variant, M, N, K, batch, ta || tb), s, lease);
     if (ws != SGEMM_STATUS_OK) return ws;
     const bool f16 = dtype == SGEMM_DTYPE_F16;
     return finish(variant > 0 ? launch_lowp_tile(a, f16, variant - 1, ta, tb, batch, s)

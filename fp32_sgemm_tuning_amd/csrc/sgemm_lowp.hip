@@ -599,10 +599,11 @@ hipError_t launch_lowp(const Args &a0, hipStream_t stream, int batch = 1) {
 #undef SGEMM_LAUNCH
 }
 
-// One alternating kernel with each of the four operand orientations.
-template <int BM, int BN, int BK, int NS>
+// One alternating kernel with each of the four operand orientations (SP:
+// its split-K form).
+template <int BM, int BN, int BK, int NS, bool SP>
 hipError_t launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int batch, hipStream_t s) {
-#define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, false, A, B>(a, s, batch)
+#define SGEMM_O(F, A, B) launch_lowp<BM, BN, BK, 2, 4, NS, F, true, SP, A, B>(a, s, batch)
     if (f16) {
         if (ta && tb) return SGEMM_O(true, true, true);
         if (ta) return SGEMM_O(true, true, false);
@@ -619,9 +620,10 @@ hipError_t launch_lowp_alt_op(const Args &a, bool f16, bool ta, bool tb, int bat
 // Launcher called from the C ABI's translation unit; `tile` picks the block
 // tile, K tile, waves and number of stages (the table of variants in the C
 // ABI's translation unit lists them in this order).  a.splits > 1 runs the
-// split-K form (built for the 128x128 two-stage kernel); ta / tb (transposed
-// operands) are built for the two alternating kernels; batch problems on
-// gridDim.z.  Returns the launch's status.
+// split-K form (built for the 128x128 two-stage kernel and the 128x128
+// alternating kernel); ta / tb (transposed operands) are built for the two
+// alternating kernels; batch problems on gridDim.z.  Returns the launch's
+// status.
 hipError_t launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb, int batch, hipStream_t s) {
 #define SGEMM_T(BM, BN, BK, WM, WN, NS, PP, SP)                                          \
     (f16 ? launch_lowp<BM, BN, BK, WM, WN, NS, true, PP, SP>(a, s, batch)                \
@@ -630,8 +632,10 @@ hipError_t launch_lowp_tile(const Args &a, bool f16, int tile, bool ta, bool tb,
     switch (tile) {
         case 1: return SGEMM_T(256, 128, 64, 2, 4, 3, false, false);
         case 2: return SGEMM_T(256, 256, 32, 2, 4, 4, false, false);
-        case 3: return launch_lowp_alt_op<256, 256, 32, 4>(a, f16, ta, tb, batch, s);
-        case 4: return launch_lowp_alt_op<128, 128, 64, 4>(a, f16, ta, tb, batch, s);
+        case 3: return launch_lowp_alt_op<256, 256, 32, 4, false>(a, f16, ta, tb, batch, s);
+        case 4:
+            if (split) return launch_lowp_alt_op<128, 128, 64, 4, true>(a, f16, ta, tb, batch, s);
+            return launch_lowp_alt_op<128, 128, 64, 4, false>(a, f16, ta, tb, batch, s);
         default:
             if (split) return SGEMM_T(128, 128, 64, 2, 2, 2, false, true);
             return SGEMM_T(128, 128, 64, 2, 2, 2, false, false);

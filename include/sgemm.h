@@ -327,16 +327,15 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
  * automatic choice); transposed operands run on the alternating-schedule
  * variants or the plain kernel, with each operand kept in LDS in its stored
  * orientation (16-byte chunks along its contiguous extent, which must be a
- * multiple of 8 elements for the fast path).  Those variants do not split
- * K.  With SGEMM_VARIANT_AUTO, operands the fast path cannot take are
- * copied as in sgemm_lowp(), transposed on the way into zero-padded
- * row-major buffers, and the product runs untransposed on the copies (where
- * it may split K, deterministically); so are transposed operands the fast
- * path takes when the predicted time of copies plus split product is at
- * most 3/4 of the alternating kernels' (a grid of few tiles with long K:
- * 512x512x8192 BF16 TN 69 -> 35 us).  An untransposed operand the fast path
- * takes as it is (K a multiple of 8) is used in place.  SGEMM_PACK = -1
- * keeps every operand in place.  Returns SGEMM_STATUS_*;
+ * multiple of 8 elements for the fast path).  With transposed operands the
+ * 128x128 alternating variant splits K on grids of few tiles, as the
+ * 128x128 two-stage kernel does for untransposed ones (same workspace
+ * rules, deterministic; 512x512x8192 BF16 TN 69 -> 25 us).  With
+ * SGEMM_VARIANT_AUTO, operands the fast path cannot take are copied as in
+ * sgemm_lowp(), transposed on the way into zero-padded row-major buffers,
+ * and the product runs untransposed on the copies (where it may split K,
+ * deterministically); an untransposed operand the fast path takes as it is
+ * (K a multiple of 8) is used in place.  Returns SGEMM_STATUS_*;
  * SGEMM_STATUS_INVALID_OP for another op code.
  */
 int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
@@ -358,9 +357,10 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * are copied into zero-padded buffers as in sgemm_lowp(), one launch per
  * operand for the whole batch (an operand of stride 0 once), when that
  * takes less time than the plain kernel and the copies fit in
- * SGEMM_MAX_COPY_BUFFER_BYTES; the rest run on the plain kernel.
- * Transposed batches of few tiles with long K are copied as for
- * sgemm_lowp_op().  Returns SGEMM_STATUS_*.
+ * SGEMM_MAX_COPY_BUFFER_BYTES; the rest run on the plain kernel.  A
+ * transposed batch on the 128x128 alternating kernel splits K as in
+ * sgemm_lowp_op(), over its problems' tiles together.  Returns
+ * SGEMM_STATUS_*.
  */
 int sgemm_lowp_strided_batched(int dtype, int op_a, int op_b, int M, int N, int K, float alpha,
                                const void *A, int lda, long long stride_a,

@@ -490,13 +490,12 @@ def test_lowp_strided_batched_split(dtype, batch, M, N, K, shared_b):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ops", [(True, False), (False, True), (True, True)], ids=["TN", "NT", "TT"])
 @pytest.mark.parametrize("shape", [(384, 256, 8192), (200, 264, 4104)], ids=lambda s: "x".join(map(str, s)))
-def test_lowp_transposed_long_k_copies(dtype, ops, shape):
-    """Transposed operands that the alternating kernels take, on a grid of
-    few tiles with long K: the automatic choice copies the transposed
-    operands into row-major buffers and runs the split untransposed product,
-    with an untransposed operand used in place.  Parity with the oracle,
-    NaN in the padding of the stored operands, beta = 0 (NaN C) and
-    beta != 0, twice in a row (the copy buffer reused), bit-identical
+def test_lowp_transposed_long_k_split(dtype, ops, shape):
+    """Transposed operands on a grid of few tiles with long K: the 128x128
+    alternating kernel splits K (the split-K hand-off on the stream's
+    workspace).  Parity with the oracle, NaN in the padding of the stored
+    operands, beta = 0 (NaN C) and beta != 0, twice in a row (the
+    workspace's counters reset by the first call), bit-identical
     repeats."""
     torch = torch_cuda()
     ta, tb = ops
@@ -506,7 +505,7 @@ def test_lowp_transposed_long_k_copies(dtype, ops, shape):
     sB = np.ascontiguousarray(B.T) if tb else B
     dA, _ = _dev16(sA, dtype, torch, ld=sA.shape[1] + 8)
     dB, _ = _dev16(sB, dtype, torch, ld=sB.shape[1] + 16)
-    print(f"[lowp long-K op] {dtype} TA={ta} TB={tb} {M}x{N}x{K}", flush=True)
+    print(f"[lowp long-K split op] {dtype} TA={ta} TB={tb} {M}x{N}x{K}", flush=True)
     for beta in (0.0, -0.75):
         ref = oracle.sgemm_ref(A, B, Cin if beta != 0.0 else None, alpha=1.5, beta=beta)
         outs = []
@@ -521,12 +520,12 @@ def test_lowp_transposed_long_k_copies(dtype, ops, shape):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ops,shared", [("TN", "B"), ("NT", "A"), ("TT", "none")])
-def test_lowp_batched_transposed_long_k_copies(dtype, ops, shared):
-    """A strided batch of transposed long-K problems on few tiles: copies of
-    the transposed operands (per problem, or once for stride 0), an
-    untransposed operand in place (stride 0 when shared), the split product
-    over the batch; every problem against the oracle, C between problems
-    never written."""
+def test_lowp_batched_transposed_long_k_split(dtype, ops, shared):
+    """A strided batch of transposed long-K problems on few tiles: the
+    128x128 alternating kernel splits K over the problems' tiles together
+    (each problem's partials and counters after those of the problems
+    before it), an operand of stride 0 shared; every problem against the
+    oracle, C between problems never written."""
     torch = torch_cuda()
     t = _tdtype(torch, dtype)
     ta, tb = ops[0] == "T", ops[1] == "T"
