@@ -1198,19 +1198,25 @@ bool lowp_fast_ok(const LowpVariant &v, int M, int N, int K, const void *A, int 
 }
 
 // The largest split-K factor a 16-bit kernel built with split-K may use:
-// the 128x128 two-stage kernel, and with transposed operands (`ops`) the
-// 128x128 alternating kernel.  The tile grid must fill less than 3/4 of the
-// kernel's workgroup slots (two per compute unit for the two-stage kernel,
-// one for the alternating one), each split keeps at least eight K tiles,
-// and the partial tiles fit the workspace.  1 for other variants.
-// (`batch` problems of one strided batch count as batch times the tiles;
-// untransposed problems keep the two-stage kernel's split, which the
-// automatic choice was measured with)
+// the 128x128 two-stage kernel and the 128x128 alternating kernel.  The tile
+// grid must fill less than 3/4 of the kernel's workgroup slots (two per
+// compute unit for the two-stage kernel, one for the alternating one), each
+// split keeps at least eight K tiles, and the partial tiles fit the
+// workspace.  1 for other variants.  Untransposed operands split on the
+// alternating kernel from 16 tiles up only: below that its deeper pipeline
+// fill costs more than it gains (BF16, split two-stage against split
+// alternating: 128x128x2048 11.5 / 12.6 us, 256x256x4096 13.9 / 15.1,
+// 384x256x8192 20.3 / 21.4; from 16 tiles the alternating one leads:
+// 512x512x8192 25.3 / 24.2, 640x640x4096 20.5 / 18.6, 1024x1024x4096
+// 24.9 / 20.7, 768x1024x16384 52.1 / 41.9).  Transposed operands (`ops`)
+// have only the alternating kernels, and split on any grid.
+// (`batch` problems of one strided batch count as batch times the tiles)
 int lowp_max_splits(int variant, int M, int N, int K, long batch = 1, bool ops = false) {
-    if (variant != 1 && !(ops && variant == 5)) return 1;
+    if (variant != 1 && variant != 5) return 1;
     const LowpVariant &v = kLowpVariants[variant];
     const long slots = variant == 1 ? 512 : 256;
     const long tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn) * batch;
+    if (variant == 5 && !ops && tiles < 16) return 1;
     if (tiles * 4 >= slots * 3 || tiles > kSplitMaxTiles) return 1;
     long s = slots / tiles;
     s = std::min(s, ceil_div(K, v.bk) / 8);

@@ -329,8 +329,9 @@ int sgemm_lowp_ex(int dtype, int M, int N, int K, float alpha,
  * orientation (16-byte chunks along its contiguous extent, which must be a
  * multiple of 8 elements for the fast path).  With transposed operands the
  * 128x128 alternating variant splits K on grids of few tiles, as the
- * 128x128 two-stage kernel does for untransposed ones (same workspace
- * rules, deterministic; 512x512x8192 BF16 TN 69 -> 25 us).  With
+ * 128x128 two-stage kernel does (same workspace
+ * rules, deterministic; 512x512x8192 BF16 TN 69 -> 25 us; untransposed
+ * operands split on it from 16 tiles up).  With
  * SGEMM_VARIANT_AUTO, operands the fast path cannot take are copied as in
  * sgemm_lowp(), transposed on the way into zero-padded row-major buffers,
  * and the product runs untransposed on the copies (where it may split K,
@@ -350,8 +351,9 @@ int sgemm_lowp_op(int dtype, int op_a, int op_b, int M, int N, int K, float alph
  * elements) and C + z*stride_c (in floats); the rules of
  * sgemm_strided_batched() (0 <= batch <= 65535, strides of A and B may be 0,
  * C problems must not overlap, one launch) and the automatic variant choice
- * over batch x tiles; an untransposed batch on the 128x128 two-stage kernel
- * splits K over its problems' tiles together (sgemm_lowp_split_factor).  Batches the fast kernels cannot take
+ * over batch x tiles; a batch on the 128x128 two-stage kernel or the 128x128
+ * alternating kernel splits K over its problems' tiles together
+ * (sgemm_lowp_split_factor for untransposed ones).  Batches the fast kernels cannot take
  * (unaligned rows, K or N not multiples of 8, or stride_a or stride_b not a
  * multiple of 8 elements, which leaves problems after the first unaligned)
  * are copied into zero-padded buffers as in sgemm_lowp(), one launch per

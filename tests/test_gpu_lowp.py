@@ -216,10 +216,11 @@ SPLIT_SHAPES = [(2048, 2048, 2048), (512, 768, 8192), (300, 520, 4104), (1000, 1
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_lowp_split_k(dtype):
-    """Split-K on small grids with long K (the 128x128 kernel, forced, and the
-    automatic choice; the alternating kernel on the same shapes): parity with the oracle,
-    bit-identical repeats (the partials are added in a fixed order) and a
-    factor above one where the shape calls for it."""
+    """Split-K on small grids with long K (the 128x128 two-stage and
+    alternating kernels, forced, and the automatic choice; the 256x256
+    alternating kernel, which does not split, on the same shapes): parity
+    with the oracle, bit-identical repeats (the partials are added in a
+    fixed order) and a factor above one where the shape calls for it."""
     torch = torch_cuda()
     names = {capi.sgemm_lowp_variant_name(v): v for v in capi.lowp_variants()}
     for M, N, K in SPLIT_SHAPES:
@@ -227,7 +228,7 @@ def test_lowp_split_k(dtype):
         dA, _ = _dev16(A, dtype, torch)
         dB, _ = _dev16(B, dtype, torch)
         ref = oracle.sgemm_ref(A, B, Cin, alpha=0.5, beta=1.5)
-        for v in (None, names["lowp_128x128x64_s2"], names["lowp_256x256x32_s4_alt"]):
+        for v in (None, names["lowp_128x128x64_s2"], names["lowp_128x128x64_s4_alt"], names["lowp_256x256x32_s4_alt"]):
             s = capi.sgemm_lowp_split_factor(v if v is not None else capi.sgemm_lowp_select_variant(
                 M, N, K, dA.data_ptr(), K, dB.data_ptr(), N), M, N, K)
             print(f"[lowp] split {dtype} {M}x{N}x{K} variant {v} factor {s}", flush=True)
@@ -241,6 +242,11 @@ def test_lowp_split_k(dtype):
             assert np.array_equal(outs[0], outs[1]), "split-K result changed between calls"
     assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 512, 768, 8192) > 1
     assert capi.sgemm_lowp_split_factor(names["lowp_128x128x64_s2"], 1000, 1000, 3000) > 1
+    alt = names["lowp_128x128x64_s4_alt"]
+    assert capi.sgemm_lowp_split_factor(alt, 512, 768, 8192) > 1            # 24 tiles
+    assert capi.sgemm_lowp_split_factor(alt, 1000, 1000, 3000) > 1
+    assert capi.sgemm_lowp_split_factor(alt, 300, 520, 4104) == 1           # 15 tiles: the two-stage kernel's
+    assert capi.sgemm_lowp_split_factor(names["lowp_256x256x32_s4_alt"], 512, 768, 8192) == 1
 
 
 OP_SHAPES = [(256, 512, 192), (304, 520, 1000), (129, 264, 72), (512, 256, 4104), (300, 200, 130)]
