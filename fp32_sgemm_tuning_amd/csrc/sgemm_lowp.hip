@@ -36,6 +36,9 @@
 //     kernel, on 16-byte chunks of 8 elements: N and K must be multiples of 8
 //     and the operands' rows 16-byte aligned; other shapes take the plain
 //     kernel with 16-bit loads.
+//   - SPLIT (the 128x128 two-stage and alternating kernels): blockIdx.y
+//     takes its share of the K tiles and the split-K hand-off of the FP32
+//     kernels adds the partial tiles in a fixed order.
 #include "sgemm_lean.hpp"
 
 namespace sgemm_mi355x {
